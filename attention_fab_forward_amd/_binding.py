@@ -1,0 +1,277 @@
+"""ctypes binding of libfab.so: argument marshalling only.
+
+Every computation runs in the library's HIP kernels; this module builds the
+problem descriptor, allocates outputs and workspace with torch on the input's
+device, and passes raw pointers plus torch's current HIP stream.  If the
+library is missing it raises: there is no fallback path.
+"""
+import ctypes
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfab.so")
+ABI_VERSION = 1
+
+SOFTMAX, GELU_ERF = 0, 1
+MASK_NONE, MASK_CAUSAL = 0, 1
+BF16, F32 = 0, 1
+
+STATUS = {
+    0: "FAB_OK", 1: "FAB_ERR_NULL_ARG", 2: "FAB_ERR_BAD_SHAPE", 3: "FAB_ERR_UNSUPPORTED",
+    4: "FAB_ERR_ALIGNMENT", 5: "FAB_ERR_WORKSPACE_TOO_SMALL", 6: "FAB_ERR_ABI_VERSION",
+    7: "FAB_ERR_HIP",
+}
+
+# every symbol include/fab.h declares
+EXPORTS = ("fab_plan", "fab_forward", "fab_backward", "fab_plan_destroy",
+           "fab_status_string", "fab_last_error", "fab_abi_version",
+           "fab_problem_size", "fab_plan_describe")
+
+
+class FabProblem(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32), ("f", ctypes.c_int32), ("mask", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("batch", ctypes.c_int64), ("heads_a", ctypes.c_int64),
+        ("heads_bc", ctypes.c_int64), ("m", ctypes.c_int64), ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64), ("p", ctypes.c_int64), ("scale", ctypes.c_float),
+        ("reserved0", ctypes.c_int32), ("a_stride", ctypes.c_int64 * 3),
+        ("bt_stride", ctypes.c_int64 * 3), ("c_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class FabError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {message}")
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libfab.so once and check its ABI; raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m attention_fab_forward_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        L.fab_plan.argtypes = [ctypes.POINTER(FabProblem), ctypes.POINTER(vp),
+                               ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.fab_plan.restype = ctypes.c_int
+        L.fab_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fab_forward.restype = ctypes.c_int
+        L.fab_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.fab_backward.restype = ctypes.c_int
+        L.fab_plan_destroy.argtypes = [vp]
+        L.fab_plan_destroy.restype = None
+        L.fab_status_string.argtypes = [ctypes.c_int]
+        L.fab_status_string.restype = ctypes.c_char_p
+        L.fab_last_error.argtypes = []
+        L.fab_last_error.restype = ctypes.c_char_p
+        L.fab_abi_version.argtypes = []
+        L.fab_abi_version.restype = ctypes.c_int32
+        L.fab_problem_size.argtypes = []
+        L.fab_problem_size.restype = ctypes.c_size_t
+        L.fab_plan_describe.argtypes = [vp, ctypes.c_char_p, sz]
+        L.fab_plan_describe.restype = ctypes.c_size_t
+        if L.fab_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libfab.so ABI {L.fab_abi_version()} != binding {ABI_VERSION}")
+        if L.fab_problem_size() != ctypes.sizeof(FabProblem):
+            raise RuntimeError("fab_problem layout differs between library and binding")
+        _lib = L
+    return _lib
+
+
+def check(status):
+    if status != 0:
+        raise FabError(status, lib().fab_last_error().decode())
+
+
+def make_problem(f, dtype, batch, heads_a, heads_bc, m, n, k, p, scale, causal=False,
+                 strides=None, abi_version=ABI_VERSION):
+    prob = FabProblem()
+    prob.abi_version = abi_version
+    prob.f, prob.dtype = f, dtype
+    prob.mask = MASK_CAUSAL if causal else MASK_NONE
+    prob.batch, prob.heads_a, prob.heads_bc = batch, heads_a, heads_bc
+    prob.m, prob.n, prob.k, prob.p = m, n, k, p
+    prob.scale = scale
+    if strides:
+        for name in ("a_stride", "bt_stride", "c_stride", "o_stride"):
+            if name in strides:
+                getattr(prob, name)[:] = list(strides[name])
+    return prob
+
+
+class Plan:
+    """A validated problem; wraps fab_plan / fab_forward / fab_backward."""
+
+    def __init__(self, prob):
+        self.prob = prob
+        self._ptr = ctypes.c_void_p()
+        fw, bw = ctypes.c_size_t(), ctypes.c_size_t()
+        check(lib().fab_plan(ctypes.byref(prob), ctypes.byref(self._ptr), ctypes.byref(fw),
+                             ctypes.byref(bw)))
+        self.fwd_workspace = fw.value
+        self.bwd_workspace = bw.value
+
+    def describe(self):
+        buf = ctypes.create_string_buffer(512)
+        lib().fab_plan_describe(self._ptr, buf, 512)
+        return buf.value.decode()
+
+    def forward_raw(self, a, bt, c, o, lse, ws, ws_bytes, stream):
+        check(lib().fab_forward(self._ptr, a, bt, c, o, lse, ws, ws_bytes, stream))
+
+    def backward_raw(self, a, bt, c, o, lse, do, da, dbt, dc, ws, ws_bytes, stream):
+        check(lib().fab_backward(self._ptr, a, bt, c, o, lse, do, da, dbt, dc, ws, ws_bytes,
+                                 stream))
+
+    def __del__(self):
+        ptr = getattr(self, "_ptr", None)
+        if ptr and _lib is not None:
+            _lib.fab_plan_destroy(ptr)
+
+
+_plans = {}
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check_tensor(name, t, ndim, device, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the same GPU as the others ({device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} needs a contiguous last dimension")
+
+
+def _strides4(t):
+    return (t.stride(0), t.stride(2), t.stride(1))
+
+
+def _get_plan(key, build):
+    plan = _plans.get(key)
+    if plan is None:
+        plan = Plan(build())
+        _plans[key] = plan
+    return plan
+
+
+def attention_plan(q, k, v, causal, scale):
+    b, m, hq, d = q.shape
+    n, hkv = k.shape[1], k.shape[2]
+    strides = {"a_stride": _strides4(q), "bt_stride": _strides4(k), "c_stride": _strides4(v),
+               "o_stride": (m * hq * v.shape[3], v.shape[3], hq * v.shape[3])}
+    key = ("softmax", q.dtype, b, hq, hkv, m, n, d, v.shape[3], float(scale), bool(causal),
+           tuple(sorted(strides.items())))
+    return _get_plan(key, lambda: make_problem(SOFTMAX, _dtype_code(q), b, hq, hkv, m, n, d,
+                                               v.shape[3], scale, causal, strides))
+
+
+def mlp_plan(a, bt, c, scale):
+    m, k = a.shape
+    n, p = bt.shape[0], c.shape[1]
+    strides = {"a_stride": (m * a.stride(0), 0, a.stride(0)),
+               "bt_stride": (n * bt.stride(0), 0, bt.stride(0)),
+               "c_stride": (n * c.stride(0), 0, c.stride(0)),
+               "o_stride": (m * p, 0, p)}
+    key = ("gelu", a.dtype, m, n, k, p, float(scale), tuple(sorted(strides.items())))
+    return _get_plan(key, lambda: make_problem(GELU_ERF, _dtype_code(a), 1, 1, 1, m, n, k, p,
+                                               scale, False, strides))
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def forward(a, bt, c, f="softmax", causal=False, scale=None):
+    """O = f(scale * A Bt^T) C on the GPU.
+
+    softmax: a = Q [b, m, hq, d], bt = K [b, n, hkv, d], c = V [b, n, hkv, d];
+    returns (O [b, m, hq, d], LSE float32 [b, hq, m]).  Default scale 1/sqrt(d).
+    gelu: a [m, k], bt [n, k], c [n, p]; returns (O [m, p], None).  Default scale 1.
+    """
+    dev, dt = a.device, a.dtype
+    if f == "softmax":
+        for name, t in (("q", a), ("k", bt), ("v", c)):
+            _check_tensor(name, t, 4, dev, dt)
+        if scale is None:
+            scale = 1.0 / float(a.shape[3]) ** 0.5
+        plan = attention_plan(a, bt, c, causal, scale)
+        b, m, hq, _ = a.shape
+        o = torch.empty((b, m, hq, c.shape[3]), dtype=dt, device=dev)
+        lse = torch.empty((b, hq, m), dtype=torch.float32, device=dev)
+    elif f == "gelu":
+        if causal:
+            raise ValueError("GeLU takes no causal mask")
+        for name, t in (("a", a), ("bt", bt), ("c", c)):
+            _check_tensor(name, t, 2, dev, dt)
+        scale = 1.0 if scale is None else scale
+        plan = mlp_plan(a, bt, c, scale)
+        o = torch.empty((a.shape[0], c.shape[1]), dtype=dt, device=dev)
+        lse = None
+    else:
+        raise ValueError(f"unknown f {f!r}")
+    ws = torch.empty(max(plan.fwd_workspace, 1), dtype=torch.uint8, device=dev)
+    plan.forward_raw(_ptr(a), _ptr(bt), _ptr(c), _ptr(o), _ptr(lse), _ptr(ws),
+                     plan.fwd_workspace, _stream())
+    return o, lse
+
+
+def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None):
+    """Gradients (dA, dBt, dC) of <dO, O> for the forward above."""
+    dev, dt = a.device, a.dtype
+    if f == "softmax":
+        for name, t in (("q", a), ("k", bt), ("v", c), ("o", o), ("do", do)):
+            _check_tensor(name, t, 4, dev, dt)
+        if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous():
+            raise ValueError("lse must be the contiguous float32 tensor from forward()")
+        if do.stride() != o.stride():
+            raise ValueError("dO must have the layout of O")
+        if scale is None:
+            scale = 1.0 / float(a.shape[3]) ** 0.5
+        plan = attention_plan(a, bt, c, causal, scale)
+        if o.stride() != (a.shape[1] * a.shape[2] * c.shape[3], a.shape[2] * c.shape[3],
+                          c.shape[3], 1):
+            raise ValueError("O must be packed [b, m, hq, d]")
+    elif f == "gelu":
+        for name, t in (("a", a), ("bt", bt), ("c", c), ("do", do)):
+            _check_tensor(name, t, 2, dev, dt)
+        scale = 1.0 if scale is None else scale
+        plan = mlp_plan(a, bt, c, scale)
+        o = lse = None
+    else:
+        raise ValueError(f"unknown f {f!r}")
+    da, dbt, dc = (torch.empty_strided(t.shape, t.stride(), dtype=dt, device=dev)
+                   for t in (a, bt, c))
+    ws = torch.empty(max(plan.bwd_workspace, 1), dtype=torch.uint8, device=dev)
+    plan.backward_raw(_ptr(a), _ptr(bt), _ptr(c), _ptr(o), _ptr(lse), _ptr(do), _ptr(da),
+                      _ptr(dbt), _ptr(dc), _ptr(ws), plan.bwd_workspace, _stream())
+    return da, dbt, dc

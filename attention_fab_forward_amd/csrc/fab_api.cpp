@@ -1,0 +1,302 @@
+// C ABI of the fused f(A.B).C library: problem validation, plans, dispatch.
+//
+// Host-only code.  fab_plan checks a problem without touching the device;
+// fab_forward / fab_backward check their pointers and workspace, then enqueue
+// the kernels of the selected variant on the caller's stream.  No call
+// allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/fab.h"
+#include "fab_internal.h"
+
+struct fab_plan_s {
+  fab_problem prob;
+  int64_t as[3], bs[3], cs[3], os[3];  // resolved {batch, head, row} strides
+  size_t fwd_ws;
+  size_t bwd_ws;
+  int mlp_splits;
+  char desc[256];
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fab_status fail(fab_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+fab_status ok() {
+  g_last_error.clear();
+  return FAB_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Resolve strides: all-zero means packed [batch, rows, heads, cols].
+void resolve(const int64_t in[3], int64_t rows, int64_t heads, int64_t cols, int64_t out[3]) {
+  if (in[0] == 0 && in[1] == 0 && in[2] == 0) {
+    out[0] = rows * heads * cols;
+    out[1] = cols;
+    out[2] = heads * cols;
+  } else {
+    out[0] = in[0];
+    out[1] = in[1];
+    out[2] = in[2];
+  }
+}
+
+fab_status check_strides(const char* name, const int64_t s[3], int64_t cols, int64_t unit) {
+  for (int i = 0; i < 3; ++i) {
+    if (s[i] < 0) return fail(FAB_ERR_BAD_SHAPE, "%s stride %d is negative", name, i);
+    if (s[i] % unit)
+      return fail(FAB_ERR_ALIGNMENT, "%s stride %d (%lld) is not a multiple of %lld elements",
+                  name, i, (long long)s[i], (long long)unit);
+  }
+  if (s[2] < cols)
+    return fail(FAB_ERR_BAD_SHAPE, "%s row stride %lld is smaller than its row length %lld", name,
+                (long long)s[2], (long long)cols);
+  return FAB_OK;
+}
+
+constexpr int64_t kMaxRows = (int64_t)1 << 30;
+
+fab::AttnArgs attn_args(const fab_plan_s* p) {
+  fab::AttnArgs a{};
+  const fab_problem& q = p->prob;
+  a.q_sb = p->as[0], a.q_sh = p->as[1], a.q_sr = p->as[2];
+  a.k_sb = p->bs[0], a.k_sh = p->bs[1], a.k_sr = p->bs[2];
+  a.v_sb = p->cs[0], a.v_sh = p->cs[1], a.v_sr = p->cs[2];
+  a.o_sb = p->os[0], a.o_sh = p->os[1], a.o_sr = p->os[2];
+  a.b = (int32_t)q.batch;
+  a.hq = (int32_t)q.heads_a;
+  a.hkv = (int32_t)q.heads_bc;
+  a.m = (int32_t)q.m;
+  a.n = (int32_t)q.n;
+  a.group = (int32_t)(q.heads_a / q.heads_bc);
+  a.scale = q.scale;
+  a.scale_log2 = q.scale * fab::kLog2eHost;
+  a.causal = q.mask == FAB_MASK_CAUSAL;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fab_abi_version(void) { return FAB_ABI_VERSION; }
+
+size_t fab_problem_size(void) { return sizeof(fab_problem); }
+
+const char* fab_status_string(fab_status s) {
+  switch (s) {
+    case FAB_OK: return "ok";
+    case FAB_ERR_NULL_ARG: return "null argument";
+    case FAB_ERR_BAD_SHAPE: return "bad shape";
+    case FAB_ERR_UNSUPPORTED: return "unsupported problem";
+    case FAB_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case FAB_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FAB_ERR_ABI_VERSION: return "ABI version mismatch";
+    case FAB_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* fab_last_error(void) { return g_last_error.c_str(); }
+
+fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_ws,
+                    size_t* bwd_ws) {
+  if (plan_out) *plan_out = nullptr;
+  if (!prob || !plan_out) return fail(FAB_ERR_NULL_ARG, "fab_plan: prob and plan_out are required");
+  const fab_problem& q = *prob;
+  if (q.abi_version != FAB_ABI_VERSION)
+    return fail(FAB_ERR_ABI_VERSION, "abi_version %d, library has %d", q.abi_version,
+                FAB_ABI_VERSION);
+  if (q.f != FAB_F_SOFTMAX && q.f != FAB_F_GELU_ERF)
+    return fail(FAB_ERR_UNSUPPORTED, "unknown function %d", q.f);
+  if (q.mask != FAB_MASK_NONE && q.mask != FAB_MASK_CAUSAL)
+    return fail(FAB_ERR_UNSUPPORTED, "unknown mask %d", q.mask);
+  if (q.dtype != FAB_BF16 && q.dtype != FAB_F32)
+    return fail(FAB_ERR_UNSUPPORTED, "unknown dtype %d", q.dtype);
+  if (q.reserved0 != 0) return fail(FAB_ERR_BAD_SHAPE, "reserved0 must be 0");
+  if (q.batch < 1 || q.heads_a < 1 || q.heads_bc < 1 || q.m < 1 || q.n < 1 || q.k < 1 || q.p < 1)
+    return fail(FAB_ERR_BAD_SHAPE, "sizes must be >= 1 (batch %lld heads %lld/%lld m %lld n %lld "
+                "k %lld p %lld)", (long long)q.batch, (long long)q.heads_a,
+                (long long)q.heads_bc, (long long)q.m, (long long)q.n, (long long)q.k,
+                (long long)q.p);
+  if (q.heads_a % q.heads_bc)
+    return fail(FAB_ERR_BAD_SHAPE, "heads_a %lld is not a multiple of heads_bc %lld",
+                (long long)q.heads_a, (long long)q.heads_bc);
+  if (q.m > kMaxRows || q.n > kMaxRows || q.batch * q.heads_a > (1 << 20))
+    return fail(FAB_ERR_UNSUPPORTED, "sizes beyond this build's limits (rows <= 2^30, "
+                "batch*heads <= 2^20)");
+  if (!std::isfinite(q.scale)) return fail(FAB_ERR_BAD_SHAPE, "scale must be finite");
+
+  const int64_t unit = q.dtype == FAB_BF16 ? 8 : 4;
+  fab_plan_s tmp{};
+  tmp.prob = q;
+  resolve(q.a_stride, q.m, q.heads_a, q.k, tmp.as);
+  resolve(q.bt_stride, q.n, q.heads_bc, q.k, tmp.bs);
+  resolve(q.c_stride, q.n, q.heads_bc, q.p, tmp.cs);
+  resolve(q.o_stride, q.m, q.heads_a, q.p, tmp.os);
+  fab_status st;
+  if ((st = check_strides("A", tmp.as, q.k, unit)) != FAB_OK) return st;
+  if ((st = check_strides("Bt", tmp.bs, q.k, unit)) != FAB_OK) return st;
+  if ((st = check_strides("C", tmp.cs, q.p, unit)) != FAB_OK) return st;
+  if ((st = check_strides("O", tmp.os, q.p, unit)) != FAB_OK) return st;
+
+  const char* dt = q.dtype == FAB_BF16 ? "bf16" : "f32";
+  if (q.f == FAB_F_SOFTMAX) {
+    if (q.k != q.p) return fail(FAB_ERR_UNSUPPORTED, "softmax needs k == p (got %lld, %lld)",
+                                (long long)q.k, (long long)q.p);
+    if (q.k != 64 && q.k != 128)
+      return fail(FAB_ERR_UNSUPPORTED, "softmax head dim %lld not in {64, 128}", (long long)q.k);
+    if (q.mask == FAB_MASK_CAUSAL && q.m != q.n)
+      return fail(FAB_ERR_UNSUPPORTED, "causal mask needs m == n (got %lld, %lld)",
+                  (long long)q.m, (long long)q.n);
+    if (!(q.scale > 0.f)) return fail(FAB_ERR_UNSUPPORTED, "softmax scale must be > 0");
+    tmp.fwd_ws = 0;
+    tmp.bwd_ws = round_up((size_t)q.batch * q.heads_a * q.m * sizeof(float), 256);
+    if (q.dtype == FAB_BF16)
+      snprintf(tmp.desc, sizeof tmp.desc,
+               "attention %s d=%lld %s group=%lld fwd[BM=%d BN=%d grid=%lld] "
+               "bwd[dq BM=%d, dkdv KB=%d QB=%d]", dt, (long long)q.k,
+               q.mask == FAB_MASK_CAUSAL ? "causal" : "full", (long long)(q.heads_a / q.heads_bc),
+               fab::kAttnFwdBM, fab::kAttnFwdBN,
+               (long long)((q.m + fab::kAttnFwdBM - 1) / fab::kAttnFwdBM * q.heads_a * q.batch),
+               fab::kAttnBwdBM, fab::kAttnBwdKB, fab::kAttnBwdQB);
+    else
+      snprintf(tmp.desc, sizeof tmp.desc, "attention %s d=%lld %s group=%lld (fp32 FMA)", dt,
+               (long long)q.k, q.mask == FAB_MASK_CAUSAL ? "causal" : "full",
+               (long long)(q.heads_a / q.heads_bc));
+  } else {
+    if (q.mask != FAB_MASK_NONE) return fail(FAB_ERR_UNSUPPORTED, "GeLU takes no mask");
+    if (q.dtype != FAB_BF16) return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP runs in bf16 only");
+    if (q.batch != 1 || q.heads_a != 1 || q.heads_bc != 1)
+      return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs batch == heads == 1");
+    if (q.k % 64 || q.p % 64)
+      return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs k and p multiples of 64");
+    if (!fab::mlp_available()) return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP not built");
+    int splits = 1;
+    tmp.fwd_ws = round_up(fab::mlp_fwd_workspace((int)q.m, (int)q.n, (int)q.k, (int)q.p, &splits), 256);
+    tmp.bwd_ws = round_up(fab::mlp_bwd_workspace((int)q.m, (int)q.n, (int)q.k, (int)q.p), 256);
+    tmp.mlp_splits = splits;
+    snprintf(tmp.desc, sizeof tmp.desc, "gelu-mlp bf16 m=%lld k=%lld n=%lld p=%lld splits=%d",
+             (long long)q.m, (long long)q.k, (long long)q.n, (long long)q.p, splits);
+  }
+  fab_plan_s* plan = new (std::nothrow) fab_plan_s(tmp);
+  if (!plan) return fail(FAB_ERR_UNSUPPORTED, "out of host memory");
+  *plan_out = plan;
+  if (fwd_ws) *fwd_ws = plan->fwd_ws;
+  if (bwd_ws) *bwd_ws = plan->bwd_ws;
+  return ok();
+}
+
+void fab_plan_destroy(fab_plan_t* plan) { delete plan; }
+
+size_t fab_plan_describe(const fab_plan_t* plan, char* buf, size_t len) {
+  if (!plan) return 0;
+  const size_t need = strlen(plan->desc);
+  if (buf && len) {
+    const size_t nc = need < len - 1 ? need : len - 1;
+    memcpy(buf, plan->desc, nc);
+    buf[nc] = 0;
+  }
+  return need;
+}
+
+fab_status fab_forward(const fab_plan_t* plan, const void* A, const void* Bt, const void* C,
+                       void* O, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!plan || !A || !Bt || !C || !O) return fail(FAB_ERR_NULL_ARG, "fab_forward: null argument");
+  const fab_problem& q = plan->prob;
+  if (!aligned16(A) || !aligned16(Bt) || !aligned16(C) || !aligned16(O))
+    return fail(FAB_ERR_ALIGNMENT, "fab_forward: tensor base pointers must be 16-byte aligned");
+  if (workspace_bytes < plan->fwd_ws)
+    return fail(FAB_ERR_WORKSPACE_TOO_SMALL, "fab_forward: workspace %zu < %zu bytes",
+                workspace_bytes, plan->fwd_ws);
+  if (plan->fwd_ws && !workspace) return fail(FAB_ERR_NULL_ARG, "fab_forward: workspace is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (q.f == FAB_F_SOFTMAX) {
+    if (!lse) return fail(FAB_ERR_NULL_ARG, "fab_forward: softmax needs lse");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+      return fail(FAB_ERR_ALIGNMENT, "fab_forward: lse must be 4-byte aligned");
+    fab::AttnArgs a = attn_args(plan);
+    a.q = A, a.k = Bt, a.v = C, a.o_out = O, a.lse = lse;
+    e = q.dtype == FAB_BF16 ? fab::launch_attn_fwd_bf16(a, (int)q.k, s)
+                            : fab::launch_attn_fwd_f32(a, (int)q.k, s);
+  } else {
+    if (lse) return fail(FAB_ERR_UNSUPPORTED, "fab_forward: GeLU takes no lse");
+    if (plan->fwd_ws && !aligned16(workspace))
+      return fail(FAB_ERR_ALIGNMENT, "fab_forward: workspace must be 16-byte aligned");
+    fab::MlpArgs a{};
+    a.a = A, a.bt = Bt, a.c = C, a.o = O, a.ws = static_cast<float*>(workspace);
+    a.a_sr = plan->as[2], a.bt_sr = plan->bs[2], a.c_sr = plan->cs[2], a.o_sr = plan->os[2];
+    a.m = (int)q.m, a.n = (int)q.n, a.k = (int)q.k, a.p = (int)q.p;
+    a.splits = plan->mlp_splits;
+    a.scale = q.scale;
+    e = fab::launch_mlp_fwd_bf16(a, s);
+  }
+  if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_forward: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, const void* C,
+                        const void* O, const float* lse, const void* dO, void* dA, void* dBt,
+                        void* dC, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !A || !Bt || !C || !dO || !dA || !dBt || !dC)
+    return fail(FAB_ERR_NULL_ARG, "fab_backward: null argument");
+  const fab_problem& q = plan->prob;
+  if (!aligned16(A) || !aligned16(Bt) || !aligned16(C) || !aligned16(dO) || !aligned16(dA) ||
+      !aligned16(dBt) || !aligned16(dC))
+    return fail(FAB_ERR_ALIGNMENT, "fab_backward: tensor base pointers must be 16-byte aligned");
+  if (workspace_bytes < plan->bwd_ws)
+    return fail(FAB_ERR_WORKSPACE_TOO_SMALL, "fab_backward: workspace %zu < %zu bytes",
+                workspace_bytes, plan->bwd_ws);
+  if (plan->bwd_ws && !workspace) return fail(FAB_ERR_NULL_ARG, "fab_backward: workspace is NULL");
+  if (plan->bwd_ws && !aligned16(workspace))
+    return fail(FAB_ERR_ALIGNMENT, "fab_backward: workspace must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (q.f == FAB_F_SOFTMAX) {
+    if (!O || !lse) return fail(FAB_ERR_NULL_ARG, "fab_backward: softmax needs O and lse");
+    if (!aligned16(O)) return fail(FAB_ERR_ALIGNMENT, "fab_backward: O must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+      return fail(FAB_ERR_ALIGNMENT, "fab_backward: lse must be 4-byte aligned");
+    fab::AttnArgs a = attn_args(plan);
+    a.q = A, a.k = Bt, a.v = C, a.o = O, a.lse_in = lse, a.dout = dO;
+    a.dq = dA, a.dk = dBt, a.dv = dC, a.delta = static_cast<float*>(workspace);
+    e = q.dtype == FAB_BF16 ? fab::launch_attn_bwd_bf16(a, (int)q.k, s)
+                            : fab::launch_attn_bwd_f32(a, (int)q.k, s);
+  } else {
+    if (O || lse) return fail(FAB_ERR_UNSUPPORTED, "fab_backward: GeLU takes no O / lse");
+    fab::MlpArgs a{};
+    a.a = A, a.bt = Bt, a.c = C, a.dout = dO, a.da = dA, a.dbt = dBt, a.dc = dC;
+    a.ws = static_cast<float*>(workspace);
+    a.a_sr = plan->as[2], a.bt_sr = plan->bs[2], a.c_sr = plan->cs[2], a.o_sr = plan->os[2];
+    a.m = (int)q.m, a.n = (int)q.n, a.k = (int)q.k, a.p = (int)q.p;
+    a.splits = plan->mlp_splits;
+    a.scale = q.scale;
+    e = fab::launch_mlp_bwd_bf16(a, s);
+  }
+  if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_backward: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

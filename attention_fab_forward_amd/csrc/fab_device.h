@@ -1,0 +1,86 @@
+// Device-side helpers shared by the HIP kernels of the fused f(A.B).C block:
+// MFMA wrappers for gfx950, bf16 packing, 16-byte global/LDS moves and the
+// lane permutation used to keep MFMA accumulator slots on contiguous indices.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fab {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D = A (32x16) * B (16x32) + C, bf16 inputs, fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32)+e] and B[8*(l/32)+e][l%32], e = 0..7, and
+// holds D[8*(r/4) + 4*(l/32) + r%4][l%32] in accumulator slot r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// MFMA row index r (0..31) of a 32-row operand -> the tile row it carries.
+// Chosen so that accumulator slot s of lane l corresponds to tile row
+// 16*(l/32) + s: rows of one lane become contiguous.
+__device__ __forceinline__ int perm_row(int r) {
+  return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+}
+// Inverse of perm_row: tile row -> MFMA row that must carry it.
+__device__ __forceinline__ int perm_row_inv(int t) {
+  const int g = t >> 4, i = t & 15;
+  return 8 * (i >> 2) + 4 * g + (i & 3);
+}
+
+// fp32 -> bf16 pair, round to nearest even (gfx950 hardware conversion).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Combine the low (sel=0) or high (sel=1) 16-bit halves of two words.
+__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void stg16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ u32x4 lds16(const char* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void sts16(char* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ void sts8(char* p, const u32x2& v) {
+  *reinterpret_cast<u32x2*>(p) = v;
+}
+__device__ __forceinline__ void sts4(char* p, uint32_t v) {
+  *reinterpret_cast<uint32_t*>(p) = v;
+}
+
+__device__ __forceinline__ float wave_xor32(float v) {
+  return __shfl_xor(v, 32, 64);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+}  // namespace fab

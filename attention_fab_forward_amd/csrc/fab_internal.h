@@ -1,0 +1,75 @@
+// Host/device argument blocks and kernel launchers of the fused f(A.B).C
+// library.  Host code in fab_api.cpp validates a problem, fills these blocks
+// and calls the launchers; each launcher enqueues its kernels on the given
+// stream and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fab {
+
+// Softmax attention: A = Q [b, m, hq, d], Bt = K [b, n, hkv, d], C = V [b, n, hkv, d].
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;      // forward output (read by the backward)
+  void* o_out;        // forward output (written by the forward)
+  float* lse;         // [b, hq, m] natural log
+  const float* lse_in;
+  const void* dout;   // dO, layout of O
+  void* dq;           // layout of Q
+  void* dk;           // layout of K
+  void* dv;           // layout of V
+  float* delta;       // workspace [b, hq, m]: rowsum(dO * O)
+  int64_t q_sb, q_sh, q_sr;
+  int64_t k_sb, k_sh, k_sr;
+  int64_t v_sb, v_sh, v_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int32_t b, hq, hkv, m, n;
+  int32_t group;      // hq / hkv
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+  int32_t causal;
+};
+
+// GeLU MLP: A [m, k], Bt [n, k], C [n, p], O [m, p] (row strides in elements).
+struct MlpArgs {
+  const void* a;
+  const void* bt;
+  const void* c;
+  void* o;
+  const void* dout;
+  void* da;
+  void* dbt;
+  void* dc;
+  float* ws;          // fp32 workspace
+  int64_t a_sr, bt_sr, c_sr, o_sr;
+  int32_t m, n, k, p;
+  int32_t splits;     // n-splits of the forward partial sums
+  float scale;
+};
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+// Forward attention tile shapes (bf16 MFMA path).
+constexpr int kAttnFwdBM = 128;   // queries per workgroup (4 waves x 32)
+constexpr int kAttnFwdBN = 64;    // keys per inner step
+constexpr int kAttnBwdBM = 128;   // dQ kernel: queries per workgroup
+constexpr int kAttnBwdKB = 128;   // dK/dV kernel: keys per workgroup (4 waves x 32)
+constexpr int kAttnBwdQB = 64;    // dK/dV kernel: queries per inner step
+
+hipError_t launch_attn_delta(const AttnArgs& a, int d, bool bf16, hipStream_t s);
+hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_bwd_f32(const AttnArgs& a, int d, hipStream_t s);
+
+bool mlp_available();
+size_t mlp_fwd_workspace(int m, int n, int k, int p, int* splits);
+size_t mlp_bwd_workspace(int m, int n, int k, int p);
+hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s);
+hipError_t launch_mlp_bwd_bf16(const MlpArgs& a, hipStream_t s);
+
+}  // namespace fab

@@ -1,0 +1,153 @@
+/*
+ * fab.h -- C ABI of the fused two-matmul block  O = f(A . B) . C  on MI355X.
+ *
+ * The unit: two consecutive matrix products with a function between them
+ * ("Memory-efficient tensor parallelism", FITEE 10.1631/FITEE.2400602,
+ * abstract).  f is either
+ *   - a scaled row softmax over the n axis, optionally under a causal index
+ *     mask (attention; "Ulysses Sequence Parallelism", section "Contexte
+ *     Technique"; causal masks as index tensors: "AutoSP", section 2.A), or
+ *   - GeLU in its erf form, applied elementwise (the MLP block; "AutoSP",
+ *     sections 2.A and 2.B).
+ * The m x n intermediate f(A.B) is computed tile by tile on chip and never
+ * written to device memory; the backward pass recomputes it from the saved
+ * per-row log-sum-exp (softmax) or from A and B (GeLU) instead of storing it
+ * ("AutoSP", section 2.B: rematerialise rather than keep activations).
+ *
+ * Shapes (per batch entry and head):
+ *   A  : m x k      (attention: Q, one query head)
+ *   Bt : n x k      (B transposed; attention: K.  MLP: nn.Linear weight layout)
+ *   C  : n x p      (attention: V)
+ *   O  : m x p
+ * softmax: O_i = sum_j P_ij C_j, P_ij = exp(S_ij - LSE_i),
+ *          S = scale * A Bt^T, masked S_ij = -inf for j > i when causal,
+ *          LSE_i = log sum_j exp(S_ij) (natural log).
+ * GeLU:    O = GeLU(scale * A Bt^T) C, GeLU(x) = x * Phi(x).
+ *
+ * Layout: every matrix has a contiguous last dimension.  Attention tensors are
+ * addressed as base + b*stride_batch + h*stride_head + row*stride_row + col
+ * (elements); leaving all three strides 0 selects the packed
+ * [batch, rows, heads, cols] layout.  Query head h reads key/value head
+ * h / (heads_a / heads_bc) (consecutive query heads share a kv head).
+ * Gradients use the strides of their primal tensor (dA like A, dO like O, ...).
+ * LSE is packed [batch, heads_a, m] float32.
+ *
+ * Ownership: the caller owns every device buffer.  The library allocates no
+ * device memory and never synchronises: all work is enqueued on the caller's
+ * stream.  Temporary device memory is passed in as `workspace`, whose size
+ * fab_plan reports.  Outputs are overwritten, not accumulated.  A plan is an
+ * immutable host object; one plan may serve concurrent calls that use
+ * distinct workspaces.
+ *
+ * Errors: every entry point returns a fab_status synchronously and never
+ * throws or aborts.  FAB_ERR_HIP reports a launch error; a fault inside a
+ * kernel surfaces at the caller's next synchronisation.  fab_last_error()
+ * returns a thread-local description of the last failure on this thread.
+ */
+#ifndef FAB_H
+#define FAB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FAB_ABI_VERSION 1
+
+typedef enum {
+  FAB_OK = 0,
+  FAB_ERR_NULL_ARG = 1,             /* a required pointer is NULL            */
+  FAB_ERR_BAD_SHAPE = 2,            /* sizes < 1, heads_a % heads_bc != 0, ... */
+  FAB_ERR_UNSUPPORTED = 3,          /* valid problem this build does not run */
+  FAB_ERR_ALIGNMENT = 4,            /* base not 16-byte aligned / bad stride  */
+  FAB_ERR_WORKSPACE_TOO_SMALL = 5,  /* workspace_bytes below the plan's need */
+  FAB_ERR_ABI_VERSION = 6,          /* prob->abi_version != FAB_ABI_VERSION  */
+  FAB_ERR_HIP = 7                   /* the HIP runtime reported an error     */
+} fab_status;
+
+typedef enum { FAB_F_SOFTMAX = 0, FAB_F_GELU_ERF = 1 } fab_function;
+typedef enum { FAB_MASK_NONE = 0, FAB_MASK_CAUSAL = 1 } fab_mask;
+typedef enum { FAB_BF16 = 0, FAB_F32 = 1 } fab_dtype;
+
+/* Full description of one problem.  Zero-initialise, then fill in. */
+typedef struct {
+  int32_t abi_version; /* must be FAB_ABI_VERSION                             */
+  int32_t f;           /* fab_function                                        */
+  int32_t mask;        /* fab_mask; GeLU requires FAB_MASK_NONE               */
+  int32_t dtype;       /* fab_dtype of A, Bt, C, O, dO and all gradients       */
+  int64_t batch;       /* >= 1                                                */
+  int64_t heads_a;     /* heads of A and O (query heads); >= 1                */
+  int64_t heads_bc;    /* heads of Bt and C (kv heads); divides heads_a       */
+  int64_t m, n, k, p;  /* matrix sizes above; causal requires m == n          */
+  float scale;         /* f is applied to scale * (A Bt^T)                    */
+  int32_t reserved0;   /* must be 0                                           */
+  /* element strides {batch, head, row}; all-zero = packed [b, rows, h, cols] */
+  int64_t a_stride[3];
+  int64_t bt_stride[3];
+  int64_t c_stride[3];
+  int64_t o_stride[3];
+} fab_problem;
+
+typedef struct fab_plan_s fab_plan_t;
+
+/* Validate `prob` and build a reusable plan.  Host only: touches no device.
+ * Supported in this build:
+ *   softmax, bf16: k == p, k in {64, 128}; any m, n >= 1; causal needs m == n.
+ *   softmax, f32:  k == p, k in {64, 128}; same rules.
+ *   GeLU, bf16:    batch == heads_a == heads_bc == 1, k and p multiples of 64,
+ *                  any m, n >= 1, mask NONE.
+ * Row strides must be multiples of 8 elements (bf16) or 4 (f32), and so must
+ * the head and batch strides.  On success *plan_out receives a plan that the
+ * caller releases with fab_plan_destroy, and the two sizes receive the bytes
+ * of device workspace fab_forward / fab_backward need (either size pointer
+ * may be NULL).  On failure *plan_out is set to NULL. */
+fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out,
+                    size_t* fwd_workspace_bytes, size_t* bwd_workspace_bytes);
+
+/* Forward pass: O = f(scale * A Bt^T) C, and for softmax the fp32 LSE rows.
+ * A, Bt, C, O: device pointers in the plan's dtype and strides.
+ * lse: device float32 [batch, heads_a, m] for softmax (required), NULL for GeLU.
+ * workspace: device memory of at least the plan's forward size (may be NULL if
+ * that size is 0).  Enqueued on `stream` (a hipStream_t; NULL = default). */
+fab_status fab_forward(const fab_plan_t* plan, const void* A, const void* Bt,
+                       const void* C, void* O, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Backward pass of L = <dO, O>: dA, dBt, dC (attention: dQ, dK, dV).
+ * O and lse must be what fab_forward returned for the same inputs (softmax;
+ * pass NULL for both with GeLU).  dO has O's layout; dA, dBt, dC have the
+ * layouts of A, Bt, C and are overwritten.  workspace: at least the plan's
+ * backward size.  Enqueued on `stream`. */
+fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt,
+                        const void* C, const void* O, const float* lse,
+                        const void* dO, void* dA, void* dBt, void* dC,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Release a plan (NULL is ignored). */
+void fab_plan_destroy(fab_plan_t* plan);
+
+/* Static English name of a status code. */
+const char* fab_status_string(fab_status s);
+
+/* Thread-local description of the last failure on the calling thread ("" if
+ * none).  Valid until the next library call on this thread. */
+const char* fab_last_error(void);
+
+/* FAB_ABI_VERSION of the loaded library. */
+int32_t fab_abi_version(void);
+
+/* sizeof(fab_problem) as compiled into the library (binding layout check). */
+size_t fab_problem_size(void);
+
+/* Writes a one-line description of the plan's kernel variant, tiles and
+ * grids into buf (truncated to len, always NUL-terminated when len > 0).
+ * Returns the number of characters the full description needs. */
+size_t fab_plan_describe(const fab_plan_t* plan, char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAB_H */

@@ -1,0 +1,107 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol and
+validates problems and arguments without touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_fab_forward_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "fab.h")) as fh:
+        text = fh.read()
+    return set(re.findall(r"\b(fab_[a-z_]+)\s*\(", text))
+
+
+def test_exports_every_declared_symbol():
+    L = B.lib()
+    names = declared_functions()
+    assert names == set(B.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_struct_size():
+    L = B.lib()
+    assert L.fab_abi_version() == B.ABI_VERSION
+    assert L.fab_problem_size() == ctypes.sizeof(B.FabProblem) == 176
+
+
+def attn(**kw):
+    base = dict(f=B.SOFTMAX, dtype=B.BF16, batch=1, heads_a=4, heads_bc=2, m=256, n=256,
+                k=128, p=128, scale=0.088, causal=True)
+    base.update(kw)
+    return B.make_problem(**base)
+
+
+def status_of(prob):
+    try:
+        B.Plan(prob)
+    except B.FabError as e:
+        return e.name
+    return "FAB_OK"
+
+
+@pytest.mark.parametrize("kw,expect", [
+    ({}, "FAB_OK"),
+    ({"dtype": B.F32, "k": 64, "p": 64}, "FAB_OK"),
+    ({"causal": False, "m": 100, "n": 300}, "FAB_OK"),
+    ({"heads_a": 3}, "FAB_ERR_BAD_SHAPE"),
+    ({"m": 0}, "FAB_ERR_BAD_SHAPE"),
+    ({"batch": 0}, "FAB_ERR_BAD_SHAPE"),
+    ({"m": 100, "n": 300}, "FAB_ERR_UNSUPPORTED"),
+    ({"k": 96, "p": 96}, "FAB_ERR_UNSUPPORTED"),
+    ({"k": 128, "p": 64}, "FAB_ERR_UNSUPPORTED"),
+    ({"scale": 0.0}, "FAB_ERR_UNSUPPORTED"),
+    ({"scale": float("nan")}, "FAB_ERR_BAD_SHAPE"),
+    ({"abi_version": 99}, "FAB_ERR_ABI_VERSION"),
+    ({"f": 7}, "FAB_ERR_UNSUPPORTED"),
+    ({"dtype": 5}, "FAB_ERR_UNSUPPORTED"),
+    ({"strides": {"a_stride": (256 * 4 * 128, 128, 4 * 128 + 4)}}, "FAB_ERR_ALIGNMENT"),
+    ({"strides": {"a_stride": (256 * 4 * 128, 128, 64)}}, "FAB_ERR_BAD_SHAPE"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": True}, "FAB_ERR_UNSUPPORTED"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "dtype": B.F32},
+     "FAB_ERR_UNSUPPORTED"),
+])
+def test_plan_validation(kw, expect):
+    assert status_of(attn(**kw)) == expect
+
+
+def test_plan_workspace_and_describe():
+    p = B.Plan(attn())
+    assert p.fwd_workspace == 0
+    assert p.bwd_workspace >= 4 * 256 * 4
+    assert "attention bf16 d=128 causal" in p.describe()
+
+
+def test_null_and_alignment_errors_before_any_launch():
+    L = B.lib()
+    p = B.Plan(attn())
+    vp = ctypes.c_void_p
+    good = vp(0x10000)
+    st = L.fab_forward(p._ptr, None, good, good, good, good, None, 0, None)
+    assert B.STATUS[st] == "FAB_ERR_NULL_ARG"
+    assert "null" in L.fab_last_error().decode()
+    st = L.fab_forward(p._ptr, vp(0x10008), good, good, good, good, None, 0, None)
+    assert B.STATUS[st] == "FAB_ERR_ALIGNMENT"
+    st = L.fab_forward(p._ptr, good, good, good, good, None, None, 0, None)
+    assert B.STATUS[st] == "FAB_ERR_NULL_ARG"
+    st = L.fab_backward(p._ptr, good, good, good, good, good, good, good, good, good, good,
+                        p.bwd_workspace - 1, None)
+    assert B.STATUS[st] == "FAB_ERR_WORKSPACE_TOO_SMALL"
+    st = L.fab_backward(p._ptr, good, good, good, good, good, good, good, good, good, None,
+                        p.bwd_workspace, None)
+    assert B.STATUS[st] == "FAB_ERR_NULL_ARG"
+    st = L.fab_plan(None, None, None, None)
+    assert B.STATUS[st] == "FAB_ERR_NULL_ARG"
+
+
+def test_status_strings():
+    L = B.lib()
+    for code in B.STATUS:
+        assert L.fab_status_string(code)
+    assert L.fab_status_string(0) == b"ok"
