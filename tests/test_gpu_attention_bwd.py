@@ -1,0 +1,130 @@
+"""GPU parity of the attention backward (dQ, dK, dV) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+from attention_fab_forward_amd.inputs import WORKLOADS, attention_inputs, random_array
+from oracle import (attention_backward, attention_backward_keys, attention_backward_rows,
+                    attention_forward)
+from fab_testutil import assert_close, assert_lse, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def run(x, dtype, causal, scale):
+    import attention_fab_forward_amd as fab
+    q, k, v, do = (to_device(x[n], dtype) for n in ("q", "k", "v", "do"))
+    o, lse = fab.forward(q, k, v, "softmax", causal, scale)
+    dq, dk, dv = fab.backward(q, k, v, o, lse, do, "softmax", causal, scale)
+    return (to_host(o), lse.cpu().numpy().astype(np.float64), to_host(dq), to_host(dk),
+            to_host(dv))
+
+
+def check(x, dtype, causal, scale):
+    o, lse, dq, dk, dv = run(x, dtype, causal, scale)
+    ro, rl = attention_forward(x["q"], x["k"], x["v"], scale, causal)
+    rq, rk, rv = attention_backward(x["q"], x["k"], x["v"], x["do"], scale, causal)
+    errs = [assert_close("O", o, ro, dtype), assert_close("dQ", dq, rq, dtype),
+            assert_close("dK", dk, rk, dtype), assert_close("dV", dv, rv, dtype)]
+    assert_lse(lse, rl, dtype)
+    print("errors O/dQ/dK/dV:", " ".join(f"{e:.2e}" for e in errs))
+
+
+def test_fp32_single_head_n256_d64():
+    w = WORKLOADS["attn_f32_h1_n256_d64"]
+    check(attention_inputs(w), "f32", False, w.scale())
+
+
+@pytest.mark.parametrize("n", [256, 1000])
+def test_bf16_causal_h32_d128_reduced(n):
+    w = WORKLOADS["attn_causal_bf16_h32_n32768_d128"]
+    check(attention_inputs(w, seq=n), "bf16", True, w.scale())
+
+
+def test_bf16_rank_share_reduced():
+    w = WORKLOADS["attn_causal_bf16_h4_n131072_d128"]
+    check(attention_inputs(w, seq=4096), "bf16", True, w.scale())
+
+
+@pytest.mark.parametrize("n", [1024, 4096])
+def test_bf16_causal_gqa_reduced(n):
+    w = WORKLOADS["attn_causal_bf16_gqa2_n1048576_d128"]
+    check(attention_inputs(w, seq=n), "bf16", True, w.scale())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,hq,hkv", [(1, 2, 1), (17, 2, 2), (65, 4, 2), (129, 3, 1),
+                                      (200, 2, 1)])
+def test_bf16_small_and_ragged(d, causal, n, hq, hkv):
+    x = {"q": random_array(61, (1, n, hq, d), 1.0, "bf16"),
+         "k": random_array(62, (1, n, hkv, d), 1.0, "bf16"),
+         "v": random_array(63, (1, n, hkv, d), 1.0, "bf16"),
+         "do": random_array(64, (1, n, hq, d), 1.0, "bf16")}
+    check(x, "bf16", causal, float(np.float32(d ** -0.5)))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 40, 300])
+def test_fp32_small_and_ragged(d, causal, n):
+    x = {"q": random_array(71, (2, n, 4, d)), "k": random_array(72, (2, n, 2, d)),
+         "v": random_array(73, (2, n, 2, d)), "do": random_array(74, (2, n, 4, d))}
+    check(x, "f32", causal, float(np.float32(d ** -0.5)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rectangular_noncausal(dtype):
+    x = {"q": random_array(81, (2, 300, 4, 128), 1.0, dtype),
+         "k": random_array(82, (2, 777, 2, 128), 1.0, dtype),
+         "v": random_array(83, (2, 777, 2, 128), 1.0, dtype),
+         "do": random_array(84, (2, 300, 4, 128), 1.0, dtype)}
+    check(x, dtype, False, 0.07)
+
+
+def identities(q, k, v, o, do, dq, dk, dv, group):
+    """Exact identities of the softmax block, checked on device outputs.
+
+    sum_j dV_j = sum over the group's heads and rows of dO (rows of P sum to 1);
+    sum_j dK_j = 0 (rows of dS sum to 0); <dV, V> = <dO, O>;
+    <dQ, Q> = <dK, K> (invariance under Q -> aQ, K -> K/a).
+    """
+    b, n, hkv, d = k.shape
+    do_g = do.reshape(b, -1, hkv, group, d).sum(axis=3)
+    lhs = dv.sum(axis=1)
+    rhs = do_g.sum(axis=1)
+    scale_v = np.abs(dv).sum(axis=1) + np.abs(do_g).sum(axis=1)
+    assert np.all(np.abs(lhs - rhs) <= 1e-2 * scale_v + 1e-3), "sum dV != sum dO"
+    assert np.all(np.abs(dk.sum(axis=1)) <= 1e-2 * np.abs(dk).sum(axis=1) + 1e-3), "sum dK != 0"
+    a, bb = np.sum(dv * v), np.sum(do * o)
+    assert abs(a - bb) <= 1e-2 * (np.sum(np.abs(dv * v)) + np.sum(np.abs(do * o))), (a, bb)
+    a, bb = np.sum(dq * q), np.sum(dk * k)
+    assert abs(a - bb) <= 1e-2 * (np.sum(np.abs(dq * q)) + np.sum(np.abs(dk * k))), (a, bb)
+
+
+def sampled(n, seed, count=16):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 63, 64, 127, 128, n // 2, n - 65, n - 64, n - 1]
+    return np.unique(np.concatenate([fixed, rng.integers(0, n, count)]))
+
+
+@pytest.mark.parametrize("key", ["attn_causal_bf16_h32_n32768_d128",
+                                 "attn_causal_bf16_h4_n131072_d128"])
+def test_full_size_sampled_and_identities(key):
+    """Full-size backward (the benchmarked launch): exact oracle rows of dQ,
+    exact late-key rows of dK / dV, and the identities over every row."""
+    w = WORKLOADS[key]
+    x = attention_inputs(w)
+    o, lse, dq, dk, dv = run(x, "bf16", True, w.scale())
+    identities(x["q"], x["k"], x["v"], o, x["do"], dq, dk, dv, w.heads_q // w.heads_kv)
+    n = w.seq
+    rows = sampled(n, w.number)
+    keys = np.unique(np.concatenate([[n - 256, n - 129, n - 128, n - 2, n - 1],
+                                     np.random.default_rng(w.number).integers(n - 256, n, 8)]))
+    for h in sorted({0, w.heads_q - 1}):
+        rq = attention_backward_rows(x["q"], x["k"], x["v"], x["do"], w.scale(), True, 0, h, rows)
+        assert_close(f"dQ head {h}", dq[0, rows, h], rq, "bf16")
+    for g in sorted({0, w.heads_kv - 1}):
+        rk, rv = attention_backward_keys(x["q"], x["k"], x["v"], x["do"], w.scale(), True, 0, g,
+                                         keys)
+        assert_close(f"dK head {g}", dk[0, keys, g], rk, "bf16")
+        assert_close(f"dV head {g}", dv[0, keys, g], rv, "bf16")
