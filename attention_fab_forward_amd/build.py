@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall",
     "-Wno-unused-function", "-Wno-unknown-pragmas",
     # keep packed-fp32 instructions out of device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

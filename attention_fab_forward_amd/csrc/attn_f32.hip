@@ -1,5 +1,5 @@
 // Softmax attention in fp32 (forward and backward), plus the backward
-// preprocessing kernel shared by both dtypes.
+// preprocessing kernel (D = rowsum(dO * O)) used by the bf16 path.
 //
 // The fp32 path keeps every operation in fp32 FMA arithmetic (no reduced
 // precision step anywhere), as the fp32 workload asks.  Its intended sizes are
@@ -193,7 +193,17 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(AttnArgs a) {
   }
   const int64_t ridx = ((int64_t)bi * a.hq + h) * a.m + q;
   const float lse2 = live ? a.lse_in[ridx] * kLog2e : 0.f;
-  const float dlt = live ? a.delta[ridx] : 0.f;
+  // D = rowsum(dO * O), accumulated in the same lane split and order as the
+  // dP dot products below, so that a row whose exact dS vanishes (a query that
+  // sees a single key) gets dP - D = 0 exactly.  Written for the dK/dV kernel.
+  float dlt = 0.f;
+  {
+    const float* orow = static_cast<const float*>(a.o) + ooff;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) dlt = fmaf(dor[i], live ? orow[i] : 0.f, dlt);
+    dlt = group_sum<T>(dlt);
+    if (live && part == 0) a.delta[ridx] = dlt;
+  }
   const float cs = a.scale_log2;
   const int kend = CAUSAL ? min(a.n, qb * QPB + QPB) : a.n;
   for (int k0 = 0; k0 < kend; k0 += kTile) {
@@ -324,8 +334,6 @@ hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
 template <int D>
 hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   constexpr int T = D / 32, RPB = 256 / T;
-  const hipError_t e = launch_attn_delta(a, D, false, s);
-  if (e != hipSuccess) return e;
   const dim3 block(256);
   const dim3 gq((unsigned)((a.m + RPB - 1) / RPB) * a.hq * a.b);
   const dim3 gk((unsigned)((a.n + RPB - 1) / RPB) * a.hkv * a.b);

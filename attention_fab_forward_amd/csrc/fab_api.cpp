@@ -189,8 +189,8 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
     if (q.dtype != FAB_BF16) return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP runs in bf16 only");
     if (q.batch != 1 || q.heads_a != 1 || q.heads_bc != 1)
       return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs batch == heads == 1");
-    if (q.k % 64 || q.p % 64)
-      return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs k and p multiples of 64");
+    if (q.k % 128 || q.p % 128 || q.k > 1024 || q.p > 1024)
+      return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs k and p multiples of 128, at most 1024");
     if (!fab::mlp_available()) return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP not built");
     int splits = 1;
     tmp.fwd_ws = round_up(fab::mlp_fwd_workspace((int)q.m, (int)q.n, (int)q.k, (int)q.p, &splits), 256);

@@ -1,0 +1,534 @@
+// GeLU MLP block O = GeLU(scale * A Bt^T) C and its backward, bf16 in / fp32
+// accumulate, on gfx950 MFMA.
+//
+// The block is the unit O = f(A B) C with f = GeLU (erf form) applied
+// elementwise ("Memory-efficient tensor parallelism" abstract; the MLP block of
+// "AutoSP" 2.A).  The m x n intermediate H = scale A Bt^T is formed one 32 x 32
+// tile at a time in registers, passed through GeLU and consumed by the second
+// product at once; it is never written to device memory.  The backward
+// recomputes H (and dG = dO C^T) per tile instead of storing activations
+// ("AutoSP" 2.B):
+//   dH = dG * GeLU'(H), dA = scale dH Bt, dBt = scale dH^T A, dC = GeLU(H)^T dO.
+//
+// Schedule ("lanes = rows" as in the attention kernels): a workgroup of 4
+// waves owns 32 rows (or 32 columns of n for the dBt/dC kernel).  The long
+// contractions of the first products (k, p <= 1024) are split across the 4
+// waves, each keeping its quarter of the resident operand in registers, and
+// the partial 32 x 32 tiles are summed through LDS.  Each wave then owns a
+// quarter of the output columns for the second product.  Operands whose
+// contraction runs along their non-contiguous axis are read from transposed
+// copies that a small kernel writes into the workspace first (copies of the
+// inputs, not of the intermediate).  The n (or m) loop is split across
+// workgroups; the fp32 partial sums are added by a final elementwise kernel.
+#include "fab_device.h"
+#include "fab_internal.h"
+
+namespace fab {
+namespace {
+
+constexpr int kPad = 64;        // padding of transposed copies' leading dimension
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__device__ __forceinline__ float gelu_f(float x) {
+  return 0.5f * x * (1.f + erff(x * 0.7071067811865476f));
+}
+__device__ __forceinline__ float gelu_grad_f(float x) {
+  const float cdf = 0.5f * (1.f + erff(x * 0.7071067811865476f));
+  return cdf + x * 0.3989422804014327f * expf(-0.5f * x * x);
+}
+
+// out[c][r] = in[r][c] for r < rows, c < cols; zero for r in [rows, ld_out).
+// in: row stride ld_in (elements); out: [cols][ld_out], ld_out % 64 == 0.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* in, int64_t ld_in,
+                                                             int rows, int cols, uint16_t* out,
+                                                             int64_t ld_out) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tid = threadIdx.x;
+  // load 64 x 64: 512 chunks of 8 elements, 2 per thread
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + 256 * u;
+    const int r = i / 8, ch = i % 8;
+    const int gr = r0 + r, gc = c0 + ch * 8;
+    u32x4 v = {0, 0, 0, 0};
+    if (gr < rows && gc < cols) v = ldg16(in + (int64_t)gr * ld_in + gc);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      tile[r][ch * 8 + 2 * w] = (uint16_t)(v[w] & 0xffff);
+      tile[r][ch * 8 + 2 * w + 1] = (uint16_t)(v[w] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + 256 * u;
+    const int c = i / 8, ch = i % 8;  // output row c0 + c, columns r0 + 8 ch ..
+    const int gc = c0 + c;
+    if (gc >= cols) continue;
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      v[w] = (uint32_t)tile[ch * 8 + 2 * w][c] | ((uint32_t)tile[ch * 8 + 2 * w + 1][c] << 16);
+    if (r0 + ch * 8 < ld_out) stg16(out + (int64_t)gc * ld_out + r0 + ch * 8, v);
+  }
+}
+
+// out[r][c] = bf16(scale * sum_s part[s][r][c]); part packed [splits][rows][cols].
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* part, int splits, int rows,
+                                                           int cols, float scale, uint16_t* out,
+                                                           int64_t ld_out) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  const int64_t total = (int64_t)rows * cols;
+  if (i >= total) return;
+  const int64_t r = i / cols, c = i % cols;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int s = 0; s < splits; ++s) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(part + (int64_t)s * total + i);
+    const f32x4 x = src[0], y = src[1];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc[w] += x[w];
+      acc[4 + w] += y[w];
+    }
+  }
+  u32x4 v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) v[w] = pack_bf16(acc[2 * w] * scale, acc[2 * w + 1] * scale);
+  stg16(out + r * ld_out + c, v);
+}
+
+// Sum the four waves' partial tiles through LDS; returns the full tile in the
+// calling lane's accumulator layout.
+__device__ __forceinline__ f32x16 reduce4(f32x16 v, float* lds, int wave, int lane) {
+  f32x4* mine = reinterpret_cast<f32x4*>(lds + (wave * 64 + lane) * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mine[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+  __syncthreads();
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(lds + (w * 64 + lane) * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 x = src[i];
+      s[4 * i] += x[0];
+      s[4 * i + 1] += x[1];
+      s[4 * i + 2] += x[2];
+      s[4 * i + 3] += x[3];
+    }
+  }
+  return s;
+}
+
+__device__ __forceinline__ void pack16(const float* x, u32x4 out[2]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) out[c][w] = pack_bf16(x[8 * c + 2 * w], x[8 * c + 2 * w + 1]);
+}
+
+__device__ __forceinline__ void store_tile_f32(float* dst, const f32x16& v) {
+  f32x4* d = reinterpret_cast<f32x4*>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+}
+
+// ---------------------------------------------------------------------------
+// forward: workgroup = 32 rows of A, one split of the n tiles
+// ---------------------------------------------------------------------------
+template <int K, int P>
+__global__ __launch_bounds__(256, 1) void mlp_fwd_kernel(MlpArgs a, const uint16_t* ct,
+                                                         int64_t ldct, int tiles_per_split,
+                                                         float* part) {
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, lg = lane >> 5;
+  const int row = blockIdx.x * 32 + lq;
+  const bool rlive = row < a.m;
+  constexpr int kq = K / 4, kc = kq / 16;
+  constexpr int pq = P / 4, pt = pq / 32;
+  const uint16_t* A = static_cast<const uint16_t*>(a.a);
+  const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
+
+  u32x4 af[kc];
+#pragma unroll
+  for (int c = 0; c < kc; ++c)
+    af[c] = rlive ? ldg16(A + (int64_t)row * a.a_sr + wave * kq + 16 * c + 8 * lg)
+                              : u32x4{0, 0, 0, 0};
+  f32x16 o[pt];
+#pragma unroll
+  for (int t = 0; t < pt; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+
+  const int ntiles = (a.n + 31) / 32;
+  const int jt0 = blockIdx.y * tiles_per_split;
+  const int jt1 = min(ntiles, jt0 + tiles_per_split);
+  for (int jt = jt0; jt < jt1; ++jt) {
+    const int n0 = jt * 32;
+    const int nrow = n0 + perm_row(lq);
+    const bool nlive = nrow < a.n;
+    const uint16_t* btrow = Bt + (int64_t)nrow * a.bt_sr + wave * kq + 8 * lg;
+    f32x16 hp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hp[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kc; ++c)
+      hp = mfma32(nlive ? ldg16(btrow + 16 * c) : u32x4{0, 0, 0, 0}, af[c], hp);
+    const f32x16 h = reduce4(hp, red, wave, lane);
+    // slot r of lane l: row `row`, column n0 + 16 lg + r
+    float g[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) g[r] = gelu_f(a.scale * h[r]);
+    u32x4 gb[2];
+    pack16(g, gb);
+#pragma unroll
+    for (int t = 0; t < pt; ++t) {
+      const uint16_t* crow = ct + (int64_t)(wave * pq + 32 * t + perm_row(lq)) * ldct + n0 + 16 * lg;
+      o[t] = mfma32(ldg16(crow), gb[0], o[t]);
+      o[t] = mfma32(ldg16(crow + 8), gb[1], o[t]);
+    }
+    __syncthreads();  // LDS partials are reused by the next tile
+  }
+  if (!rlive) return;
+  float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.p + wave * pq + 16 * lg;
+#pragma unroll
+  for (int t = 0; t < pt; ++t) store_tile_f32(dst + 32 * t, o[t]);
+}
+
+// ---------------------------------------------------------------------------
+// backward, dA: workgroup = 32 rows of A, one split of the n tiles
+// ---------------------------------------------------------------------------
+template <int K, int P>
+__global__ __launch_bounds__(256, 1) void mlp_bwd_da_kernel(MlpArgs a, const uint16_t* btt,
+                                                            int64_t ldbtt, int tiles_per_split,
+                                                            float* part) {
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, lg = lane >> 5;
+  const int row = blockIdx.x * 32 + lq;
+  const bool rlive = row < a.m;
+  constexpr int kq = K / 4, kc = kq / 16, kt = kq / 32;
+  constexpr int pq = P / 4, pc = pq / 16;
+  const uint16_t* A = static_cast<const uint16_t*>(a.a);
+  const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
+  const uint16_t* Cm = static_cast<const uint16_t*>(a.c);
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
+
+  u32x4 af[kc], df[pc];
+#pragma unroll
+  for (int c = 0; c < kc; ++c)
+    af[c] = rlive ? ldg16(A + (int64_t)row * a.a_sr + wave * kq + 16 * c + 8 * lg)
+                  : u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int c = 0; c < pc; ++c)
+    df[c] = rlive ? ldg16(dO + (int64_t)row * a.o_sr + wave * pq + 16 * c + 8 * lg)
+                  : u32x4{0, 0, 0, 0};
+  f32x16 acc[kt];
+#pragma unroll
+  for (int t = 0; t < kt; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+
+  const int ntiles = (a.n + 31) / 32;
+  const int jt0 = blockIdx.y * tiles_per_split;
+  const int jt1 = min(ntiles, jt0 + tiles_per_split);
+  for (int jt = jt0; jt < jt1; ++jt) {
+    const int n0 = jt * 32;
+    const int nrow = n0 + perm_row(lq);
+    const bool nlive = nrow < a.n;
+    const uint16_t* btrow = Bt + (int64_t)nrow * a.bt_sr + wave * kq + 8 * lg;
+    const uint16_t* crow = Cm + (int64_t)nrow * a.c_sr + wave * pq + 8 * lg;
+    f32x16 hp, gp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hp[r] = gp[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kc; ++c)
+      hp = mfma32(nlive ? ldg16(btrow + 16 * c) : u32x4{0, 0, 0, 0}, af[c], hp);
+#pragma unroll
+    for (int c = 0; c < pc; ++c)
+      gp = mfma32(nlive ? ldg16(crow + 16 * c) : u32x4{0, 0, 0, 0}, df[c], gp);
+    const f32x16 h = reduce4(hp, red, wave, lane);
+    __syncthreads();
+    const f32x16 dg = reduce4(gp, red, wave, lane);
+    // slot r of lane l: row `row`, column n0 + 16 lg + r
+    float dh[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dh[r] = dg[r] * gelu_grad_f(a.scale * h[r]);
+    u32x4 db[2];
+    pack16(dh, db);
+#pragma unroll
+    for (int t = 0; t < kt; ++t) {
+      const uint16_t* trow = btt + (int64_t)(wave * kq + 32 * t + perm_row(lq)) * ldbtt + n0 + 16 * lg;
+      acc[t] = mfma32(ldg16(trow), db[0], acc[t]);
+      acc[t] = mfma32(ldg16(trow + 8), db[1], acc[t]);
+    }
+    __syncthreads();
+  }
+  if (!rlive) return;
+  float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.k + wave * kq + 16 * lg;
+#pragma unroll
+  for (int t = 0; t < kt; ++t) store_tile_f32(dst + 32 * t, acc[t]);
+}
+
+// ---------------------------------------------------------------------------
+// backward, dBt (WANT_DB) or dC (!WANT_DB): workgroup = 32 columns of n, one
+// split of the m tiles.  dBt needs H and dG; dC needs only G = GeLU(H).
+// ---------------------------------------------------------------------------
+template <int K, int P, bool WANT_DB>
+__global__ __launch_bounds__(256, 1) void mlp_bwd_col_kernel(MlpArgs a, const uint16_t* xt,
+                                                             int64_t ldxt, int tiles_per_split,
+                                                             float* part) {
+  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lq = lane & 31, lg = lane >> 5;
+  const int col = blockIdx.x * 32 + lq;  // index along n
+  const bool clive = col < a.n;
+  constexpr int kq = K / 4, kc = kq / 16;
+  constexpr int pq = P / 4, pc = WANT_DB ? pq / 16 : 1;
+  // output columns of this kernel: k (dBt) or p (dC), a quarter per wave
+  constexpr int oq = WANT_DB ? kq : pq, ot = oq / 32;
+  const uint16_t* A = static_cast<const uint16_t*>(a.a);
+  const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
+  const uint16_t* Cm = static_cast<const uint16_t*>(a.c);
+  const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
+
+  u32x4 bf[kc], cf[pc];
+#pragma unroll
+  for (int c = 0; c < kc; ++c)
+    bf[c] = clive ? ldg16(Bt + (int64_t)col * a.bt_sr + wave * kq + 16 * c + 8 * lg)
+                  : u32x4{0, 0, 0, 0};
+  if constexpr (WANT_DB) {
+#pragma unroll
+    for (int c = 0; c < pc; ++c)
+      cf[c] = clive ? ldg16(Cm + (int64_t)col * a.c_sr + wave * pq + 16 * c + 8 * lg)
+                    : u32x4{0, 0, 0, 0};
+  }
+  f32x16 acc[ot];
+#pragma unroll
+  for (int t = 0; t < ot; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+
+  const int mtiles = (a.m + 31) / 32;
+  const int it0 = blockIdx.y * tiles_per_split;
+  const int it1 = min(mtiles, it0 + tiles_per_split);
+  for (int it = it0; it < it1; ++it) {
+    const int r0 = it * 32;
+    const int arow = r0 + perm_row(lq);
+    const bool alive = arow < a.m;
+    const uint16_t* ap = A + (int64_t)arow * a.a_sr + wave * kq + 8 * lg;
+    f32x16 hp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hp[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < kc; ++c)
+      hp = mfma32(alive ? ldg16(ap + 16 * c) : u32x4{0, 0, 0, 0}, bf[c], hp);
+    const f32x16 h = reduce4(hp, red, wave, lane);
+    // slot r of lane l: column `col`, row r0 + 16 lg + r
+    float x[16];
+    if constexpr (WANT_DB) {
+      const uint16_t* op = dO + (int64_t)arow * a.o_sr + wave * pq + 8 * lg;
+      f32x16 gp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) gp[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < pc; ++c)
+        gp = mfma32(alive ? ldg16(op + 16 * c) : u32x4{0, 0, 0, 0}, cf[c], gp);
+      __syncthreads();
+      const f32x16 dg = reduce4(gp, red, wave, lane);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = dg[r] * gelu_grad_f(a.scale * h[r]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = gelu_f(a.scale * h[r]);
+    }
+    u32x4 xb[2];
+    pack16(x, xb);
+#pragma unroll
+    for (int t = 0; t < ot; ++t) {
+      const uint16_t* trow = xt + (int64_t)(wave * oq + 32 * t + perm_row(lq)) * ldxt + r0 + 16 * lg;
+      acc[t] = mfma32(ldg16(trow), xb[0], acc[t]);
+      acc[t] = mfma32(ldg16(trow + 8), xb[1], acc[t]);
+    }
+    __syncthreads();
+  }
+  if (!clive) return;
+  const int ocols = WANT_DB ? a.k : a.p;
+  float* dst = part + ((int64_t)blockIdx.y * a.n + col) * ocols + wave * oq + 16 * lg;
+#pragma unroll
+  for (int t = 0; t < ot; ++t) store_tile_f32(dst + 32 * t, acc[t]);
+}
+
+struct MlpLayout {
+  int split_rows;   // splits of the n loop for the row-block kernels
+  int split_cols;   // splits of the m loop for the column-block kernel
+  int64_t m_pad, n_pad;
+  size_t fwd_ct, fwd_part, fwd_total;
+  size_t bwd_btt, bwd_at, bwd_dot, bwd_pa, bwd_pb, bwd_pc, bwd_total;
+};
+
+int pick_splits(int blocks, int tiles) {
+  int s = (256 + blocks - 1) / blocks;
+  if (s > tiles) s = tiles;
+  return s < 1 ? 1 : s;
+}
+
+MlpLayout layout(int m, int n, int k, int p) {
+  MlpLayout L{};
+  const int mb = (m + 31) / 32, nb = (n + 31) / 32;
+  L.split_rows = pick_splits(mb, nb);
+  L.split_cols = pick_splits(nb, mb);
+  L.m_pad = (int64_t)round_up(m, kPad);
+  L.n_pad = (int64_t)round_up(n, kPad);
+  size_t off = 0;
+  L.fwd_ct = off;
+  off = round_up(off + (size_t)p * L.n_pad * 2, 256);
+  L.fwd_part = off;
+  off = round_up(off + (size_t)L.split_rows * m * p * 4, 256);
+  L.fwd_total = off;
+  off = 0;
+  L.bwd_btt = off;
+  off = round_up(off + (size_t)k * L.n_pad * 2, 256);
+  L.bwd_at = off;
+  off = round_up(off + (size_t)k * L.m_pad * 2, 256);
+  L.bwd_dot = off;
+  off = round_up(off + (size_t)p * L.m_pad * 2, 256);
+  L.bwd_pa = off;
+  off = round_up(off + (size_t)L.split_rows * m * k * 4, 256);
+  L.bwd_pb = off;
+  off = round_up(off + (size_t)L.split_cols * n * k * 4, 256);
+  L.bwd_pc = off;
+  off = round_up(off + (size_t)L.split_cols * n * p * 4, 256);
+  L.bwd_total = off;
+  return L;
+}
+
+hipError_t transpose(const void* in, int64_t ld_in, int rows, int cols, void* out, int64_t ld_out,
+                     hipStream_t s) {
+  const dim3 grid((unsigned)((ld_out + 63) / 64), (unsigned)((cols + 63) / 64)), block(256);
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, block, 0, s,
+                     static_cast<const uint16_t*>(in), ld_in, rows, cols,
+                     static_cast<uint16_t*>(out), ld_out);
+  return hipGetLastError();
+}
+
+hipError_t reduce(const float* part, int splits, int rows, int cols, float scale, void* out,
+                  int64_t ld_out, hipStream_t s) {
+  const int64_t total = (int64_t)rows * cols / 8;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  hipLaunchKernelGGL(reduce_parts_kernel, grid, block, 0, s, part, splits, rows, cols, scale,
+                     static_cast<uint16_t*>(out), ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool mlp_available() { return true; }
+
+size_t mlp_fwd_workspace(int m, int n, int k, int p, int* splits) {
+  const MlpLayout L = layout(m, n, k, p);
+  *splits = L.split_rows;
+  return L.fwd_total;
+}
+
+size_t mlp_bwd_workspace(int m, int n, int k, int p) { return layout(m, n, k, p).bwd_total; }
+
+namespace {
+
+template <int K, int P>
+hipError_t fwd_kp(const MlpArgs& a, const MlpLayout& L, uint16_t* ct, float* part, hipStream_t s) {
+  const int ntiles = (a.n + 31) / 32;
+  const int per = (ntiles + L.split_rows - 1) / L.split_rows;
+  const dim3 grid((unsigned)((a.m + 31) / 32), (unsigned)L.split_rows), block(256);
+  hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, ct, L.n_pad, per, part);
+  return hipGetLastError();
+}
+
+template <int K, int P>
+hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const uint16_t* btt, const uint16_t* at,
+                  const uint16_t* dot, float* pa, float* pb, float* pc, hipStream_t s) {
+  const int ntiles = (a.n + 31) / 32, mtiles = (a.m + 31) / 32;
+  const int per_n = (ntiles + L.split_rows - 1) / L.split_rows;
+  const int per_m = (mtiles + L.split_cols - 1) / L.split_cols;
+  const dim3 block(256);
+  hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)mtiles, (unsigned)L.split_rows),
+                     block, 0, s, a, btt, L.n_pad, per_n, pa);
+  hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, true>),
+                     dim3((unsigned)ntiles, (unsigned)L.split_cols), block, 0, s, a, at, L.m_pad,
+                     per_m, pb);
+  hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, false>),
+                     dim3((unsigned)ntiles, (unsigned)L.split_cols), block, 0, s, a, dot, L.m_pad,
+                     per_m, pc);
+  return hipGetLastError();
+}
+
+// Calls fn.template operator()<K, P>() for the supported sizes.
+template <typename F>
+hipError_t dispatch_kp(int k, int p, F&& fn) {
+#define FAB_MLP_P(K)                                  \
+  switch (p) {                                        \
+    case 128: return fn.template operator()<K, 128>(); \
+    case 256: return fn.template operator()<K, 256>(); \
+    case 512: return fn.template operator()<K, 512>(); \
+    case 1024: return fn.template operator()<K, 1024>(); \
+  }                                                   \
+  return hipErrorInvalidValue;
+  switch (k) {
+    case 128: { FAB_MLP_P(128) }
+    case 256: { FAB_MLP_P(256) }
+    case 512: { FAB_MLP_P(512) }
+    case 1024: { FAB_MLP_P(1024) }
+  }
+#undef FAB_MLP_P
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool mlp_shape_supported(int k, int p) {
+  auto ok = [](int x) { return x == 128 || x == 256 || x == 512 || x == 1024; };
+  return ok(k) && ok(p);
+}
+
+hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s) {
+  if (!mlp_shape_supported(a.k, a.p)) return hipErrorInvalidValue;
+  const MlpLayout L = layout(a.m, a.n, a.k, a.p);
+  char* ws = reinterpret_cast<char*>(a.ws);
+  uint16_t* ct = reinterpret_cast<uint16_t*>(ws + L.fwd_ct);
+  float* part = reinterpret_cast<float*>(ws + L.fwd_part);
+  hipError_t e = transpose(a.c, a.c_sr, a.n, a.p, ct, L.n_pad, s);
+  if (e != hipSuccess) return e;
+  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() { return fwd_kp<K, P>(a, L, ct, part, s); });
+  if (e != hipSuccess) return e;
+  return reduce(part, L.split_rows, a.m, a.p, 1.f, a.o, a.o_sr, s);
+}
+
+hipError_t launch_mlp_bwd_bf16(const MlpArgs& a, hipStream_t s) {
+  if (!mlp_shape_supported(a.k, a.p)) return hipErrorInvalidValue;
+  const MlpLayout L = layout(a.m, a.n, a.k, a.p);
+  char* ws = reinterpret_cast<char*>(a.ws);
+  uint16_t* btt = reinterpret_cast<uint16_t*>(ws + L.bwd_btt);
+  uint16_t* at = reinterpret_cast<uint16_t*>(ws + L.bwd_at);
+  uint16_t* dot = reinterpret_cast<uint16_t*>(ws + L.bwd_dot);
+  float* pa = reinterpret_cast<float*>(ws + L.bwd_pa);
+  float* pb = reinterpret_cast<float*>(ws + L.bwd_pb);
+  float* pc = reinterpret_cast<float*>(ws + L.bwd_pc);
+  hipError_t e;
+  if ((e = transpose(a.bt, a.bt_sr, a.n, a.k, btt, L.n_pad, s)) != hipSuccess) return e;
+  if ((e = transpose(a.a, a.a_sr, a.m, a.k, at, L.m_pad, s)) != hipSuccess) return e;
+  if ((e = transpose(a.dout, a.o_sr, a.m, a.p, dot, L.m_pad, s)) != hipSuccess) return e;
+  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() {
+    return bwd_kp<K, P>(a, L, btt, at, dot, pa, pb, pc, s);
+  });
+  if (e != hipSuccess) return e;
+  if ((e = reduce(pa, L.split_rows, a.m, a.k, a.scale, a.da, a.a_sr, s)) != hipSuccess) return e;
+  if ((e = reduce(pb, L.split_cols, a.n, a.k, a.scale, a.dbt, a.bt_sr, s)) != hipSuccess) return e;
+  return reduce(pc, L.split_cols, a.n, a.p, 1.f, a.dc, a.c_sr, s);
+}
+
+}  // namespace fab

@@ -96,8 +96,8 @@ typedef struct fab_plan_s fab_plan_t;
  * Supported in this build:
  *   softmax, bf16: k == p, k in {64, 128}; any m, n >= 1; causal needs m == n.
  *   softmax, f32:  k == p, k in {64, 128}; same rules.
- *   GeLU, bf16:    batch == heads_a == heads_bc == 1, k and p multiples of 64,
- *                  any m, n >= 1, mask NONE.
+ *   GeLU, bf16:    batch == heads_a == heads_bc == 1, k and p multiples of 128
+ *                  and at most 1024, any m, n >= 1, mask NONE.
  * Row strides must be multiples of 8 elements (bf16) or 4 (f32), and so must
  * the head and batch strides.  On success *plan_out receives a plan that the
  * caller releases with fab_plan_destroy, and the two sizes receive the bytes

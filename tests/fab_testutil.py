@@ -3,8 +3,10 @@
 Error measure (the reading used throughout): per-row normwise relative error
 max_i ||g_i - r_i||_inf / ||r_i||_inf over rows (one d-vector per batch, head
 and token for attention; one matrix row for the MLP), where rows whose
-reference norm is below 1e-6 of the largest row norm are compared against that
-floor instead.  Tolerances: 1e-2 for bf16 inputs with fp32 accumulation,
+reference norm is below 1e-3 of the largest row norm are compared against that
+floor instead.  The floor exists because some gradient rows vanish by exact
+cancellation (the causal first query's dQ: its only score has dS = P (dP - D)
+= 0), and rounding noise relative to an exact zero is no error measure.  Tolerances: 1e-2 for bf16 inputs with fp32 accumulation,
 1e-5 for the fp32 path.  LSE uses absolute error: 1e-3 (bf16), 1e-5 (fp32).
 """
 import numpy as np
@@ -21,7 +23,7 @@ def row_rel_err(got, ref):
     g = got.reshape(-1, got.shape[-1])
     r = ref.reshape(-1, ref.shape[-1])
     rn = np.abs(r).max(axis=1)
-    floor = 1e-6 * max(rn.max(), 1e-300)
+    floor = 1e-3 * max(rn.max(), 1e-300)
     err = np.abs(g - r).max(axis=1) / np.maximum(rn, floor)
     return float(err.max()) if err.size else 0.0
 
