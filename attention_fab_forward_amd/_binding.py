@@ -27,7 +27,8 @@ STATUS = {
 # every symbol include/fab.h declares
 EXPORTS = ("fab_plan", "fab_forward", "fab_backward", "fab_plan_destroy",
            "fab_status_string", "fab_last_error", "fab_abi_version",
-           "fab_problem_size", "fab_plan_describe")
+           "fab_problem_size", "fab_plan_describe", "fab_plan_set_timing",
+           "fab_plan_kernel_times", "fab_plan_reset_kernel_times")
 
 
 class FabProblem(ctypes.Structure):
@@ -85,6 +86,14 @@ def lib():
         L.fab_problem_size.restype = ctypes.c_size_t
         L.fab_plan_describe.argtypes = [vp, ctypes.c_char_p, sz]
         L.fab_plan_describe.restype = ctypes.c_size_t
+        L.fab_plan_set_timing.argtypes = [vp, ctypes.c_int]
+        L.fab_plan_set_timing.restype = ctypes.c_int
+        L.fab_plan_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_char_p),
+                                            ctypes.POINTER(ctypes.c_int),
+                                            ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+        L.fab_plan_kernel_times.restype = ctypes.c_int
+        L.fab_plan_reset_kernel_times.argtypes = [vp]
+        L.fab_plan_reset_kernel_times.restype = ctypes.c_int
         if L.fab_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libfab.so ABI {L.fab_abi_version()} != binding {ABI_VERSION}")
         if L.fab_problem_size() != ctypes.sizeof(FabProblem):
@@ -130,6 +139,23 @@ class Plan:
         buf = ctypes.create_string_buffer(512)
         lib().fab_plan_describe(self._ptr, buf, 512)
         return buf.value.decode()
+
+    def set_timing(self, enable=True):
+        check(lib().fab_plan_set_timing(self._ptr, 1 if enable else 0))
+
+    def reset_kernel_times(self):
+        check(lib().fab_plan_reset_kernel_times(self._ptr))
+
+    def kernel_times(self):
+        """{kernel name: (launches, total ms)} since the last reset (waits for them)."""
+        cap = 32
+        names = (ctypes.c_char_p * cap)()
+        counts = (ctypes.c_int * cap)()
+        totals = (ctypes.c_double * cap)()
+        k = lib().fab_plan_kernel_times(self._ptr, names, counts, totals, cap)
+        if k < 0:
+            raise FabError(7, lib().fab_last_error().decode())
+        return {names[i].decode(): (counts[i], totals[i]) for i in range(min(k, cap))}
 
     def forward_raw(self, a, bt, c, o, lse, ws, ws_bytes, stream):
         check(lib().fab_forward(self._ptr, a, bt, c, o, lse, ws, ws_bytes, stream))

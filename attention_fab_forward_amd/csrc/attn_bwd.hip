@@ -453,11 +453,11 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   const int nqb = (a.m + kAttnBwdBM - 1) / kAttnBwdBM;
   const dim3 gk((unsigned)nkb * a.hkv * a.b), gq((unsigned)nqb * a.hq * a.b);
   if (a.causal) {
-    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, true>), gk, block, 0, s, a);
-    hipLaunchKernelGGL((attn_dq_bf16_kernel<D, true>), gq, block, 0, s, a);
+    FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, true>), gk, block, 0, s, a));
+    FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, true>), gq, block, 0, s, a));
   } else {
-    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, false>), gk, block, 0, s, a);
-    hipLaunchKernelGGL((attn_dq_bf16_kernel<D, false>), gq, block, 0, s, a);
+    FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, false>), gk, block, 0, s, a));
+    FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, false>), gq, block, 0, s, a));
   }
   return hipGetLastError();
 }

@@ -325,9 +325,9 @@ hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
   constexpr int QPB = 256 / (D / 32);
   const dim3 grid((unsigned)((a.m + QPB - 1) / QPB) * a.hq * a.b), block(256);
   if (a.causal)
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), grid, block, 0, s, a);
+    FAB_TIMED("attn_fwd_f32", s, hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), grid, block, 0, s, a));
   else
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), grid, block, 0, s, a);
+    FAB_TIMED("attn_fwd_f32", s, hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), grid, block, 0, s, a));
   return hipGetLastError();
 }
 
@@ -338,11 +338,11 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   const dim3 gq((unsigned)((a.m + RPB - 1) / RPB) * a.hq * a.b);
   const dim3 gk((unsigned)((a.n + RPB - 1) / RPB) * a.hkv * a.b);
   if (a.causal) {
-    hipLaunchKernelGGL((attn_dq_f32_kernel<D, true>), gq, block, 0, s, a);
-    hipLaunchKernelGGL((attn_dkdv_f32_kernel<D, true>), gk, block, 0, s, a);
+    FAB_TIMED("attn_bwd_dq_f32", s, hipLaunchKernelGGL((attn_dq_f32_kernel<D, true>), gq, block, 0, s, a));
+    FAB_TIMED("attn_bwd_dkdv_f32", s, hipLaunchKernelGGL((attn_dkdv_f32_kernel<D, true>), gk, block, 0, s, a));
   } else {
-    hipLaunchKernelGGL((attn_dq_f32_kernel<D, false>), gq, block, 0, s, a);
-    hipLaunchKernelGGL((attn_dkdv_f32_kernel<D, false>), gk, block, 0, s, a);
+    FAB_TIMED("attn_bwd_dq_f32", s, hipLaunchKernelGGL((attn_dq_f32_kernel<D, false>), gq, block, 0, s, a));
+    FAB_TIMED("attn_bwd_dkdv_f32", s, hipLaunchKernelGGL((attn_dkdv_f32_kernel<D, false>), gk, block, 0, s, a));
   }
   return hipGetLastError();
 }
@@ -356,11 +356,11 @@ hipError_t launch_attn_delta(const AttnArgs& a, int d, bool bf16, hipStream_t s)
   const int rpb = 256 / lpr;
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
   if (bf16) {
-    if (d == 128) hipLaunchKernelGGL((attn_delta_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_delta_kernel<64, true>), grid, block, 0, s, a);
+    if (d == 128) FAB_TIMED("attn_bwd_delta", s, hipLaunchKernelGGL((attn_delta_kernel<128, true>), grid, block, 0, s, a));
+    else FAB_TIMED("attn_bwd_delta", s, hipLaunchKernelGGL((attn_delta_kernel<64, true>), grid, block, 0, s, a));
   } else {
-    if (d == 128) hipLaunchKernelGGL((attn_delta_kernel<128, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_delta_kernel<64, false>), grid, block, 0, s, a);
+    if (d == 128) FAB_TIMED("attn_bwd_delta", s, hipLaunchKernelGGL((attn_delta_kernel<128, false>), grid, block, 0, s, a));
+    else FAB_TIMED("attn_bwd_delta", s, hipLaunchKernelGGL((attn_delta_kernel<64, false>), grid, block, 0, s, a));
   }
   return hipGetLastError();
 }

@@ -259,9 +259,9 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int nqb = (a.m + kAttnFwdBM - 1) / kAttnFwdBM;
   const dim3 grid((unsigned)nqb * a.hq * a.b), block(256);
   if (a.causal)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), grid, block, 0, s, a);
+    FAB_TIMED("attn_fwd_bf16", s, hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), grid, block, 0, s, a));
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), grid, block, 0, s, a);
+    FAB_TIMED("attn_fwd_bf16", s, hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, false>), grid, block, 0, s, a));
   return hipGetLastError();
 }
 

@@ -10,13 +10,107 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/fab.h"
 #include "fab_internal.h"
 
+namespace {
+
+// Event-pair recorder behind fab_plan_set_timing.  Events are created once and
+// reused; each record brackets one kernel on the stream it was launched on.
+struct KernelTimer {
+  struct Rec {
+    const char* name;
+    hipEvent_t start, stop;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> free_events;
+  std::map<std::string, std::pair<int, double>> totals;
+  const char* pending = nullptr;
+  hipEvent_t pending_start = nullptr;
+  bool failed = false;
+
+  hipEvent_t get() {
+    if (!free_events.empty()) {
+      hipEvent_t e = free_events.back();
+      free_events.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+      failed = true;
+      return nullptr;
+    }
+    return e;
+  }
+  void begin(const char* name, hipStream_t s) {
+    pending = name;
+    pending_start = get();
+    if (pending_start) hipEventRecord(pending_start, s);
+  }
+  void end(hipStream_t s) {
+    hipEvent_t stop = get();
+    if (stop && pending_start) {
+      hipEventRecord(stop, s);
+      recs.push_back({pending, pending_start, stop});
+    }
+    pending = nullptr;
+    pending_start = nullptr;
+  }
+  // Waits for every recorded pair and folds it into the totals.
+  void drain() {
+    for (Rec& r : recs) {
+      float ms = 0.f;
+      if (hipEventSynchronize(r.stop) == hipSuccess && hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+        auto& t = totals[r.name];
+        t.first += 1;
+        t.second += ms;
+      } else {
+        failed = true;
+      }
+      free_events.push_back(r.start);
+      free_events.push_back(r.stop);
+    }
+    recs.clear();
+  }
+  ~KernelTimer() {
+    for (Rec& r : recs) {
+      hipEventSynchronize(r.stop);
+      free_events.push_back(r.start);
+      free_events.push_back(r.stop);
+    }
+    for (hipEvent_t e : free_events) hipEventDestroy(e);
+  }
+};
+
+thread_local KernelTimer* t_active_timer = nullptr;
+
+// Makes `timer` the target of timer_begin / timer_end for one library call.
+struct TimerScope {
+  explicit TimerScope(KernelTimer* timer) { t_active_timer = timer; }
+  ~TimerScope() { t_active_timer = nullptr; }
+};
+
+}  // namespace
+
+namespace fab {
+void timer_begin(const char* kernel, hipStream_t s) {
+  if (t_active_timer) t_active_timer->begin(kernel, s);
+}
+void timer_end(hipStream_t s) {
+  if (t_active_timer) t_active_timer->end(s);
+}
+}  // namespace fab
+
 struct fab_plan_s {
+  std::mutex timer_mu;
+  KernelTimer* timer = nullptr;  // owned; non-null while timing is enabled
+  ~fab_plan_s() { delete timer; }
   fab_problem prob;
   int64_t as[3], bs[3], cs[3], os[3];  // resolved {batch, head, row} strides
   size_t fwd_ws;
@@ -148,7 +242,7 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
   if (!std::isfinite(q.scale)) return fail(FAB_ERR_BAD_SHAPE, "scale must be finite");
 
   const int64_t unit = q.dtype == FAB_BF16 ? 8 : 4;
-  fab_plan_s tmp{};
+  fab_plan_s tmp;
   tmp.prob = q;
   resolve(q.a_stride, q.m, q.heads_a, q.k, tmp.as);
   resolve(q.bt_stride, q.n, q.heads_bc, q.k, tmp.bs);
@@ -199,8 +293,17 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
     snprintf(tmp.desc, sizeof tmp.desc, "gelu-mlp bf16 m=%lld k=%lld n=%lld p=%lld splits=%d",
              (long long)q.m, (long long)q.k, (long long)q.n, (long long)q.p, splits);
   }
-  fab_plan_s* plan = new (std::nothrow) fab_plan_s(tmp);
+  fab_plan_s* plan = new (std::nothrow) fab_plan_s;
   if (!plan) return fail(FAB_ERR_UNSUPPORTED, "out of host memory");
+  plan->prob = tmp.prob;
+  memcpy(plan->as, tmp.as, sizeof tmp.as);
+  memcpy(plan->bs, tmp.bs, sizeof tmp.bs);
+  memcpy(plan->cs, tmp.cs, sizeof tmp.cs);
+  memcpy(plan->os, tmp.os, sizeof tmp.os);
+  plan->fwd_ws = tmp.fwd_ws;
+  plan->bwd_ws = tmp.bwd_ws;
+  plan->mlp_splits = tmp.mlp_splits;
+  memcpy(plan->desc, tmp.desc, sizeof tmp.desc);
   *plan_out = plan;
   if (fwd_ws) *fwd_ws = plan->fwd_ws;
   if (bwd_ws) *bwd_ws = plan->bwd_ws;
@@ -208,6 +311,52 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
 }
 
 void fab_plan_destroy(fab_plan_t* plan) { delete plan; }
+
+fab_status fab_plan_set_timing(fab_plan_t* plan, int enable) {
+  if (!plan) return fail(FAB_ERR_NULL_ARG, "fab_plan_set_timing: plan is NULL");
+  std::lock_guard<std::mutex> lock(plan->timer_mu);
+  if (enable && !plan->timer) {
+    plan->timer = new (std::nothrow) KernelTimer;
+    if (!plan->timer) return fail(FAB_ERR_UNSUPPORTED, "out of host memory");
+  } else if (!enable && plan->timer) {
+    delete plan->timer;
+    plan->timer = nullptr;
+  }
+  return ok();
+}
+
+int fab_plan_kernel_times(fab_plan_t* plan, const char** names, int* counts, double* total_ms,
+                          int capacity) {
+  if (!plan) return -1;
+  std::lock_guard<std::mutex> lock(plan->timer_mu);
+  if (!plan->timer) return 0;
+  plan->timer->drain();
+  if (plan->timer->failed) {
+    fail(FAB_ERR_HIP, "fab_plan_kernel_times: a HIP event call failed");
+    return -1;
+  }
+  int i = 0;
+  for (auto& kv : plan->timer->totals) {
+    if (i < capacity) {
+      // names point at the static strings the launchers pass
+      if (names) names[i] = kv.first.c_str();
+      if (counts) counts[i] = kv.second.first;
+      if (total_ms) total_ms[i] = kv.second.second;
+    }
+    ++i;
+  }
+  return i;
+}
+
+fab_status fab_plan_reset_kernel_times(fab_plan_t* plan) {
+  if (!plan) return fail(FAB_ERR_NULL_ARG, "fab_plan_reset_kernel_times: plan is NULL");
+  std::lock_guard<std::mutex> lock(plan->timer_mu);
+  if (plan->timer) {
+    plan->timer->drain();
+    plan->timer->totals.clear();
+  }
+  return ok();
+}
 
 size_t fab_plan_describe(const fab_plan_t* plan, char* buf, size_t len) {
   if (!plan) return 0;
@@ -233,6 +382,7 @@ fab_status fab_forward(const fab_plan_t* plan, const void* A, const void* Bt, co
   if (plan->fwd_ws && !workspace) return fail(FAB_ERR_NULL_ARG, "fab_forward: workspace is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  TimerScope scope(plan->timer);
   if (q.f == FAB_F_SOFTMAX) {
     if (!lse) return fail(FAB_ERR_NULL_ARG, "fab_forward: softmax needs lse");
     if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
@@ -274,6 +424,7 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, c
     return fail(FAB_ERR_ALIGNMENT, "fab_backward: workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
+  TimerScope scope(plan->timer);
   if (q.f == FAB_F_SOFTMAX) {
     if (!O || !lse) return fail(FAB_ERR_NULL_ARG, "fab_backward: softmax needs O and lse");
     if (!aligned16(O)) return fail(FAB_ERR_ALIGNMENT, "fab_backward: O must be 16-byte aligned");

@@ -53,6 +53,20 @@ struct MlpArgs {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// Optional per-kernel timing of one call (see fab_plan_set_timing): launchers
+// bracket every kernel they enqueue with these; both are no-ops unless the
+// calling thread is inside a timed fab_forward / fab_backward.
+void timer_begin(const char* kernel, hipStream_t s);
+void timer_end(hipStream_t s);
+
+// Bracket a kernel launch: FAB_TIMED("name", stream, hipLaunchKernelGGL(...)).
+#define FAB_TIMED(name, stream, ...) \
+  do {                               \
+    ::fab::timer_begin(name, stream); \
+    __VA_ARGS__;                     \
+    ::fab::timer_end(stream);        \
+  } while (0)
+
 // Forward attention tile shapes (bf16 MFMA path).
 constexpr int kAttnFwdBM = 128;   // queries per workgroup (4 waves x 32)
 constexpr int kAttnFwdBN = 64;    // keys per inner step

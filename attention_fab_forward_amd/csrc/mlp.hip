@@ -411,9 +411,9 @@ MlpLayout layout(int m, int n, int k, int p) {
 hipError_t transpose(const void* in, int64_t ld_in, int rows, int cols, void* out, int64_t ld_out,
                      hipStream_t s) {
   const dim3 grid((unsigned)((ld_out + 63) / 64), (unsigned)((cols + 63) / 64)), block(256);
-  hipLaunchKernelGGL(transpose_bf16_kernel, grid, block, 0, s,
+  FAB_TIMED("mlp_transpose", s, hipLaunchKernelGGL(transpose_bf16_kernel, grid, block, 0, s,
                      static_cast<const uint16_t*>(in), ld_in, rows, cols,
-                     static_cast<uint16_t*>(out), ld_out);
+                     static_cast<uint16_t*>(out), ld_out));
   return hipGetLastError();
 }
 
@@ -421,8 +421,8 @@ hipError_t reduce(const float* part, int splits, int rows, int cols, float scale
                   int64_t ld_out, hipStream_t s) {
   const int64_t total = (int64_t)rows * cols / 8;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  hipLaunchKernelGGL(reduce_parts_kernel, grid, block, 0, s, part, splits, rows, cols, scale,
-                     static_cast<uint16_t*>(out), ld_out);
+  FAB_TIMED("mlp_reduce", s, hipLaunchKernelGGL(reduce_parts_kernel, grid, block, 0, s, part, splits, rows, cols, scale,
+                     static_cast<uint16_t*>(out), ld_out));
   return hipGetLastError();
 }
 
@@ -445,7 +445,7 @@ hipError_t fwd_kp(const MlpArgs& a, const MlpLayout& L, uint16_t* ct, float* par
   const int ntiles = (a.n + 31) / 32;
   const int per = (ntiles + L.split_rows - 1) / L.split_rows;
   const dim3 grid((unsigned)((a.m + 31) / 32), (unsigned)L.split_rows), block(256);
-  hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, ct, L.n_pad, per, part);
+  FAB_TIMED("mlp_fwd", s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, ct, L.n_pad, per, part));
   return hipGetLastError();
 }
 
@@ -456,14 +456,14 @@ hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const uint16_t* btt, con
   const int per_n = (ntiles + L.split_rows - 1) / L.split_rows;
   const int per_m = (mtiles + L.split_cols - 1) / L.split_cols;
   const dim3 block(256);
-  hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)mtiles, (unsigned)L.split_rows),
-                     block, 0, s, a, btt, L.n_pad, per_n, pa);
-  hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, true>),
+  FAB_TIMED("mlp_bwd_da", s, hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)mtiles, (unsigned)L.split_rows),
+                     block, 0, s, a, btt, L.n_pad, per_n, pa));
+  FAB_TIMED("mlp_bwd_dbt", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, true>),
                      dim3((unsigned)ntiles, (unsigned)L.split_cols), block, 0, s, a, at, L.m_pad,
-                     per_m, pb);
-  hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, false>),
+                     per_m, pb));
+  FAB_TIMED("mlp_bwd_dc", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, false>),
                      dim3((unsigned)ntiles, (unsigned)L.split_cols), block, 0, s, a, dot, L.m_pad,
-                     per_m, pc);
+                     per_m, pc));
   return hipGetLastError();
 }
 

@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused two-matmul block O = f(A.B).C on one MI355X.
+
+Step = one forward + backward pass of causal softmax attention, bf16,
+batch 1, 32 heads, n = 32768, d = 128 (scale 1/sqrt(128)), on seeded synthetic
+N(0, 1) inputs already resident in device memory.  Throughput is algorithmic
+TFLOP/s: forward 4*d flops and backward 10*d flops (its five products, one
+recomputation of S included) per unmasked (query, key) pair, n(n+1)/2 pairs
+per head.
+
+Also reported on the same line: per-kernel durations from HIP events recorded
+around every kernel on the launch stream (the roofline entry uses the
+dominant kernel), peak device memory versus sequence length for the long-
+context grouped-query geometry, a secondary GeLU-MLP measurement, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk, dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "attn_causal_bf16_h32_n32768_d128"
+MLP_WORKLOAD = "mlp_gelu_m4096_k1024_n4096_p1024"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attention_flops(w):
+    pairs = w.seq * (w.seq + 1) // 2 if w.causal else w.seq * w.seq
+    unit = pairs * w.heads_q * w.batch
+    return 4 * w.d * unit, 10 * w.d * unit, unit
+
+
+def device_inputs(w, torch):
+    from attention_fab_forward_amd.inputs import attention_inputs
+    x = attention_inputs(w)
+    dev = {}
+    for name in ("q", "k", "v", "do"):
+        dev[name] = torch.from_numpy(x[name]).to(torch.bfloat16).cuda()
+    return x, dev
+
+
+def time_attention(w, steps, warmup, torch, fab_binding):
+    x, t = device_inputs(w, torch)
+    plan = fab_binding.attention_plan(t["q"], t["k"], t["v"], True, w.scale())
+    log(f"plan: {plan.describe()}")
+    b, n, hq, d = t["q"].shape
+    o = torch.empty_like(t["q"])
+    lse = torch.empty((b, hq, n), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["v"])
+    ws = torch.empty(max(plan.bwd_workspace, plan.fwd_workspace, 1), dtype=torch.uint8,
+                     device="cuda")
+    P = fab_binding._ptr
+    stream = torch.cuda.current_stream()
+    sp = fab_binding.ctypes.c_void_p(stream.cuda_stream)
+
+    def fwd():
+        plan.forward_raw(P(t["q"]), P(t["k"]), P(t["v"]), P(o), P(lse), P(ws), plan.fwd_workspace,
+                         sp)
+
+    def bwd():
+        plan.backward_raw(P(t["q"]), P(t["k"]), P(t["v"]), P(o), P(lse), P(t["do"]), P(dq),
+                          P(dk), P(dv), P(ws), plan.bwd_workspace, sp)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    # main timed region: K full steps, per-kernel events enabled
+    plan.set_timing(True)
+    plan.reset_kernel_times()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = e0.elapsed_time(e1) / steps
+    kernels = plan.kernel_times()
+    plan.set_timing(False)
+
+    # forward alone (timing off)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / steps
+    return {"step_ms": step_ms, "fwd_ms": fwd_ms, "wall_s": wall, "kernels": kernels,
+            "inputs": x}
+
+
+def kernel_flops(w):
+    """Algorithmic flops each attention kernel carries per launch."""
+    _, _, unit = attention_flops(w)
+    d = w.d
+    return {
+        "attn_fwd_bf16": 4 * d * unit,        # S = QK^T and O = PV
+        "attn_bwd_dkdv_bf16": 8 * d * unit,   # S (recompute), dP, dV, dK
+        "attn_bwd_dq_bf16": 2 * d * unit,     # dQ (its S, dP recomputes are extra work)
+        "attn_bwd_delta": 0,
+    }
+
+
+def kernel_bytes(w):
+    """Algorithmic HBM bytes of the memory-bound preprocessing kernel."""
+    rows = w.batch * w.heads_q * w.seq
+    return {"attn_bwd_delta": rows * w.d * 2 * 2 + rows * 4}
+
+
+def peak_hbm_sweep(torch, fab, exps=range(12, 18)):
+    """Peak device memory of forward + backward versus n (grouped-query geometry
+    of the long-context workload: 2 query heads, 1 kv head, d = 128)."""
+    out = []
+    for e in exps:
+        n = 1 << e
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        q = torch.randn(1, n, 2, 128, device="cuda", dtype=torch.bfloat16)
+        k = torch.randn(1, n, 1, 128, device="cuda", dtype=torch.bfloat16)
+        v = torch.randn(1, n, 1, 128, device="cuda", dtype=torch.bfloat16)
+        do = torch.randn_like(q)
+        o, lse = fab.forward(q, k, v, "softmax", True)
+        fwd_peak = torch.cuda.max_memory_allocated() - base
+        grads = fab.backward(q, k, v, o, lse, do, "softmax", True)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        out.append({"n": n, "fwd_peak_bytes": int(fwd_peak), "fwd_bwd_peak_bytes": int(peak)})
+        del q, k, v, do, o, lse, grads
+    ns = [r["n"] for r in out]
+    ys = [r["fwd_bwd_peak_bytes"] for r in out]
+    # least-squares a + b n and the largest relative residual
+    mn = sum(ns) / len(ns)
+    my = sum(ys) / len(ys)
+    b = sum((x - mn) * (y - my) for x, y in zip(ns, ys)) / sum((x - mn) ** 2 for x in ns)
+    a = my - b * mn
+    resid = max(abs(y - (a + b * x)) / y for x, y in zip(ns, ys))
+    ratios = [ys[i + 1] / ys[i] for i in range(len(ys) - 1)]
+    return {"geometry": "causal, 2 query heads / 1 kv head, d=128, bf16, fwd+bwd",
+            "points": out, "bytes_per_token": b, "max_rel_residual_linear_fit": resid,
+            "doubling_ratios": ratios}
+
+
+def time_mlp(steps, warmup, torch, fab_binding):
+    from attention_fab_forward_amd.inputs import WORKLOADS, mlp_inputs
+    w = WORKLOADS[MLP_WORKLOAD]
+    x = mlp_inputs(w)
+    t = {k: torch.from_numpy(v).to(torch.bfloat16).cuda() for k, v in x.items()}
+    plan = fab_binding.mlp_plan(t["a"], t["bt"], t["c"], 1.0)
+    m, k = t["a"].shape
+    n, p = t["bt"].shape[0], t["c"].shape[1]
+    o = torch.empty((m, p), dtype=torch.bfloat16, device="cuda")
+    da, dbt, dc = torch.empty_like(t["a"]), torch.empty_like(t["bt"]), torch.empty_like(t["c"])
+    ws = torch.empty(max(plan.fwd_workspace, plan.bwd_workspace, 1), dtype=torch.uint8,
+                     device="cuda")
+    P = fab_binding._ptr
+    stream = torch.cuda.current_stream()
+    sp = fab_binding.ctypes.c_void_p(stream.cuda_stream)
+    fwd = lambda: plan.forward_raw(P(t["a"]), P(t["bt"]), P(t["c"]), P(o), None, P(ws),
+                                   plan.fwd_workspace, sp)
+    bwd = lambda: plan.backward_raw(P(t["a"]), P(t["bt"]), P(t["c"]), None, None, P(t["do"]),
+                                    P(da), P(dbt), P(dc), P(ws), plan.bwd_workspace, sp)
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    plan.set_timing(True)
+    plan.reset_kernel_times()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kernels = plan.kernel_times()
+    plan.set_timing(False)
+    e0.record(stream)
+    for _ in range(steps):
+        fwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / steps
+    step_ms = sum(v[1] for v in kernels.values()) / steps
+    gemm = 2 * m * k * n
+    fwd_fl, bwd_fl = 2 * gemm, 5 * gemm
+    return {"workload": MLP_WORKLOAD, "fwd_ms": fwd_ms, "fwd_bwd_ms": step_ms,
+            "fwd_tflops": fwd_fl / fwd_ms / 1e9, "fwd_bwd_tflops": (fwd_fl + bwd_fl) / step_ms / 1e9,
+            "kernels_avg_ms": {k_: v[1] / v[0] for k_, v in kernels.items()}}
+
+
+def cpu_baseline(w, x, seconds):
+    """The oracle, unchanged, on a bounded sample: the last rows of head 0 of the
+    benchmarked workload (forward rows and their full backward work), processed
+    in 32-row chunks by a pool of host threads until `seconds` have passed."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    scale = w.scale()
+    n = w.seq
+    chunk = 32
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+
+    def work(r1):
+        rows = np.arange(r1 - chunk, r1)
+        oracle.attention_forward_rows(q, k, v, scale, True, 0, 0, rows)
+        oracle.attention_backward_rows(q, k, v, do, scale, True, 0, 0, rows)
+        return rows
+
+    done = []
+    t0 = time.perf_counter()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx:
+        ctx.__enter__()
+    try:
+        with ThreadPoolExecutor(max_workers=cores) as ex:
+            r1 = n
+            while time.perf_counter() - t0 < seconds and r1 - chunk >= 0:
+                batch = []
+                for _ in range(cores):
+                    if r1 - chunk < 0:
+                        break
+                    batch.append(r1)
+                    r1 -= chunk
+                for rows in ex.map(work, batch):
+                    done.append(rows)
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    elapsed = time.perf_counter() - t0
+    rows = np.concatenate(done)
+    flops = float(np.sum(14.0 * w.d * (rows + 1)))
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": elapsed,
+            "sample": f"{len(rows)} query rows [{int(rows.min())}, {n}) of head 0 of {WORKLOAD}: "
+                      "forward rows plus their backward work (fp64 numpy, full-width rows); "
+                      "rate = algorithmic fwd+bwd flops of those rows / wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the memory sweep and the MLP measurement")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this build has "
+              "no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_fab_forward_amd as fab
+    from attention_fab_forward_amd import _binding as fab_binding
+    from attention_fab_forward_amd.inputs import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fab.lib()
+
+    w = WORKLOADS[WORKLOAD]
+    fwd_fl, bwd_fl, unit = attention_flops(w)
+    log(f"workload {WORKLOAD}: {unit} unmasked pairs, fwd {fwd_fl:.3e} flop, bwd {bwd_fl:.3e} flop")
+    r = time_attention(w, args.steps, args.warmup, torch, fab_binding)
+    step_ms, fwd_ms = r["step_ms"], r["fwd_ms"]
+    value = (fwd_fl + bwd_fl) / step_ms / 1e9
+    kflops = kernel_flops(w)
+    kbytes = kernel_bytes(w)
+    kern = {}
+    for name, (cnt, tot) in r["kernels"].items():
+        avg = tot / cnt
+        entry = {"launches": cnt, "avg_ms": avg}
+        if kflops.get(name):
+            entry["tflops"] = kflops[name] / avg / 1e9
+        if kbytes.get(name):
+            entry["gbs"] = kbytes[name] / avg / 1e6
+        kern[name] = entry
+    dom = max(kern, key=lambda k_: kern[k_]["avg_ms"] * kern[k_]["launches"])
+    if kflops.get(dom):
+        ach = kflops[dom] / kern[dom]["avg_ms"] / 1e9
+        roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None, "kernel": dom,
+                "flops_per_launch": kflops[dom], "avg_launch_ms": kern[dom]["avg_ms"]}
+    else:
+        ach = kbytes[dom] / kern[dom]["avg_ms"] / 1e6
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+    log(f"step {step_ms:.3f} ms ({value:.1f} TFLOP/s), fwd {fwd_ms:.3f} ms; kernels: "
+        + ", ".join(f"{k_} {v['avg_ms']:.3f} ms" for k_, v in kern.items()))
+
+    extras = {}
+    if not args.no_extras:
+        log("peak-memory sweep ...")
+        extras["peak_hbm_vs_seq"] = peak_hbm_sweep(torch, fab)
+        log("mlp ...")
+        extras["mlp"] = time_mlp(max(3, args.steps), args.warmup, torch, fab_binding)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline ({args.cpu_seconds:.0f} s) ...")
+        cpu = cpu_baseline(w, r["inputs"], args.cpu_seconds)
+
+    line = {
+        "metric": "f(AB)C fwd / fwd+bwd TFLOP/s and % bf16 MFMA peak; peak HBM vs seq len",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16)",
+        "config": {"workload": WORKLOAD, "batch": w.batch, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "seq_len": w.seq, "head_dim": w.d, "mask": "causal",
+                   "step": "forward + backward", "parallelism": "single GPU"},
+        "pct_bf16_peak": 100.0 * value / BF16_PEAK_TFLOPS,
+        "fwd_tflops": fwd_fl / fwd_ms / 1e9,
+        "fwd_pct_bf16_peak": 100.0 * fwd_fl / fwd_ms / 1e9 / BF16_PEAK_TFLOPS,
+        "fwd_ms": fwd_ms,
+        "kernels": kern,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    line.update(extras)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -146,6 +146,24 @@ size_t fab_problem_size(void);
  * Returns the number of characters the full description needs. */
 size_t fab_plan_describe(const fab_plan_t* plan, char* buf, size_t len);
 
+/* Per-kernel timing, for measurement.  While enabled on a plan, every
+ * fab_forward / fab_backward made with it records a HIP event on the caller's
+ * stream before and after each kernel it enqueues (host-side event objects;
+ * no device memory).  Calls on a plan with timing enabled must not overlap
+ * across threads.  enable = 0 releases the events. */
+fab_status fab_plan_set_timing(fab_plan_t* plan, int enable);
+
+/* Waits for the recorded events, adds their durations into per-kernel totals
+ * and writes up to `capacity` entries: kernel name (static string valid until
+ * the next reset or fab_plan_set_timing), number of timed launches and total
+ * milliseconds.  Any output pointer may be NULL.  Returns the number of
+ * distinct kernels (0 if timing is off), or -1 on a HIP error. */
+int fab_plan_kernel_times(fab_plan_t* plan, const char** names, int* counts,
+                          double* total_ms, int capacity);
+
+/* Waits for pending events and clears the per-kernel totals. */
+fab_status fab_plan_reset_kernel_times(fab_plan_t* plan);
+
 #ifdef __cplusplus
 }
 #endif
