@@ -125,6 +125,43 @@ def kernel_bytes(w):
     return {"attn_bwd_delta": rows * w.d * 2 * 2 + rows * 4}
 
 
+# rocprofv3 names and source files of the kernels bench.py reports
+ROCPROF_NAMES = {
+    "attn_fwd_bf16": ("attn_fwd_bf16_kernel<128, true>", "attn_fwd.hip"),
+    "attn_bwd_dkdv_bf16": ("attn_dkdv_bf16_kernel<128, true>", "attn_bwd.hip"),
+    "attn_bwd_dq_bf16": ("attn_dq_bf16_kernel<128, true>", "attn_bwd.hip"),
+    "attn_bwd_delta": ("attn_delta_kernel<128, true>", "attn_f32.hip"),
+}
+
+
+def source_hash(src):
+    """sha256[:16] over a kernel's source file and the shared device headers."""
+    import hashlib
+    csrc = os.path.join(ROOT, "attention_fab_forward_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (src, "fab_device.h", "fab_internal.h"):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when that summary is missing or was taken from different kernel sources."""
+    if kernel not in ROCPROF_NAMES:
+        return None
+    rname, src = ROCPROF_NAMES[kernel]
+    path = os.path.join(ROOT, "profiles", f"{WORKLOAD}.hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    want = f"{src}:{source_hash(src)}"
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith(rname) and line.rstrip().endswith(want):
+                return float(line.split()[-2])
+    return None
+
+
 def peak_hbm_sweep(torch, fab, exps=range(12, 18)):
     """Peak device memory of forward + backward versus n (grouped-query geometry
     of the long-context workload: 2 query heads, 1 kv head, d = 128)."""
@@ -209,9 +246,10 @@ def time_mlp(steps, warmup, torch, fab_binding):
 
 
 def cpu_baseline(w, x, seconds):
-    """The oracle, unchanged, on a bounded sample: the last rows of head 0 of the
-    benchmarked workload (forward rows and their full backward work), processed
-    in 32-row chunks by a pool of host threads until `seconds` have passed."""
+    """The oracle, unchanged, on a bounded sample of the benchmarked workload:
+    query rows (forward rows and their full backward work), taken in 32-row
+    chunks from the last row of head 0 downwards, then head 1, ..., by a pool of
+    host threads until `seconds` have passed."""
     from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle
@@ -225,12 +263,14 @@ def cpu_baseline(w, x, seconds):
     chunk = 32
     q, k, v, do = x["q"], x["k"], x["v"], x["do"]
 
-    def work(r1):
+    def work(item):
+        h, r1 = item
         rows = np.arange(r1 - chunk, r1)
-        oracle.attention_forward_rows(q, k, v, scale, True, 0, 0, rows)
-        oracle.attention_backward_rows(q, k, v, do, scale, True, 0, 0, rows)
+        oracle.attention_forward_rows(q, k, v, scale, True, 0, h, rows)
+        oracle.attention_backward_rows(q, k, v, do, scale, True, 0, h, rows)
         return rows
 
+    order = [(h, r1) for h in range(w.heads_q) for r1 in range(n, chunk - 1, -chunk)]
     done = []
     t0 = time.perf_counter()
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
@@ -238,16 +278,11 @@ def cpu_baseline(w, x, seconds):
         ctx.__enter__()
     try:
         with ThreadPoolExecutor(max_workers=cores) as ex:
-            r1 = n
-            while time.perf_counter() - t0 < seconds and r1 - chunk >= 0:
-                batch = []
-                for _ in range(cores):
-                    if r1 - chunk < 0:
-                        break
-                    batch.append(r1)
-                    r1 -= chunk
-                for rows in ex.map(work, batch):
-                    done.append(rows)
+            pos = 0
+            while time.perf_counter() - t0 < seconds and pos < len(order):
+                batch = order[pos:pos + cores]
+                pos += len(batch)
+                done.extend(ex.map(work, batch))
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
@@ -256,9 +291,10 @@ def cpu_baseline(w, x, seconds):
     flops = float(np.sum(14.0 * w.d * (rows + 1)))
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": elapsed,
-            "sample": f"{len(rows)} query rows [{int(rows.min())}, {n}) of head 0 of {WORKLOAD}: "
-                      "forward rows plus their backward work (fp64 numpy, full-width rows); "
-                      "rate = algorithmic fwd+bwd flops of those rows / wall time"}
+            "sample": f"{len(rows)} query rows ({len(rows) / (n * w.heads_q):.1%} of the rows) of "
+                      f"{WORKLOAD}, last rows of head 0 first: forward rows plus their backward "
+                      "work (fp64 numpy, full-width rows); rate = algorithmic fwd+bwd flops of "
+                      "those rows / wall time"}
 
 
 def main():
@@ -267,10 +303,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the memory sweep and the MLP measurement")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run a plain device copy of this many MiB "
+                         "three times (reference reading for hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -308,14 +347,24 @@ def main():
     if kflops.get(dom):
         ach = kflops[dom] / kern[dom]["avg_ms"] / 1e9
         roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / BF16_PEAK_TFLOPS, "traffic": None, "kernel": dom,
+                "frac": ach / BF16_PEAK_TFLOPS, "traffic": measured_traffic(dom), "kernel": dom,
                 "flops_per_launch": kflops[dom], "avg_launch_ms": kern[dom]["avg_ms"]}
     else:
         ach = kbytes[dom] / kern[dom]["avg_ms"] / 1e6
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+                "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "kernel": dom}
     log(f"step {step_ms:.3f} ms ({value:.1f} TFLOP/s), fwd {fwd_ms:.3f} ms; kernels: "
         + ", ".join(f"{k_} {v['avg_ms']:.3f} ms" for k_, v in kern.items()))
+
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB copied 3 times")
+        del src, dst
 
     extras = {}
     if not args.no_extras:
