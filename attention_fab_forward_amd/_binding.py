@@ -11,7 +11,8 @@ import threading
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfab.so")
+LIB_PATH = os.environ.get("FAB_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfab.so")
 ABI_VERSION = 1
 
 SOFTMAX, GELU_ERF = 0, 1

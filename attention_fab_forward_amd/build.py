@@ -39,9 +39,9 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+def _compile(src, build_dir, defines):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,25 +52,28 @@ def _compile(src):
     return obj, noise
 
 
-def build(jobs=None, verbose=False):
-    """Compile every source in csrc/ and link libfab.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs=None, verbose=False, out=OUT, defines=(), build_dir=BUILD):
+    """Compile every source in csrc/ and link libfab.so; returns its path.
+
+    `defines` are extra preprocessor definitions (tile-shape experiments write
+    their library to another `out` path)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(_compile, srcs))
+        results = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
     objs = [r[0] for r in results]
     if verbose:
         for _, noise in results:
             for ln in noise:
                 print(ln, file=sys.stderr)
-    tmp = OUT + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link of libfab.so failed:\n" + res.stderr)
-    os.replace(tmp, OUT)
-    return OUT
+    os.replace(tmp, out)
+    return out
 
 
 def main(argv=None):

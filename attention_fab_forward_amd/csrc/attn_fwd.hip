@@ -1,28 +1,34 @@
 // Softmax attention forward, bf16 in / fp32 accumulate, on gfx950 MFMA.
 //
 // Computes O = softmax(scale * Q K^T [+ causal mask]) V and the per-row
-// log-sum-exp, one query block per workgroup, streaming key/value blocks
-// through LDS so the n x n score matrix is never stored (FlashAttention-style
-// tiling: "Ulysses Sequence Parallelism", section "Contexte Technique"; causal
-// masks defined from indices: "AutoSP", section 2.A).  The running row
-// maximum and sum follow the usual online-softmax rescaling, which leaves the
-// result equal to the plain definition.
+// log-sum-exp, one block of query rows per workgroup, streaming key/value
+// blocks through LDS so the n x n score matrix is never stored
+// (FlashAttention-style tiling: "Ulysses Sequence Parallelism", section
+// "Contexte Technique"; causal masks defined from indices: "AutoSP", section
+// 2.A).  The running row maximum and sum are the usual online-softmax
+// rescaling, which leaves the result equal to the plain definition.
 //
-// Layout choices (per wave of 64 lanes, 32 queries):
-//  * S^T = K Q^T is formed with v_mfma_f32_32x32x16_bf16, K as the A operand
-//    (from LDS) and Q^T as the B operand (held in registers for the whole
-//    kernel).  Lane l then owns query l%32, so row max / row sum are in-lane
-//    reductions plus one exchange with lane l^32.
-//  * K rows are stored in LDS in perm_row order, which makes accumulator slot
-//    s of lane l hold key 16*(l/32)+s: each lane's probabilities for 8
-//    consecutive keys become directly the B operand of the P.V product.
-//  * O^T = V^T P^T uses V^T (d x keys) as the A operand; V is transposed while
-//    being staged into LDS, with d rows also in perm_row order so each lane
-//    ends up owning 16 consecutive output columns.
-//  * Two LDS stages: tile j+1 is fetched into registers while tile j is
-//    computed, then written to the other stage; one barrier per step.
-//  * Causal blocks are visited longest-first; blocks above the diagonal are
-//    never loaded, and a wave skips blocks that are fully masked for it.
+// Layout choices (workgroup = 4 waves, each wave 64 queries = two 32-query
+// MFMA tiles that share every LDS fragment read):
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K is the A operand (from LDS),
+//    Q^T the B operand (registers, whole kernel).  Lane l owns query l%32 of
+//    each tile, so row max / row sum are in-lane plus one exchange with lane
+//    l^32, and an output rescale is one scalar per lane.
+//  * K rows sit in LDS in perm_row order, so accumulator slot s of lane l holds
+//    key 16*(l/32)+s and the lane's 8 consecutive probabilities are directly
+//    the B operand of O^T = V^T P^T.
+//  * V stays in its natural [key][d] layout in LDS; the V^T A operand is read
+//    with the transposing ds_read_b64_tr_b16, the source lanes addressing the
+//    d columns in perm_row order so every lane owns 16 consecutive outputs.
+//  * K and V tiles are copied global -> LDS asynchronously
+//    (global_load_lds_dwordx4, no register staging) into two stages; each LDS
+//    row is 16-byte-chunk XOR-swizzled so the MFMA operand reads are free of
+//    bank conflicts, the swizzle being applied on the global address side.
+//  * The running maximum is only moved when a block's maximum exceeds it by
+//    more than 2^8 (probabilities then stay below 256, well inside bf16), so
+//    the accumulator rescale is rare.
+//  * Causal blocks are dispatched longest-first; blocks above the diagonal
+//    are never loaded; a wave skips key blocks fully masked for it.
 #include "fab_device.h"
 #include "fab_internal.h"
 
@@ -31,94 +37,59 @@ namespace {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = kAttnFwdBM;
-  static constexpr int BN = kAttnFwdBN;
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int KP = D * 2 + 16;         // K row pitch in LDS (bytes)
-  static constexpr int VP = BN * 2 + 16;        // V^T row pitch (bytes), one row per d
-  static constexpr int KBYTES = BN * KP;
-  static constexpr int STAGE = KBYTES + D * VP;
-  static constexpr int KLOADS = BN * CPR / 256; // K chunks per thread per tile
-  static constexpr int KPT = BN * CPR / 256;    // keys per thread in V staging
-  static constexpr int KQ = BN / KPT;           // key groups in V staging
-  static constexpr int DT = D / 32;             // 32-wide output tiles
-  static constexpr int DC = D / 16;             // 16-deep contraction chunks
+  static constexpr int BN = kAttnFwdBN;     // keys per step
+  static constexpr int QT = kAttnFwdQT;     // 32-query tiles per wave
+  static constexpr int BM = 128 * QT;       // queries per workgroup
+  static constexpr int CPR = D / 8;         // 16-byte chunks per row
+  static constexpr int RB = D * 2;          // row bytes (no padding)
+  static constexpr int TILE = BN * RB;      // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int RPI = 1024 / RB;     // rows per 1 KiB async copy
+  static constexpr int CPW = TILE / 1024 / 4;  // async copies per wave per tile
+  static constexpr int DT = D / 32;         // 32-wide output tiles
+  static constexpr int DC = D / 16;         // 16-deep contraction chunks
 };
 
+// Physical 16-byte chunk of logical chunk c in row r.
 template <int D>
-struct Stage {
-  u32x4 k[FwdCfg<D>::KLOADS];
-  u32x4 v[FwdCfg<D>::KPT];
-};
-
+__device__ __forceinline__ int k_swz(int r, int c) { return c ^ (r & (FwdCfg<D>::CPR - 1)); }
 template <int D>
-__device__ __forceinline__ void fetch_tile(Stage<D>& st, const uint16_t* kbase,
-                                           const uint16_t* vbase, int64_t k_sr,
-                                           int64_t v_sr, int key0, int n, int tid) {
-  using C = FwdCfg<D>;
-  const int c = tid % C::CPR;
-#pragma unroll
-  for (int u = 0; u < C::KLOADS; ++u) {
-    const int r = tid / C::CPR + (256 / C::CPR) * u;
-    const int key = key0 + r;
-    st.k[u] = key < n ? ldg16(kbase + (int64_t)key * k_sr + c * 8) : u32x4{0, 0, 0, 0};
-  }
-  const int wave = tid >> 6, lane = tid & 63;
-  const int kq = lane % C::KQ;
-  const int dc = (64 / C::KQ) * wave + lane / C::KQ;
-#pragma unroll
-  for (int u = 0; u < C::KPT; ++u) {
-    const int key = key0 + C::KPT * kq + u;
-    st.v[u] = key < n ? ldg16(vbase + (int64_t)key * v_sr + dc * 8) : u32x4{0, 0, 0, 0};
-  }
+__device__ __forceinline__ int v_swz(int r, int c) {
+  return c ^ ((4 * (r & 3)) & (FwdCfg<D>::CPR - 1));
 }
 
+// Issue the async copies of key block [key0, key0 + BN) of K and V into one
+// LDS stage.  Wave w fills 1 KiB blocks [w * CPW, (w+1) * CPW) of each tile.
+// Rows past n are clamped to row n-1 (their scores are masked, so their
+// probabilities are zero).
 template <int D>
-__device__ __forceinline__ void store_tile(const Stage<D>& st, char* stage, int tid) {
+__device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase,
+                                           int64_t k_sr, int64_t v_sr, int key0, int n,
+                                           char* stage, int wave, int lane) {
   using C = FwdCfg<D>;
-  const int c = tid % C::CPR;
 #pragma unroll
-  for (int u = 0; u < C::KLOADS; ++u) {
-    const int r = tid / C::CPR + (256 / C::CPR) * u;
-    const int pos = perm_row_inv(r & 31) + (r & ~31);
-    sts16(stage + pos * C::KP + c * 16, st.k[u]);
-  }
-  char* vt = stage + C::KBYTES;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int kq = lane % C::KQ;
-  const int dc = (64 / C::KQ) * wave + lane / C::KQ;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int d = dc * 8 + i;
-    const int row = perm_row_inv(d & 31) + (d & ~31);
-    char* dst = vt + row * C::VP + C::KPT * kq * 2;
-    const int w = i >> 1;
-    if constexpr (C::KPT == 4) {
-      u32x2 val;
-      if (i & 1) {
-        val[0] = pick_hi(st.v[0][w], st.v[1][w]);
-        val[1] = pick_hi(st.v[2][w], st.v[3][w]);
-      } else {
-        val[0] = pick_lo(st.v[0][w], st.v[1][w]);
-        val[1] = pick_lo(st.v[2][w], st.v[3][w]);
-      }
-      sts8(dst, val);
-    } else {
-      const uint32_t val = (i & 1) ? pick_hi(st.v[0][w], st.v[1][w])
-                                   : pick_lo(st.v[0][w], st.v[1][w]);
-      sts4(dst, val);
-    }
+  for (int i = 0; i < C::CPW; ++i) {
+    const int blk = wave * C::CPW + i;           // 1 KiB block index within the tile
+    const int r = blk * C::RPI + lane / C::CPR;  // LDS row written by this lane
+    const int pc = lane % C::CPR;                // physical chunk written by this lane
+    const int kr = perm_row(r & 31) + (r & ~31);  // K: LDS row r holds tile key perm_row(r)
+    const int kkey = min(key0 + kr, n - 1);
+    const int vkey = min(key0 + r, n - 1);
+    g2lds16(kbase + (int64_t)kkey * k_sr + 8 * k_swz<D>(r, pc), stage + blk * 1024);
+    g2lds16(vbase + (int64_t)vkey * v_sr + 8 * v_swz<D>(r, pc), stage + C::TILE + blk * 1024);
   }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  constexpr int QT = C::QT;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
+  const int l16 = lane & 15, g16 = lane >> 4;
 
   const int nqb = (a.m + C::BM - 1) / C::BM;
   int id = blockIdx.x;
@@ -133,130 +104,183 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
 
-  const int q0 = qb * C::BM + wave * 32;
-  const int myq = q0 + lq;
+  const int q0 = qb * C::BM + wave * 32 * QT;  // first query of this wave
   const bool wave_live = q0 < a.m;
-
-  // Q^T fragments: lane holds Q[myq][16c + 8lg .. +7] for every chunk c.
-  u32x4 qf[C::DC];
+  int myq[QT];
 #pragma unroll
-  for (int c = 0; c < C::DC; ++c)
-    qf[c] = myq < a.m ? ldg16(qbase + (int64_t)myq * a.q_sr + 16 * c + 8 * lg)
-                      : u32x4{0, 0, 0, 0};
+  for (int qt = 0; qt < QT; ++qt) myq[qt] = q0 + 32 * qt + lq;
 
   const int kend = CAUSAL ? min(a.n, qb * C::BM + C::BM) : a.n;
   const int nkb = (kend + C::BN - 1) / C::BN;
+  issue_tile<D>(kbase, vbase, a.k_sr, a.v_sr, 0, a.n, smem, wave, lane);
 
-  f32x16 o[C::DT];
+  // Q^T fragments: lane holds Q[myq][16c + 8lg .. +7] for every chunk c.
+  u32x4 qf[QT][C::DC];
 #pragma unroll
-  for (int t = 0; t < C::DT; ++t)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int c = 0; c < C::DC; ++c)
+      qf[qt][c] = myq[qt] < a.m ? ldg16(qbase + (int64_t)myq[qt] * a.q_sr + 16 * c + 8 * lg)
+                                : u32x4{0, 0, 0, 0};
+
+  f32x16 o[QT][C::DT];
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qt][t][r] = 0.f;
+    m_run[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
   const float cs = a.scale_log2;
 
-  Stage<D> pre;
-  fetch_tile<D>(pre, kbase, vbase, a.k_sr, a.v_sr, 0, a.n, tid);
-  store_tile<D>(pre, smem, tid);
+  // Transposed V^T reads (ds_read_b64_tr_b16): this lane, as source lane
+  // s = l16 of its 16-lane group, addresses key row s/4 of a 4-key group and
+  // the 4 d columns starting at D_u = 16(u%2) + 8(g%2) + 4(u/2), u = s%4,
+  // which hands lane l the d column perm_row(l%32) of the 32-wide tile.
+  const int u = l16 & 3;
+  const int tr_d = 16 * (u & 1) + 8 * (g16 & 1) + 4 * (u >> 1);  // + 32 t
+  const int tr_row = l16 >> 2;
+
+  wait_vmem();
   __syncthreads();
 
   for (int kb = 0; kb < nkb; ++kb) {
     const bool more = kb + 1 < nkb;
-    if (more) fetch_tile<D>(pre, kbase, vbase, a.k_sr, a.v_sr, (kb + 1) * C::BN, a.n, tid);
+    if (more)
+      issue_tile<D>(kbase, vbase, a.k_sr, a.v_sr, (kb + 1) * C::BN, a.n,
+                    smem + ((kb + 1) & 1) * C::STAGE, wave, lane);
 
     const int key0 = kb * C::BN;
     const char* kbuf = smem + (kb & 1) * C::STAGE;
-    const char* vbuf = kbuf + C::KBYTES;
-    const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 31);
+    const char* vbuf = kbuf + C::TILE;
+    const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 32 * QT - 1);
     if (wave_work) {
-      f32x16 s[2];
+      // S^T tiles: [query tile][32-key sub-block]
+      f32x16 s[QT][2];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[qt][sb][r] = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
+        const int row = 32 * sb + lq;
+        const char* krow = kbuf + row * C::RB;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-        const char* krow = kbuf + (32 * sb + lq) * C::KP + lg * 16;
+        for (int c = 0; c < C::DC; ++c) {
+          const u32x4 kf = lds16(krow + 16 * k_swz<D>(row, 2 * c + lg));
 #pragma unroll
-        for (int c = 0; c < C::DC; ++c) s[sb] = mfma32(lds16(krow + c * 32), qf[c], s[sb]);
+          for (int qt = 0; qt < QT; ++qt) s[qt][sb] = mfma32(kf, qf[qt][c], s[qt][sb]);
+        }
       }
       const bool need_mask = (CAUSAL && key0 + C::BN - 1 > q0) || (key0 + C::BN > a.n);
       if (need_mask) {
 #pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = key0 + 32 * sb + 16 * lg + r;
+              if ((CAUSAL && key > myq[qt]) || key >= a.n) s[qt][sb][r] = -INFINITY;
+            }
+      }
+      u32x4 pb[QT][2][2];
+      bool rescale = false;
+      float alpha[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        float mx = -INFINITY;
+#pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qt][sb][r]);
+        mx = fmaxf(mx, wave_xor32(mx)) * cs;
+        // move the reference maximum only when p would otherwise exceed 2^8
+        const float m_new = mx > m_run[qt] + 8.f ? mx : m_run[qt];
+        alpha[qt] = fast_exp2(m_run[qt] - m_new);
+        rescale |= m_new != m_run[qt];
+        float lsum = 0.f;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          float p[16];
+#pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * sb + 16 * lg + r;
-            if ((CAUSAL && key > myq) || key >= a.n) s[sb][r] = -INFINITY;
+            p[r] = fast_exp2(s[qt][sb][r] * cs - m_new);
+            lsum += p[r];
           }
-      }
-      float mx = -INFINITY;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+          for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m_run, mx * cs);
-      const float alpha = fast_exp2(m_run - m_new);
-      float lsum = 0.f;
-      u32x4 pb[2][2];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(s[sb][r] * cs - m_new);
-          lsum += p[r];
+            for (int w = 0; w < 4; ++w)
+              pb[qt][sb][c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
         }
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) pb[sb][c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
+        l_run[qt] = l_run[qt] * alpha[qt] + lsum;
+        m_run[qt] = m_new;
       }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      if (__ballot(alpha != 1.f)) {
+      if (__ballot(rescale)) {
 #pragma unroll
-        for (int t = 0; t < C::DT; ++t)
+        for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+          for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qt][t][r] *= alpha[qt];
       }
 #pragma unroll
       for (int t = 0; t < C::DT; ++t) {
-        const char* vrow = vbuf + (32 * t + lq) * C::VP + lg * 32;
+        const int dcol = 32 * t + tr_d;    // first of the 4 d columns this lane addresses
+        const int cbyte = 2 * (dcol & 7);  // byte offset inside its 16-byte chunk
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int c = 0; c < 2; ++c) o[t] = mfma32(lds16(vrow + (32 * sb + 8 * c) * 2), pb[sb][c], o[t]);
+          for (int c = 0; c < 2; ++c) {
+            // keys 32 sb + 16 lg + 8 c + e, e = 0..7, read as two 4-key groups
+            const int r0 = 32 * sb + 16 * (g16 >> 1) + 8 * c + tr_row;
+            const int r1 = r0 + 4;
+            const u32x2 lo = lds_tr8(vbuf + r0 * C::RB + 16 * v_swz<D>(r0, dcol >> 3) + cbyte);
+            const u32x2 hi = lds_tr8(vbuf + r1 * C::RB + 16 * v_swz<D>(r1, dcol >> 3) + cbyte);
+            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) o[qt][t] = mfma32(vf, pb[qt][sb][c], o[qt][t]);
+          }
       }
     }
-    if (more) store_tile<D>(pre, smem + ((kb + 1) & 1) * C::STAGE, tid);
+    wait_vmem();
     __syncthreads();
   }
 
   if (!wave_live) return;
-  const float l_tot = l_run + wave_xor32(l_run);
-  if (myq < a.m) {
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = static_cast<uint16_t*>(a.o_out) + bi * a.o_sb + h * a.o_sh +
-                     (int64_t)myq * a.o_sr + 16 * lg;
 #pragma unroll
-    for (int t = 0; t < C::DT; ++t) {
-      u32x4 lo, hi;
+  for (int qt = 0; qt < QT; ++qt) {
+    const float l_tot = l_run[qt] + wave_xor32(l_run[qt]);
+    if (myq[qt] < a.m) {
+      const float inv = 1.f / l_tot;
+      uint16_t* orow = static_cast<uint16_t*>(a.o_out) + bi * a.o_sb + h * a.o_sh +
+                       (int64_t)myq[qt] * a.o_sr + 16 * lg;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        lo[w] = pack_bf16(o[t][2 * w] * inv, o[t][2 * w + 1] * inv);
-        hi[w] = pack_bf16(o[t][8 + 2 * w] * inv, o[t][8 + 2 * w + 1] * inv);
+      for (int t = 0; t < C::DT; ++t) {
+        u32x4 lo, hi;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          lo[w] = pack_bf16(o[qt][t][2 * w] * inv, o[qt][t][2 * w + 1] * inv);
+          hi[w] = pack_bf16(o[qt][t][8 + 2 * w] * inv, o[qt][t][8 + 2 * w + 1] * inv);
+        }
+        stg16(orow + 32 * t, lo);
+        stg16(orow + 32 * t + 8, hi);
       }
-      stg16(orow + 32 * t, lo);
-      stg16(orow + 32 * t + 8, hi);
+      if (lg == 0)
+        a.lse[((int64_t)bi * a.hq + h) * a.m + myq[qt]] = (m_run[qt] + fast_log2(l_tot)) * kLn2;
     }
-    if (lg == 0)
-      a.lse[((int64_t)bi * a.hq + h) * a.m + myq] = (m_run + fast_log2(l_tot)) * kLn2;
   }
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
-  const int nqb = (a.m + kAttnFwdBM - 1) / kAttnFwdBM;
+  const int nqb = (a.m + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
   const dim3 grid((unsigned)nqb * a.hq * a.b), block(256);
   if (a.causal)
     FAB_TIMED("attn_fwd_bf16", s, hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), grid, block, 0, s, a));

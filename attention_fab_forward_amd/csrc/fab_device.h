@@ -76,6 +76,29 @@ __device__ __forceinline__ void sts4(char* p, uint32_t v) {
   *reinterpret_cast<uint32_t*>(p) = v;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element j = element (i % 4) of the 8-byte value
+// addressed by lane 4 j + i / 4 of the same group.
+__device__ __forceinline__ u32x2 lds_tr8(const char* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane i of
+// the wave writes LDS bytes [lds_base + 16 i, lds_base + 16 i + 16).  lds_base
+// must be wave-uniform.  Completion is tracked by the vector-memory counter.
+__device__ __forceinline__ void g2lds16(const void* gsrc, char* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_base), 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) with the export and LDS counters left unconstrained
+// (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 __device__ __forceinline__ float wave_xor32(float v) {
   return __shfl_xor(v, 32, 64);
 }

@@ -68,7 +68,11 @@ void timer_end(hipStream_t s);
   } while (0)
 
 // Forward attention tile shapes (bf16 MFMA path).
-constexpr int kAttnFwdBM = 128;   // queries per workgroup (4 waves x 32)
+#ifndef FAB_FWD_QT
+#define FAB_FWD_QT 2
+#endif
+constexpr int kAttnFwdQT = FAB_FWD_QT;      // 32-query MFMA tiles per wave
+constexpr int kAttnFwdBM = 128 * kAttnFwdQT;  // queries per workgroup (4 waves)
 constexpr int kAttnFwdBN = 64;    // keys per inner step
 constexpr int kAttnBwdBM = 128;   // dQ kernel: queries per workgroup
 constexpr int kAttnBwdKB = 128;   // dK/dV kernel: keys per workgroup (4 waves x 32)
