@@ -25,173 +25,113 @@ namespace {
 
 template <int D>
 struct BwdCfg {
-  static constexpr int CPR = D / 8;         // 16-byte chunks per row
-  static constexpr int NP = D * 2 + 16;     // natural tile row pitch (bytes)
-  static constexpr int TILE = 64;           // rows of a streamed tile
-  static constexpr int TP = TILE * 2 + 16;  // transposed tile row pitch (bytes)
-  static constexpr int NBYTES = TILE * NP;
-  static constexpr int TBYTES = D * TP;
-  static constexpr int RPT = TILE * CPR / 256;  // rows per thread (transposing staging)
-  static constexpr int RQ = TILE / RPT;         // row groups in transposing staging
-  static constexpr int NLOADS = TILE * CPR / 256;
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int RB = D * 2;           // row bytes (no padding)
+  static constexpr int TILE = 64;            // rows of a streamed tile
+  static constexpr int TBYTES = TILE * RB;   // bytes of one tile
+  static constexpr int RPI = 1024 / RB;      // rows per 1 KiB async copy
+  static constexpr int CPW = TBYTES / 1024 / 4;  // async copies per wave per tile
   static constexpr int DT = D / 32;
   static constexpr int DC = D / 16;
 };
 
-// Rows [r0, r0 + 64) of a [rows, D] bf16 matrix, loaded so that each thread
-// holds RPT consecutive rows of one 16-byte column chunk (ready for both a
-// natural and a transposed LDS write).  Rows >= nrows read as zero.
+// Streamed 64-row tiles live in LDS with tile row x at LDS row
+// perm_row_inv(x % 32) + 32 (x / 32) (so MFMA row r of a 32-row group reads
+// tile row perm_row(r)), and logical 16-byte chunk c of LDS row r at physical
+// chunk c ^ (r % CPR).
 template <int D>
-struct TTile {
-  u32x4 v[BwdCfg<D>::RPT];
-};
+__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & (BwdCfg<D>::CPR - 1)); }
+__device__ __forceinline__ int lds_row_of(int x) { return perm_row_inv(x & 31) + (x & ~31); }
 
+// Async copy of rows [r0, r0 + 64) of a [rows, D] matrix (row stride sr) into
+// a tile as above; rows at or past nrows are clamped to nrows - 1 (callers
+// mask them).
 template <int D>
-__device__ __forceinline__ void ttile_fetch(TTile<D>& t, const uint16_t* base, int64_t sr,
-                                            int r0, int nrows, int tid) {
+__device__ __forceinline__ void issue_tile(const uint16_t* base, int64_t sr, int r0, int nrows,
+                                           char* dst, int wave, int lane) {
   using C = BwdCfg<D>;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int rq = lane % C::RQ;
-  const int dc = (64 / C::RQ) * wave + lane / C::RQ;
 #pragma unroll
-  for (int u = 0; u < C::RPT; ++u) {
-    const int r = r0 + C::RPT * rq + u;
-    t.v[u] = r < nrows ? ldg16(base + (int64_t)r * sr + dc * 8) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < C::CPW; ++i) {
+    const int blk = wave * C::CPW + i;
+    const int r = blk * C::RPI + lane / C::CPR;  // LDS row this lane writes
+    const int pc = lane % C::CPR;                // physical chunk this lane writes
+    const int x = perm_row(r & 31) + (r & ~31);  // tile row held by LDS row r
+    const int row = min(r0 + x, nrows - 1);
+    g2lds16(base + (int64_t)row * sr + 8 * swz<D>(r, pc), dst + blk * 1024);
   }
 }
 
-// Natural layout: LDS row perm_row_inv(r) holds tile row r (per 32-row group).
+// MFMA operand with rows = tile rows (32 sb + perm_row(l % 32)) and k = the
+// 16 columns 16 c .. 16 c + 15 (this lane: columns 16 c + 8 (l / 32) + 0..7).
 template <int D>
-__device__ __forceinline__ void ttile_store_natural(const TTile<D>& t, char* dst, int tid) {
-  using C = BwdCfg<D>;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int rq = lane % C::RQ;
-  const int dc = (64 / C::RQ) * wave + lane / C::RQ;
-#pragma unroll
-  for (int u = 0; u < C::RPT; ++u) {
-    const int r = C::RPT * rq + u;
-    const int pos = perm_row_inv(r & 31) + (r & ~31);
-    sts16(dst + pos * C::NP + dc * 16, t.v[u]);
-  }
+__device__ __forceinline__ u32x4 read_nat(const char* tile, int sb, int c, int lq, int lg) {
+  const int r = 32 * sb + lq;
+  return lds16(tile + r * BwdCfg<D>::RB + 16 * swz<D>(r, 2 * c + lg));
 }
 
-// Transposed layout: LDS row (perm order of d) holds the 64 tile rows of one
-// column d, contiguous.
+// Transposed MFMA operand: rows = columns d = 32 t + perm_row(l % 32), k = tile
+// rows 32 sb + 16 (l / 32) + 8 c + e, e = 0..7, read with ds_read_b64_tr_b16
+// (within a 16-lane group, lane i gets element i % 4 of the 8 bytes that lane
+// 4 j + i / 4 addresses, for j = 0..3).  tr_d / tr_row: this lane's column
+// offset D_u = 16 (u%2) + 8 (g%2) + 4 (u/2), u = (l%16) % 4, and row (l%16)/4.
 template <int D>
-__device__ __forceinline__ void ttile_store_transposed(const TTile<D>& t, char* dst, int tid) {
+__device__ __forceinline__ u32x4 read_tr(const char* tile, int t, int sb, int c, int lg,
+                                         int tr_d, int tr_row) {
   using C = BwdCfg<D>;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int rq = lane % C::RQ;
-  const int dc = (64 / C::RQ) * wave + lane / C::RQ;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int d = dc * 8 + i;
-    const int row = perm_row_inv(d & 31) + (d & ~31);
-    char* p = dst + row * C::TP + C::RPT * rq * 2;
-    const int w = i >> 1;
-    if constexpr (C::RPT == 4) {
-      u32x2 val;
-      if (i & 1) {
-        val[0] = pick_hi(t.v[0][w], t.v[1][w]);
-        val[1] = pick_hi(t.v[2][w], t.v[3][w]);
-      } else {
-        val[0] = pick_lo(t.v[0][w], t.v[1][w]);
-        val[1] = pick_lo(t.v[2][w], t.v[3][w]);
-      }
-      sts8(p, val);
-    } else {
-      sts4(p, (i & 1) ? pick_hi(t.v[0][w], t.v[1][w]) : pick_lo(t.v[0][w], t.v[1][w]));
-    }
-  }
+  const int dcol = 32 * t + tr_d;
+  const int cbyte = 2 * (dcol & 7);
+  const int x0 = 32 * sb + 16 * lg + 8 * c + tr_row;
+  const int r0 = lds_row_of(x0), r1 = lds_row_of(x0 + 4);
+  const u32x2 lo = lds_tr8(tile + r0 * C::RB + 16 * swz<D>(r0, dcol >> 3) + cbyte);
+  const u32x2 hi = lds_tr8(tile + r1 * C::RB + 16 * swz<D>(r1, dcol >> 3) + cbyte);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// Plain natural tile: thread t loads chunk t % CPR of rows t / CPR + k*(256/CPR).
-template <int D>
-struct NTile {
-  u32x4 v[BwdCfg<D>::NLOADS];
-};
-
-template <int D>
-__device__ __forceinline__ void ntile_fetch(NTile<D>& t, const uint16_t* base, int64_t sr,
-                                            int r0, int nrows, int tid) {
-  using C = BwdCfg<D>;
-  const int c = tid % C::CPR;
-#pragma unroll
-  for (int u = 0; u < C::NLOADS; ++u) {
-    const int r = r0 + tid / C::CPR + (256 / C::CPR) * u;
-    t.v[u] = r < nrows ? ldg16(base + (int64_t)r * sr + c * 8) : u32x4{0, 0, 0, 0};
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void ntile_store(const NTile<D>& t, char* dst, int tid) {
-  using C = BwdCfg<D>;
-  const int c = tid % C::CPR;
-#pragma unroll
-  for (int u = 0; u < C::NLOADS; ++u) {
-    const int r = tid / C::CPR + (256 / C::CPR) * u;
-    const int pos = perm_row_inv(r & 31) + (r & ~31);
-    sts16(dst + pos * C::NP + c * 16, t.v[u]);
-  }
+// 64 consecutive fp32 values (clamped at `count`) into LDS, one wave.
+__device__ __forceinline__ void issue_vec64(const float* src, int i0, int count, char* dst,
+                                            int lane) {
+  const int i = min(i0 + lane, count - 1);
+  __builtin_amdgcn_global_load_lds(src + i, (lds_void*)dst, 4, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV
+// dK, dV: workgroup = 128 keys (4 waves x 32) of one kv head; query blocks of
+// 64 (all query heads of the group) stream through two LDS stages.
 // ---------------------------------------------------------------------------
 template <int D>
 struct DkdvStage {
   static constexpr int Q = 0;
-  static constexpr int DO = BwdCfg<D>::NBYTES;
-  static constexpr int QT = 2 * BwdCfg<D>::NBYTES;
-  static constexpr int DOT = QT + BwdCfg<D>::TBYTES;
-  static constexpr int LSE = DOT + BwdCfg<D>::TBYTES;
-  static constexpr int DLT = LSE + 64 * 4;
-  static constexpr int BYTES = DLT + 64 * 4;
+  static constexpr int DO = BwdCfg<D>::TBYTES;
+  static constexpr int LSE = 2 * BwdCfg<D>::TBYTES;
+  static constexpr int DLT = LSE + 256;
+  static constexpr int BYTES = DLT + 256;
 };
 
 template <int D>
-struct DkdvPrefetch {
-  TTile<D> q, dout;
-  float lse2, dlt;
-};
-
-template <int D>
-__device__ __forceinline__ void dkdv_fetch(DkdvPrefetch<D>& pf, const AttnArgs& a, int bi, int h,
-                                           int q0, int tid) {
+__device__ __forceinline__ void dkdv_issue(const AttnArgs& a, int bi, int h, int q0, char* st,
+                                           int wave, int lane) {
+  using S = DkdvStage<D>;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const uint16_t* ob = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
-  ttile_fetch<D>(pf.q, qb, a.q_sr, q0, a.m, tid);
-  ttile_fetch<D>(pf.dout, ob, a.o_sr, q0, a.m, tid);
-  if (tid < 64) {
-    const int q = q0 + tid;
-    const int64_t r = ((int64_t)bi * a.hq + h) * a.m + q;
-    pf.lse2 = q < a.m ? a.lse_in[r] * kLog2e : INFINITY;
-    pf.dlt = q < a.m ? a.delta[r] : 0.f;
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void dkdv_store(const DkdvPrefetch<D>& pf, char* st, int tid) {
-  using S = DkdvStage<D>;
-  ttile_store_natural<D>(pf.q, st + S::Q, tid);
-  ttile_store_natural<D>(pf.dout, st + S::DO, tid);
-  ttile_store_transposed<D>(pf.q, st + S::QT, tid);
-  ttile_store_transposed<D>(pf.dout, st + S::DOT, tid);
-  if (tid < 64) {
-    reinterpret_cast<float*>(st + S::LSE)[tid] = pf.lse2;
-    reinterpret_cast<float*>(st + S::DLT)[tid] = pf.dlt;
-  }
+  issue_tile<D>(qb, a.q_sr, q0, a.m, st + S::Q, wave, lane);
+  issue_tile<D>(ob, a.o_sr, q0, a.m, st + S::DO, wave, lane);
+  const int64_t r = ((int64_t)bi * a.hq + h) * a.m;
+  if (wave == 0) issue_vec64(a.lse_in + r, q0, a.m, st + S::LSE, lane);
+  if (wave == 1) issue_vec64(a.delta + r, q0, a.m, st + S::DLT, lane);
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using S = DkdvStage<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * S::BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
+  const int l16 = lane & 15, g16 = lane >> 4;
+  const int tr_d = 16 * (l16 & 1) + 8 * (g16 & 1) + 4 * ((l16 >> 1) & 1);
+  const int tr_row = l16 >> 2;
 
   int id = blockIdx.x;
   const int g = id % a.hkv;
@@ -201,6 +141,14 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const int kblk = id;  // causal: low key blocks see the most queries, so they go first
   const int k0w = kblk * kAttnBwdKB + wave * 32;
   const int mykey = k0w + lq;
+
+  const float cs = a.scale_log2;
+  const int qb_first = CAUSAL ? (kblk * kAttnBwdKB) / C::TILE : 0;
+  const int nqb = (a.m + C::TILE - 1) / C::TILE;
+  const int steps_per_head = nqb - qb_first;
+  const int steps = steps_per_head * a.group;
+  const bool wave_live = k0w < a.n;
+  if (steps > 0) dkdv_issue<D>(a, bi, g * a.group, qb_first * C::TILE, smem, wave, lane);
 
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
@@ -216,53 +164,42 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   for (int t = 0; t < C::DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
-
-  const float cs = a.scale_log2;
-  const int qb_first = CAUSAL ? (kblk * kAttnBwdKB) / C::TILE : 0;
-  const int nqb = (a.m + C::TILE - 1) / C::TILE;
-  const int steps_per_head = nqb - qb_first;
-  const int steps = steps_per_head * a.group;
-  const bool wave_live = k0w < a.n;
-
-  DkdvPrefetch<D> pf;
-  if (steps > 0) {
-    dkdv_fetch<D>(pf, a, bi, g * a.group, qb_first * C::TILE, tid);
-    dkdv_store<D>(pf, smem, tid);
-  }
+  wait_vmem();
   __syncthreads();
 
   for (int step = 0; step < steps; ++step) {
-    const bool more = step + 1 < steps;
-    if (more) {
+    if (step + 1 < steps) {
       const int nh = (step + 1) / steps_per_head, nq = (step + 1) % steps_per_head;
-      dkdv_fetch<D>(pf, a, bi, g * a.group + nh, (qb_first + nq) * C::TILE, tid);
+      dkdv_issue<D>(a, bi, g * a.group + nh, (qb_first + nq) * C::TILE,
+                    smem + ((step + 1) & 1) * S::BYTES, wave, lane);
     }
     const int q0 = (qb_first + step % steps_per_head) * C::TILE;
     const char* st = smem + (step & 1) * S::BYTES;
     // A wave skips a query block when every query precedes all its keys.
     const bool wave_work = wave_live && (!CAUSAL || q0 + C::TILE - 1 >= k0w);
     if (wave_work) {
-      const bool need_mask = CAUSAL && q0 < k0w + 31;
+      const bool need_mask = (CAUSAL && q0 < k0w + 31) || q0 + C::TILE > a.m;
 #pragma unroll
       for (int sq = 0; sq < 2; ++sq) {
         f32x16 s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-        const char* qrow = st + S::Q + (32 * sq + lq) * C::NP + lg * 16;
-        const char* orow = st + S::DO + (32 * sq + lq) * C::NP + lg * 16;
 #pragma unroll
         for (int c = 0; c < C::DC; ++c) {
-          s = mfma32(lds16(qrow + c * 32), kf[c], s);
-          dp = mfma32(lds16(orow + c * 32), vf[c], dp);
+          s = mfma32(read_nat<D>(st + S::Q, sq, c, lq, lg), kf[c], s);
+          dp = mfma32(read_nat<D>(st + S::DO, sq, c, lq, lg), vf[c], dp);
         }
         // accumulator slot r holds query q0 + 32 sq + 16 lg + r for key `mykey`
-        const float* lse2 = reinterpret_cast<const float*>(st + S::LSE) + 32 * sq + 16 * lg;
+        const float* lse = reinterpret_cast<const float*>(st + S::LSE) + 32 * sq + 16 * lg;
         const float* dlt = reinterpret_cast<const float*>(st + S::DLT) + 32 * sq + 16 * lg;
         float p[16], ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(s[r] * cs - lse2[r]);
-          if (need_mask && q0 + 32 * sq + 16 * lg + r < mykey) pr = 0.f;
+          float pr = fast_exp2(s[r] * cs - lse[r] * kLog2e);
+          if (need_mask) {
+            const int q = q0 + 32 * sq + 16 * lg + r;
+            if ((CAUSAL && q < mykey) || q >= a.m) pr = 0.f;
+          }
           p[r] = pr;
           ds[r] = pr * (dp[r] - dlt[r]);
         }
@@ -275,18 +212,15 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
             db[c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
           }
 #pragma unroll
-        for (int t = 0; t < C::DT; ++t) {
-          const char* trow_o = st + S::DOT + (32 * t + lq) * C::TP + lg * 32 + 64 * sq;
-          const char* trow_q = st + S::QT + (32 * t + lq) * C::TP + lg * 32 + 64 * sq;
+        for (int t = 0; t < C::DT; ++t)
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
-            dv[t] = mfma32(lds16(trow_o + 16 * c), pb[c], dv[t]);
-            dk[t] = mfma32(lds16(trow_q + 16 * c), db[c], dk[t]);
+            dv[t] = mfma32(read_tr<D>(st + S::DO, t, sq, c, lg, tr_d, tr_row), pb[c], dv[t]);
+            dk[t] = mfma32(read_tr<D>(st + S::Q, t, sq, c, lg, tr_d, tr_row), db[c], dk[t]);
           }
-        }
       }
     }
-    if (more) dkdv_store<D>(pf, smem + ((step + 1) & 1) * S::BYTES, tid);
+    wait_vmem();
     __syncthreads();
   }
 
@@ -313,27 +247,31 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ
+// dQ: workgroup = 4 waves x 32 QT queries of one query head; key blocks of 64
+// stream through two LDS stages (K and V tiles; K^T is read transposed).
 // ---------------------------------------------------------------------------
 template <int D>
 struct DqStage {
   static constexpr int K = 0;
-  static constexpr int V = BwdCfg<D>::NBYTES;
-  static constexpr int KT = 2 * BwdCfg<D>::NBYTES;
-  static constexpr int BYTES = KT + BwdCfg<D>::TBYTES;
+  static constexpr int V = BwdCfg<D>::TBYTES;
+  static constexpr int BYTES = 2 * BwdCfg<D>::TBYTES;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(AttnArgs a) {
+template <int D, bool CAUSAL, int QT>
+__global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using S = DqStage<D>;
-  __shared__ __attribute__((aligned(16))) char smem[S::BYTES];
+  constexpr int BM = 128 * QT;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * S::BYTES];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
+  const int l16 = lane & 15, g16 = lane >> 4;
+  const int tr_d = 16 * (l16 & 1) + 8 * (g16 & 1) + 4 * ((l16 >> 1) & 1);
+  const int tr_row = l16 >> 2;
 
-  const int nqb = (a.m + kAttnBwdBM - 1) / kAttnBwdBM;
+  const int nqb = (a.m + BM - 1) / BM;
   int id = blockIdx.x;
   const int h = id % a.hq;
   id /= a.hq;
@@ -342,105 +280,123 @@ __global__ __launch_bounds__(256, 2) void attn_dq_bf16_kernel(AttnArgs a) {
   const int qb = CAUSAL ? (nqb - 1 - id) : id;
   const int g = h / a.group;
 
-  const int q0 = qb * kAttnBwdBM + wave * 32;
-  const int myq = q0 + lq;
-  const bool live = myq < a.m;
+  const int q0 = qb * BM + wave * 32 * QT;
   const bool wave_live = q0 < a.m;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
+  const int kend = CAUSAL ? min(a.n, qb * BM + BM) : a.n;
+  const int nkb = (kend + C::TILE - 1) / C::TILE;
+  issue_tile<D>(kbase, a.k_sr, 0, a.n, smem + S::K, wave, lane);
+  issue_tile<D>(vbase, a.v_sr, 0, a.n, smem + S::V, wave, lane);
 
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const uint16_t* obase = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
-
-  u32x4 qf[C::DC], df[C::DC];
+  int myq[QT];
+  u32x4 qf[QT][C::DC], df[QT][C::DC];
+  float lse2[QT], dlt[QT];
 #pragma unroll
-  for (int c = 0; c < C::DC; ++c) {
-    qf[c] = live ? ldg16(qbase + (int64_t)myq * a.q_sr + 16 * c + 8 * lg) : u32x4{0, 0, 0, 0};
-    df[c] = live ? ldg16(obase + (int64_t)myq * a.o_sr + 16 * c + 8 * lg) : u32x4{0, 0, 0, 0};
+  for (int qt = 0; qt < QT; ++qt) {
+    myq[qt] = q0 + 32 * qt + lq;
+    const bool live = myq[qt] < a.m;
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) {
+      qf[qt][c] = live ? ldg16(qbase + (int64_t)myq[qt] * a.q_sr + 16 * c + 8 * lg)
+                       : u32x4{0, 0, 0, 0};
+      df[qt][c] = live ? ldg16(obase + (int64_t)myq[qt] * a.o_sr + 16 * c + 8 * lg)
+                       : u32x4{0, 0, 0, 0};
+    }
+    const int64_t ridx = ((int64_t)bi * a.hq + h) * a.m + myq[qt];
+    lse2[qt] = live ? a.lse_in[ridx] * kLog2e : INFINITY;
+    dlt[qt] = live ? a.delta[ridx] : 0.f;
   }
-  const int64_t ridx = ((int64_t)bi * a.hq + h) * a.m + myq;
-  const float lse2 = live ? a.lse_in[ridx] * kLog2e : INFINITY;
-  const float dlt = live ? a.delta[ridx] : 0.f;
-
-  f32x16 dq[C::DT];
+  f32x16 dq[QT][C::DT];
 #pragma unroll
-  for (int t = 0; t < C::DT; ++t)
+  for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dq[t][r] = 0.f;
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[qt][t][r] = 0.f;
   const float cs = a.scale_log2;
-
-  const int kend = CAUSAL ? min(a.n, qb * kAttnBwdBM + kAttnBwdBM) : a.n;
-  const int nkb = (kend + C::TILE - 1) / C::TILE;
-
-  TTile<D> kpre;
-  NTile<D> vpre;
-  ttile_fetch<D>(kpre, kbase, a.k_sr, 0, a.n, tid);
-  ntile_fetch<D>(vpre, vbase, a.v_sr, 0, a.n, tid);
+  wait_vmem();
+  __syncthreads();
 
   for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    ttile_store_natural<D>(kpre, smem + S::K, tid);
-    ttile_store_transposed<D>(kpre, smem + S::KT, tid);
-    ntile_store<D>(vpre, smem + S::V, tid);
-    __syncthreads();
     if (kb + 1 < nkb) {
-      ttile_fetch<D>(kpre, kbase, a.k_sr, (kb + 1) * C::TILE, a.n, tid);
-      ntile_fetch<D>(vpre, vbase, a.v_sr, (kb + 1) * C::TILE, a.n, tid);
+      char* nst = smem + ((kb + 1) & 1) * S::BYTES;
+      issue_tile<D>(kbase, a.k_sr, (kb + 1) * C::TILE, a.n, nst + S::K, wave, lane);
+      issue_tile<D>(vbase, a.v_sr, (kb + 1) * C::TILE, a.n, nst + S::V, wave, lane);
     }
+    const char* st = smem + (kb & 1) * S::BYTES;
     const int key0 = kb * C::TILE;
-    const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 31);
-    if (!wave_work) continue;
-    const bool need_mask = (CAUSAL && key0 + C::TILE - 1 > q0) || (key0 + C::TILE > a.n);
+    const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 32 * QT - 1);
+    if (wave_work) {
+      const bool need_mask = (CAUSAL && key0 + C::TILE - 1 > q0) || (key0 + C::TILE > a.n);
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      f32x16 s, dp;
+      for (int sb = 0; sb < 2; ++sb) {
+        f32x16 s[QT], dp[QT];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-      const char* krow = smem + S::K + (32 * sb + lq) * C::NP + lg * 16;
-      const char* vrow = smem + S::V + (32 * sb + lq) * C::NP + lg * 16;
+        for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int c = 0; c < C::DC; ++c) {
-        s = mfma32(lds16(krow + c * 32), qf[c], s);
-        dp = mfma32(lds16(vrow + c * 32), df[c], dp);
-      }
-      // accumulator slot r holds key key0 + 32 sb + 16 lg + r for query `myq`
-      float ds[16];
+          for (int r = 0; r < 16; ++r) s[qt][r] = dp[qt][r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(s[r] * cs - lse2);
-        if (need_mask) {
-          const int key = key0 + 32 * sb + 16 * lg + r;
-          if ((CAUSAL && key > myq) || key >= a.n) p = 0.f;
+        for (int c = 0; c < C::DC; ++c) {
+          const u32x4 kfr = read_nat<D>(st + S::K, sb, c, lq, lg);
+          const u32x4 vfr = read_nat<D>(st + S::V, sb, c, lq, lg);
+#pragma unroll
+          for (int qt = 0; qt < QT; ++qt) {
+            s[qt] = mfma32(kfr, qf[qt][c], s[qt]);
+            dp[qt] = mfma32(vfr, df[qt][c], dp[qt]);
+          }
         }
-        ds[r] = p * (dp[r] - dlt);
-      }
-      u32x4 db[2];
+        // accumulator slot r holds key key0 + 32 sb + 16 lg + r for query myq[qt]
+        u32x4 db[QT][2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int qt = 0; qt < QT; ++qt) {
+          float ds[16];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) db[c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
+          for (int r = 0; r < 16; ++r) {
+            float p = fast_exp2(s[qt][r] * cs - lse2[qt]);
+            if (need_mask) {
+              const int key = key0 + 32 * sb + 16 * lg + r;
+              if ((CAUSAL && key > myq[qt]) || key >= a.n) p = 0.f;
+            }
+            ds[r] = p * (dp[qt][r] - dlt[qt]);
+          }
 #pragma unroll
-      for (int t = 0; t < C::DT; ++t) {
-        const char* trow = smem + S::KT + (32 * t + lq) * C::TP + lg * 32 + 64 * sb;
+          for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) dq[t] = mfma32(lds16(trow + 16 * c), db[c], dq[t]);
+            for (int w = 0; w < 4; ++w) db[qt][c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
+        }
+#pragma unroll
+        for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const u32x4 kt = read_tr<D>(st + S::K, t, sb, c, lg, tr_d, tr_row);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) dq[qt][t] = mfma32(kt, db[qt][c], dq[qt][t]);
+          }
       }
     }
+    wait_vmem();
+    __syncthreads();
   }
 
-  if (!live) return;
-  uint16_t* out = static_cast<uint16_t*>(a.dq) + bi * a.q_sb + h * a.q_sh +
-                  (int64_t)myq * a.q_sr + 16 * lg;
 #pragma unroll
-  for (int t = 0; t < C::DT; ++t) {
-    u32x4 lo, hi;
+  for (int qt = 0; qt < QT; ++qt) {
+    if (myq[qt] >= a.m) continue;
+    uint16_t* out = static_cast<uint16_t*>(a.dq) + bi * a.q_sb + h * a.q_sh +
+                    (int64_t)myq[qt] * a.q_sr + 16 * lg;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      lo[w] = pack_bf16(dq[t][2 * w] * a.scale, dq[t][2 * w + 1] * a.scale);
-      hi[w] = pack_bf16(dq[t][8 + 2 * w] * a.scale, dq[t][8 + 2 * w + 1] * a.scale);
+    for (int t = 0; t < C::DT; ++t) {
+      u32x4 lo, hi;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        lo[w] = pack_bf16(dq[qt][t][2 * w] * a.scale, dq[qt][t][2 * w + 1] * a.scale);
+        hi[w] = pack_bf16(dq[qt][t][8 + 2 * w] * a.scale, dq[qt][t][8 + 2 * w + 1] * a.scale);
+      }
+      stg16(out + 32 * t, lo);
+      stg16(out + 32 * t + 8, hi);
     }
-    stg16(out + 32 * t, lo);
-    stg16(out + 32 * t + 8, hi);
   }
 }
 
@@ -449,15 +405,16 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   hipError_t e = launch_attn_delta(a, D, true, s);
   if (e != hipSuccess) return e;
   const dim3 block(256);
+  constexpr int QT = kAttnBwdQT;
   const int nkb = (a.n + kAttnBwdKB - 1) / kAttnBwdKB;
-  const int nqb = (a.m + kAttnBwdBM - 1) / kAttnBwdBM;
+  const int nqb = (a.m + 128 * QT - 1) / (128 * QT);
   const dim3 gk((unsigned)nkb * a.hkv * a.b), gq((unsigned)nqb * a.hq * a.b);
   if (a.causal) {
     FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, true>), gk, block, 0, s, a));
-    FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, true>), gq, block, 0, s, a));
+    FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, true, QT>), gq, block, 0, s, a));
   } else {
     FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, false>), gk, block, 0, s, a));
-    FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, false>), gq, block, 0, s, a));
+    FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, false, QT>), gq, block, 0, s, a));
   }
   return hipGetLastError();
 }

@@ -74,7 +74,11 @@ void timer_end(hipStream_t s);
 constexpr int kAttnFwdQT = FAB_FWD_QT;      // 32-query MFMA tiles per wave
 constexpr int kAttnFwdBM = 128 * kAttnFwdQT;  // queries per workgroup (4 waves)
 constexpr int kAttnFwdBN = 64;    // keys per inner step
-constexpr int kAttnBwdBM = 128;   // dQ kernel: queries per workgroup
+#ifndef FAB_BWD_QT
+#define FAB_BWD_QT 1
+#endif
+constexpr int kAttnBwdQT = FAB_BWD_QT;        // dQ kernel: 32-query tiles per wave
+constexpr int kAttnBwdBM = 128 * kAttnBwdQT;  // dQ kernel: queries per workgroup
 constexpr int kAttnBwdKB = 128;   // dK/dV kernel: keys per workgroup (4 waves x 32)
 constexpr int kAttnBwdQB = 64;    // dK/dV kernel: queries per inner step
 
