@@ -27,6 +27,15 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The attention kernels keep MFMA accumulators in
+# arch VGPRs (their softmax / gradient math reads them every step; AGPR
+# residency would add a copy per element).
+FILE_FLAGS = {
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def hipcc():
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -41,7 +50,8 @@ def sources():
 
 def _compile(src, build_dir, defines):
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc(), *FLAGS, *extra, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -37,10 +37,15 @@ struct BwdCfg {
 
 // Streamed 64-row tiles live in LDS with tile row x at LDS row
 // perm_row_inv(x % 32) + 32 (x / 32) (so MFMA row r of a 32-row group reads
-// tile row perm_row(r)), and logical 16-byte chunk c of LDS row r at physical
-// chunk c ^ (r % CPR).
+// tile row perm_row(r)), and logical 16-byte chunk c of LDS row r = 4a + b
+// (b = r % 4, a = (r / 4) % 4) at physical chunk c ^ (4 b + a).  The XOR value
+// differs across any 16 aligned rows (conflict-free 16-byte row reads) and its
+// upper two bits differ across 4 aligned rows (conflict-free transposing reads
+// of 4 rows x 64 bytes).
 template <int D>
-__device__ __forceinline__ int swz(int r, int c) { return c ^ (r & (BwdCfg<D>::CPR - 1)); }
+__device__ __forceinline__ int swz(int r, int c) {
+  return c ^ ((((r & 3) << 2) | ((r >> 2) & 3)) & (BwdCfg<D>::CPR - 1));
+}
 __device__ __forceinline__ int lds_row_of(int x) { return perm_row_inv(x & 31) + (x & ~31); }
 
 // Async copy of rows [r0, r0 + 64) of a [rows, D] matrix (row stride sr) into

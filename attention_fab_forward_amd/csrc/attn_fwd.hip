@@ -8,8 +8,8 @@
 // 2.A).  The running row maximum and sum are the usual online-softmax
 // rescaling, which leaves the result equal to the plain definition.
 //
-// Layout choices (workgroup = 4 waves, each wave 64 queries = two 32-query
-// MFMA tiles that share every LDS fragment read):
+// Layout choices (workgroup = 4 waves, each wave 32 QT queries; with QT = 2
+// the two 32-query MFMA tiles share every LDS fragment read):
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K is the A operand (from LDS),
 //    Q^T the B operand (registers, whole kernel).  Lane l owns query l%32 of
 //    each tile, so row max / row sum are in-lane plus one exchange with lane
@@ -81,7 +81,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, FwdCfg<D>::QT == 1 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
   using C = FwdCfg<D>;
   constexpr int QT = C::QT;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];

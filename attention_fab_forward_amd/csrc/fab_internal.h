@@ -69,7 +69,7 @@ void timer_end(hipStream_t s);
 
 // Forward attention tile shapes (bf16 MFMA path).
 #ifndef FAB_FWD_QT
-#define FAB_FWD_QT 2
+#define FAB_FWD_QT 1
 #endif
 constexpr int kAttnFwdQT = FAB_FWD_QT;      // 32-query MFMA tiles per wave
 constexpr int kAttnFwdBM = 128 * kAttnFwdQT;  // queries per workgroup (4 waves)
