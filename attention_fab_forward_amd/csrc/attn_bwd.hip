@@ -49,20 +49,53 @@ __device__ __forceinline__ int swz(int r, int c) {
 __device__ __forceinline__ int lds_row_of(int x) { return perm_row_inv(x & 31) + (x & ~31); }
 
 // Async copy of rows [r0, r0 + 64) of a [rows, D] matrix (row stride sr) into
-// a tile as above; rows at or past nrows are clamped to nrows - 1 (callers
-// mask them).
+// a tile as above.  Lane j of wave copy i writes LDS row
+// r = (w * CPW + i) * RPI + j / CPR, physical chunk j % CPR; its byte offset
+// inside the source block is fixed for the whole kernel and precomputed.
 template <int D>
-__device__ __forceinline__ void issue_tile(const uint16_t* base, int64_t sr, int r0, int nrows,
-                                           char* dst, int wave, int lane) {
+struct TileOffsets {
+  uint32_t off[BwdCfg<D>::CPW];  // byte offset of this lane's 16 bytes within a block
+};
+
+// Tile row copied by lane `lane` of wave `wave` in copy i.
+template <int D>
+__device__ __forceinline__ int tile_row_of_copy(int wave, int lane, int i) {
   using C = BwdCfg<D>;
+  const int r = (wave * C::CPW + i) * C::RPI + lane / C::CPR;
+  return perm_row(r & 31) + (r & ~31);
+}
+
+template <int D>
+__device__ __forceinline__ TileOffsets<D> tile_offsets(int64_t sr, int wave, int lane) {
+  using C = BwdCfg<D>;
+  TileOffsets<D> t;
 #pragma unroll
   for (int i = 0; i < C::CPW; ++i) {
-    const int blk = wave * C::CPW + i;
-    const int r = blk * C::RPI + lane / C::CPR;  // LDS row this lane writes
-    const int pc = lane % C::CPR;                // physical chunk this lane writes
-    const int x = perm_row(r & 31) + (r & ~31);  // tile row held by LDS row r
-    const int row = min(r0 + x, nrows - 1);
-    g2lds16(base + (int64_t)row * sr + 8 * swz<D>(r, pc), dst + blk * 1024);
+    const int r = (wave * C::CPW + i) * C::RPI + lane / C::CPR;
+    t.off[i] = (uint32_t)(2 * (tile_row_of_copy<D>(wave, lane, i) * sr + 8 * swz<D>(r, lane % C::CPR)));
+  }
+  return t;
+}
+
+// Rows at or past nrows (ragged last tile only) are clamped to nrows - 1;
+// callers mask them.
+template <int D>
+__device__ __forceinline__ void issue_tile(const TileOffsets<D>& t, const uint16_t* base,
+                                           int64_t sr, int r0, int nrows, char* dst, int wave,
+                                           int lane) {
+  using C = BwdCfg<D>;
+  const char* b = reinterpret_cast<const char*>(base + (int64_t)r0 * sr);
+  char* d = dst + wave * C::CPW * 1024;
+  if (r0 + C::TILE <= nrows) {
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) g2lds16(b + t.off[i], d + i * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const int x = tile_row_of_copy<D>(wave, lane, i);
+      const int64_t shift = min(x, nrows - 1 - r0) - x;
+      g2lds16(b + t.off[i] + 2 * shift * sr, d + i * 1024);
+    }
   }
 }
 
@@ -113,26 +146,28 @@ struct DkdvStage {
 };
 
 template <int D>
-__device__ __forceinline__ void dkdv_issue(const AttnArgs& a, int bi, int h, int q0, char* st,
-                                           int wave, int lane) {
+__device__ __forceinline__ void dkdv_issue(const AttnArgs& a, const TileOffsets<D>& tq,
+                                           const TileOffsets<D>& to, int bi, int h, int q0,
+                                           char* st, int wave, int lane) {
   using S = DkdvStage<D>;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const uint16_t* ob = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
-  issue_tile<D>(qb, a.q_sr, q0, a.m, st + S::Q, wave, lane);
-  issue_tile<D>(ob, a.o_sr, q0, a.m, st + S::DO, wave, lane);
+  issue_tile<D>(tq, qb, a.q_sr, q0, a.m, st + S::Q, wave, lane);
+  issue_tile<D>(to, ob, a.o_sr, q0, a.m, st + S::DO, wave, lane);
   const int64_t r = ((int64_t)bi * a.hq + h) * a.m;
   if (wave == 0) issue_vec64(a.lse_in + r, q0, a.m, st + S::LSE, lane);
   if (wave == 1) issue_vec64(a.delta + r, q0, a.m, st + S::DLT, lane);
 }
 
-template <int D, bool CAUSAL>
+// SAME: Q and dO have equal row strides, so one set of copy offsets serves both.
+template <int D, bool CAUSAL, bool SAME>
 __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using S = DkdvStage<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * S::BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
   const int l16 = lane & 15, g16 = lane >> 4;
   const int tr_d = 16 * (l16 & 1) + 8 * (g16 & 1) + 4 * ((l16 >> 1) & 1);
@@ -153,7 +188,9 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const int steps_per_head = nqb - qb_first;
   const int steps = steps_per_head * a.group;
   const bool wave_live = k0w < a.n;
-  if (steps > 0) dkdv_issue<D>(a, bi, g * a.group, qb_first * C::TILE, smem, wave, lane);
+  const TileOffsets<D> tq = tile_offsets<D>(a.q_sr, wave, lane);
+  const TileOffsets<D> to = SAME ? tq : tile_offsets<D>(a.o_sr, wave, lane);
+  if (steps > 0) dkdv_issue<D>(a, tq, to, bi, g * a.group, qb_first * C::TILE, smem, wave, lane);
 
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
@@ -175,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   for (int step = 0; step < steps; ++step) {
     if (step + 1 < steps) {
       const int nh = (step + 1) / steps_per_head, nq = (step + 1) % steps_per_head;
-      dkdv_issue<D>(a, bi, g * a.group + nh, (qb_first + nq) * C::TILE,
+      dkdv_issue<D>(a, tq, to, bi, g * a.group + nh, (qb_first + nq) * C::TILE,
                     smem + ((step + 1) & 1) * S::BYTES, wave, lane);
     }
     const int q0 = (qb_first + step % steps_per_head) * C::TILE;
@@ -262,7 +299,8 @@ struct DqStage {
   static constexpr int BYTES = 2 * BwdCfg<D>::TBYTES;
 };
 
-template <int D, bool CAUSAL, int QT>
+// SAME: K and V have equal row strides, so one set of copy offsets serves both.
+template <int D, bool CAUSAL, int QT, bool SAME>
 __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using S = DqStage<D>;
@@ -270,7 +308,7 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   __shared__ __attribute__((aligned(1024))) char smem[2 * S::BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
   const int l16 = lane & 15, g16 = lane >> 4;
   const int tr_d = 16 * (l16 & 1) + 8 * (g16 & 1) + 4 * ((l16 >> 1) & 1);
@@ -291,8 +329,10 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
   const int kend = CAUSAL ? min(a.n, qb * BM + BM) : a.n;
   const int nkb = (kend + C::TILE - 1) / C::TILE;
-  issue_tile<D>(kbase, a.k_sr, 0, a.n, smem + S::K, wave, lane);
-  issue_tile<D>(vbase, a.v_sr, 0, a.n, smem + S::V, wave, lane);
+  const TileOffsets<D> tk = tile_offsets<D>(a.k_sr, wave, lane);
+  const TileOffsets<D> tv = SAME ? tk : tile_offsets<D>(a.v_sr, wave, lane);
+  issue_tile<D>(tk, kbase, a.k_sr, 0, a.n, smem + S::K, wave, lane);
+  issue_tile<D>(tv, vbase, a.v_sr, 0, a.n, smem + S::V, wave, lane);
 
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const uint16_t* obase = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
@@ -328,8 +368,8 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   for (int kb = 0; kb < nkb; ++kb) {
     if (kb + 1 < nkb) {
       char* nst = smem + ((kb + 1) & 1) * S::BYTES;
-      issue_tile<D>(kbase, a.k_sr, (kb + 1) * C::TILE, a.n, nst + S::K, wave, lane);
-      issue_tile<D>(vbase, a.v_sr, (kb + 1) * C::TILE, a.n, nst + S::V, wave, lane);
+      issue_tile<D>(tk, kbase, a.k_sr, (kb + 1) * C::TILE, a.n, nst + S::K, wave, lane);
+      issue_tile<D>(tv, vbase, a.v_sr, (kb + 1) * C::TILE, a.n, nst + S::V, wave, lane);
     }
     const char* st = smem + (kb & 1) * S::BYTES;
     const int key0 = kb * C::TILE;
@@ -414,13 +454,18 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   const int nkb = (a.n + kAttnBwdKB - 1) / kAttnBwdKB;
   const int nqb = (a.m + 128 * QT - 1) / (128 * QT);
   const dim3 gk((unsigned)nkb * a.hkv * a.b), gq((unsigned)nqb * a.hq * a.b);
+  const bool same_qo = a.q_sr == a.o_sr, same_kv = a.k_sr == a.v_sr;
+#define FAB_DKDV(C, S) FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, C, S>), gk, block, 0, s, a))
+#define FAB_DQ(C, S) FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, C, QT, S>), gq, block, 0, s, a))
   if (a.causal) {
-    FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, true>), gk, block, 0, s, a));
-    FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, true, QT>), gq, block, 0, s, a));
+    if (same_qo) FAB_DKDV(true, true); else FAB_DKDV(true, false);
+    if (same_kv) FAB_DQ(true, true); else FAB_DQ(true, false);
   } else {
-    FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, false>), gk, block, 0, s, a));
-    FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, false, QT>), gq, block, 0, s, a));
+    if (same_qo) FAB_DKDV(false, true); else FAB_DKDV(false, false);
+    if (same_kv) FAB_DQ(false, true); else FAB_DQ(false, false);
   }
+#undef FAB_DKDV
+#undef FAB_DQ
   return hipGetLastError();
 }
 

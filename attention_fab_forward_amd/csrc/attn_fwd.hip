@@ -58,25 +58,67 @@ __device__ __forceinline__ int v_swz(int r, int c) {
   return c ^ ((4 * (r & 3)) & (FwdCfg<D>::CPR - 1));
 }
 
-// Issue the async copies of key block [key0, key0 + BN) of K and V into one
-// LDS stage.  Wave w fills 1 KiB blocks [w * CPW, (w+1) * CPW) of each tile.
-// Rows past n are clamped to row n-1 (their scores are masked, so their
-// probabilities are zero).
+// Async copies of one key block of K and V into an LDS stage.  Wave w fills
+// 1 KiB blocks [w * CPW, (w+1) * CPW) of each tile; lane j of copy i writes
+// LDS row r = (w * CPW + i) * RPI + j / CPR, physical chunk j % CPR.  The
+// per-lane element offsets inside a block are fixed for the whole kernel, so
+// they are computed once; each step only advances the wave-uniform base.
 template <int D>
-__device__ __forceinline__ void issue_tile(const uint16_t* kbase, const uint16_t* vbase,
-                                           int64_t k_sr, int64_t v_sr, int key0, int n,
-                                           char* stage, int wave, int lane) {
+struct TileOffsets {
+  uint32_t k[FwdCfg<D>::CPW], v[FwdCfg<D>::CPW];  // byte offsets within a block
+};
+
+// LDS row written by lane `lane` of wave `wave` in copy i; K holds tile key
+// perm_row(r) there, V tile key r.
+template <int D>
+__device__ __forceinline__ int copy_row(int wave, int lane, int i) {
   using C = FwdCfg<D>;
+  return (wave * C::CPW + i) * C::RPI + lane / C::CPR;
+}
+
+template <int D>
+__device__ __forceinline__ TileOffsets<D> tile_offsets(int64_t k_sr, int64_t v_sr, int wave,
+                                                       int lane) {
+  using C = FwdCfg<D>;
+  TileOffsets<D> t;
 #pragma unroll
   for (int i = 0; i < C::CPW; ++i) {
-    const int blk = wave * C::CPW + i;           // 1 KiB block index within the tile
-    const int r = blk * C::RPI + lane / C::CPR;  // LDS row written by this lane
-    const int pc = lane % C::CPR;                // physical chunk written by this lane
-    const int kr = perm_row(r & 31) + (r & ~31);  // K: LDS row r holds tile key perm_row(r)
-    const int kkey = min(key0 + kr, n - 1);
-    const int vkey = min(key0 + r, n - 1);
-    g2lds16(kbase + (int64_t)kkey * k_sr + 8 * k_swz<D>(r, pc), stage + blk * 1024);
-    g2lds16(vbase + (int64_t)vkey * v_sr + 8 * v_swz<D>(r, pc), stage + C::TILE + blk * 1024);
+    const int r = copy_row<D>(wave, lane, i);
+    const int pc = lane % C::CPR;
+    const int kr = perm_row(r & 31) + (r & ~31);
+    t.k[i] = (uint32_t)(2 * (kr * k_sr + 8 * k_swz<D>(r, pc)));
+    t.v[i] = (uint32_t)(2 * (r * v_sr + 8 * v_swz<D>(r, pc)));
+  }
+  return t;
+}
+
+// Rows past n (only in a ragged last block) are clamped to row n - 1: their
+// scores are masked, so their probabilities are zero.
+template <int D>
+__device__ __forceinline__ void issue_tile(const TileOffsets<D>& t, const uint16_t* kbase,
+                                           const uint16_t* vbase, int64_t k_sr, int64_t v_sr,
+                                           int key0, int n, char* stage, int wave, int lane) {
+  using C = FwdCfg<D>;
+  const char* kb = reinterpret_cast<const char*>(kbase + (int64_t)key0 * k_sr);
+  const char* vb = reinterpret_cast<const char*>(vbase + (int64_t)key0 * v_sr);
+  char* kdst = stage + wave * C::CPW * 1024;
+  char* vdst = kdst + C::TILE;
+  if (key0 + C::BN <= n) {
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      g2lds16(kb + t.k[i], kdst + i * 1024);
+      g2lds16(vb + t.v[i], vdst + i * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const int r = copy_row<D>(wave, lane, i);
+      const int kr = perm_row(r & 31) + (r & ~31);
+      const int64_t kc = min(kr, n - 1 - key0) - kr;  // row shifts for clamping
+      const int64_t vc = min(r, n - 1 - key0) - r;
+      g2lds16(kb + t.k[i] + 2 * kc * k_sr, kdst + i * 1024);
+      g2lds16(vb + t.v[i] + 2 * vc * v_sr, vdst + i * 1024);
+    }
   }
 }
 
@@ -87,7 +129,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::QT == 1 ? 2 : 1) void attn_fwd_bf16
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
   const int l16 = lane & 15, g16 = lane >> 4;
 
@@ -112,7 +154,8 @@ __global__ __launch_bounds__(256, FwdCfg<D>::QT == 1 ? 2 : 1) void attn_fwd_bf16
 
   const int kend = CAUSAL ? min(a.n, qb * C::BM + C::BM) : a.n;
   const int nkb = (kend + C::BN - 1) / C::BN;
-  issue_tile<D>(kbase, vbase, a.k_sr, a.v_sr, 0, a.n, smem, wave, lane);
+  const TileOffsets<D> toff = tile_offsets<D>(a.k_sr, a.v_sr, wave, lane);
+  issue_tile<D>(toff, kbase, vbase, a.k_sr, a.v_sr, 0, a.n, smem, wave, lane);
 
   // Q^T fragments: lane holds Q[myq][16c + 8lg .. +7] for every chunk c.
   u32x4 qf[QT][C::DC];
@@ -150,7 +193,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::QT == 1 ? 2 : 1) void attn_fwd_bf16
   for (int kb = 0; kb < nkb; ++kb) {
     const bool more = kb + 1 < nkb;
     if (more)
-      issue_tile<D>(kbase, vbase, a.k_sr, a.v_sr, (kb + 1) * C::BN, a.n,
+      issue_tile<D>(toff, kbase, vbase, a.k_sr, a.v_sr, (kb + 1) * C::BN, a.n,
                     smem + ((kb + 1) & 1) * C::STAGE, wave, lane);
 
     const int key0 = kb * C::BN;
