@@ -155,8 +155,78 @@ __device__ __forceinline__ void dkdv_issue(const AttnArgs& a, const TileOffsets<
   issue_tile<D>(tq, qb, a.q_sr, q0, a.m, st + S::Q, wave, lane);
   issue_tile<D>(to, ob, a.o_sr, q0, a.m, st + S::DO, wave, lane);
   const int64_t r = ((int64_t)bi * a.hq + h) * a.m;
-  if (wave == 0) issue_vec64(a.lse_in + r, q0, a.m, st + S::LSE, lane);
+  if (wave == 0) issue_vec64(a.lse2 + r, q0, a.m, st + S::LSE, lane);
   if (wave == 1) issue_vec64(a.delta + r, q0, a.m, st + S::DLT, lane);
+}
+
+// One 64-query block against this wave's 32 keys.  Accumulator slot r of the
+// S / dP tiles holds query q0 + 32 sq + 16 (l / 32) + r for key `mykey`.  The
+// dP accumulator starts from -D (staged in LDS), so it ends as dP - D.
+// need_mask (wave-uniform; diagonal and ragged blocks only): masked scores are
+// set to -inf, which the exponential turns into zero probabilities.  The
+// masking is one uniform branch over the 16 scores rather than a select per
+// probability, so full blocks pay nothing for it.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void dkdv_block(const char* st, const u32x4 (&kf)[BwdCfg<D>::DC],
+                                           const u32x4 (&vf)[BwdCfg<D>::DC],
+                                           f32x16 (&dk)[BwdCfg<D>::DT], f32x16 (&dv)[BwdCfg<D>::DT],
+                                           bool need_mask, int q0, int mykey, int m, float cs,
+                                           int lq, int lg, int tr_d, int tr_row) {
+  using C = BwdCfg<D>;
+  using S = DkdvStage<D>;
+#pragma unroll
+  for (int sq = 0; sq < 2; ++sq) {
+    const f32x4* l2 = reinterpret_cast<const f32x4*>(st + S::LSE) + 8 * sq + 4 * lg;
+    const f32x4* nd = reinterpret_cast<const f32x4*>(st + S::DLT) + 8 * sq + 4 * lg;
+    f32x16 s, dp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 x = nd[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[4 * j + e] = 0.f;
+        dp[4 * j + e] = x[e];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) {
+      s = mfma32(read_nat<D>(st + S::Q, sq, c, lq, lg), kf[c], s);
+      dp = mfma32(read_nat<D>(st + S::DO, sq, c, lq, lg), vf[c], dp);
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 32 * sq + 16 * lg + r;
+        if ((CAUSAL && q < mykey) || q >= m) s[r] = -INFINITY;
+      }
+    }
+    float p[16], ds[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 lse2 = l2[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * j + e;
+        p[r] = fast_exp2(fmaf(s[r], cs, -lse2[e]));
+        ds[r] = p[r] * dp[r];
+      }
+    }
+    u32x4 pb[2], db[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        pb[c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
+        db[c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
+      }
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        dv[t] = mfma32(read_tr<D>(st + S::DO, t, sq, c, lg, tr_d, tr_row), pb[c], dv[t]);
+        dk[t] = mfma32(read_tr<D>(st + S::Q, t, sq, c, lg, tr_d, tr_row), db[c], dk[t]);
+      }
+  }
 }
 
 // SAME: Q and dO have equal row strides, so one set of copy offsets serves both.
@@ -221,46 +291,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
     const bool wave_work = wave_live && (!CAUSAL || q0 + C::TILE - 1 >= k0w);
     if (wave_work) {
       const bool need_mask = (CAUSAL && q0 < k0w + 31) || q0 + C::TILE > a.m;
-#pragma unroll
-      for (int sq = 0; sq < 2; ++sq) {
-        f32x16 s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < C::DC; ++c) {
-          s = mfma32(read_nat<D>(st + S::Q, sq, c, lq, lg), kf[c], s);
-          dp = mfma32(read_nat<D>(st + S::DO, sq, c, lq, lg), vf[c], dp);
-        }
-        // accumulator slot r holds query q0 + 32 sq + 16 lg + r for key `mykey`
-        const float* lse = reinterpret_cast<const float*>(st + S::LSE) + 32 * sq + 16 * lg;
-        const float* dlt = reinterpret_cast<const float*>(st + S::DLT) + 32 * sq + 16 * lg;
-        float p[16], ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(s[r] * cs - lse[r] * kLog2e);
-          if (need_mask) {
-            const int q = q0 + 32 * sq + 16 * lg + r;
-            if ((CAUSAL && q < mykey) || q >= a.m) pr = 0.f;
-          }
-          p[r] = pr;
-          ds[r] = pr * (dp[r] - dlt[r]);
-        }
-        u32x4 pb[2], db[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            pb[c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
-            db[c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
-          }
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            dv[t] = mfma32(read_tr<D>(st + S::DO, t, sq, c, lg, tr_d, tr_row), pb[c], dv[t]);
-            dk[t] = mfma32(read_tr<D>(st + S::Q, t, sq, c, lg, tr_d, tr_row), db[c], dk[t]);
-          }
-      }
+      dkdv_block<D, CAUSAL>(st, kf, vf, dk, dv, need_mask, q0, mykey, a.m, cs, lq, lg, tr_d,
+                            tr_row);
     }
     wait_vmem();
     __syncthreads();
@@ -298,6 +330,70 @@ struct DqStage {
   static constexpr int V = BwdCfg<D>::TBYTES;
   static constexpr int BYTES = 2 * BwdCfg<D>::TBYTES;
 };
+
+// One 64-key block against this wave's 32 QT queries.  Accumulator slot r of
+// the S / dP tiles holds key key0 + 32 sb + 16 (l / 32) + r for query myq[qt].
+// need_mask (wave-uniform; diagonal or ragged blocks): masked scores are set
+// to -inf in one uniform branch, so full blocks pay nothing for masking.
+template <int D, bool CAUSAL, int QT>
+__device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][BwdCfg<D>::DC],
+                                         const u32x4 (&df)[QT][BwdCfg<D>::DC],
+                                         f32x16 (&dq)[QT][BwdCfg<D>::DT], const int (&myq)[QT],
+                                         const float (&lse2)[QT], const float (&ndl)[QT],
+                                         bool need_mask, int key0, int n, float cs, int lq, int lg,
+                                         int tr_d, int tr_row) {
+  using C = BwdCfg<D>;
+  using S = DqStage<D>;
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    f32x16 s[QT], dp[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qt][r] = dp[qt][r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) {
+      const u32x4 kfr = read_nat<D>(st + S::K, sb, c, lq, lg);
+      const u32x4 vfr = read_nat<D>(st + S::V, sb, c, lq, lg);
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        s[qt] = mfma32(kfr, qf[qt][c], s[qt]);
+        dp[qt] = mfma32(vfr, df[qt][c], dp[qt]);
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * sb + 16 * lg + r;
+          if ((CAUSAL && key > myq[qt]) || key >= n) s[qt][r] = -INFINITY;
+        }
+    }
+    u32x4 db[QT][2];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(s[qt][r], cs, -lse2[qt]));
+        ds[r] = p * (dp[qt][r] + ndl[qt]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) db[qt][c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
+    }
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 kt = read_tr<D>(st + S::K, t, sb, c, lg, tr_d, tr_row);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) dq[qt][t] = mfma32(kt, db[qt][c], dq[qt][t]);
+      }
+  }
+}
 
 // SAME: K and V have equal row strides, so one set of copy offsets serves both.
 template <int D, bool CAUSAL, int QT, bool SAME>
@@ -338,7 +434,7 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   const uint16_t* obase = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
   int myq[QT];
   u32x4 qf[QT][C::DC], df[QT][C::DC];
-  float lse2[QT], dlt[QT];
+  float lse2[QT], ndl[QT];  // LSE * log2(e) and -D of the lane's query
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     myq[qt] = q0 + 32 * qt + lq;
@@ -351,8 +447,8 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
                        : u32x4{0, 0, 0, 0};
     }
     const int64_t ridx = ((int64_t)bi * a.hq + h) * a.m + myq[qt];
-    lse2[qt] = live ? a.lse_in[ridx] * kLog2e : INFINITY;
-    dlt[qt] = live ? a.delta[ridx] : 0.f;
+    lse2[qt] = live ? a.lse2[ridx] : INFINITY;
+    ndl[qt] = live ? a.delta[ridx] : 0.f;
   }
   f32x16 dq[QT][C::DT];
 #pragma unroll
@@ -375,52 +471,9 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
     const int key0 = kb * C::TILE;
     const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 32 * QT - 1);
     if (wave_work) {
-      const bool need_mask = (CAUSAL && key0 + C::TILE - 1 > q0) || (key0 + C::TILE > a.n);
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        f32x16 s[QT], dp[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[qt][r] = dp[qt][r] = 0.f;
-#pragma unroll
-        for (int c = 0; c < C::DC; ++c) {
-          const u32x4 kfr = read_nat<D>(st + S::K, sb, c, lq, lg);
-          const u32x4 vfr = read_nat<D>(st + S::V, sb, c, lq, lg);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) {
-            s[qt] = mfma32(kfr, qf[qt][c], s[qt]);
-            dp[qt] = mfma32(vfr, df[qt][c], dp[qt]);
-          }
-        }
-        // accumulator slot r holds key key0 + 32 sb + 16 lg + r for query myq[qt]
-        u32x4 db[QT][2];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          float ds[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float p = fast_exp2(s[qt][r] * cs - lse2[qt]);
-            if (need_mask) {
-              const int key = key0 + 32 * sb + 16 * lg + r;
-              if ((CAUSAL && key > myq[qt]) || key >= a.n) p = 0.f;
-            }
-            ds[r] = p * (dp[qt][r] - dlt[qt]);
-          }
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) db[qt][c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
-        }
-#pragma unroll
-        for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const u32x4 kt = read_tr<D>(st + S::K, t, sb, c, lg, tr_d, tr_row);
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) dq[qt][t] = mfma32(kt, db[qt][c], dq[qt][t]);
-          }
-      }
+      const bool need_mask = (CAUSAL && key0 + C::TILE - 1 > q0) || key0 + C::TILE > a.n;
+      dq_block<D, CAUSAL, QT>(st, qf, df, dq, myq, lse2, ndl, need_mask, key0, a.n, cs, lq, lg,
+                              tr_d, tr_row);
     }
     wait_vmem();
     __syncthreads();
@@ -445,11 +498,49 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   }
 }
 
+// ---------------------------------------------------------------------------
+// Preprocessing, one row per LPR lanes (16 bytes of dO and O each):
+// delta[row] = -rowsum(dO * O) (fp32, from the bf16 values) and
+// lse2[row] = LSE * log2(e), the two per-query constants both kernels use.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(AttnArgs a) {
+  constexpr int LPR = D * 2 / 16;
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // over b * hq * m
+  const int part = tid % LPR;
+  const int64_t total = (int64_t)a.b * a.hq * a.m;
+  float acc = 0.f;
+  if (row < total) {
+    const int64_t i = row % a.m, bh = row / a.m;
+    const int h = (int)(bh % a.hq), bi = (int)(bh / a.hq);
+    const int64_t off = bi * a.o_sb + h * a.o_sh + i * a.o_sr + part * 8;
+    const u32x4 x = ldg16(static_cast<const uint16_t*>(a.o) + off);
+    const u32x4 y = ldg16(static_cast<const uint16_t*>(a.dout) + off);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      acc += bf16_lo(x[w]) * bf16_lo(y[w]) + bf16_hi(x[w]) * bf16_hi(y[w]);
+  }
+#pragma unroll
+  for (int sft = 1; sft < LPR; sft <<= 1) acc += __shfl_xor(acc, sft, 64);
+  if (row < total && part == 0) {
+    a.delta[row] = -acc;
+    a.lse2[row] = a.lse_in[row] * kLog2e;
+  }
+}
+
 template <int D>
 hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
-  hipError_t e = launch_attn_delta(a, D, true, s);
-  if (e != hipSuccess) return e;
   const dim3 block(256);
+  {
+    constexpr int rpb = 256 / (D * 2 / 16);
+    const int64_t rows = (int64_t)a.b * a.hq * a.m;
+    const dim3 gp((unsigned)((rows + rpb - 1) / rpb));
+    FAB_TIMED("attn_bwd_prep", s, hipLaunchKernelGGL((attn_bwd_prep_bf16_kernel<D>), gp, block, 0, s, a));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   constexpr int QT = kAttnBwdQT;
   const int nkb = (a.n + kAttnBwdKB - 1) / kAttnBwdKB;
   const int nqb = (a.m + 128 * QT - 1) / (128 * QT);

@@ -123,44 +123,6 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// backward preprocessing: delta[b, h, i] = sum_d dO[i, d] * O[i, d]  (fp32)
-// LPR lanes per row, each covering 16 bytes of the row.
-// ---------------------------------------------------------------------------
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void attn_delta_kernel(AttnArgs a) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int LPR = D * ES / 16;
-  constexpr int RPB = 256 / LPR;
-  const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // over b * hq * m
-  const int part = tid % LPR;
-  const int64_t total = (int64_t)a.b * a.hq * a.m;
-  float acc = 0.f;
-  int64_t i = 0, bh = 0;
-  if (row < total) {
-    i = row % a.m;
-    bh = row / a.m;
-    const int h = (int)(bh % a.hq), bi = (int)(bh / a.hq);
-    const int64_t off = bi * a.o_sb + h * a.o_sh + i * a.o_sr;
-    if constexpr (BF16) {
-      const u32x4 x = ldg16(static_cast<const uint16_t*>(a.o) + off + part * 8);
-      const u32x4 y = ldg16(static_cast<const uint16_t*>(a.dout) + off + part * 8);
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        acc += bf16_lo(x[w]) * bf16_lo(y[w]) + bf16_hi(x[w]) * bf16_hi(y[w]);
-    } else {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.o) + off + part * 4);
-      const f32x4 y = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.dout) + off + part * 4);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc = fmaf(x[w], y[w], acc);
-    }
-  }
-#pragma unroll
-  for (int sft = 1; sft < LPR; sft <<= 1) acc += __shfl_xor(acc, sft, 64);
-  if (row < total && part == 0) a.delta[row] = acc;
-}
-
-// ---------------------------------------------------------------------------
 // dQ: one row group per query, loop over keys
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
@@ -348,22 +310,6 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-hipError_t launch_attn_delta(const AttnArgs& a, int d, bool bf16, hipStream_t s) {
-  const int64_t rows = (int64_t)a.b * a.hq * a.m;
-  const int es = bf16 ? 2 : 4;
-  const int lpr = d * es / 16;
-  const int rpb = 256 / lpr;
-  const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
-  if (bf16) {
-    if (d == 128) FAB_TIMED("attn_bwd_delta", s, hipLaunchKernelGGL((attn_delta_kernel<128, true>), grid, block, 0, s, a));
-    else FAB_TIMED("attn_bwd_delta", s, hipLaunchKernelGGL((attn_delta_kernel<64, true>), grid, block, 0, s, a));
-  } else {
-    if (d == 128) FAB_TIMED("attn_bwd_delta", s, hipLaunchKernelGGL((attn_delta_kernel<128, false>), grid, block, 0, s, a));
-    else FAB_TIMED("attn_bwd_delta", s, hipLaunchKernelGGL((attn_delta_kernel<64, false>), grid, block, 0, s, a));
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t s) {
   if (d == 128) return fwd_d<128>(a, s);

@@ -265,7 +265,9 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
                   (long long)q.m, (long long)q.n);
     if (!(q.scale > 0.f)) return fail(FAB_ERR_UNSUPPORTED, "softmax scale must be > 0");
     tmp.fwd_ws = 0;
-    tmp.bwd_ws = round_up((size_t)q.batch * q.heads_a * q.m * sizeof(float), 256);
+    // per query row: delta (both paths) and LSE * log2(e) (bf16 path)
+    const size_t rows = (size_t)q.batch * q.heads_a * q.m;
+    tmp.bwd_ws = round_up(rows * sizeof(float) * (q.dtype == FAB_BF16 ? 2 : 1), 256);
     if (q.dtype == FAB_BF16)
       snprintf(tmp.desc, sizeof tmp.desc,
                "attention %s d=%lld %s group=%lld fwd[BM=%d BN=%d grid=%lld] "
@@ -433,6 +435,7 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, c
     fab::AttnArgs a = attn_args(plan);
     a.q = A, a.k = Bt, a.v = C, a.o = O, a.lse_in = lse, a.dout = dO;
     a.dq = dA, a.dk = dBt, a.dv = dC, a.delta = static_cast<float*>(workspace);
+    a.lse2 = a.delta + (size_t)q.batch * q.heads_a * q.m;
     e = q.dtype == FAB_BF16 ? fab::launch_attn_bwd_bf16(a, (int)q.k, s)
                             : fab::launch_attn_bwd_f32(a, (int)q.k, s);
   } else {

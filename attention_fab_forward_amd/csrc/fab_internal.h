@@ -22,7 +22,8 @@ struct AttnArgs {
   void* dq;           // layout of Q
   void* dk;           // layout of K
   void* dv;           // layout of V
-  float* delta;       // workspace [b, hq, m]: rowsum(dO * O)
+  float* delta;       // workspace [b, hq, m]: rowsum(dO * O); negated on the bf16 path
+  float* lse2;        // workspace [b, hq, m] (bf16 path): LSE * log2(e)
   int64_t q_sb, q_sh, q_sr;
   int64_t k_sb, k_sh, k_sr;
   int64_t v_sb, v_sh, v_sr;
@@ -82,7 +83,6 @@ constexpr int kAttnBwdBM = 128 * kAttnBwdQT;  // dQ kernel: queries per workgrou
 constexpr int kAttnBwdKB = 128;   // dK/dV kernel: keys per workgroup (4 waves x 32)
 constexpr int kAttnBwdQB = 64;    // dK/dV kernel: queries per inner step
 
-hipError_t launch_attn_delta(const AttnArgs& a, int d, bool bf16, hipStream_t s);
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t s);

@@ -115,14 +115,15 @@ def kernel_flops(w):
         "attn_fwd_bf16": 4 * d * unit,        # S = QK^T and O = PV
         "attn_bwd_dkdv_bf16": 8 * d * unit,   # S (recompute), dP, dV, dK
         "attn_bwd_dq_bf16": 2 * d * unit,     # dQ (its S, dP recomputes are extra work)
-        "attn_bwd_delta": 0,
+        "attn_bwd_prep": 0,
     }
 
 
 def kernel_bytes(w):
     """Algorithmic HBM bytes of the memory-bound preprocessing kernel."""
     rows = w.batch * w.heads_q * w.seq
-    return {"attn_bwd_delta": rows * w.d * 2 * 2 + rows * 4}
+    # reads O and dO (bf16) and the LSE; writes -D and LSE * log2(e) (fp32)
+    return {"attn_bwd_prep": rows * w.d * 2 * 2 + rows * 4 * 3}
 
 
 # rocprofv3 names and source files of the kernels bench.py reports
@@ -130,7 +131,7 @@ ROCPROF_NAMES = {
     "attn_fwd_bf16": ("attn_fwd_bf16_kernel<128, true>", "attn_fwd.hip"),
     "attn_bwd_dkdv_bf16": ("attn_dkdv_bf16_kernel<128, true, true>", "attn_bwd.hip"),
     "attn_bwd_dq_bf16": ("attn_dq_bf16_kernel<128, true, 1, true>", "attn_bwd.hip"),
-    "attn_bwd_delta": ("attn_delta_kernel<128, true>", "attn_f32.hip"),
+    "attn_bwd_prep": ("attn_bwd_prep_bf16_kernel<128>", "attn_bwd.hip"),
 }
 
 
