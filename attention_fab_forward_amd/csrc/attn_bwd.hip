@@ -30,7 +30,6 @@ struct BwdCfg {
   static constexpr int TILE = 64;            // rows of a streamed tile
   static constexpr int TBYTES = TILE * RB;   // bytes of one tile
   static constexpr int RPI = 1024 / RB;      // rows per 1 KiB async copy
-  static constexpr int CPW = TBYTES / 1024 / 4;  // async copies per wave per tile
   static constexpr int DT = D / 32;
   static constexpr int DC = D / 16;
 };
@@ -49,50 +48,56 @@ __device__ __forceinline__ int swz(int r, int c) {
 __device__ __forceinline__ int lds_row_of(int x) { return perm_row_inv(x & 31) + (x & ~31); }
 
 // Async copy of rows [r0, r0 + 64) of a [rows, D] matrix (row stride sr) into
-// a tile as above.  Lane j of wave copy i writes LDS row
+// a tile as above, shared by NW waves: each does CPW = TBYTES / 1 KiB / NW
+// 1 KiB copies.  Lane j of wave copy i writes LDS row
 // r = (w * CPW + i) * RPI + j / CPR, physical chunk j % CPR; its byte offset
 // inside the source block is fixed for the whole kernel and precomputed.
-template <int D>
+template <int D, int NW>
 struct TileOffsets {
-  uint32_t off[BwdCfg<D>::CPW];  // byte offset of this lane's 16 bytes within a block
+  static constexpr int CPW = BwdCfg<D>::TBYTES / 1024 / NW;
+  static_assert(CPW * NW * 1024 == BwdCfg<D>::TBYTES, "tile copies must split evenly");
+  uint32_t off[CPW];  // byte offset of this lane's 16 bytes within a block
 };
 
 // Tile row copied by lane `lane` of wave `wave` in copy i.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ int tile_row_of_copy(int wave, int lane, int i) {
   using C = BwdCfg<D>;
-  const int r = (wave * C::CPW + i) * C::RPI + lane / C::CPR;
+  const int r = (wave * TileOffsets<D, NW>::CPW + i) * C::RPI + lane / C::CPR;
   return perm_row(r & 31) + (r & ~31);
 }
 
-template <int D>
-__device__ __forceinline__ TileOffsets<D> tile_offsets(int64_t sr, int wave, int lane) {
+template <int D, int NW>
+__device__ __forceinline__ TileOffsets<D, NW> tile_offsets(int64_t sr, int wave, int lane) {
   using C = BwdCfg<D>;
-  TileOffsets<D> t;
+  using T = TileOffsets<D, NW>;
+  T t;
 #pragma unroll
-  for (int i = 0; i < C::CPW; ++i) {
-    const int r = (wave * C::CPW + i) * C::RPI + lane / C::CPR;
-    t.off[i] = (uint32_t)(2 * (tile_row_of_copy<D>(wave, lane, i) * sr + 8 * swz<D>(r, lane % C::CPR)));
+  for (int i = 0; i < T::CPW; ++i) {
+    const int r = (wave * T::CPW + i) * C::RPI + lane / C::CPR;
+    t.off[i] = (uint32_t)(2 * (tile_row_of_copy<D, NW>(wave, lane, i) * sr +
+                               8 * swz<D>(r, lane % C::CPR)));
   }
   return t;
 }
 
 // Rows at or past nrows (ragged last tile only) are clamped to nrows - 1;
 // callers mask them.
-template <int D>
-__device__ __forceinline__ void issue_tile(const TileOffsets<D>& t, const uint16_t* base,
+template <int D, int NW>
+__device__ __forceinline__ void issue_tile(const TileOffsets<D, NW>& t, const uint16_t* base,
                                            int64_t sr, int r0, int nrows, char* dst, int wave,
                                            int lane) {
   using C = BwdCfg<D>;
+  using T = TileOffsets<D, NW>;
   const char* b = reinterpret_cast<const char*>(base + (int64_t)r0 * sr);
-  char* d = dst + wave * C::CPW * 1024;
+  char* d = dst + wave * T::CPW * 1024;
   if (r0 + C::TILE <= nrows) {
 #pragma unroll
-    for (int i = 0; i < C::CPW; ++i) g2lds16(b + t.off[i], d + i * 1024);
+    for (int i = 0; i < T::CPW; ++i) g2lds16(b + t.off[i], d + i * 1024);
   } else {
 #pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
-      const int x = tile_row_of_copy<D>(wave, lane, i);
+    for (int i = 0; i < T::CPW; ++i) {
+      const int x = tile_row_of_copy<D, NW>(wave, lane, i);
       const int64_t shift = min(x, nrows - 1 - r0) - x;
       g2lds16(b + t.off[i] + 2 * shift * sr, d + i * 1024);
     }
@@ -133,108 +138,54 @@ __device__ __forceinline__ void issue_vec64(const float* src, int i0, int count,
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 128 keys (4 waves x 32) of one kv head; query blocks of
-// 64 (all query heads of the group) stream through two LDS stages.
+// dK, dV: workgroup = 128 keys of one kv head in 4 groups of 32, each group
+// served by a pair of waves with split roles, so that each wave's registers
+// (one 32-key accumulator, one operand set) leave room for two waves per SIMD:
+//  * P wave (waves 0-3): holds K; S = Q K^T, P = exp2(S scale log2e - LSE
+//    log2e); hands P (fp32) to its partner through LDS; dV^T += dO^T P.
+//  * dS wave (waves 4-7): holds V; dP - D = dO V^T - D; dS = P (dP - D);
+//    dK^T += Q^T dS.
+// Query blocks of 64 (all query heads of the group) stream through two LDS
+// stages; each step has two barriers: P written -> P read, and end of step
+// (stage and P buffer released).
 // ---------------------------------------------------------------------------
+constexpr int kDkdvWaves = 8;
+
 template <int D>
-struct DkdvStage {
-  static constexpr int Q = 0;
+struct DkdvLds {
+  static constexpr int Q = 0;                          // per stage
   static constexpr int DO = BwdCfg<D>::TBYTES;
-  static constexpr int LSE = 2 * BwdCfg<D>::TBYTES;
-  static constexpr int DLT = LSE + 256;
-  static constexpr int BYTES = DLT + 256;
+  static constexpr int LSE = 2 * BwdCfg<D>::TBYTES;    // LSE * log2(e), 64 floats
+  static constexpr int DLT = LSE + 256;                // -D, 64 floats
+  static constexpr int STAGE = DLT + 256;
+  static constexpr int PX = 2 * STAGE;                 // P exchange: [group][sq][j][lane] f32x4
+  static constexpr int PX_GROUP = 2 * 4 * 64 * 16;     // 8 KiB per 32-key group
+  static constexpr int BYTES = PX + 4 * PX_GROUP;
 };
 
 template <int D>
-__device__ __forceinline__ void dkdv_issue(const AttnArgs& a, const TileOffsets<D>& tq,
-                                           const TileOffsets<D>& to, int bi, int h, int q0,
-                                           char* st, int wave, int lane) {
-  using S = DkdvStage<D>;
+__device__ __forceinline__ void dkdv_issue(const AttnArgs& a, const TileOffsets<D, kDkdvWaves>& tq,
+                                           const TileOffsets<D, kDkdvWaves>& to, int bi, int h,
+                                           int q0, char* st, int wave, int lane) {
+  using L = DkdvLds<D>;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const uint16_t* ob = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
-  issue_tile<D>(tq, qb, a.q_sr, q0, a.m, st + S::Q, wave, lane);
-  issue_tile<D>(to, ob, a.o_sr, q0, a.m, st + S::DO, wave, lane);
+  issue_tile<D, kDkdvWaves>(tq, qb, a.q_sr, q0, a.m, st + L::Q, wave, lane);
+  issue_tile<D, kDkdvWaves>(to, ob, a.o_sr, q0, a.m, st + L::DO, wave, lane);
   const int64_t r = ((int64_t)bi * a.hq + h) * a.m;
-  if (wave == 0) issue_vec64(a.lse2 + r, q0, a.m, st + S::LSE, lane);
-  if (wave == 1) issue_vec64(a.delta + r, q0, a.m, st + S::DLT, lane);
-}
-
-// One 64-query block against this wave's 32 keys.  Accumulator slot r of the
-// S / dP tiles holds query q0 + 32 sq + 16 (l / 32) + r for key `mykey`.  The
-// dP accumulator starts from -D (staged in LDS), so it ends as dP - D.
-// need_mask (wave-uniform; diagonal and ragged blocks only): masked scores are
-// set to -inf, which the exponential turns into zero probabilities.  The
-// masking is one uniform branch over the 16 scores rather than a select per
-// probability, so full blocks pay nothing for it.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ void dkdv_block(const char* st, const u32x4 (&kf)[BwdCfg<D>::DC],
-                                           const u32x4 (&vf)[BwdCfg<D>::DC],
-                                           f32x16 (&dk)[BwdCfg<D>::DT], f32x16 (&dv)[BwdCfg<D>::DT],
-                                           bool need_mask, int q0, int mykey, int m, float cs,
-                                           int lq, int lg, int tr_d, int tr_row) {
-  using C = BwdCfg<D>;
-  using S = DkdvStage<D>;
-#pragma unroll
-  for (int sq = 0; sq < 2; ++sq) {
-    const f32x4* l2 = reinterpret_cast<const f32x4*>(st + S::LSE) + 8 * sq + 4 * lg;
-    const f32x4* nd = reinterpret_cast<const f32x4*>(st + S::DLT) + 8 * sq + 4 * lg;
-    f32x16 s, dp;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 x = nd[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[4 * j + e] = 0.f;
-        dp[4 * j + e] = x[e];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < C::DC; ++c) {
-      s = mfma32(read_nat<D>(st + S::Q, sq, c, lq, lg), kf[c], s);
-      dp = mfma32(read_nat<D>(st + S::DO, sq, c, lq, lg), vf[c], dp);
-    }
-    if (need_mask) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + 32 * sq + 16 * lg + r;
-        if ((CAUSAL && q < mykey) || q >= m) s[r] = -INFINITY;
-      }
-    }
-    float p[16], ds[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x4 lse2 = l2[j];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * j + e;
-        p[r] = fast_exp2(fmaf(s[r], cs, -lse2[e]));
-        ds[r] = p[r] * dp[r];
-      }
-    }
-    u32x4 pb[2], db[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        pb[c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
-        db[c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
-      }
-#pragma unroll
-    for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        dv[t] = mfma32(read_tr<D>(st + S::DO, t, sq, c, lg, tr_d, tr_row), pb[c], dv[t]);
-        dk[t] = mfma32(read_tr<D>(st + S::Q, t, sq, c, lg, tr_d, tr_row), db[c], dk[t]);
-      }
-  }
+  if (wave == 0) issue_vec64(a.lse2 + r, q0, a.m, st + L::LSE, lane);
+  if (wave == 1) issue_vec64(a.delta + r, q0, a.m, st + L::DLT, lane);
 }
 
 // SAME: Q and dO have equal row strides, so one set of copy offsets serves both.
+// Accumulator slot r of the S / dP tiles of query sub-block sq holds query
+// q0 + 32 sq + 16 (l / 32) + r for the lane's key k0 + l % 32.
 template <int D, bool CAUSAL, bool SAME>
-__global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
-  using S = DkdvStage<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * S::BYTES];
+  using L = DkdvLds<D>;
+  using TO = TileOffsets<D, kDkdvWaves>;
+  __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -242,6 +193,8 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const int l16 = lane & 15, g16 = lane >> 4;
   const int tr_d = 16 * (l16 & 1) + 8 * (g16 & 1) + 4 * ((l16 >> 1) & 1);
   const int tr_row = l16 >> 2;
+  const bool p_role = wave < 4;
+  const int kg = wave & 3;  // 32-key group
 
   int id = blockIdx.x;
   const int g = id % a.hkv;
@@ -249,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const int bi = id % a.b;
   id /= a.b;
   const int kblk = id;  // causal: low key blocks see the most queries, so they go first
-  const int k0w = kblk * kAttnBwdKB + wave * 32;
+  const int k0w = kblk * kAttnBwdKB + kg * 32;
   const int mykey = k0w + lq;
 
   const float cs = a.scale_log2;
@@ -257,66 +210,150 @@ __global__ __launch_bounds__(256, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const int nqb = (a.m + C::TILE - 1) / C::TILE;
   const int steps_per_head = nqb - qb_first;
   const int steps = steps_per_head * a.group;
-  const bool wave_live = k0w < a.n;
-  const TileOffsets<D> tq = tile_offsets<D>(a.q_sr, wave, lane);
-  const TileOffsets<D> to = SAME ? tq : tile_offsets<D>(a.o_sr, wave, lane);
+  const bool group_live = k0w < a.n;
+  const TO tq = tile_offsets<D, kDkdvWaves>(a.q_sr, wave, lane);
+  const TO to = SAME ? tq : tile_offsets<D, kDkdvWaves>(a.o_sr, wave, lane);
   if (steps > 0) dkdv_issue<D>(a, tq, to, bi, g * a.group, qb_first * C::TILE, smem, wave, lane);
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
-  u32x4 kf[C::DC], vf[C::DC];
+  // this wave's operand: K (P wave) or V (dS wave) rows of its 32 keys
+  u32x4 kv[C::DC];
+  {
+    const uint16_t* base =
+        p_role ? static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh + (int64_t)mykey * a.k_sr
+               : static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh + (int64_t)mykey * a.v_sr;
 #pragma unroll
-  for (int c = 0; c < C::DC; ++c) {
-    const bool ok = mykey < a.n;
-    kf[c] = ok ? ldg16(kbase + (int64_t)mykey * a.k_sr + 16 * c + 8 * lg) : u32x4{0, 0, 0, 0};
-    vf[c] = ok ? ldg16(vbase + (int64_t)mykey * a.v_sr + 16 * c + 8 * lg) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < C::DC; ++c)
+      kv[c] = mykey < a.n ? ldg16(base + 16 * c + 8 * lg) : u32x4{0, 0, 0, 0};
   }
-  f32x16 dk[C::DT], dv[C::DT];
+  f32x16 acc[C::DT];  // dV^T (P wave) or dK^T (dS wave), unscaled
 #pragma unroll
   for (int t = 0; t < C::DT; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk[t][r] = dv[t][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+  f32x4* px = reinterpret_cast<f32x4*>(smem + L::PX + kg * L::PX_GROUP) + lane;
   wait_vmem();
   __syncthreads();
 
-  for (int step = 0; step < steps; ++step) {
+  // The two roles run separate copies of the step loop (same barriers per
+  // step), so each loop keeps only its own role's invariants in registers.
+  auto prefetch = [&](int step) {
     if (step + 1 < steps) {
       const int nh = (step + 1) / steps_per_head, nq = (step + 1) % steps_per_head;
       dkdv_issue<D>(a, tq, to, bi, g * a.group + nh, (qb_first + nq) * C::TILE,
-                    smem + ((step + 1) & 1) * S::BYTES, wave, lane);
+                    smem + ((step + 1) & 1) * L::STAGE, wave, lane);
     }
-    const int q0 = (qb_first + step % steps_per_head) * C::TILE;
-    const char* st = smem + (step & 1) * S::BYTES;
-    // A wave skips a query block when every query precedes all its keys.
-    const bool wave_work = wave_live && (!CAUSAL || q0 + C::TILE - 1 >= k0w);
-    if (wave_work) {
-      const bool need_mask = (CAUSAL && q0 < k0w + 31) || q0 + C::TILE > a.m;
-      dkdv_block<D, CAUSAL>(st, kf, vf, dk, dv, need_mask, q0, mykey, a.m, cs, lq, lg, tr_d,
-                            tr_row);
+  };
+  if (p_role) {
+    for (int step = 0; step < steps; ++step) {
+      prefetch(step);
+      const int q0 = (qb_first + step % steps_per_head) * C::TILE;
+      const char* st = smem + (step & 1) * L::STAGE;
+      // A key group skips a query block when every query precedes all its keys.
+      const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 >= k0w);
+      u32x4 pb[2][2];
+      if (work) {
+        const bool need_mask = (CAUSAL && q0 < k0w + 31) || q0 + C::TILE > a.m;
+#pragma unroll
+        for (int sq = 0; sq < 2; ++sq) {
+          f32x16 s;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+          for (int c = 0; c < C::DC; ++c) s = mfma32(read_nat<D>(st + L::Q, sq, c, lq, lg), kv[c], s);
+          if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int q = q0 + 32 * sq + 16 * lg + r;
+              if ((CAUSAL && q < mykey) || q >= a.m) s[r] = -INFINITY;
+            }
+          }
+          const f32x4* l2 = reinterpret_cast<const f32x4*>(st + L::LSE) + 8 * sq + 4 * lg;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 lse2 = l2[j];
+            f32x4 p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[4 * j + e], cs, -lse2[e]));
+            px[(4 * sq + j) * 64] = p;
+            pb[sq][j >> 1][2 * (j & 1)] = pack_bf16(p[0], p[1]);
+            pb[sq][j >> 1][2 * (j & 1) + 1] = pack_bf16(p[2], p[3]);
+          }
+        }
+      }
+      __syncthreads();  // P visible to the dS waves
+      if (work) {
+#pragma unroll
+        for (int sq = 0; sq < 2; ++sq)
+#pragma unroll
+          for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              acc[t] = mfma32(read_tr<D>(st + L::DO, t, sq, c, lg, tr_d, tr_row), pb[sq][c], acc[t]);
+      }
+      wait_vmem();
+      __syncthreads();
     }
-    wait_vmem();
-    __syncthreads();
+  } else {
+    for (int step = 0; step < steps; ++step) {
+      prefetch(step);
+      const int q0 = (qb_first + step % steps_per_head) * C::TILE;
+      const char* st = smem + (step & 1) * L::STAGE;
+      const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 >= k0w);
+      f32x16 dp[2];
+      if (work) {
+#pragma unroll
+        for (int sq = 0; sq < 2; ++sq) {
+          const f32x4* nd = reinterpret_cast<const f32x4*>(st + L::DLT) + 8 * sq + 4 * lg;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 x = nd[j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[sq][4 * j + e] = x[e];
+          }
+#pragma unroll
+          for (int c = 0; c < C::DC; ++c)
+            dp[sq] = mfma32(read_nat<D>(st + L::DO, sq, c, lq, lg), kv[c], dp[sq]);
+        }
+      }
+      __syncthreads();  // P from the partner wave
+      if (work) {
+#pragma unroll
+        for (int sq = 0; sq < 2; ++sq) {
+          u32x4 db[2];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 p = px[(4 * sq + j) * 64];
+            db[j >> 1][2 * (j & 1)] = pack_bf16(p[0] * dp[sq][4 * j], p[1] * dp[sq][4 * j + 1]);
+            db[j >> 1][2 * (j & 1) + 1] =
+                pack_bf16(p[2] * dp[sq][4 * j + 2], p[3] * dp[sq][4 * j + 3]);
+          }
+#pragma unroll
+          for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+              acc[t] = mfma32(read_tr<D>(st + L::Q, t, sq, c, lg, tr_d, tr_row), db[c], acc[t]);
+        }
+      }
+      wait_vmem();
+      __syncthreads();
+    }
   }
 
-  if (!wave_live || mykey >= a.n) return;
-  uint16_t* dkrow = static_cast<uint16_t*>(a.dk) + bi * a.k_sb + g * a.k_sh +
-                    (int64_t)mykey * a.k_sr + 16 * lg;
-  uint16_t* dvrow = static_cast<uint16_t*>(a.dv) + bi * a.v_sb + g * a.v_sh +
-                    (int64_t)mykey * a.v_sr + 16 * lg;
+  if (!group_live || mykey >= a.n) return;
+  const float osc = p_role ? 1.f : a.scale;
+  uint16_t* row = p_role ? static_cast<uint16_t*>(a.dv) + bi * a.v_sb + g * a.v_sh + (int64_t)mykey * a.v_sr
+                         : static_cast<uint16_t*>(a.dk) + bi * a.k_sb + g * a.k_sh + (int64_t)mykey * a.k_sr;
+  row += 16 * lg;
 #pragma unroll
   for (int t = 0; t < C::DT; ++t) {
-    u32x4 k0, k1, v0, v1;
+    u32x4 lo, hi;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      k0[w] = pack_bf16(dk[t][2 * w] * a.scale, dk[t][2 * w + 1] * a.scale);
-      k1[w] = pack_bf16(dk[t][8 + 2 * w] * a.scale, dk[t][8 + 2 * w + 1] * a.scale);
-      v0[w] = pack_bf16(dv[t][2 * w], dv[t][2 * w + 1]);
-      v1[w] = pack_bf16(dv[t][8 + 2 * w], dv[t][8 + 2 * w + 1]);
+      lo[w] = pack_bf16(acc[t][2 * w] * osc, acc[t][2 * w + 1] * osc);
+      hi[w] = pack_bf16(acc[t][8 + 2 * w] * osc, acc[t][8 + 2 * w + 1] * osc);
     }
-    stg16(dkrow + 32 * t, k0);
-    stg16(dkrow + 32 * t + 8, k1);
-    stg16(dvrow + 32 * t, v0);
-    stg16(dvrow + 32 * t + 8, v1);
+    stg16(row + 32 * t, lo);
+    stg16(row + 32 * t + 8, hi);
   }
 }
 
@@ -425,10 +462,10 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
   const int kend = CAUSAL ? min(a.n, qb * BM + BM) : a.n;
   const int nkb = (kend + C::TILE - 1) / C::TILE;
-  const TileOffsets<D> tk = tile_offsets<D>(a.k_sr, wave, lane);
-  const TileOffsets<D> tv = SAME ? tk : tile_offsets<D>(a.v_sr, wave, lane);
-  issue_tile<D>(tk, kbase, a.k_sr, 0, a.n, smem + S::K, wave, lane);
-  issue_tile<D>(tv, vbase, a.v_sr, 0, a.n, smem + S::V, wave, lane);
+  const TileOffsets<D, 4> tk = tile_offsets<D, 4>(a.k_sr, wave, lane);
+  const TileOffsets<D, 4> tv = SAME ? tk : tile_offsets<D, 4>(a.v_sr, wave, lane);
+  issue_tile<D, 4>(tk, kbase, a.k_sr, 0, a.n, smem + S::K, wave, lane);
+  issue_tile<D, 4>(tv, vbase, a.v_sr, 0, a.n, smem + S::V, wave, lane);
 
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const uint16_t* obase = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
@@ -464,8 +501,8 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   for (int kb = 0; kb < nkb; ++kb) {
     if (kb + 1 < nkb) {
       char* nst = smem + ((kb + 1) & 1) * S::BYTES;
-      issue_tile<D>(tk, kbase, a.k_sr, (kb + 1) * C::TILE, a.n, nst + S::K, wave, lane);
-      issue_tile<D>(tv, vbase, a.v_sr, (kb + 1) * C::TILE, a.n, nst + S::V, wave, lane);
+      issue_tile<D, 4>(tk, kbase, a.k_sr, (kb + 1) * C::TILE, a.n, nst + S::K, wave, lane);
+      issue_tile<D, 4>(tv, vbase, a.v_sr, (kb + 1) * C::TILE, a.n, nst + S::V, wave, lane);
     }
     const char* st = smem + (kb & 1) * S::BYTES;
     const int key0 = kb * C::TILE;
@@ -546,7 +583,7 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   const int nqb = (a.m + 128 * QT - 1) / (128 * QT);
   const dim3 gk((unsigned)nkb * a.hkv * a.b), gq((unsigned)nqb * a.hq * a.b);
   const bool same_qo = a.q_sr == a.o_sr, same_kv = a.k_sr == a.v_sr;
-#define FAB_DKDV(C, S) FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, C, S>), gk, block, 0, s, a))
+#define FAB_DKDV(C, S) FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, C, S>), gk, dim3(64 * kDkdvWaves), 0, s, a))
 #define FAB_DQ(C, S) FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, C, QT, S>), gq, block, 0, s, a))
   if (a.causal) {
     if (same_qo) FAB_DKDV(true, true); else FAB_DKDV(true, false);
