@@ -7,14 +7,16 @@
 //   dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
 //
 // Deterministic two-kernel schedule (no atomics):
-//  * attn_dkdv_bf16_kernel: one workgroup per 128 keys (4 waves x 32 keys)
-//    of one kv head.  K and V stay in registers; query blocks of 64 (and all
-//    query heads of the group) stream through a double-buffered LDS in both
-//    natural and transposed layouts.  dK^T and dV^T accumulate in registers.
-//  * attn_dq_bf16_kernel: one workgroup per 128 queries (4 waves x 32) of one
-//    query head.  Q, dO, LSE and D stay in registers; key blocks of 64 stream
-//    through LDS (K and V natural, K transposed).  dQ^T accumulates in
-//    registers.  S and dP are recomputed here rather than exchanged.
+//  * attn_dkdv_bf16_kernel: one workgroup per 128 keys of one kv head, in four
+//    32-key groups each served by a pair of waves with split roles (P / dV and
+//    dP / dS / dK).  K and V stay in registers; query blocks of 64 (and all
+//    query heads of the group) stream through a double-buffered LDS.  dK^T and
+//    dV^T accumulate in registers.
+//  * attn_dq_bf16_kernel: one workgroup per 32 x NW queries (NW waves, 8 by
+//    default) of one query head.  Q, dO, LSE and D stay in registers; key
+//    blocks of 64 stream through LDS (K and V natural, K read transposed).
+//    dQ^T accumulates in registers.  S and dP are recomputed here rather than
+//    exchanged.
 // MFMA layout conventions are those of the forward kernel (perm_row order
 // makes accumulator slots contiguous along the lane's row).
 #include "fab_device.h"
@@ -196,12 +198,12 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const bool p_role = wave < 4;
   const int kg = wave & 3;  // 32-key group
 
-  int id = blockIdx.x;
-  const int g = id % a.hkv;
-  id /= a.hkv;
-  const int bi = id % a.b;
-  id /= a.b;
-  const int kblk = id;  // causal: low key blocks see the most queries, so they go first
+  // head-major logical order; causal: low key blocks see the most queries, so
+  // they go first
+  const int nkb = (a.n + kAttnBwdKB - 1) / kAttnBwdKB;
+  const int lid = xcd_order(blockIdx.x, (int)gridDim.x);
+  const int kblk = lid % nkb, gh = lid / nkb;
+  const int g = gh % a.hkv, bi = gh / a.hkv;
   const int k0w = kblk * kAttnBwdKB + kg * 32;
   const int mykey = k0w + lq;
 
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup = 4 waves x 32 QT queries of one query head; key blocks of 64
+// dQ: workgroup = NW waves x 32 QT queries of one query head; key blocks of 64
 // stream through two LDS stages (K and V tiles; K^T is read transposed).
 // ---------------------------------------------------------------------------
 template <int D>
@@ -434,10 +436,12 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
 
 // SAME: K and V have equal row strides, so one set of copy offsets serves both.
 template <int D, bool CAUSAL, int QT, bool SAME>
-__global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kAttnDqWaves, QT == 1 ? 8 / kAttnDqWaves : 1) void
+attn_dq_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using S = DqStage<D>;
-  constexpr int BM = 128 * QT;
+  constexpr int NW = kAttnDqWaves;
+  constexpr int BM = 32 * NW * QT;
   __shared__ __attribute__((aligned(1024))) char smem[2 * S::BYTES];
 
   const int tid = threadIdx.x;
@@ -448,12 +452,10 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   const int tr_row = l16 >> 2;
 
   const int nqb = (a.m + BM - 1) / BM;
-  int id = blockIdx.x;
-  const int h = id % a.hq;
-  id /= a.hq;
-  const int bi = id % a.b;
-  id /= a.b;
-  const int qb = CAUSAL ? (nqb - 1 - id) : id;
+  const int lid = xcd_order(blockIdx.x, (int)gridDim.x);
+  const int qi = lid % nqb, bh = lid / nqb;
+  const int h = bh % a.hq, bi = bh / a.hq;
+  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
   const int g = h / a.group;
 
   const int q0 = qb * BM + wave * 32 * QT;
@@ -462,10 +464,10 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
   const int kend = CAUSAL ? min(a.n, qb * BM + BM) : a.n;
   const int nkb = (kend + C::TILE - 1) / C::TILE;
-  const TileOffsets<D, 4> tk = tile_offsets<D, 4>(a.k_sr, wave, lane);
-  const TileOffsets<D, 4> tv = SAME ? tk : tile_offsets<D, 4>(a.v_sr, wave, lane);
-  issue_tile<D, 4>(tk, kbase, a.k_sr, 0, a.n, smem + S::K, wave, lane);
-  issue_tile<D, 4>(tv, vbase, a.v_sr, 0, a.n, smem + S::V, wave, lane);
+  const TileOffsets<D, NW> tk = tile_offsets<D, NW>(a.k_sr, wave, lane);
+  const TileOffsets<D, NW> tv = SAME ? tk : tile_offsets<D, NW>(a.v_sr, wave, lane);
+  issue_tile<D, NW>(tk, kbase, a.k_sr, 0, a.n, smem + S::K, wave, lane);
+  issue_tile<D, NW>(tv, vbase, a.v_sr, 0, a.n, smem + S::V, wave, lane);
 
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const uint16_t* obase = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
@@ -501,8 +503,8 @@ __global__ __launch_bounds__(256, QT == 1 ? 2 : 1) void attn_dq_bf16_kernel(Attn
   for (int kb = 0; kb < nkb; ++kb) {
     if (kb + 1 < nkb) {
       char* nst = smem + ((kb + 1) & 1) * S::BYTES;
-      issue_tile<D, 4>(tk, kbase, a.k_sr, (kb + 1) * C::TILE, a.n, nst + S::K, wave, lane);
-      issue_tile<D, 4>(tv, vbase, a.v_sr, (kb + 1) * C::TILE, a.n, nst + S::V, wave, lane);
+      issue_tile<D, NW>(tk, kbase, a.k_sr, (kb + 1) * C::TILE, a.n, nst + S::K, wave, lane);
+      issue_tile<D, NW>(tv, vbase, a.v_sr, (kb + 1) * C::TILE, a.n, nst + S::V, wave, lane);
     }
     const char* st = smem + (kb & 1) * S::BYTES;
     const int key0 = kb * C::TILE;
@@ -580,11 +582,11 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   }
   constexpr int QT = kAttnBwdQT;
   const int nkb = (a.n + kAttnBwdKB - 1) / kAttnBwdKB;
-  const int nqb = (a.m + 128 * QT - 1) / (128 * QT);
+  const int nqb = (a.m + kAttnBwdBM - 1) / kAttnBwdBM;
   const dim3 gk((unsigned)nkb * a.hkv * a.b), gq((unsigned)nqb * a.hq * a.b);
   const bool same_qo = a.q_sr == a.o_sr, same_kv = a.k_sr == a.v_sr;
 #define FAB_DKDV(C, S) FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, C, S>), gk, dim3(64 * kDkdvWaves), 0, s, a))
-#define FAB_DQ(C, S) FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, C, QT, S>), gq, block, 0, s, a))
+#define FAB_DQ(C, S) FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, C, QT, S>), gq, dim3(64 * kAttnDqWaves), 0, s, a))
   if (a.causal) {
     if (same_qo) FAB_DKDV(true, true); else FAB_DKDV(true, false);
     if (same_kv) FAB_DQ(true, true); else FAB_DQ(true, false);

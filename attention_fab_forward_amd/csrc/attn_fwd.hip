@@ -8,8 +8,10 @@
 // 2.A).  The running row maximum and sum are the usual online-softmax
 // rescaling, which leaves the result equal to the plain definition.
 //
-// Layout choices (workgroup = 4 waves, each wave 32 QT queries; with QT = 2
-// the two 32-query MFMA tiles share every LDS fragment read):
+// Layout choices (workgroup = NW waves, 8 by default so that the 256 queries
+// of a workgroup share every K / V tile copied into LDS; each wave takes 32 QT
+// queries, and with QT = 2 the two 32-query MFMA tiles share every LDS
+// fragment read):
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: K is the A operand (from LDS),
 //    Q^T the B operand (registers, whole kernel).  Lane l owns query l%32 of
 //    each tile, so row max / row sum are in-lane plus one exchange with lane
@@ -39,13 +41,15 @@ template <int D>
 struct FwdCfg {
   static constexpr int BN = kAttnFwdBN;     // keys per step
   static constexpr int QT = kAttnFwdQT;     // 32-query tiles per wave
-  static constexpr int BM = 128 * QT;       // queries per workgroup
+  static constexpr int NW = kAttnFwdWaves;  // waves per workgroup
+  static constexpr int BM = 32 * NW * QT;   // queries per workgroup
   static constexpr int CPR = D / 8;         // 16-byte chunks per row
   static constexpr int RB = D * 2;          // row bytes (no padding)
   static constexpr int TILE = BN * RB;      // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;
   static constexpr int RPI = 1024 / RB;     // rows per 1 KiB async copy
-  static constexpr int CPW = TILE / 1024 / 4;  // async copies per wave per tile
+  static constexpr int CPW = TILE / 1024 / NW;  // async copies per wave per tile
+  static_assert(CPW * NW * 1024 == TILE, "tile copies must split evenly over the waves");
   static constexpr int DT = D / 32;         // 32-wide output tiles
   static constexpr int DC = D / 16;         // 16-deep contraction chunks
 };
@@ -123,7 +127,8 @@ __device__ __forceinline__ void issue_tile(const TileOffsets<D>& t, const uint16
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, FwdCfg<D>::QT == 1 ? 2 : 1) void attn_fwd_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * FwdCfg<D>::NW, FwdCfg<D>::QT == 1 ? 8 / FwdCfg<D>::NW : 1) void
+attn_fwd_bf16_kernel(AttnArgs a) {
   using C = FwdCfg<D>;
   constexpr int QT = C::QT;
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
@@ -134,12 +139,11 @@ __global__ __launch_bounds__(256, FwdCfg<D>::QT == 1 ? 2 : 1) void attn_fwd_bf16
   const int l16 = lane & 15, g16 = lane >> 4;
 
   const int nqb = (a.m + C::BM - 1) / C::BM;
-  int id = blockIdx.x;
-  const int h = id % a.hq;
-  id /= a.hq;
-  const int bi = id % a.b;
-  id /= a.b;
-  const int qb = CAUSAL ? (nqb - 1 - id) : id;
+  // head-major logical order, longest query blocks of a head first
+  const int lid = xcd_order(blockIdx.x, (int)gridDim.x);
+  const int qi = lid % nqb, bh = lid / nqb;
+  const int h = bh % a.hq, bi = bh / a.hq;
+  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
   const int g = h / a.group;
 
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
@@ -324,7 +328,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::QT == 1 ? 2 : 1) void attn_fwd_bf16
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
   const int nqb = (a.m + FwdCfg<D>::BM - 1) / FwdCfg<D>::BM;
-  const dim3 grid((unsigned)nqb * a.hq * a.b), block(256);
+  const dim3 grid((unsigned)nqb * a.hq * a.b), block(64 * FwdCfg<D>::NW);
   if (a.causal)
     FAB_TIMED("attn_fwd_bf16", s, hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, true>), grid, block, 0, s, a));
   else

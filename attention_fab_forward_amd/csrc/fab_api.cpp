@@ -16,7 +16,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/fab.h"
+#include "fab.h"
 #include "fab_internal.h"
 
 namespace {

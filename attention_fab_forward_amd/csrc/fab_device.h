@@ -103,6 +103,17 @@ __device__ __forceinline__ float wave_xor32(float v) {
   return __shfl_xor(v, 32, 64);
 }
 
+
+// Workgroup i runs on XCD i % 8 (each XCD has its own L2).  Returns a logical
+// index such that XCD x executes the contiguous logical range
+// [x * per, (x + 1) * per), per = total / 8; a tail beyond 8 * per keeps its
+// index.  Bijective on [0, total).
+__device__ __forceinline__ int xcd_order(int id, int total) {
+  const int per = total / 8;
+  if (id >= 8 * per) return id;
+  return (id % 8) * per + id / 8;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -72,14 +72,22 @@ void timer_end(hipStream_t s);
 #ifndef FAB_FWD_QT
 #define FAB_FWD_QT 1
 #endif
-constexpr int kAttnFwdQT = FAB_FWD_QT;      // 32-query MFMA tiles per wave
-constexpr int kAttnFwdBM = 128 * kAttnFwdQT;  // queries per workgroup (4 waves)
+#ifndef FAB_FWD_WAVES
+#define FAB_FWD_WAVES 8
+#endif
+constexpr int kAttnFwdQT = FAB_FWD_QT;        // 32-query MFMA tiles per wave
+constexpr int kAttnFwdWaves = FAB_FWD_WAVES;  // waves per workgroup
+constexpr int kAttnFwdBM = 32 * kAttnFwdWaves * kAttnFwdQT;  // queries per workgroup
 constexpr int kAttnFwdBN = 64;    // keys per inner step
 #ifndef FAB_BWD_QT
 #define FAB_BWD_QT 1
 #endif
+#ifndef FAB_DQ_WAVES
+#define FAB_DQ_WAVES 8
+#endif
 constexpr int kAttnBwdQT = FAB_BWD_QT;        // dQ kernel: 32-query tiles per wave
-constexpr int kAttnBwdBM = 128 * kAttnBwdQT;  // dQ kernel: queries per workgroup
+constexpr int kAttnDqWaves = FAB_DQ_WAVES;    // dQ kernel: waves per workgroup
+constexpr int kAttnBwdBM = 32 * kAttnDqWaves * kAttnBwdQT;  // dQ kernel: queries per workgroup
 constexpr int kAttnBwdKB = 128;   // dK/dV kernel: keys per workgroup (4 waves x 32)
 constexpr int kAttnBwdQB = 64;    // dK/dV kernel: queries per inner step
 
