@@ -95,13 +95,13 @@ __device__ __forceinline__ void issue_tile(const TileOffsets<D, NW>& t, const ui
   char* d = dst + wave * T::CPW * 1024;
   if (r0 + C::TILE <= nrows) {
 #pragma unroll
-    for (int i = 0; i < T::CPW; ++i) g2lds16(b + t.off[i], d + i * 1024);
+    for (int i = 0; i < T::CPW; ++i) dma16(b, t.off[i], d + i * 1024);
   } else {
 #pragma unroll
     for (int i = 0; i < T::CPW; ++i) {
       const int x = tile_row_of_copy<D, NW>(wave, lane, i);
       const int64_t shift = min(x, nrows - 1 - r0) - x;
-      g2lds16(b + t.off[i] + 2 * shift * sr, d + i * 1024);
+      dma16_at(b + t.off[i] + 2 * shift * sr, d + i * 1024);
     }
   }
 }
@@ -136,7 +136,7 @@ __device__ __forceinline__ u32x4 read_tr(const char* tile, int t, int sb, int c,
 __device__ __forceinline__ void issue_vec64(const float* src, int i0, int count, char* dst,
                                             int lane) {
   const int i = min(i0 + lane, count - 1);
-  __builtin_amdgcn_global_load_lds(src + i, (lds_void*)dst, 4, 0, 0);
+  dma4_at(src + i, dst);
 }
 
 // ---------------------------------------------------------------------------
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
   f32x4* px = reinterpret_cast<f32x4*>(smem + L::PX + kg * L::PX_GROUP) + lane;
   wait_vmem();
-  __syncthreads();
+  lds_barrier();
 
   // The two roles run separate copies of the step loop (same barriers per
   // step), so each loop keeps only its own role's invariants in registers.
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
           }
         }
       }
-      __syncthreads();  // P visible to the dS waves
+      lds_barrier();  // P visible to the dS waves
       if (work) {
 #pragma unroll
         for (int sq = 0; sq < 2; ++sq)
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
               acc[t] = mfma32(read_tr<D>(st + L::DO, t, sq, c, lg, tr_d, tr_row), pb[sq][c], acc[t]);
       }
       wait_vmem();
-      __syncthreads();
+      lds_barrier();
     }
   } else {
     for (int step = 0; step < steps; ++step) {
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
             dp[sq] = mfma32(read_nat<D>(st + L::DO, sq, c, lq, lg), kv[c], dp[sq]);
         }
       }
-      __syncthreads();  // P from the partner wave
+      lds_barrier();  // P from the partner wave
       if (work) {
 #pragma unroll
         for (int sq = 0; sq < 2; ++sq) {
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
         }
       }
       wait_vmem();
-      __syncthreads();
+      lds_barrier();
     }
   }
 
@@ -498,7 +498,7 @@ attn_dq_bf16_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) dq[qt][t][r] = 0.f;
   const float cs = a.scale_log2;
   wait_vmem();
-  __syncthreads();
+  lds_barrier();
 
   for (int kb = 0; kb < nkb; ++kb) {
     if (kb + 1 < nkb) {
@@ -515,7 +515,7 @@ attn_dq_bf16_kernel(AttnArgs a) {
                               tr_d, tr_row);
     }
     wait_vmem();
-    __syncthreads();
+    lds_barrier();
   }
 
 #pragma unroll

@@ -110,8 +110,8 @@ __device__ __forceinline__ void issue_tile(const TileOffsets<D>& t, const uint16
   if (key0 + C::BN <= n) {
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
-      g2lds16(kb + t.k[i], kdst + i * 1024);
-      g2lds16(vb + t.v[i], vdst + i * 1024);
+      dma16(kb, t.k[i], kdst + i * 1024);
+      dma16(vb, t.v[i], vdst + i * 1024);
     }
   } else {
 #pragma unroll
@@ -120,8 +120,8 @@ __device__ __forceinline__ void issue_tile(const TileOffsets<D>& t, const uint16
       const int kr = perm_row(r & 31) + (r & ~31);
       const int64_t kc = min(kr, n - 1 - key0) - kr;  // row shifts for clamping
       const int64_t vc = min(r, n - 1 - key0) - r;
-      g2lds16(kb + t.k[i] + 2 * kc * k_sr, kdst + i * 1024);
-      g2lds16(vb + t.v[i] + 2 * vc * v_sr, vdst + i * 1024);
+      dma16_at(kb + t.k[i] + 2 * kc * k_sr, kdst + i * 1024);
+      dma16_at(vb + t.v[i] + 2 * vc * v_sr, vdst + i * 1024);
     }
   }
 }
@@ -192,7 +192,7 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   const int tr_row = l16 >> 2;
 
   wait_vmem();
-  __syncthreads();
+  lds_barrier();
 
   for (int kb = 0; kb < nkb; ++kb) {
     const bool more = kb + 1 < nkb;
@@ -297,7 +297,7 @@ attn_fwd_bf16_kernel(AttnArgs a) {
       }
     }
     wait_vmem();
-    __syncthreads();
+    lds_barrier();
   }
 
   if (!wave_live) return;

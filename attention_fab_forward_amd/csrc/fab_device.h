@@ -91,8 +91,47 @@ __device__ __forceinline__ u32x2 lds_tr8(const char* p) {
 // Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane i of
 // the wave writes LDS bytes [lds_base + 16 i, lds_base + 16 i + 16).  lds_base
 // must be wave-uniform.  Completion is tracked by the vector-memory counter.
-__device__ __forceinline__ void g2lds16(const void* gsrc, char* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)(lds_base), 16, 0, 0);
+// Asynchronous global -> LDS copies (gfx950 global_load_lds): lane i's bytes
+// land at LDS byte address lds + size * i, lds wave-uniform (passed in M0).
+// They are issued as inline assembly so the compiler does not track them: its
+// own tracking waits for every copy in flight before any transposing LDS
+// read, which would serialise the prefetch with the compute.  Callers wait
+// for their copies (wait_vmem) before the barrier that publishes them, and no
+// compiler-generated code here keeps a value in M0.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from base + voff (base wave-uniform, voff per lane, >= 0).
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, const char* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr(lds)), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+// 16 bytes per lane from a per-lane 64-bit address.
+__device__ __forceinline__ void dma16_at(const void* addr, const char* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_addr(lds)), "v"(addr)
+               : "memory", "m0");
+}
+// 4 bytes per lane from a per-lane 64-bit address.
+__device__ __forceinline__ void dma4_at(const void* addr, const char* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_addr(lds)), "v"(addr)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Workgroup barrier ordering LDS accesses only: unlike __syncthreads it does
+// not wait for outstanding global memory operations (the copies in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // s_waitcnt vmcnt(0) with the export and LDS counters left unconstrained
