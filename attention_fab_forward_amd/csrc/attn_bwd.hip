@@ -390,6 +390,7 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[qt][r] = dp[qt][r] = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < C::DC; ++c) {
       const u32x4 kfr = read_nat<D>(st + S::K, sb, c, lq, lg);
@@ -400,6 +401,7 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
         dp[qt] = mfma32(vfr, df[qt][c], dp[qt]);
       }
     }
+    if constexpr (QT == 1) sched_lds_mfma<2 * C::DC, 1, 4>();
     if (need_mask) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
@@ -431,6 +433,7 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) dq[qt][t] = mfma32(kt, db[qt][c], dq[qt][t]);
       }
+    if constexpr (QT == 1) sched_lds_mfma<2 * C::DT, 2, 2>();
   }
 }
 

@@ -214,16 +214,15 @@ attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[qt][sb][r] = 0.f;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int row = 32 * sb + lq;
-        const char* krow = kbuf + row * C::RB;
+      for (int c = 0; c < C::DC; ++c)
 #pragma unroll
-        for (int c = 0; c < C::DC; ++c) {
-          const u32x4 kf = lds16(krow + 16 * k_swz<D>(row, 2 * c + lg));
+        for (int sb = 0; sb < 2; ++sb) {
+          const int row = 32 * sb + lq;
+          const u32x4 kf = lds16(kbuf + row * C::RB + 16 * k_swz<D>(row, 2 * c + lg));
 #pragma unroll
           for (int qt = 0; qt < QT; ++qt) s[qt][sb] = mfma32(kf, qf[qt][c], s[qt][sb]);
         }
-      }
+      if constexpr (QT == 1) sched_lds_mfma<2 * C::DC, 1, 4>();
       const bool need_mask = (CAUSAL && key0 + C::BN - 1 > q0) || (key0 + C::BN > a.n);
       if (need_mask) {
 #pragma unroll
