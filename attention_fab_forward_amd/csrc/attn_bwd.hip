@@ -260,8 +260,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
           f32x16 s;
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-          for (int c = 0; c < C::DC; ++c) s = mfma32(read_nat<D>(st + L::Q, sq, c, lq, lg), kv[c], s);
+          lds_mfma_pipeline<C::DC, 4>(
+              [&](int c) { return read_nat<D>(st + L::Q, sq, c, lq, lg); },
+              [&](int c, const u32x4& x) { s = mfma32(x, kv[c], s); });
           if (need_mask) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -284,13 +285,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
       }
       lds_barrier();  // P visible to the dS waves
       if (work) {
-#pragma unroll
-        for (int sq = 0; sq < 2; ++sq)
-#pragma unroll
-          for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-              acc[t] = mfma32(read_tr<D>(st + L::DO, t, sq, c, lg, tr_d, tr_row), pb[sq][c], acc[t]);
+        // operand i: query sub-block i / (2 DT), output tile (i / 2) % DT, chunk i % 2
+        lds_mfma_pipeline<4 * C::DT, 4>(
+            [&](int i) {
+              return read_tr<D>(st + L::DO, (i / 2) % C::DT, i / (2 * C::DT), i % 2, lg, tr_d, tr_row);
+            },
+            [&](int i, const u32x4& x) {
+              acc[(i / 2) % C::DT] = mfma32(x, pb[i / (2 * C::DT)][i % 2], acc[(i / 2) % C::DT]);
+            });
       }
       wait_vmem();
       lds_barrier();
@@ -312,9 +314,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) dp[sq][4 * j + e] = x[e];
           }
-#pragma unroll
-          for (int c = 0; c < C::DC; ++c)
-            dp[sq] = mfma32(read_nat<D>(st + L::DO, sq, c, lq, lg), kv[c], dp[sq]);
+          lds_mfma_pipeline<C::DC, 4>(
+              [&](int c) { return read_nat<D>(st + L::DO, sq, c, lq, lg); },
+              [&](int c, const u32x4& x) { dp[sq] = mfma32(x, kv[c], dp[sq]); });
         }
       }
       lds_barrier();  // P from the partner wave
@@ -329,11 +331,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
             db[j >> 1][2 * (j & 1) + 1] =
                 pack_bf16(p[2] * dp[sq][4 * j + 2], p[3] * dp[sq][4 * j + 3]);
           }
-#pragma unroll
-          for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-              acc[t] = mfma32(read_tr<D>(st + L::Q, t, sq, c, lg, tr_d, tr_row), db[c], acc[t]);
+          lds_mfma_pipeline<2 * C::DT, 4>(
+              [&](int i) { return read_tr<D>(st + L::Q, i / 2, sq, i % 2, lg, tr_d, tr_row); },
+              [&](int i, const u32x4& x) { acc[i / 2] = mfma32(x, db[i % 2], acc[i / 2]); });
         }
       }
       wait_vmem();

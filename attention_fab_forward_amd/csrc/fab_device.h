@@ -143,6 +143,24 @@ __device__ __forceinline__ void sched_lds_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
 }
 
+// Software-pipelined run of N MFMAs whose A operands come from LDS:
+// read(i) issues the LDS reads of operand i, mma(i, x) consumes it.  Operands
+// are requested DEPTH MFMAs ahead through a ring of DEPTH registers sets, and
+// scheduling barriers (VALU, SALU and transcendental work may still move
+// across them) keep the compiler from sinking the reads next to their uses.
+template <int N, int DEPTH, class Read, class Mma>
+__device__ __forceinline__ void lds_mfma_pipeline(Read read, Mma mma) {
+  u32x4 buf[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH && i < N; ++i) buf[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    mma(i, buf[i % DEPTH]);
+    if (i + DEPTH < N) buf[i % DEPTH] = read(i + DEPTH);
+    __builtin_amdgcn_sched_barrier(0x0406);
+  }
+}
+
 // Workgroup barrier ordering LDS accesses only: unlike __syncthreads it does
 // not wait for outstanding global memory operations (the copies in flight).
 __device__ __forceinline__ void lds_barrier() {
