@@ -390,18 +390,24 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[qt][r] = dp[qt][r] = 0.f;
-    __builtin_amdgcn_sched_barrier(0);
+    // operand i: d chunk c = i / 2 of K (i even, for S) or V (i odd, for dP)
+    auto kv_read = [&](int i) { return read_nat<D>(st + (i % 2 ? S::V : S::K), sb, i / 2, lq, lg); };
+    if constexpr (QT == 1) {
+      lds_mfma_pipeline<2 * C::DC, 4>(kv_read, [&](int i, const u32x4& x) {
+        if (i % 2) dp[0] = mfma32(x, df[0][i / 2], dp[0]);
+        else s[0] = mfma32(x, qf[0][i / 2], s[0]);
+      });
+    } else {
 #pragma unroll
-    for (int c = 0; c < C::DC; ++c) {
-      const u32x4 kfr = read_nat<D>(st + S::K, sb, c, lq, lg);
-      const u32x4 vfr = read_nat<D>(st + S::V, sb, c, lq, lg);
+      for (int i = 0; i < 2 * C::DC; ++i) {
+        const u32x4 x = kv_read(i);
 #pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        s[qt] = mfma32(kfr, qf[qt][c], s[qt]);
-        dp[qt] = mfma32(vfr, df[qt][c], dp[qt]);
+        for (int qt = 0; qt < QT; ++qt) {
+          if (i % 2) dp[qt] = mfma32(x, df[qt][i / 2], dp[qt]);
+          else s[qt] = mfma32(x, qf[qt][i / 2], s[qt]);
+        }
       }
     }
-    if constexpr (QT == 1) sched_lds_mfma<2 * C::DC, 1, 4>();
     if (need_mask) {
 #pragma unroll
       for (int qt = 0; qt < QT; ++qt)
@@ -425,15 +431,20 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
 #pragma unroll
         for (int w = 0; w < 4; ++w) db[qt][c][w] = pack_bf16(ds[8 * c + 2 * w], ds[8 * c + 2 * w + 1]);
     }
+    // operand i: output tile t = i % DT, key chunk c = i / DT
+    auto kt_read = [&](int i) { return read_tr<D>(st + S::K, i % C::DT, sb, i / C::DT, lg, tr_d, tr_row); };
+    if constexpr (QT == 1) {
+      lds_mfma_pipeline<2 * C::DT, 4>(kt_read, [&](int i, const u32x4& x) {
+        dq[0][i % C::DT] = mfma32(x, db[0][i / C::DT], dq[0][i % C::DT]);
+      });
+    } else {
 #pragma unroll
-    for (int t = 0; t < C::DT; ++t)
+      for (int i = 0; i < 2 * C::DT; ++i) {
+        const u32x4 x = kt_read(i);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 kt = read_tr<D>(st + S::K, t, sb, c, lg, tr_d, tr_row);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) dq[qt][t] = mfma32(kt, db[qt][c], dq[qt][t]);
+        for (int qt = 0; qt < QT; ++qt) dq[qt][i % C::DT] = mfma32(x, db[qt][i / C::DT], dq[qt][i % C::DT]);
       }
-    if constexpr (QT == 1) sched_lds_mfma<2 * C::DT, 2, 2>();
+    }
   }
 }
 

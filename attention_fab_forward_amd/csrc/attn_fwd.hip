@@ -213,16 +213,23 @@ attn_fwd_bf16_kernel(AttnArgs a) {
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[qt][sb][r] = 0.f;
+      // operand i: d chunk c = i / 2 of key sub-block sb = i % 2
+      auto k_read = [&](int i) {
+        const int row = 32 * (i % 2) + lq;
+        return lds16(kbuf + row * C::RB + 16 * k_swz<D>(row, 2 * (i / 2) + lg));
+      };
+      if constexpr (QT == 1) {
+        lds_mfma_pipeline<2 * C::DC, 4>(k_read, [&](int i, const u32x4& x) {
+          s[0][i % 2] = mfma32(x, qf[0][i / 2], s[0][i % 2]);
+        });
+      } else {
 #pragma unroll
-      for (int c = 0; c < C::DC; ++c)
+        for (int i = 0; i < 2 * C::DC; ++i) {
+          const u32x4 kf = k_read(i);
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const int row = 32 * sb + lq;
-          const u32x4 kf = lds16(kbuf + row * C::RB + 16 * k_swz<D>(row, 2 * c + lg));
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) s[qt][sb] = mfma32(kf, qf[qt][c], s[qt][sb]);
+          for (int qt = 0; qt < QT; ++qt) s[qt][i % 2] = mfma32(kf, qf[qt][i / 2], s[qt][i % 2]);
         }
-      if constexpr (QT == 1) sched_lds_mfma<2 * C::DC, 1, 4>();
+      }
       const bool need_mask = (CAUSAL && key0 + C::BN - 1 > q0) || (key0 + C::BN > a.n);
       if (need_mask) {
 #pragma unroll
@@ -276,23 +283,31 @@ attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[qt][t][r] *= alpha[qt];
       }
-#pragma unroll
-      for (int t = 0; t < C::DT; ++t) {
+      // operand i: output tile t = i % DT, keys 32 sb + 16 lg + 8 c + e with
+      // (sb, c) = (i / DT / 2, i / DT % 2), read as two 4-key groups
+      auto v_read = [&](int i) {
+        const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
         const int dcol = 32 * t + tr_d;    // first of the 4 d columns this lane addresses
         const int cbyte = 2 * (dcol & 7);  // byte offset inside its 16-byte chunk
+        const int r0 = 32 * sb + 16 * (g16 >> 1) + 8 * c + tr_row;
+        const int r1 = r0 + 4;
+        const u32x2 lo = lds_tr8(vbuf + r0 * C::RB + 16 * v_swz<D>(r0, dcol >> 3) + cbyte);
+        const u32x2 hi = lds_tr8(vbuf + r1 * C::RB + 16 * v_swz<D>(r1, dcol >> 3) + cbyte);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      if constexpr (QT == 1) {
+        lds_mfma_pipeline<4 * C::DT, 4>(v_read, [&](int i, const u32x4& x) {
+          const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
+          o[0][t] = mfma32(x, pb[0][sb][c], o[0][t]);
+        });
+      } else {
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+        for (int i = 0; i < 4 * C::DT; ++i) {
+          const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
+          const u32x4 vf = v_read(i);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            // keys 32 sb + 16 lg + 8 c + e, e = 0..7, read as two 4-key groups
-            const int r0 = 32 * sb + 16 * (g16 >> 1) + 8 * c + tr_row;
-            const int r1 = r0 + 4;
-            const u32x2 lo = lds_tr8(vbuf + r0 * C::RB + 16 * v_swz<D>(r0, dcol >> 3) + cbyte);
-            const u32x2 hi = lds_tr8(vbuf + r1 * C::RB + 16 * v_swz<D>(r1, dcol >> 3) + cbyte);
-            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) o[qt][t] = mfma32(vf, pb[qt][sb][c], o[qt][t]);
-          }
+          for (int qt = 0; qt < QT; ++qt) o[qt][t] = mfma32(vf, pb[qt][sb][c], o[qt][t]);
+        }
       }
     }
     wait_vmem();

@@ -126,23 +126,6 @@ __device__ __forceinline__ void dma4_at(const void* addr, const char* lds) {
 }
 #pragma clang diagnostic pop
 
-// Scheduling hint for a straight run of N MFMAs each fed by R LDS reads: the
-// reads of the first P MFMAs go out at once, then the scheduler alternates
-// one MFMA with the R reads of the MFMA P places later, so each operand is
-// requested P MFMAs (32 cycles each) before its use instead of just before
-// it.  Instructions of other kinds are placed freely around these groups.
-template <int N, int R, int P>
-__device__ __forceinline__ void sched_lds_mfma() {
-  static_assert(N > P && P > 0 && R > 0, "bad pipeline shape");
-  __builtin_amdgcn_sched_group_barrier(0x100, P * R, 0);  // DS reads
-#pragma unroll
-  for (int i = 0; i < N - P; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
-}
-
 // Software-pipelined run of N MFMAs whose A operands come from LDS:
 // read(i) issues the LDS reads of operand i, mma(i, x) consumes it.  Operands
 // are requested DEPTH MFMAs ahead through a ring of DEPTH registers sets, and
