@@ -96,42 +96,47 @@ __device__ __forceinline__ TileOffsets<D> tile_offsets(int64_t k_sr, int64_t v_s
   return t;
 }
 
-// Rows past n (only in a ragged last block) are clamped to row n - 1: their
-// scores are masked, so their probabilities are zero.
-template <int D>
-__device__ __forceinline__ void issue_tile(const TileOffsets<D>& t, const uint16_t* kbase,
-                                           const uint16_t* vbase, int64_t k_sr, int64_t v_sr,
-                                           int key0, int n, char* stage, int wave, int lane) {
+// Async copy of key block [key0, key0 + BN) of K (perm_row row order) or V
+// (natural order) into an LDS tile.  Rows past n (only in a ragged last block)
+// are clamped to row n - 1: their scores are masked, so their probabilities
+// are zero.
+template <int D, bool IS_K>
+__device__ __forceinline__ void issue_kv(const TileOffsets<D>& t, const uint16_t* base,
+                                         int64_t sr, int key0, int n, char* tile, int wave,
+                                         int lane) {
   using C = FwdCfg<D>;
-  const char* kb = reinterpret_cast<const char*>(kbase + (int64_t)key0 * k_sr);
-  const char* vb = reinterpret_cast<const char*>(vbase + (int64_t)key0 * v_sr);
-  char* kdst = stage + wave * C::CPW * 1024;
-  char* vdst = kdst + C::TILE;
+  const char* src = reinterpret_cast<const char*>(base + (int64_t)key0 * sr);
+  char* dst = tile + wave * C::CPW * 1024;
   if (key0 + C::BN <= n) {
 #pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
-      dma16(kb, t.k[i], kdst + i * 1024);
-      dma16(vb, t.v[i], vdst + i * 1024);
-    }
+    for (int i = 0; i < C::CPW; ++i) dma16(src, IS_K ? t.k[i] : t.v[i], dst + i * 1024);
   } else {
 #pragma unroll
     for (int i = 0; i < C::CPW; ++i) {
       const int r = copy_row<D>(wave, lane, i);
-      const int kr = perm_row(r & 31) + (r & ~31);
-      const int64_t kc = min(kr, n - 1 - key0) - kr;  // row shifts for clamping
-      const int64_t vc = min(r, n - 1 - key0) - r;
-      dma16_at(kb + t.k[i] + 2 * kc * k_sr, kdst + i * 1024);
-      dma16_at(vb + t.v[i] + 2 * vc * v_sr, vdst + i * 1024);
+      const int kr = IS_K ? perm_row(r & 31) + (r & ~31) : r;
+      const int64_t shift = min(kr, n - 1 - key0) - kr;  // row shift for clamping
+      dma16_at(src + (IS_K ? t.k[i] : t.v[i]) + 2 * shift * sr, dst + i * 1024);
     }
   }
 }
 
+// Software pipeline over key blocks: while the softmax of block j runs on the
+// VALU, the MFMAs of S for block j+1 are already issued, so the two overlap
+// inside each wave.  K tiles are therefore copied two blocks ahead and V tiles
+// one block ahead (two LDS buffers each).  Iteration j:
+//   copy K[j+2] -> Kbuf[j % 2], V[j+1] -> Vbuf[(j+1) % 2]
+//   mask S[j] (diagonal / ragged blocks), softmax(S[j]) || S[j+1] = K[j+1] Q^T
+//   rescale O if the running maximum moved, O += V[j]^T P[j]^T
+//   wait for this wave's copies, barrier
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * FwdCfg<D>::NW, FwdCfg<D>::QT == 1 ? 8 / FwdCfg<D>::NW : 1) void
+__global__ __launch_bounds__(64 * FwdCfg<D>::NW, 8 / FwdCfg<D>::NW) void
 attn_fwd_bf16_kernel(AttnArgs a) {
   using C = FwdCfg<D>;
-  constexpr int QT = C::QT;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
+  static_assert(C::QT == 1, "the pipelined forward takes one 32-query tile per wave");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * C::TILE];
+  auto kbuf = [&](int i) { return smem + (i & 1) * C::TILE; };        // K tile buffers
+  auto vbuf = [&](int i) { return smem + (2 + (i & 1)) * C::TILE; };  // V tile buffers
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -150,37 +155,36 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
 
-  const int q0 = qb * C::BM + wave * 32 * QT;  // first query of this wave
-  const bool wave_live = q0 < a.m;
-  int myq[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) myq[qt] = q0 + 32 * qt + lq;
+  const int q0 = qb * C::BM + wave * 32;  // first query of this wave
+  const int myq = q0 + lq;
 
   const int kend = CAUSAL ? min(a.n, qb * C::BM + C::BM) : a.n;
-  const int nkb = (kend + C::BN - 1) / C::BN;
+  const int nkb = (kend + C::BN - 1) / C::BN;  // key blocks of the workgroup
+  // key blocks this wave computes (causal: up to the one holding its last query)
+  const int nkw = q0 >= a.m ? 0 : CAUSAL ? min(nkb, (q0 + 31) / C::BN + 1) : nkb;
   const TileOffsets<D> toff = tile_offsets<D>(a.k_sr, a.v_sr, wave, lane);
-  issue_tile<D>(toff, kbase, vbase, a.k_sr, a.v_sr, 0, a.n, smem, wave, lane);
+  auto copy_k = [&](int kb) {
+    issue_kv<D, true>(toff, kbase, a.k_sr, kb * C::BN, a.n, kbuf(kb), wave, lane);
+  };
+  auto copy_v = [&](int kb) {
+    issue_kv<D, false>(toff, vbase, a.v_sr, kb * C::BN, a.n, vbuf(kb), wave, lane);
+  };
+  copy_k(0);
+  copy_v(0);
+  if (nkb > 1) copy_k(1);
 
   // Q^T fragments: lane holds Q[myq][16c + 8lg .. +7] for every chunk c.
-  u32x4 qf[QT][C::DC];
+  u32x4 qf[C::DC];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-    for (int c = 0; c < C::DC; ++c)
-      qf[qt][c] = myq[qt] < a.m ? ldg16(qbase + (int64_t)myq[qt] * a.q_sr + 16 * c + 8 * lg)
-                                : u32x4{0, 0, 0, 0};
+  for (int c = 0; c < C::DC; ++c)
+    qf[c] = myq < a.m ? ldg16(qbase + (int64_t)myq * a.q_sr + 16 * c + 8 * lg) : u32x4{0, 0, 0, 0};
 
-  f32x16 o[QT][C::DT];
-  float m_run[QT], l_run[QT];
+  f32x16 o[C::DT];
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
+  for (int t = 0; t < C::DT; ++t)
 #pragma unroll
-    for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[qt][t][r] = 0.f;
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
   const float cs = a.scale_log2;
 
   // Transposed V^T reads (ds_read_b64_tr_b16): this lane, as source lane
@@ -191,151 +195,142 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   const int tr_d = 16 * (u & 1) + 8 * (g16 & 1) + 4 * (u >> 1);  // + 32 t
   const int tr_row = l16 >> 2;
 
+  // S^T of one key block: s[sb] holds keys 32 sb + 16 lg + r (slot r) of query
+  // myq.  Operand i: d chunk c = i / 2 of key sub-block sb = i % 2.
+  auto compute_s = [&](f32x16 (&s)[2], const char* kt) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+    lds_mfma_pipeline<2 * C::DC, 4>(
+        [&](int i) {
+          const int row = 32 * (i % 2) + lq;
+          return lds16(kt + row * C::RB + 16 * k_swz<D>(row, 2 * (i / 2) + lg));
+        },
+        [&](int i, const u32x4& x) { s[i % 2] = mfma32(x, qf[i / 2], s[i % 2]); });
+  };
+
+  // One pipelined step on key block kb (NEXT: also compute S of block kb + 1).
+  f32x16 s[2];
+  auto step = [&]<bool NEXT>(int kb) {
+    const int key0 = kb * C::BN;
+    if ((CAUSAL && key0 + C::BN - 1 > q0) || key0 + C::BN > a.n) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * sb + 16 * lg + r;
+          if ((CAUSAL && key > myq) || key >= a.n) s[sb][r] = -INFINITY;
+        }
+    }
+    f32x16 sn[2];
+    if constexpr (NEXT) compute_s(sn, kbuf(kb + 1));
+    // online softmax of block kb (VALU, overlapping the MFMAs above)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+    mx = pair_max(mx) * cs;
+    // move the reference maximum only when p would otherwise exceed 2^8
+    const float m_new = mx > m_run + 8.f ? mx : m_run;
+    const float alpha = fast_exp2(m_run - m_new);
+    const bool rescale = m_new != m_run;
+    float lsum = 0.f;
+    u32x4 pb[2][2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(s[sb][r], cs, -m_new));
+        lsum += p[r];
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pb[sb][c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
+    }
+    l_run = l_run * alpha + lsum;
+    m_run = m_new;
+    if (__ballot(rescale)) {
+#pragma unroll
+      for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+    }
+    // O^T += V^T P^T.  Operand i: output tile t = i % DT, keys
+    // 32 sb + 16 lg + 8 c + e with (sb, c) = (i / DT / 2, i / DT % 2), read as
+    // two 4-key groups.
+    const char* vt = vbuf(kb);
+    lds_mfma_pipeline<4 * C::DT, 4>(
+        [&](int i) {
+          const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
+          const int dcol = 32 * t + tr_d;    // first of the 4 d columns this lane addresses
+          const int cbyte = 2 * (dcol & 7);  // byte offset inside its 16-byte chunk
+          const int r0 = 32 * sb + 16 * (g16 >> 1) + 8 * c + tr_row;
+          const int r1 = r0 + 4;
+          const u32x2 lo = lds_tr8(vt + r0 * C::RB + 16 * v_swz<D>(r0, dcol >> 3) + cbyte);
+          const u32x2 hi = lds_tr8(vt + r1 * C::RB + 16 * v_swz<D>(r1, dcol >> 3) + cbyte);
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        },
+        [&](int i, const u32x4& x) {
+          const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
+          o[t] = mfma32(x, pb[sb][c], o[t]);
+        });
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) s[sb] = sn[sb];
+    }
+  };
+  // copies issued at the top of iteration kb
+  auto prefetch = [&](int kb) {
+    if (kb + 2 < nkb) copy_k(kb + 2);
+    if (kb + 1 < nkb) copy_v(kb + 1);
+  };
+
   wait_vmem();
   lds_barrier();
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (more)
-      issue_tile<D>(toff, kbase, vbase, a.k_sr, a.v_sr, (kb + 1) * C::BN, a.n,
-                    smem + ((kb + 1) & 1) * C::STAGE, wave, lane);
-
-    const int key0 = kb * C::BN;
-    const char* kbuf = smem + (kb & 1) * C::STAGE;
-    const char* vbuf = kbuf + C::TILE;
-    const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 32 * QT - 1);
-    if (wave_work) {
-      // S^T tiles: [query tile][32-key sub-block]
-      f32x16 s[QT][2];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[qt][sb][r] = 0.f;
-      // operand i: d chunk c = i / 2 of key sub-block sb = i % 2
-      auto k_read = [&](int i) {
-        const int row = 32 * (i % 2) + lq;
-        return lds16(kbuf + row * C::RB + 16 * k_swz<D>(row, 2 * (i / 2) + lg));
-      };
-      if constexpr (QT == 1) {
-        lds_mfma_pipeline<2 * C::DC, 4>(k_read, [&](int i, const u32x4& x) {
-          s[0][i % 2] = mfma32(x, qf[0][i / 2], s[0][i % 2]);
-        });
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2 * C::DC; ++i) {
-          const u32x4 kf = k_read(i);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) s[qt][i % 2] = mfma32(kf, qf[qt][i / 2], s[qt][i % 2]);
-        }
-      }
-      const bool need_mask = (CAUSAL && key0 + C::BN - 1 > q0) || (key0 + C::BN > a.n);
-      if (need_mask) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = key0 + 32 * sb + 16 * lg + r;
-              if ((CAUSAL && key > myq[qt]) || key >= a.n) s[qt][sb][r] = -INFINITY;
-            }
-      }
-      u32x4 pb[QT][2][2];
-      bool rescale = false;
-      float alpha[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qt][sb][r]);
-        mx = fmaxf(mx, wave_xor32(mx)) * cs;
-        // move the reference maximum only when p would otherwise exceed 2^8
-        const float m_new = mx > m_run[qt] + 8.f ? mx : m_run[qt];
-        alpha[qt] = fast_exp2(m_run[qt] - m_new);
-        rescale |= m_new != m_run[qt];
-        float lsum = 0.f;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          float p[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            p[r] = fast_exp2(s[qt][sb][r] * cs - m_new);
-            lsum += p[r];
-          }
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-              pb[qt][sb][c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
-        }
-        l_run[qt] = l_run[qt] * alpha[qt] + lsum;
-        m_run[qt] = m_new;
-      }
-      if (__ballot(rescale)) {
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qt][t][r] *= alpha[qt];
-      }
-      // operand i: output tile t = i % DT, keys 32 sb + 16 lg + 8 c + e with
-      // (sb, c) = (i / DT / 2, i / DT % 2), read as two 4-key groups
-      auto v_read = [&](int i) {
-        const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
-        const int dcol = 32 * t + tr_d;    // first of the 4 d columns this lane addresses
-        const int cbyte = 2 * (dcol & 7);  // byte offset inside its 16-byte chunk
-        const int r0 = 32 * sb + 16 * (g16 >> 1) + 8 * c + tr_row;
-        const int r1 = r0 + 4;
-        const u32x2 lo = lds_tr8(vbuf + r0 * C::RB + 16 * v_swz<D>(r0, dcol >> 3) + cbyte);
-        const u32x2 hi = lds_tr8(vbuf + r1 * C::RB + 16 * v_swz<D>(r1, dcol >> 3) + cbyte);
-        return u32x4{lo[0], lo[1], hi[0], hi[1]};
-      };
-      if constexpr (QT == 1) {
-        lds_mfma_pipeline<4 * C::DT, 4>(v_read, [&](int i, const u32x4& x) {
-          const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
-          o[0][t] = mfma32(x, pb[0][sb][c], o[0][t]);
-        });
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4 * C::DT; ++i) {
-          const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
-          const u32x4 vf = v_read(i);
-#pragma unroll
-          for (int qt = 0; qt < QT; ++qt) o[qt][t] = mfma32(vf, pb[qt][sb][c], o[qt][t]);
-        }
-      }
-    }
+  if (nkw > 0) compute_s(s, kbuf(0));
+  lds_barrier();  // K[0] fully read before iteration 0 copies K[2] over it
+  int kb = 0;
+  for (; kb + 1 < nkw; ++kb) {
+    prefetch(kb);
+    step.template operator()<true>(kb);
+    wait_vmem();
+    lds_barrier();
+  }
+  if (kb < nkw) {
+    prefetch(kb);
+    step.template operator()<false>(kb);
+    wait_vmem();
+    lds_barrier();
+    ++kb;
+  }
+  for (; kb < nkb; ++kb) {  // blocks past this wave's last query: copies only
+    prefetch(kb);
     wait_vmem();
     lds_barrier();
   }
 
-  if (!wave_live) return;
+  if (nkw == 0) return;
+  const float l_tot = pair_sum(l_run);
+  if (myq < a.m) {
+    const float inv = 1.f / l_tot;
+    uint16_t* orow = static_cast<uint16_t*>(a.o_out) + bi * a.o_sb + h * a.o_sh +
+                     (int64_t)myq * a.o_sr + 16 * lg;
 #pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const float l_tot = l_run[qt] + wave_xor32(l_run[qt]);
-    if (myq[qt] < a.m) {
-      const float inv = 1.f / l_tot;
-      uint16_t* orow = static_cast<uint16_t*>(a.o_out) + bi * a.o_sb + h * a.o_sh +
-                       (int64_t)myq[qt] * a.o_sr + 16 * lg;
+    for (int t = 0; t < C::DT; ++t) {
+      u32x4 lo, hi;
 #pragma unroll
-      for (int t = 0; t < C::DT; ++t) {
-        u32x4 lo, hi;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          lo[w] = pack_bf16(o[qt][t][2 * w] * inv, o[qt][t][2 * w + 1] * inv);
-          hi[w] = pack_bf16(o[qt][t][8 + 2 * w] * inv, o[qt][t][8 + 2 * w + 1] * inv);
-        }
-        stg16(orow + 32 * t, lo);
-        stg16(orow + 32 * t + 8, hi);
+      for (int w = 0; w < 4; ++w) {
+        lo[w] = pack_bf16(o[t][2 * w] * inv, o[t][2 * w + 1] * inv);
+        hi[w] = pack_bf16(o[t][8 + 2 * w] * inv, o[t][8 + 2 * w + 1] * inv);
       }
-      if (lg == 0)
-        a.lse[((int64_t)bi * a.hq + h) * a.m + myq[qt]] = (m_run[qt] + fast_log2(l_tot)) * kLn2;
+      stg16(orow + 32 * t, lo);
+      stg16(orow + 32 * t + 8, hi);
     }
+    if (lg == 0) a.lse[((int64_t)bi * a.hq + h) * a.m + myq] = (m_run + fast_log2(l_tot)) * kLn2;
   }
 }
 

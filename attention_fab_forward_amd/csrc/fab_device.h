@@ -156,8 +156,16 @@ __device__ __forceinline__ void lds_barrier() {
 // (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
-__device__ __forceinline__ float wave_xor32(float v) {
-  return __shfl_xor(v, 32, 64);
+// Combine each lane's value with that of lane l ^ 32 (v_permlane32_swap:
+// afterwards one register holds x[l % 32], the other x[l % 32 + 32] in every
+// lane).
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 
