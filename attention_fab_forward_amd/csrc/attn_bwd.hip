@@ -198,11 +198,11 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const bool p_role = wave < 4;
   const int kg = wave & 3;  // 32-key group
 
-  // head-major logical order; causal: low key blocks see the most queries, so
-  // they go first
+  // causal: low key blocks see the most queries, so they go first (see
+  // xcd_map for the XCD-aware order)
   const int nkb = (a.n + kAttnBwdKB - 1) / kAttnBwdKB;
-  const int lid = xcd_order(blockIdx.x, (int)gridDim.x);
-  const int kblk = lid % nkb, gh = lid / nkb;
+  int gh, kblk;
+  xcd_map(blockIdx.x, a.b * a.hkv, nkb, gh, kblk);
   const int g = gh % a.hkv, bi = gh / a.hkv;
   const int k0w = kblk * kAttnBwdKB + kg * 32;
   const int mykey = k0w + lq;
@@ -466,8 +466,8 @@ attn_dq_bf16_kernel(AttnArgs a) {
   const int tr_row = l16 >> 2;
 
   const int nqb = (a.m + BM - 1) / BM;
-  const int lid = xcd_order(blockIdx.x, (int)gridDim.x);
-  const int qi = lid % nqb, bh = lid / nqb;
+  int bh, qi;
+  xcd_map(blockIdx.x, a.b * a.hq, nqb, bh, qi);
   const int h = bh % a.hq, bi = bh / a.hq;
   const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
   const int g = h / a.group;

@@ -144,9 +144,9 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   const int l16 = lane & 15, g16 = lane >> 4;
 
   const int nqb = (a.m + C::BM - 1) / C::BM;
-  // head-major logical order, longest query blocks of a head first
-  const int lid = xcd_order(blockIdx.x, (int)gridDim.x);
-  const int qi = lid % nqb, bh = lid / nqb;
+  // longest query blocks of a head first, XCD-aware (see xcd_map)
+  int bh, qi;
+  xcd_map(blockIdx.x, a.b * a.hq, nqb, bh, qi);
   const int h = bh % a.hq, bi = bh / a.hq;
   const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
   const int g = h / a.group;

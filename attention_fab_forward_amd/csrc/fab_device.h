@@ -169,14 +169,31 @@ __device__ __forceinline__ float pair_sum(float v) {
 }
 
 
-// Workgroup i runs on XCD i % 8 (each XCD has its own L2).  Returns a logical
-// index such that XCD x executes the contiguous logical range
-// [x * per, (x + 1) * per), per = total / 8; a tail beyond 8 * per keeps its
-// index.  Bijective on [0, total).
-__device__ __forceinline__ int xcd_order(int id, int total) {
-  const int per = total / 8;
-  if (id >= 8 * per) return id;
-  return (id % 8) * per + id / 8;
+// Workgroup i runs on XCD i % 8 (8 XCDs, each with its own L2).  Maps i to
+// (head slot, block) for H head slots of nb blocks each, block 0 being the
+// longest (causal work varies along the blocks), so that the workgroups an XCD
+// runs together share one head's K / V in its L2 and every XCD gets the same
+// mix of long and short blocks:
+//  * H a multiple of 8: XCD x takes whole heads [x H / 8, (x + 1) H / 8), head
+//    by head, blocks in order;
+//  * 8 a multiple of H (and s = 8 / H dividing nb): head x / s is spread over s
+//    XCDs, XCD x taking its blocks x % s, x % s + s, ... in order;
+//  * otherwise plain head-major order.
+// Bijective on [0, H nb) in every case.
+__device__ __forceinline__ void xcd_map(int i, int H, int nb, int& head, int& blk) {
+  if (H % 8 == 0) {
+    const int per = H / 8 * nb;
+    const int lid = (i % 8) * per + i / 8;
+    head = lid / nb;
+    blk = lid % nb;
+  } else if (8 % H == 0 && nb % (8 / H) == 0) {
+    const int s = 8 / H, x = i % 8;
+    head = x / s;
+    blk = x % s + s * (i / 8);
+  } else {
+    head = i / nb;
+    blk = i % nb;
+  }
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -78,33 +78,82 @@ def time_attention(w, steps, warmup, torch, fab_binding):
         bwd()
     torch.cuda.synchronize()
 
-    # main timed region: K full steps, per-kernel events enabled
+    # main timed region: K full steps, per-kernel events enabled, an event
+    # between steps for the per-step spread
     plan.set_timing(True)
     plan.reset_kernel_times()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for i in range(steps):
         fwd()
         bwd()
-    e1.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = e0.elapsed_time(e1) / steps
+    step_ms = ev[0].elapsed_time(ev[-1]) / steps
+    per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     kernels = plan.kernel_times()
     plan.set_timing(False)
 
-    # forward alone (timing off)
+    def spread(fn):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(steps):
+            fn()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        d = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        return evs[0].elapsed_time(evs[-1]) / steps, d
+
+    fwd_ms, fwd_d = spread(fwd)  # forward alone (timing off)
+    bwd_ms, bwd_d = spread(bwd)  # backward alone, on the fixed forward outputs
+    stats = lambda d: {"median": d[len(d) // 2], "min": d[0], "max": d[-1]}
+    return {"step_ms": step_ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
+            "kernels": kernels, "inputs": x,
+            "spread_ms": {"step": stats(per_step), "fwd": stats(fwd_d), "bwd": stats(bwd_d)}}
+
+
+def time_workload(key, reps, torch, fab):
+    """Forward and backward time of another attention configuration, on
+    N(0, 1) inputs drawn on the device (torch generator seeded per tensor)."""
+    from attention_fab_forward_amd.inputs import WORKLOADS
+    w = WORKLOADS[key]
+    gen = torch.Generator(device="cuda")
+    c = {"attn_causal_bf16_h4_n131072_d128": 4, "attn_causal_bf16_gqa2_n1048576_d128": 5}.get(key, 9)
+
+    def draw(t, heads):
+        gen.manual_seed(1000 * c + t)
+        return torch.randn(w.batch, w.seq, heads, w.d, device="cuda", dtype=torch.float32,
+                           generator=gen).to(torch.bfloat16)
+
+    q, k, v, do = draw(1, w.heads_q), draw(2, w.heads_kv), draw(3, w.heads_kv), draw(4, w.heads_q)
+    o, lse = fab.forward(q, k, v, "softmax", w.causal, w.scale())
+    grads = fab.backward(q, k, v, o, lse, do, "softmax", w.causal, w.scale())
+    del grads
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(steps):
-        fwd()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = e0.elapsed_time(e1) / steps
-    return {"step_ms": step_ms, "fwd_ms": fwd_ms, "wall_s": wall, "kernels": kernels,
-            "inputs": x}
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fms, bms = [], []
+    for _ in range(reps):
+        e[0].record()
+        o, lse = fab.forward(q, k, v, "softmax", w.causal, w.scale())
+        e[1].record()
+        grads = fab.backward(q, k, v, o, lse, do, "softmax", w.causal, w.scale())
+        e[2].record()
+        torch.cuda.synchronize()
+        fms.append(e[0].elapsed_time(e[1]))
+        bms.append(e[1].elapsed_time(e[2]))
+        del grads
+    fwd_fl, bwd_fl, _ = attention_flops(w)
+    fm, bm = sorted(fms)[len(fms) // 2], sorted(bms)[len(bms) // 2]
+    del q, k, v, do, o, lse
+    torch.cuda.empty_cache()
+    return {"fwd_ms": fm, "bwd_ms": bm, "fwd_tflops": fwd_fl / fm / 1e9,
+            "fwd_bwd_tflops": (fwd_fl + bwd_fl) / (fm + bm) / 1e9,
+            "fwd_bwd_pct_bf16_peak": 100.0 * (fwd_fl + bwd_fl) / (fm + bm) / 1e9 / BF16_PEAK_TFLOPS,
+            "reps": reps, "inputs": "N(0,1) drawn on the device, seeded per tensor"}
 
 
 def kernel_flops(w):
@@ -163,7 +212,7 @@ def measured_traffic(kernel):
     return None
 
 
-def peak_hbm_sweep(torch, fab, exps=range(12, 18)):
+def peak_hbm_sweep(torch, fab, exps=range(12, 21)):
     """Peak device memory of forward + backward versus n (grouped-query geometry
     of the long-context workload: 2 query heads, 1 kv head, d = 128)."""
     out = []
@@ -371,6 +420,13 @@ def main():
     if not args.no_extras:
         log("peak-memory sweep ...")
         extras["peak_hbm_vs_seq"] = peak_hbm_sweep(torch, fab)
+        log("other workloads ...")
+        extras["workloads"] = {
+            "attn_causal_bf16_h4_n131072_d128": time_workload(
+                "attn_causal_bf16_h4_n131072_d128", 3, torch, fab),
+            "attn_causal_bf16_gqa2_n1048576_d128": time_workload(
+                "attn_causal_bf16_gqa2_n1048576_d128", 1, torch, fab),
+        }
         log("mlp ...")
         extras["mlp"] = time_mlp(max(3, args.steps), args.warmup, torch, fab_binding)
     cpu = None
@@ -398,6 +454,8 @@ def main():
         "fwd_tflops": fwd_fl / fwd_ms / 1e9,
         "fwd_pct_bf16_peak": 100.0 * fwd_fl / fwd_ms / 1e9 / BF16_PEAK_TFLOPS,
         "fwd_ms": fwd_ms,
+        "bwd_ms": r["bwd_ms"],
+        "spread_ms": r["spread_ms"],
         "kernels": kern,
         "roofline": roof,
         "cpu_baseline": cpu,
