@@ -13,7 +13,7 @@ import torch
 
 LIB_PATH = os.environ.get("FAB_LIBRARY") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libfab.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 SOFTMAX, GELU_ERF = 0, 1
 MASK_NONE, MASK_CAUSAL = 0, 1
@@ -29,7 +29,7 @@ STATUS = {
 EXPORTS = ("fab_plan", "fab_forward", "fab_backward", "fab_plan_destroy",
            "fab_status_string", "fab_last_error", "fab_abi_version",
            "fab_problem_size", "fab_plan_describe", "fab_plan_set_timing",
-           "fab_plan_kernel_times", "fab_plan_reset_kernel_times")
+           "fab_plan_kernel_times", "fab_plan_reset_kernel_times", "fab_merge")
 
 
 class FabProblem(ctypes.Structure):
@@ -40,7 +40,8 @@ class FabProblem(ctypes.Structure):
         ("k", ctypes.c_int64), ("p", ctypes.c_int64), ("scale", ctypes.c_float),
         ("reserved0", ctypes.c_int32), ("a_stride", ctypes.c_int64 * 3),
         ("bt_stride", ctypes.c_int64 * 3), ("c_stride", ctypes.c_int64 * 3),
-        ("o_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3), ("q_offset", ctypes.c_int64),
+        ("k_offset", ctypes.c_int64),
     ]
 
 
@@ -95,6 +96,8 @@ def lib():
         L.fab_plan_kernel_times.restype = ctypes.c_int
         L.fab_plan_reset_kernel_times.argtypes = [vp]
         L.fab_plan_reset_kernel_times.restype = ctypes.c_int
+        L.fab_merge.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.fab_merge.restype = ctypes.c_int
         if L.fab_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libfab.so ABI {L.fab_abi_version()} != binding {ABI_VERSION}")
         if L.fab_problem_size() != ctypes.sizeof(FabProblem):
@@ -109,7 +112,7 @@ def check(status):
 
 
 def make_problem(f, dtype, batch, heads_a, heads_bc, m, n, k, p, scale, causal=False,
-                 strides=None, abi_version=ABI_VERSION):
+                 strides=None, abi_version=ABI_VERSION, q_offset=0, k_offset=0):
     prob = FabProblem()
     prob.abi_version = abi_version
     prob.f, prob.dtype = f, dtype
@@ -117,6 +120,7 @@ def make_problem(f, dtype, batch, heads_a, heads_bc, m, n, k, p, scale, causal=F
     prob.batch, prob.heads_a, prob.heads_bc = batch, heads_a, heads_bc
     prob.m, prob.n, prob.k, prob.p = m, n, k, p
     prob.scale = scale
+    prob.q_offset, prob.k_offset = q_offset, k_offset
     if strides:
         for name in ("a_stride", "bt_stride", "c_stride", "o_stride"):
             if name in strides:
@@ -165,6 +169,9 @@ class Plan:
         check(lib().fab_backward(self._ptr, a, bt, c, o, lse, do, da, dbt, dc, ws, ws_bytes,
                                  stream))
 
+    def merge_raw(self, oa, la, ob, lb, oo, lo, stream):
+        check(lib().fab_merge(self._ptr, oa, la, ob, lb, oo, lo, stream))
+
     def __del__(self):
         ptr = getattr(self, "_ptr", None)
         if ptr and _lib is not None:
@@ -211,15 +218,16 @@ def _get_plan(key, build):
     return plan
 
 
-def attention_plan(q, k, v, causal, scale):
+def attention_plan(q, k, v, causal, scale, q_offset=0, k_offset=0):
     b, m, hq, d = q.shape
     n, hkv = k.shape[1], k.shape[2]
     strides = {"a_stride": _strides4(q), "bt_stride": _strides4(k), "c_stride": _strides4(v),
                "o_stride": (m * hq * v.shape[3], v.shape[3], hq * v.shape[3])}
     key = ("softmax", q.dtype, b, hq, hkv, m, n, d, v.shape[3], float(scale), bool(causal),
-           tuple(sorted(strides.items())))
+           tuple(sorted(strides.items())), int(q_offset), int(k_offset))
     return _get_plan(key, lambda: make_problem(SOFTMAX, _dtype_code(q), b, hq, hkv, m, n, d,
-                                               v.shape[3], scale, causal, strides))
+                                               v.shape[3], scale, causal, strides,
+                                               q_offset=q_offset, k_offset=k_offset))
 
 
 def mlp_plan(a, bt, c, scale):
@@ -238,11 +246,13 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def forward(a, bt, c, f="softmax", causal=False, scale=None):
+def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offset=0):
     """O = f(scale * A Bt^T) C on the GPU.
 
     softmax: a = Q [b, m, hq, d], bt = K [b, n, hkv, d], c = V [b, n, hkv, d];
     returns (O [b, m, hq, d], LSE float32 [b, hq, m]).  Default scale 1/sqrt(d).
+    causal: key j is visible to query i iff k_offset + j <= q_offset + i; rows
+    that see no key get O = 0, LSE = -inf.
     gelu: a [m, k], bt [n, k], c [n, p]; returns (O [m, p], None).  Default scale 1.
     """
     dev, dt = a.device, a.dtype
@@ -251,7 +261,7 @@ def forward(a, bt, c, f="softmax", causal=False, scale=None):
             _check_tensor(name, t, 4, dev, dt)
         if scale is None:
             scale = 1.0 / float(a.shape[3]) ** 0.5
-        plan = attention_plan(a, bt, c, causal, scale)
+        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset)
         b, m, hq, _ = a.shape
         o = torch.empty((b, m, hq, c.shape[3]), dtype=dt, device=dev)
         lse = torch.empty((b, hq, m), dtype=torch.float32, device=dev)
@@ -272,8 +282,11 @@ def forward(a, bt, c, f="softmax", causal=False, scale=None):
     return o, lse
 
 
-def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None):
-    """Gradients (dA, dBt, dC) of <dO, O> for the forward above."""
+def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None, q_offset=0,
+             k_offset=0):
+    """Gradients (dA, dBt, dC) of <dO, O> for the forward above.  Over a key
+    range (offsets) pass the merged O and LSE of all keys: dA is then the
+    range's contribution to dQ."""
     dev, dt = a.device, a.dtype
     if f == "softmax":
         for name, t in (("q", a), ("k", bt), ("v", c), ("o", o), ("do", do)):
@@ -284,7 +297,7 @@ def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None):
             raise ValueError("dO must have the layout of O")
         if scale is None:
             scale = 1.0 / float(a.shape[3]) ** 0.5
-        plan = attention_plan(a, bt, c, causal, scale)
+        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset)
         if o.stride() != (a.shape[1] * a.shape[2] * c.shape[3], a.shape[2] * c.shape[3],
                           c.shape[3], 1):
             raise ValueError("O must be packed [b, m, hq, d]")
@@ -302,3 +315,26 @@ def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None):
     plan.backward_raw(_ptr(a), _ptr(bt), _ptr(c), _ptr(o), _ptr(lse), _ptr(do), _ptr(da),
                       _ptr(dbt), _ptr(dc), _ptr(ws), plan.bwd_workspace, _stream())
     return da, dbt, dc
+
+
+def merge(o_a, lse_a, o_b, lse_b, out=None):
+    """Merge two softmax results over disjoint key sets of the same queries
+    (fab_merge).  o_* [b, m, hq, d] packed, lse_* float32 [b, hq, m].  Returns
+    (O, LSE); out=(o, lse) writes there (may be (o_a, lse_a))."""
+    dev, dt = o_a.device, o_a.dtype
+    for name, t in (("o_a", o_a), ("o_b", o_b)):
+        _check_tensor(name, t, 4, dev, dt)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be packed [b, m, hq, d]")
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous float32 tensor on {dev}")
+    b, m, hq, d = o_a.shape
+    if o_b.shape != o_a.shape or lse_a.shape != (b, hq, m) or lse_b.shape != (b, hq, m):
+        raise ValueError("shape mismatch between the two parts")
+    o, lse = out if out is not None else (torch.empty_like(o_a), torch.empty_like(lse_a))
+    key = ("merge", dt, b, hq, m, d)
+    plan = _get_plan(key, lambda: make_problem(SOFTMAX, _dtype_code(o_a), b, hq, hq, m, m, d, d,
+                                               1.0, False, None))
+    plan.merge_raw(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse), _stream())
+    return o, lse

@@ -208,9 +208,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const int mykey = k0w + lq;
 
   const float cs = a.scale_log2;
-  const int qb_first = CAUSAL ? (kblk * kAttnBwdKB) / C::TILE : 0;
+  // first query block holding a query that sees the workgroup's first key
+  const int qb_first = CAUSAL ? max(0, kblk * kAttnBwdKB - a.diag) / C::TILE : 0;
   const int nqb = (a.m + C::TILE - 1) / C::TILE;
-  const int steps_per_head = nqb - qb_first;
+  const int steps_per_head = max(0, nqb - qb_first);
   const int steps = steps_per_head * a.group;
   const bool group_live = k0w < a.n;
   const TO tq = tile_offsets<D, kDkdvWaves>(a.q_sr, wave, lane);
@@ -251,10 +252,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
       const int q0 = (qb_first + step % steps_per_head) * C::TILE;
       const char* st = smem + (step & 1) * L::STAGE;
       // A key group skips a query block when every query precedes all its keys.
-      const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 >= k0w);
+      const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 + a.diag >= k0w);
       u32x4 pb[2][2];
       if (work) {
-        const bool need_mask = (CAUSAL && q0 < k0w + 31) || q0 + C::TILE > a.m;
+        const bool need_mask = (CAUSAL && q0 + a.diag < k0w + 31) || q0 + C::TILE > a.m;
 #pragma unroll
         for (int sq = 0; sq < 2; ++sq) {
           f32x16 s;
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int q = q0 + 32 * sq + 16 * lg + r;
-              if ((CAUSAL && q < mykey) || q >= a.m) s[r] = -INFINITY;
+              if ((CAUSAL && q + a.diag < mykey) || q >= a.m) s[r] = -INFINITY;
             }
           }
           const f32x4* l2 = reinterpret_cast<const f32x4*>(st + L::LSE) + 8 * sq + 4 * lg;
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
       prefetch(step);
       const int q0 = (qb_first + step % steps_per_head) * C::TILE;
       const char* st = smem + (step & 1) * L::STAGE;
-      const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 >= k0w);
+      const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 + a.diag >= k0w);
       f32x16 dp[2];
       if (work) {
 #pragma unroll
@@ -379,8 +380,8 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
                                          const u32x4 (&df)[QT][BwdCfg<D>::DC],
                                          f32x16 (&dq)[QT][BwdCfg<D>::DT], const int (&myq)[QT],
                                          const float (&lse2)[QT], const float (&ndl)[QT],
-                                         bool need_mask, int key0, int n, float cs, int lq, int lg,
-                                         int tr_d, int tr_row) {
+                                         bool need_mask, int key0, int n, int diag, float cs, int lq,
+                                         int lg, int tr_d, int tr_row) {
   using C = BwdCfg<D>;
   using S = DqStage<D>;
 #pragma unroll
@@ -414,7 +415,7 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * sb + 16 * lg + r;
-          if ((CAUSAL && key > myq[qt]) || key >= n) s[qt][r] = -INFINITY;
+          if ((CAUSAL && key > myq[qt] + diag) || key >= n) s[qt][r] = -INFINITY;
         }
     }
     u32x4 db[QT][2];
@@ -476,7 +477,7 @@ attn_dq_bf16_kernel(AttnArgs a) {
   const bool wave_live = q0 < a.m;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + bi * a.v_sb + g * a.v_sh;
-  const int kend = CAUSAL ? min(a.n, qb * BM + BM) : a.n;
+  const int kend = CAUSAL ? min(a.n, max(0, qb * BM + BM + a.diag)) : a.n;
   const int nkb = (kend + C::TILE - 1) / C::TILE;
   const TileOffsets<D, NW> tk = tile_offsets<D, NW>(a.k_sr, wave, lane);
   const TileOffsets<D, NW> tv = SAME ? tk : tile_offsets<D, NW>(a.v_sr, wave, lane);
@@ -522,11 +523,11 @@ attn_dq_bf16_kernel(AttnArgs a) {
     }
     const char* st = smem + (kb & 1) * S::BYTES;
     const int key0 = kb * C::TILE;
-    const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 32 * QT - 1);
+    const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 32 * QT - 1 + a.diag);
     if (wave_work) {
-      const bool need_mask = (CAUSAL && key0 + C::TILE - 1 > q0) || key0 + C::TILE > a.n;
-      dq_block<D, CAUSAL, QT>(st, qf, df, dq, myq, lse2, ndl, need_mask, key0, a.n, cs, lq, lg,
-                              tr_d, tr_row);
+      const bool need_mask = (CAUSAL && key0 + C::TILE - 1 > q0 + a.diag) || key0 + C::TILE > a.n;
+      dq_block<D, CAUSAL, QT>(st, qf, df, dq, myq, lse2, ndl, need_mask, key0, a.n, a.diag, cs, lq,
+                              lg, tr_d, tr_row);
     }
     wait_vmem();
     lds_barrier();
@@ -579,7 +580,9 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(AttnArgs a) {
   for (int sft = 1; sft < LPR; sft <<= 1) acc += __shfl_xor(acc, sft, 64);
   if (row < total && part == 0) {
     a.delta[row] = -acc;
-    a.lse2[row] = a.lse_in[row] * kLog2e;
+    // a row without keys (LSE = -inf) gets +inf, so its P = exp2(S - inf) = 0
+    const float l = a.lse_in[row];
+    a.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
   }
 }
 

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
   }
   float m_run = -INFINITY, l_run = 0.f;
   const float cs = a.scale_log2;
-  const int kend = CAUSAL ? min(a.n, qb * QPB + QPB) : a.n;
+  const int kend = CAUSAL ? min(a.n, max(0, qb * QPB + QPB + a.diag)) : a.n;
   for (int k0 = 0; k0 < kend; k0 += kTile) {
     __syncthreads();
     stage_f32<D>(ks, kbase, a.k_sr, k0, a.n, tid, 256);
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
       for (int i = 0; i < 32; ++i) acc = fmaf(qr[i], ks[j * D + part * 32 + i], acc);
       acc = group_sum<T>(acc);
       const int key = k0 + j;
-      const bool dead = key >= a.n || (CAUSAL && key > q);
+      const bool dead = key >= a.n || (CAUSAL && key > q + a.diag);
       s[j] = dead ? -INFINITY : acc * cs;
       mx = fmaxf(mx, s[j]);
     }
@@ -111,7 +111,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
     m_run = m_new;
   }
   if (q >= a.m) return;
-  const float inv = 1.f / l_run;
+  // a row that saw no key (offset causal masks): O = 0, LSE = -inf
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   float* orow = static_cast<float*>(a.o_out) + bi * a.o_sb + h * a.o_sh + (int64_t)q * a.o_sr +
                 part * 32;
 #pragma unroll
@@ -119,7 +120,8 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
     f32x4 v = {o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv};
     *reinterpret_cast<f32x4*>(orow + i) = v;
   }
-  if (part == 0) a.lse[((int64_t)bi * a.hq + h) * a.m + q] = (m_run + log2f(l_run)) * kLn2;
+  if (part == 0)
+    a.lse[((int64_t)bi * a.hq + h) * a.m + q] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(AttnArgs a) {
     if (live && part == 0) a.delta[ridx] = dlt;
   }
   const float cs = a.scale_log2;
-  const int kend = CAUSAL ? min(a.n, qb * QPB + QPB) : a.n;
+  const int kend = CAUSAL ? min(a.n, max(0, qb * QPB + QPB + a.diag)) : a.n;
   for (int k0 = 0; k0 < kend; k0 += kTile) {
     __syncthreads();
     stage_f32<D>(ks, kbase, a.k_sr, k0, a.n, tid, 256);
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(AttnArgs a) {
       sacc = group_sum<T>(sacc);
       dpacc = group_sum<T>(dpacc);
       const int key = k0 + j;
-      const bool dead = !live || key >= a.n || (CAUSAL && key > q);
+      const bool dead = !live || key >= a.n || (CAUSAL && key > q + a.diag);
       const float p = dead ? 0.f : exp2f(sacc * cs - lse2);
       const float ds = p * (dpacc - dlt);
 #pragma unroll
@@ -232,7 +234,8 @@ __global__ __launch_bounds__(256) void attn_dkdv_f32_kernel(AttnArgs a) {
     dv[i] = 0.f;
   }
   const float cs = a.scale_log2;
-  const int qstart = CAUSAL ? (kblk * KPB / kTile) * kTile : 0;
+  // first query tile holding a query that sees the block's first key
+  const int qstart = CAUSAL ? (max(0, kblk * KPB - a.diag) / kTile) * kTile : 0;
   for (int hh = 0; hh < a.group; ++hh) {
     const int h = g * a.group + hh;
     const float* qbase = static_cast<const float*>(a.q) + bi * a.q_sb + h * a.q_sh;
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(256) void attn_dkdv_f32_kernel(AttnArgs a) {
         sacc = group_sum<T>(sacc);
         dpacc = group_sum<T>(dpacc);
         const int qi = q0 + j;
-        const bool dead = !live || qi >= a.m || (CAUSAL && key > qi);
+        const bool dead = !live || qi >= a.m || (CAUSAL && key > qi + a.diag);
         const float p = dead ? 0.f : exp2f(sacc * cs - lses[j]);
         const float ds = p * (dpacc - dls[j]);
 #pragma unroll

@@ -158,10 +158,14 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   const int q0 = qb * C::BM + wave * 32;  // first query of this wave
   const int myq = q0 + lq;
 
-  const int kend = CAUSAL ? min(a.n, qb * C::BM + C::BM) : a.n;
+  // keys up to the last one visible to the workgroup's last query
+  const int kend = CAUSAL ? min(a.n, max(0, qb * C::BM + C::BM + a.diag)) : a.n;
   const int nkb = (kend + C::BN - 1) / C::BN;  // key blocks of the workgroup
-  // key blocks this wave computes (causal: up to the one holding its last query)
-  const int nkw = q0 >= a.m ? 0 : CAUSAL ? min(nkb, (q0 + 31) / C::BN + 1) : nkb;
+  // key blocks this wave computes (causal: up to the one holding the last key
+  // its last query sees)
+  const int nkw = q0 >= a.m ? 0
+                  : CAUSAL ? (q0 + 31 + a.diag < 0 ? 0 : min(nkb, (q0 + 31 + a.diag) / C::BN + 1))
+                           : nkb;
   const TileOffsets<D> toff = tile_offsets<D>(a.k_sr, a.v_sr, wave, lane);
   auto copy_k = [&](int kb) {
     issue_kv<D, true>(toff, kbase, a.k_sr, kb * C::BN, a.n, kbuf(kb), wave, lane);
@@ -214,13 +218,13 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   f32x16 s[2];
   auto step = [&]<bool NEXT>(int kb) {
     const int key0 = kb * C::BN;
-    if ((CAUSAL && key0 + C::BN - 1 > q0) || key0 + C::BN > a.n) {
+    if ((CAUSAL && key0 + C::BN - 1 > q0 + a.diag) || key0 + C::BN > a.n) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + 32 * sb + 16 * lg + r;
-          if ((CAUSAL && key > myq) || key >= a.n) s[sb][r] = -INFINITY;
+          if ((CAUSAL && key > myq + a.diag) || key >= a.n) s[sb][r] = -INFINITY;
         }
     }
     f32x16 sn[2];
@@ -234,7 +238,10 @@ attn_fwd_bf16_kernel(AttnArgs a) {
     mx = pair_max(mx) * cs;
     // move the reference maximum only when p would otherwise exceed 2^8
     const float m_new = mx > m_run + 8.f ? mx : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
+    // a row that has seen no key yet (offset causal masks) keeps m = -inf and
+    // takes 0 as the exponent reference: its probabilities are exactly 0
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_ref);
     const bool rescale = m_new != m_run;
     float lsum = 0.f;
     u32x4 pb[2][2];
@@ -243,7 +250,7 @@ attn_fwd_bf16_kernel(AttnArgs a) {
       float p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(s[sb][r], cs, -m_new));
+        p[r] = fast_exp2(fmaf(s[sb][r], cs, -m_ref));
         lsum += p[r];
       }
 #pragma unroll
@@ -313,10 +320,10 @@ attn_fwd_bf16_kernel(AttnArgs a) {
     lds_barrier();
   }
 
-  if (nkw == 0) return;
+  // rows that saw no key (offset causal masks): O = 0, LSE = -inf
   const float l_tot = pair_sum(l_run);
   if (myq < a.m) {
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = static_cast<uint16_t*>(a.o_out) + bi * a.o_sb + h * a.o_sh +
                      (int64_t)myq * a.o_sr + 16 * lg;
 #pragma unroll
@@ -330,7 +337,9 @@ attn_fwd_bf16_kernel(AttnArgs a) {
       stg16(orow + 32 * t, lo);
       stg16(orow + 32 * t + 8, hi);
     }
-    if (lg == 0) a.lse[((int64_t)bi * a.hq + h) * a.m + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+    if (lg == 0)
+      a.lse[((int64_t)bi * a.hq + h) * a.m + myq] =
+          l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

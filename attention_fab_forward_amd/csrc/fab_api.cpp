@@ -6,6 +6,7 @@
 // allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -186,6 +187,8 @@ fab::AttnArgs attn_args(const fab_plan_s* p) {
   a.scale = q.scale;
   a.scale_log2 = q.scale * fab::kLog2eHost;
   a.causal = q.mask == FAB_MASK_CAUSAL;
+  const int64_t diag = q.q_offset - q.k_offset;
+  a.diag = (int32_t)std::min<int64_t>(std::max<int64_t>(diag, -q.m - 1), q.n);
   return a;
 }
 
@@ -240,6 +243,9 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
     return fail(FAB_ERR_UNSUPPORTED, "sizes beyond this build's limits (rows <= 2^30, "
                 "batch*heads <= 2^20)");
   if (!std::isfinite(q.scale)) return fail(FAB_ERR_BAD_SHAPE, "scale must be finite");
+  if (q.q_offset < -((int64_t)1 << 40) || q.q_offset > ((int64_t)1 << 40) ||
+      q.k_offset < -((int64_t)1 << 40) || q.k_offset > ((int64_t)1 << 40))
+    return fail(FAB_ERR_BAD_SHAPE, "mask offsets beyond +-2^40");
 
   const int64_t unit = q.dtype == FAB_BF16 ? 8 : 4;
   fab_plan_s tmp;
@@ -260,9 +266,6 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
                                 (long long)q.k, (long long)q.p);
     if (q.k != 64 && q.k != 128)
       return fail(FAB_ERR_UNSUPPORTED, "softmax head dim %lld not in {64, 128}", (long long)q.k);
-    if (q.mask == FAB_MASK_CAUSAL && q.m != q.n)
-      return fail(FAB_ERR_UNSUPPORTED, "causal mask needs m == n (got %lld, %lld)",
-                  (long long)q.m, (long long)q.n);
     if (!(q.scale > 0.f)) return fail(FAB_ERR_UNSUPPORTED, "softmax scale must be > 0");
     tmp.fwd_ws = 0;
     // per query row: delta (both paths) and LSE * log2(e) (bf16 path)
@@ -282,6 +285,7 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
                (long long)(q.heads_a / q.heads_bc));
   } else {
     if (q.mask != FAB_MASK_NONE) return fail(FAB_ERR_UNSUPPORTED, "GeLU takes no mask");
+    if (q.q_offset || q.k_offset) return fail(FAB_ERR_UNSUPPORTED, "GeLU takes no mask offsets");
     if (q.dtype != FAB_BF16) return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP runs in bf16 only");
     if (q.batch != 1 || q.heads_a != 1 || q.heads_bc != 1)
       return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs batch == heads == 1");
@@ -450,6 +454,29 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, c
     e = fab::launch_mlp_bwd_bf16(a, s);
   }
   if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_backward: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fab_status fab_merge(const fab_plan_t* plan, const void* O_a, const float* lse_a,
+                     const void* O_b, const float* lse_b, void* O_out, float* lse_out,
+                     void* stream) {
+  if (!plan || !O_a || !lse_a || !O_b || !lse_b || !O_out || !lse_out)
+    return fail(FAB_ERR_NULL_ARG, "fab_merge: null argument");
+  const fab_problem& q = plan->prob;
+  if (q.f != FAB_F_SOFTMAX) return fail(FAB_ERR_UNSUPPORTED, "fab_merge: needs a softmax plan");
+  if (!aligned16(O_a) || !aligned16(O_b) || !aligned16(O_out))
+    return fail(FAB_ERR_ALIGNMENT, "fab_merge: O pointers must be 16-byte aligned");
+  const uintptr_t lmask = reinterpret_cast<uintptr_t>(lse_a) | reinterpret_cast<uintptr_t>(lse_b) |
+                          reinterpret_cast<uintptr_t>(lse_out);
+  if (lmask & 3u) return fail(FAB_ERR_ALIGNMENT, "fab_merge: lse pointers must be 4-byte aligned");
+  fab::MergeArgs a{};
+  a.oa = O_a, a.ob = O_b, a.oo = O_out, a.la = lse_a, a.lb = lse_b, a.lo = lse_out;
+  a.o_sb = plan->os[0], a.o_sh = plan->os[1], a.o_sr = plan->os[2];
+  a.b = (int32_t)q.batch, a.hq = (int32_t)q.heads_a, a.m = (int32_t)q.m;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TimerScope scope(plan->timer);
+  const hipError_t e = fab::launch_attn_merge(a, (int)q.p, q.dtype == FAB_BF16, s);
+  if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_merge: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -33,6 +33,22 @@ struct AttnArgs {
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   int32_t causal;
+  // causal: key j is visible to query i iff j <= i + diag (diag = global
+  // query offset - key offset, clamped to [-m - 1, n]: beyond that range every
+  // row sees all keys or none)
+  int32_t diag;
+};
+
+// Merge of two partial softmax results (fab_merge): packed LSE [b, hq, m].
+struct MergeArgs {
+  const void* oa;
+  const void* ob;
+  void* oo;
+  const float* la;
+  const float* lb;
+  float* lo;
+  int64_t o_sb, o_sh, o_sr;
+  int32_t b, hq, m;
 };
 
 // GeLU MLP: A [m, k], Bt [n, k], C [n, p], O [m, p] (row strides in elements).
@@ -92,6 +108,7 @@ constexpr int kAttnBwdKB = 128;   // dK/dV kernel: keys per workgroup (4 waves x
 constexpr int kAttnBwdQB = 64;    // dK/dV kernel: queries per inner step
 
 hipError_t launch_attn_fwd_bf16(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_merge(const MergeArgs& a, int d, bool bf16, hipStream_t s);
 hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_bwd_f32(const AttnArgs& a, int d, hipStream_t s);

@@ -20,8 +20,10 @@
  *   C  : n x p      (attention: V)
  *   O  : m x p
  * softmax: O_i = sum_j P_ij C_j, P_ij = exp(S_ij - LSE_i),
- *          S = scale * A Bt^T, masked S_ij = -inf for j > i when causal,
- *          LSE_i = log sum_j exp(S_ij) (natural log).
+ *          S = scale * A Bt^T, masked S_ij = -inf when causal and key j lies
+ *          after query i (global positions: k_offset + j > q_offset + i),
+ *          LSE_i = log sum_j exp(S_ij) (natural log).  A row that sees no key
+ *          gets O_i = 0 and LSE_i = -inf.
  * GeLU:    O = GeLU(scale * A Bt^T) C, GeLU(x) = x * Phi(x).
  *
  * Layout: every matrix has a contiguous last dimension.  Attention tensors are
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FAB_ABI_VERSION 1
+#define FAB_ABI_VERSION 2
 
 typedef enum {
   FAB_OK = 0,
@@ -80,7 +82,7 @@ typedef struct {
   int64_t batch;       /* >= 1                                                */
   int64_t heads_a;     /* heads of A and O (query heads); >= 1                */
   int64_t heads_bc;    /* heads of Bt and C (kv heads); divides heads_a       */
-  int64_t m, n, k, p;  /* matrix sizes above; causal requires m == n          */
+  int64_t m, n, k, p;  /* matrix sizes above                                  */
   float scale;         /* f is applied to scale * (A Bt^T)                    */
   int32_t reserved0;   /* must be 0                                           */
   /* element strides {batch, head, row}; all-zero = packed [b, rows, h, cols] */
@@ -88,13 +90,21 @@ typedef struct {
   int64_t bt_stride[3];
   int64_t c_stride[3];
   int64_t o_stride[3];
+  /* Causal mask positions: query row i sits at global position q_offset + i,
+   * key row j at k_offset + j (a rank or a split holding a slice of the
+   * sequence; "Ulysses Sequence Parallelism", Analyse: ring attention passes
+   * key blocks between ranks).  Only the difference matters; both 0 for the
+   * plain causal mask over one full sequence.  Must be 0 for GeLU. */
+  int64_t q_offset;
+  int64_t k_offset;
 } fab_problem;
 
 typedef struct fab_plan_s fab_plan_t;
 
 /* Validate `prob` and build a reusable plan.  Host only: touches no device.
  * Supported in this build:
- *   softmax, bf16: k == p, k in {64, 128}; any m, n >= 1; causal needs m == n.
+ *   softmax, bf16: k == p, k in {64, 128}; any m, n >= 1; causal with any
+ *                  offsets.
  *   softmax, f32:  k == p, k in {64, 128}; same rules.
  *   GeLU, bf16:    batch == heads_a == heads_bc == 1, k and p multiples of 128
  *                  and at most 1024, any m, n >= 1, mask NONE.
@@ -124,6 +134,26 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt,
                         const void* C, const void* O, const float* lse,
                         const void* dO, void* dA, void* dBt, void* dC,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Merge two softmax results over disjoint key sets of the same queries (for
+ * instance two key ranges computed by fab_forward with k_offset set): with
+ * weights w_x = exp(LSE_x - LSE),
+ *   LSE = log(exp(LSE_a) + exp(LSE_b)),  O = w_a O_a + w_b O_b,
+ * which is the result over the union of the key sets (the ring / key-sharded
+ * attention step: "Ulysses Sequence Parallelism", Analyse; FITEE abstract,
+ * B and C exchanged in sub-blocks).  Applied pairwise it merges any number of
+ * parts in any order.
+ * plan: a softmax plan; O_a, O_b, O_out: device pointers with the plan's O
+ * layout and dtype; lse_a, lse_b, lse_out: device float32 [batch, heads_a, m].
+ * O_out / lse_out may be O_a / lse_a (in-place accumulation) but must not
+ * partially overlap any input.  A row whose two LSE are both -inf gets O = 0,
+ * LSE = -inf.  Computed in fp32, O rounded to the dtype.  Enqueued on stream.
+ * Backward over key ranges: pass the merged O and LSE to fab_backward for
+ * each range; dK, dV are that range's, and dA is its contribution to dQ (the
+ * caller sums the ranges' dA). */
+fab_status fab_merge(const fab_plan_t* plan, const void* O_a, const float* lse_a,
+                     const void* O_b, const float* lse_b, void* O_out, float* lse_out,
+                     void* stream);
 
 /* Release a plan (NULL is ignored). */
 void fab_plan_destroy(fab_plan_t* plan);

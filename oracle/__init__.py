@@ -11,6 +11,7 @@ from .fab_oracle import (  # noqa: F401
     attention_backward_rows,
     attention_backward_keys,
     attention_probs,
+    attention_merge,
     mlp_forward,
     mlp_backward,
     mlp_forward_rows,

@@ -20,7 +20,15 @@ What it computes (the plain definition, not the tiled algorithm):
   Parallelism", section 2.A (index recomputation).  Reading taken: key j is
   visible to query i iff j <= i, in global indices, since a rank holds the full
   sequence for its heads (Ulysses page, "Contexte Technique"; AutoSP 2.A,
-  buffer resizing).
+  buffer resizing).  For a slice of the sequence (a key range passed around a
+  ring of ranks: Ulysses page, "Analyse") the global positions are
+  q_offset + i and k_offset + j, i.e. key j is visible iff
+  j <= i + diag with diag = q_offset - k_offset.  A query row that sees no
+  key has O = 0 and LSE = -inf.
+* Merging two results over disjoint key sets of the same queries:
+  LSE = log(e^LSE_a + e^LSE_b), O = e^(LSE_a - LSE) O_a + e^(LSE_b - LSE) O_b,
+  which is the softmax over the union (it follows from the definition of the
+  softmax as exp(S - LSE)).
 * f = GeLU in its erf form, applied elementwise (the MLP block of AutoSP 2.A
   and 2.B).  Phi is the standard normal CDF.
 * Backward passes are the derivative of the same definitions; recomputing the
@@ -93,37 +101,50 @@ def _kv_of(h, hq, hkv):
 # softmax attention
 # ---------------------------------------------------------------------------
 
-def attention_probs(qh, kh, scale, causal, rows):
+def attention_probs(qh, kh, scale, causal, rows, diag=0):
     """Full-width probability rows P[rows, :] for one (batch, head).
 
-    qh: [|rows|, d] query rows; kh: [n, d] keys; rows: global query indices.
-    Returns (P, M, Z): P_ij = exp(S_ij - M_i) / Z_i with S = scale * q k^T,
-    M_i = max_j S_ij and Z_i = sum_j exp(S_ij - M_i).
+    qh: [|rows|, d] query rows; kh: [n, d] keys; rows: query indices; causal:
+    key j visible iff j <= row + diag.  Returns (P, M, Z): P_ij =
+    exp(S_ij - M_i) / Z_i with S = scale * q k^T, M_i = max_j S_ij and
+    Z_i = sum_j exp(S_ij - M_i).  A row with no visible key has P = 0,
+    M = 0, Z = 0 (so M + log Z = -inf).
     """
     s = float(scale) * (qh @ kh.T)
     if causal:
         cols = np.arange(kh.shape[0])
-        s[cols[None, :] > np.asarray(rows)[:, None]] = -np.inf
+        s[cols[None, :] > np.asarray(rows)[:, None] + int(diag)] = -np.inf
     mx = s.max(axis=1)
+    mx = np.where(np.isfinite(mx), mx, 0.0)
     e = np.exp(s - mx[:, None])
     z = e.sum(axis=1)
-    return e / z[:, None], mx, z
+    with np.errstate(invalid="ignore", divide="ignore"):
+        p = np.where(z[:, None] > 0, e / np.where(z > 0, z, 1.0)[:, None], 0.0)
+    return p, mx, z
 
 
-def _attn_fwd_block(q, k, v, scale, causal, b, h, hkv, r0, r1, o, lse):
+def _lse(mx, z):
+    with np.errstate(divide="ignore"):
+        return mx + np.log(z)
+
+
+def _attn_fwd_block(q, k, v, scale, causal, b, h, hkv, r0, r1, o, lse, diag=0):
     g = _kv_of(h, q.shape[2], hkv)
     rows = np.arange(r0, r1)
-    p, mx, z = attention_probs(q[b, r0:r1, h], k[b, :, g], scale, causal, rows)
+    p, mx, z = attention_probs(q[b, r0:r1, h], k[b, :, g], scale, causal, rows, diag)
     o[b, r0:r1, h] = p @ v[b, :, g]
-    lse[b, h, r0:r1] = mx + np.log(z)
+    lse[b, h, r0:r1] = _lse(mx, z)
 
 
-def attention_forward(q, k, v, scale, causal=False, workers=None, block_rows=None):
+def attention_forward(q, k, v, scale, causal=False, workers=None, block_rows=None,
+                      q_offset=0, k_offset=0):
     """O = softmax(scale * Q K^T [+ causal mask]) V and LSE, per (batch, head).
 
     q [b, m, Hq, d], k [b, n, Hkv, d], v [b, n, Hkv, dv] -> (o [b, m, Hq, dv],
-    lse [b, Hq, m]).
+    lse [b, Hq, m]).  Causal positions: query i at q_offset + i, key j at
+    k_offset + j.
     """
+    diag = int(q_offset) - int(k_offset)
     q, k, v = _f64(q), _f64(k), _f64(v)
     b, m, hq, _ = q.shape
     hkv = k.shape[2]
@@ -134,7 +155,7 @@ def attention_forward(q, k, v, scale, causal=False, workers=None, block_rows=Non
         for h in range(hq):
             for r0, r1 in _blocks(m, k.shape[1], block_rows):
                 tasks.append(lambda bi=bi, h=h, r0=r0, r1=r1: _attn_fwd_block(
-                    q, k, v, scale, causal, bi, h, hkv, r0, r1, o, lse))
+                    q, k, v, scale, causal, bi, h, hkv, r0, r1, o, lse, diag))
     _run(tasks, workers)
     return o, lse
 
@@ -145,16 +166,16 @@ def attention_forward_rows(q, k, v, scale, causal, b, h, rows):
     g = _kv_of(h, q.shape[2], k.shape[2])
     qh = _f64(q[b, rows, h])
     p, mx, z = attention_probs(qh, _f64(k[b, :, g]), scale, causal, rows)
-    return p @ _f64(v[b, :, g]), mx + np.log(z)
+    return p @ _f64(v[b, :, g]), _lse(mx, z)
 
 
-def _attn_bwd_rows(qh, kh, vh, doh, scale, causal, rows):
+def _attn_bwd_rows(qh, kh, vh, doh, scale, causal, rows, diag=0):
     """Gradient pieces for a set of full query rows of one head.
 
     dP = dO V^T; D_i = sum_j P_ij dP_ij; dS = P * (dP - D);
     dQ = scale dS K; dK = scale dS^T Q; dV = P^T dO.
     """
-    p, _, _ = attention_probs(qh, kh, scale, causal, rows)
+    p, _, _ = attention_probs(qh, kh, scale, causal, rows, diag)
     dp = doh @ vh.T
     dd = (p * dp).sum(axis=1)
     ds = p * (dp - dd[:, None])
@@ -164,8 +185,11 @@ def _attn_bwd_rows(qh, kh, vh, doh, scale, causal, rows):
     return dq, dk, dv
 
 
-def attention_backward(q, k, v, do, scale, causal=False, workers=None, block_rows=None):
-    """(dQ, dK, dV) of L = <dO, O> for O = attention_forward(q, k, v)."""
+def attention_backward(q, k, v, do, scale, causal=False, workers=None, block_rows=None,
+                       q_offset=0, k_offset=0):
+    """(dQ, dK, dV) of L = <dO, O> for O = attention_forward(q, k, v) (same
+    causal positions)."""
+    diag = int(q_offset) - int(k_offset)
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     b, m, hq, _ = q.shape
     n, hkv = k.shape[1], k.shape[2]
@@ -176,7 +200,7 @@ def attention_backward(q, k, v, do, scale, causal=False, workers=None, block_row
         g = _kv_of(h, hq, hkv)
         dqb, dkb, dvb = _attn_bwd_rows(q[bi, r0:r1, h], k[bi, :, g], v[bi, :, g],
                                        do[bi, r0:r1, h], scale, causal,
-                                       np.arange(r0, r1))
+                                       np.arange(r0, r1), diag)
         dq[bi, r0:r1, h] = dqb
         return bi, g, dkb, dvb
 
@@ -228,6 +252,21 @@ def attention_backward_keys(q, k, v, do, scale, causal, b, g, keys, block_rows=N
             dk += float(scale) * (ds.T @ qh)
             dv += p[:, keys].T @ doh
     return dk, dv
+
+
+def attention_merge(o_a, lse_a, o_b, lse_b):
+    """Softmax result over the union of two disjoint key sets from the two
+    parts' results: LSE = log(e^LSE_a + e^LSE_b), O = sum_x e^(LSE_x - LSE) O_x.
+    o_* [b, m, Hq, dv], lse_* [b, Hq, m]; rows with both LSE = -inf give O = 0,
+    LSE = -inf."""
+    o_a, o_b, lse_a, lse_b = _f64(o_a), _f64(o_b), _f64(lse_a), _f64(lse_b)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        lse = np.logaddexp(lse_a, lse_b)
+        wa = np.where(np.isfinite(lse), np.exp(lse_a - lse), 0.0)
+        wb = np.where(np.isfinite(lse), np.exp(lse_b - lse), 0.0)
+    # weights [b, Hq, m] -> [b, m, Hq, 1]
+    wa, wb = wa.transpose(0, 2, 1)[..., None], wb.transpose(0, 2, 1)[..., None]
+    return wa * o_a + wb * o_b, lse
 
 
 # ---------------------------------------------------------------------------
@@ -298,7 +337,7 @@ def mlp_backward(a, bt, c, do, scale=1.0, workers=None, block_rows=None):
 # brute-force scalar loops (tiny shapes only)
 # ---------------------------------------------------------------------------
 
-def brute_attention_forward(q, k, v, scale, causal=False):
+def brute_attention_forward(q, k, v, scale, causal=False, q_offset=0, k_offset=0):
     """Scalar-loop attention with math.exp; same layouts as attention_forward."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     b, m, hq, d = q.shape
@@ -309,7 +348,10 @@ def brute_attention_forward(q, k, v, scale, causal=False):
         for h in range(hq):
             g = h // (hq // hkv)
             for i in range(m):
-                keys = [j for j in range(n) if not (causal and j > i)]
+                keys = [j for j in range(n) if not (causal and k_offset + j > q_offset + i)]
+                if not keys:  # no visible key: O = 0, LSE = -inf
+                    lse[bi, h, i] = -math.inf
+                    continue
                 s = {}
                 for j in keys:
                     acc = 0.0
@@ -325,7 +367,7 @@ def brute_attention_forward(q, k, v, scale, causal=False):
     return o, lse
 
 
-def brute_attention_backward(q, k, v, do, scale, causal=False):
+def brute_attention_backward(q, k, v, do, scale, causal=False, q_offset=0, k_offset=0):
     """Scalar-loop gradients of <dO, O> by the chain rule through softmax."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     b, m, hq, d = q.shape
@@ -335,7 +377,9 @@ def brute_attention_backward(q, k, v, do, scale, causal=False):
         for h in range(hq):
             g = h // (hq // hkv)
             for i in range(m):
-                keys = [j for j in range(n) if not (causal and j > i)]
+                keys = [j for j in range(n) if not (causal and k_offset + j > q_offset + i)]
+                if not keys:  # the row sees no key: no gradient flows through it
+                    continue
                 s = {j: float(scale) * sum(q[bi, i, h, t] * k[bi, j, g, t]
                                            for t in range(d)) for j in keys}
                 top = max(s.values())

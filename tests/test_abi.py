@@ -28,7 +28,8 @@ def test_exports_every_declared_symbol():
 def test_abi_version_and_struct_size():
     L = B.lib()
     assert L.fab_abi_version() == B.ABI_VERSION
-    assert L.fab_problem_size() == ctypes.sizeof(B.FabProblem) == 176
+    assert L.fab_abi_version() == 2
+    assert L.fab_problem_size() == ctypes.sizeof(B.FabProblem) == 192
 
 
 def attn(**kw):
@@ -53,7 +54,12 @@ def status_of(prob):
     ({"heads_a": 3}, "FAB_ERR_BAD_SHAPE"),
     ({"m": 0}, "FAB_ERR_BAD_SHAPE"),
     ({"batch": 0}, "FAB_ERR_BAD_SHAPE"),
-    ({"m": 100, "n": 300}, "FAB_ERR_UNSUPPORTED"),
+    ({"m": 100, "n": 300}, "FAB_OK"),  # causal with m != n: offsets place the rows
+    ({"m": 100, "n": 300, "q_offset": 200}, "FAB_OK"),
+    ({"k_offset": -5, "q_offset": 7}, "FAB_OK"),
+    ({"q_offset": 1 << 41}, "FAB_ERR_BAD_SHAPE"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "q_offset": 3},
+     "FAB_ERR_UNSUPPORTED"),
     ({"k": 96, "p": 96}, "FAB_ERR_UNSUPPORTED"),
     ({"k": 128, "p": 64}, "FAB_ERR_UNSUPPORTED"),
     ({"scale": 0.0}, "FAB_ERR_UNSUPPORTED"),
@@ -105,3 +111,20 @@ def test_status_strings():
     for code in B.STATUS:
         assert L.fab_status_string(code)
     assert L.fab_status_string(0) == b"ok"
+
+
+def test_merge_argument_errors_before_any_launch():
+    L = B.lib()
+    p = B.Plan(attn())
+    vp = ctypes.c_void_p
+    good = vp(0x10000)
+    st = L.fab_merge(p._ptr, good, good, None, good, good, good, None)
+    assert B.STATUS[st] == "FAB_ERR_NULL_ARG"
+    st = L.fab_merge(p._ptr, vp(0x10008), good, good, good, good, good, None)
+    assert B.STATUS[st] == "FAB_ERR_ALIGNMENT"
+    st = L.fab_merge(p._ptr, good, vp(0x10002), good, good, good, good, None)
+    assert B.STATUS[st] == "FAB_ERR_ALIGNMENT"
+    g = B.Plan(attn(f=B.GELU_ERF, heads_a=1, heads_bc=1, causal=False, m=128, n=128, k=128,
+                    p=128, scale=1.0))
+    st = L.fab_merge(g._ptr, good, good, good, good, good, good, None)
+    assert B.STATUS[st] == "FAB_ERR_UNSUPPORTED"

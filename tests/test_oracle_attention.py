@@ -12,7 +12,7 @@ import pytest
 
 from oracle import (attention_backward, attention_backward_keys,
                     attention_backward_rows, attention_forward,
-                    attention_forward_rows, attention_probs,
+                    attention_forward_rows, attention_merge, attention_probs,
                     brute_attention_backward, brute_attention_forward)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -231,3 +231,85 @@ def test_row_blocks_do_not_change_result():
     gb = attention_backward(q, k, v, do, 0.5, True, block_rows=5, workers=3)
     for x, y in zip(ga, gb):
         np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# causal positions for a slice of the sequence (q_offset / k_offset) and the
+# merge of results over disjoint key sets
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("q_offset,k_offset", [(0, 0), (7, 3), (3, 7), (0, 5), (100, 0),
+                                               (0, 100)])
+def test_offset_mask_brute_force(q_offset, k_offset):
+    q, k, v, do = qkv(21, b=1, m=6, n=5, hq=2, hkv=1, d=3, dv=4)
+    scale = 0.7
+    o, lse = attention_forward(q, k, v, scale, True, q_offset=q_offset, k_offset=k_offset)
+    ob, lb = brute_attention_forward(q, k, v, scale, True, q_offset, k_offset)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-13)
+    grads = attention_backward(q, k, v, do, scale, True, q_offset=q_offset, k_offset=k_offset)
+    brute = brute_attention_backward(q, k, v, do, scale, True, q_offset, k_offset)
+    for g, gb in zip(grads, brute):
+        np.testing.assert_allclose(g, gb, rtol=0, atol=1e-12)
+
+
+def test_offset_mask_against_torch_explicit_mask():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    q, k, v, do = qkv(22, b=1, m=11, n=17, hq=2, hkv=2, d=8)
+    scale, q_offset, k_offset = 0.3, 9, 2  # every row sees >= 8 keys
+    o, lse = attention_forward(q, k, v, scale, True, q_offset=q_offset, k_offset=k_offset)
+    allow = (k_offset + np.arange(17))[None, :] <= (q_offset + np.arange(11))[:, None]
+    tq, tk, tv = (torch.tensor(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    to = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(allow), scale=scale)
+    np.testing.assert_allclose(o, to.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+
+
+def test_offset_limits():
+    q, k, v, _ = qkv(23, b=1, m=6, n=8, hq=1, hkv=1, d=4)
+    full, lf = attention_forward(q, k, v, 0.5, False)
+    # every row sees every key once q_offset - k_offset >= n - 1
+    o, lse = attention_forward(q, k, v, 0.5, True, q_offset=7, k_offset=0)
+    np.testing.assert_allclose(o, full, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, lf, rtol=0, atol=1e-14)
+    # no row sees a key once q_offset + m - 1 < k_offset
+    o, lse = attention_forward(q, k, v, 0.5, True, q_offset=0, k_offset=6)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cuts", [(5,), (3, 8), (1, 2, 11)])
+def test_key_split_merge_equals_full(causal, cuts):
+    """Splitting the keys into ranges (each placed by its k_offset), then merging
+    the per-range results pairwise in any order, gives the full result."""
+    q, k, v, _ = qkv(24, b=2, m=12, n=12, hq=4, hkv=2, d=6)
+    scale = 0.45
+    full, lf = attention_forward(q, k, v, scale, causal)
+    bounds = [0, *cuts, 12]
+    parts = [attention_forward(q, k[:, a:b], v[:, a:b], scale, causal, q_offset=0, k_offset=a)
+             for a, b in zip(bounds[:-1], bounds[1:])]
+    o, lse = parts[-1]
+    for po, pl in reversed(parts[:-1]):  # right to left
+        o, lse = attention_merge(po, pl, o, lse)
+    np.testing.assert_allclose(o, full, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lf, rtol=0, atol=1e-13)
+
+
+def test_merge_closed_form_and_empty_rows():
+    # a 2-key softmax split into two 1-key parts: O_x = V_x, LSE_x = S_x
+    o_a = np.full((1, 1, 1, 2), 3.0)
+    o_b = np.full((1, 1, 1, 2), -1.0)
+    la, lb = np.array([[[0.25]]]), np.array([[[1.0]]])
+    o, lse = attention_merge(o_a, la, o_b, lb)
+    pa = math.exp(0.25) / (math.exp(0.25) + math.exp(1.0))
+    np.testing.assert_allclose(o[0, 0, 0], [3 * pa - (1 - pa)] * 2, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, math.log(math.exp(0.25) + math.exp(1.0)), rtol=0, atol=1e-15)
+    # an empty part leaves the other unchanged; two empty parts give O = 0, -inf
+    o, lse = attention_merge(o_a, la, np.zeros_like(o_b), np.array([[[-np.inf]]]))
+    np.testing.assert_array_equal(o, o_a)
+    np.testing.assert_array_equal(lse, la)
+    o, lse = attention_merge(np.zeros_like(o_a), np.array([[[-np.inf]]]), np.zeros_like(o_b),
+                             np.array([[[-np.inf]]]))
+    assert np.all(o == 0) and np.isneginf(lse).all()
