@@ -247,6 +247,33 @@ def peak_hbm_sweep(torch, fab, exps=range(12, 21)):
             "doubling_ratios": ratios}
 
 
+def time_merge(w, reps, torch, fab):
+    """HBM rate of the merge of two partial results (fab_merge) at the size of
+    the benchmarked attention output: reads two O and two LSE, writes one of
+    each."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    shape = (w.batch, w.seq, w.heads_q, w.d)
+    oa = torch.randn(shape, device="cuda", generator=gen).to(torch.bfloat16)
+    ob = torch.randn(shape, device="cuda", generator=gen).to(torch.bfloat16)
+    la = torch.randn((w.batch, w.heads_q, w.seq), device="cuda", generator=gen)
+    lb = torch.randn((w.batch, w.heads_q, w.seq), device="cuda", generator=gen)
+    oo, lo = torch.empty_like(oa), torch.empty_like(la)
+    fab.merge(oa, la, ob, lb, out=(oo, lo))
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fab.merge(oa, la, ob, lb, out=(oo, lo))
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 3 * oa.numel() * 2 + 3 * la.numel() * 4
+    return {"ms": ms, "bytes": nbytes, "gbs": nbytes / ms / 1e6,
+            "frac_hbm_peak": nbytes / ms / 1e6 / HBM_PEAK_GBS,
+            "shape": f"O {list(shape)} bf16, LSE {[w.batch, w.heads_q, w.seq]} fp32"}
+
+
 def time_mlp(steps, warmup, torch, fab_binding):
     from attention_fab_forward_amd.inputs import WORKLOADS, mlp_inputs
     w = WORKLOADS[MLP_WORKLOAD]
@@ -427,6 +454,8 @@ def main():
             "attn_causal_bf16_gqa2_n1048576_d128": time_workload(
                 "attn_causal_bf16_gqa2_n1048576_d128", 1, torch, fab),
         }
+        log("merge ...")
+        extras["merge"] = time_merge(w, 20, torch, fab)
         log("mlp ...")
         extras["mlp"] = time_mlp(max(3, args.steps), args.warmup, torch, fab_binding)
     cpu = None
