@@ -239,17 +239,28 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
 
   // The two roles run separate copies of the step loop (same barriers per
   // step), so each loop keeps only its own role's invariants in registers.
-  auto prefetch = [&](int step) {
-    if (step + 1 < steps) {
-      const int nh = (step + 1) / steps_per_head, nq = (step + 1) % steps_per_head;
+  // Step s covers query block qb_first + s % steps_per_head of query head
+  // g * group + s / steps_per_head; the loops advance (head, block) counters
+  // instead of dividing.  prefetch copies the tiles of the step after (nh, nq).
+  auto prefetch = [&](int step, int nh, int nq) {
+    if (step + 1 < steps)
       dkdv_issue<D>(a, tq, to, bi, g * a.group + nh, (qb_first + nq) * C::TILE,
                     smem + ((step + 1) & 1) * L::STAGE, wave, lane);
+  };
+  auto advance = [&](int& hh, int& qq) {
+    if (++qq == steps_per_head) {
+      qq = 0;
+      ++hh;
     }
   };
   if (p_role) {
+    int hc = 0, qc = 0;  // (head, block) of this step
     for (int step = 0; step < steps; ++step) {
-      prefetch(step);
-      const int q0 = (qb_first + step % steps_per_head) * C::TILE;
+      int hn = hc, qn = qc;
+      advance(hn, qn);
+      prefetch(step, hn, qn);
+      const int q0 = (qb_first + qc) * C::TILE;
+      hc = hn, qc = qn;
       const char* st = smem + (step & 1) * L::STAGE;
       // A key group skips a query block when every query precedes all its keys.
       const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 + a.diag >= k0w);
@@ -299,9 +310,13 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
       lds_barrier();
     }
   } else {
+    int hc = 0, qc = 0;  // (head, block) of this step
     for (int step = 0; step < steps; ++step) {
-      prefetch(step);
-      const int q0 = (qb_first + step % steps_per_head) * C::TILE;
+      int hn = hc, qn = qc;
+      advance(hn, qn);
+      prefetch(step, hn, qn);
+      const int q0 = (qb_first + qc) * C::TILE;
+      hc = hn, qc = qn;
       const char* st = smem + (step & 1) * L::STAGE;
       const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 + a.diag >= k0w);
       f32x16 dp[2];
