@@ -121,14 +121,6 @@ __device__ __forceinline__ void issue_kv(const TileOffsets<D>& t, const uint16_t
   }
 }
 
-// Software pipeline over key blocks: while the softmax of block j runs on the
-// VALU, the MFMAs of S for block j+1 are already issued, so the two overlap
-// inside each wave.  K tiles are therefore copied two blocks ahead and V tiles
-// one block ahead (two LDS buffers each).  Iteration j:
-//   copy K[j+2] -> Kbuf[j % 2], V[j+1] -> Vbuf[(j+1) % 2]
-//   mask S[j] (diagonal / ragged blocks), softmax(S[j]) || S[j+1] = K[j+1] Q^T
-//   rescale O if the running maximum moved, O += V[j]^T P[j]^T
-//   wait for this wave's copies, barrier
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * FwdCfg<D>::NW, 8 / FwdCfg<D>::NW) void
 attn_fwd_bf16_kernel(AttnArgs a) {
@@ -174,8 +166,6 @@ attn_fwd_bf16_kernel(AttnArgs a) {
     issue_kv<D, false>(toff, vbase, a.v_sr, kb * C::BN, a.n, vbuf(kb), wave, lane);
   };
   copy_k(0);
-  copy_v(0);
-  if (nkb > 1) copy_k(1);
 
   // Q^T fragments: lane holds Q[myq][16c + 8lg .. +7] for every chunk c.
   u32x4 qf[C::DC];
@@ -214,10 +204,13 @@ attn_fwd_bf16_kernel(AttnArgs a) {
         [&](int i, const u32x4& x) { s[i % 2] = mfma32(x, qf[i / 2], s[i % 2]); });
   };
 
-  // One pipelined step on key block kb (NEXT: also compute S of block kb + 1).
+  // Online softmax of block j on the VALU: mask, row maximum, P_j (bf16,
+  // packed as the next MFMA's B operand), row sum, O rescale when the running
+  // maximum moves.
   f32x16 s[2];
-  auto step = [&]<bool NEXT>(int kb) {
-    const int key0 = kb * C::BN;
+  u32x4 pb[2][2];
+  auto softmax = [&](int j) {
+    const int key0 = j * C::BN;
     if ((CAUSAL && key0 + C::BN - 1 > q0 + a.diag) || key0 + C::BN > a.n) {
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -227,9 +220,6 @@ attn_fwd_bf16_kernel(AttnArgs a) {
           if ((CAUSAL && key > myq + a.diag) || key >= a.n) s[sb][r] = -INFINITY;
         }
     }
-    f32x16 sn[2];
-    if constexpr (NEXT) compute_s(sn, kbuf(kb + 1));
-    // online softmax of block kb (VALU, overlapping the MFMAs above)
     float mx = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -244,7 +234,6 @@ attn_fwd_bf16_kernel(AttnArgs a) {
     const float alpha = fast_exp2(m_run - m_ref);
     const bool rescale = m_new != m_run;
     float lsum = 0.f;
-    u32x4 pb[2][2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       float p[16];
@@ -266,10 +255,12 @@ attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     }
-    // O^T += V^T P^T.  Operand i: output tile t = i % DT, keys
-    // 32 sb + 16 lg + 8 c + e with (sb, c) = (i / DT / 2, i / DT % 2), read as
-    // two 4-key groups.
-    const char* vt = vbuf(kb);
+  };
+  // O^T += V_j^T P_j^T.  Operand i: output tile t = i % DT, keys
+  // 32 sb + 16 lg + 8 c + e with (sb, c) = (i / DT / 2, i / DT % 2), read as
+  // two 4-key groups.
+  auto pv = [&](int j) {
+    const char* vt = vbuf(j);
     lds_mfma_pipeline<4 * C::DT, 4>(
         [&](int i) {
           const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
@@ -285,39 +276,44 @@ attn_fwd_bf16_kernel(AttnArgs a) {
           const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
           o[t] = mfma32(x, pb[sb][c], o[t]);
         });
-    if constexpr (NEXT) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) s[sb] = sn[sb];
-    }
   };
-  // copies issued at the top of iteration kb
-  auto prefetch = [&](int kb) {
-    if (kb + 2 < nkb) copy_k(kb + 2);
-    if (kb + 1 < nkb) copy_v(kb + 1);
+  // copies issued in iteration j: K[j + 1] and V[j] (their buffers held
+  // K[j - 1] and V[j - 2], read by both groups before the previous barrier)
+  auto copy_step = [&](int j) {
+    if (j + 1 < nkb) copy_k(j + 1);
+    if (j < nkb) copy_v(j);
   };
 
   wait_vmem();
   lds_barrier();
-  if (nkw > 0) compute_s(s, kbuf(0));
-  lds_barrier();  // K[0] fully read before iteration 0 copies K[2] over it
-  int kb = 0;
-  for (; kb + 1 < nkw; ++kb) {
-    prefetch(kb);
-    step.template operator()<true>(kb);
-    wait_vmem();
-    lds_barrier();
-  }
-  if (kb < nkw) {
-    prefetch(kb);
-    step.template operator()<false>(kb);
-    wait_vmem();
-    lds_barrier();
-    ++kb;
-  }
-  for (; kb < nkb; ++kb) {  // blocks past this wave's last query: copies only
-    prefetch(kb);
-    wait_vmem();
-    lds_barrier();
+  // Two wave groups in ping-pong: waves 0-3 and 4-7 (one of each per SIMD).
+  // Iteration j has two phases separated by barriers; a wave's MFMA phase
+  // (S_j = K_j Q^T and O += V_{j-1} P_{j-1}) overlaps the other group's VALU
+  // phase (softmax of its S) on the same SIMD:
+  //   group 0:  [copies j, MFMA j]  |  [softmax j]      then wait for copies
+  //   group 1:  [copies j, softmax j-1]  |  [MFMA j]    then wait for copies
+  // Both groups run j = 0 .. nkb with two barriers per iteration.
+  if (wave < 4) {
+    int j = 0;
+    for (; j <= nkb; ++j) {
+      copy_step(j);
+      if (j < nkw) compute_s(s, kbuf(j));
+      if (j >= 1 && j <= nkw) pv(j - 1);
+      lds_barrier();
+      if (j < nkw) softmax(j);
+      wait_vmem();
+      lds_barrier();
+    }
+  } else {
+    for (int j = 0; j <= nkb; ++j) {
+      copy_step(j);
+      if (j >= 1 && j <= nkw) softmax(j - 1);
+      lds_barrier();
+      if (j < nkw) compute_s(s, kbuf(j));
+      if (j >= 1 && j <= nkw) pv(j - 1);
+      wait_vmem();
+      lds_barrier();
+    }
   }
 
   // rows that saw no key (offset causal masks): O = 0, LSE = -inf
