@@ -99,9 +99,10 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* part, in
   stg16(out + r * ld_out + c, v);
 }
 
-// Sum the four waves' partial tiles through LDS; returns the full tile in the
-// calling lane's accumulator layout.
-__device__ __forceinline__ f32x16 reduce4(f32x16 v, float* lds, int wave, int lane) {
+// Sum the NW waves' partial tiles through LDS (NW * 4 KiB); returns the full
+// tile in the calling lane's accumulator layout.
+template <int NW>
+__device__ __forceinline__ f32x16 reduce_waves(f32x16 v, float* lds, int wave, int lane) {
   f32x4* mine = reinterpret_cast<f32x4*>(lds + (wave * 64 + lane) * 16);
 #pragma unroll
   for (int i = 0; i < 4; ++i) mine[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
@@ -110,7 +111,7 @@ __device__ __forceinline__ f32x16 reduce4(f32x16 v, float* lds, int wave, int la
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const f32x4* src = reinterpret_cast<const f32x4*>(lds + (w * 64 + lane) * 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -122,6 +123,9 @@ __device__ __forceinline__ f32x16 reduce4(f32x16 v, float* lds, int wave, int la
     }
   }
   return s;
+}
+__device__ __forceinline__ f32x16 reduce4(f32x16 v, float* lds, int wave, int lane) {
+  return reduce_waves<4>(v, lds, wave, lane);
 }
 
 __device__ __forceinline__ void pack16(const float* x, u32x4 out[2]) {
@@ -140,17 +144,25 @@ __device__ __forceinline__ void store_tile_f32(float* dst, const f32x16& v) {
 // ---------------------------------------------------------------------------
 // forward: workgroup = 32 rows of A, one split of the n tiles
 // ---------------------------------------------------------------------------
+// NW waves split the first product's contraction (k / NW each, summed through
+// LDS) and the output columns (p / NW each).
 template <int K, int P>
-__global__ __launch_bounds__(256, 1) void mlp_fwd_kernel(MlpArgs a, const uint16_t* ct,
+constexpr int mlp_fwd_waves() { return (K >= 128 && P >= 256) ? 8 : 4; }
+
+template <int K, int P>
+__global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(MlpArgs a, const uint16_t* ct,
                                                          int64_t ldct, int tiles_per_split,
                                                          float* part) {
-  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
+  constexpr int NW = mlp_fwd_waves<K, P>();
+  __shared__ __attribute__((aligned(16))) float red[NW * 64 * 16];  // partial H tiles
+  __shared__ __attribute__((aligned(16))) uint32_t gsh[64 * 8];     // G tile, bf16 pairs
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
   const int row = blockIdx.x * 32 + lq;
   const bool rlive = row < a.m;
-  constexpr int kq = K / 4, kc = kq / 16;
-  constexpr int pq = P / 4, pt = pq / 32;
+  constexpr int kq = K / NW, kc = kq / 16;
+  constexpr int pq = P / NW, pt = pq / 32;
+  static_assert(kc >= 1 && pt >= 1, "each wave needs a 16-deep slice of k and 32 columns of p");
   const uint16_t* A = static_cast<const uint16_t*>(a.a);
   const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
 
@@ -168,31 +180,64 @@ __global__ __launch_bounds__(256, 1) void mlp_fwd_kernel(MlpArgs a, const uint16
   const int ntiles = (a.n + 31) / 32;
   const int jt0 = blockIdx.y * tiles_per_split;
   const int jt1 = min(ntiles, jt0 + tiles_per_split);
+  // Operands are loaded one phase ahead of their use: the Bt fragments of
+  // tile jt + 1 right after the first product of tile jt, and the C^T
+  // fragments of tile jt at its top, so both loads overlap the barriers, the
+  // reduction and the GeLU instead of stalling the MFMAs.
+  u32x4 bfr[kc];
+  auto load_bt = [&](int jt) {
+    const int nrow = jt * 32 + perm_row(lq);
+    const uint16_t* btrow = Bt + (int64_t)nrow * a.bt_sr + wave * kq + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < kc; ++c) bfr[c] = nrow < a.n ? ldg16(btrow + 16 * c) : u32x4{0, 0, 0, 0};
+  };
+  if (jt0 < jt1) load_bt(jt0);
   for (int jt = jt0; jt < jt1; ++jt) {
     const int n0 = jt * 32;
-    const int nrow = n0 + perm_row(lq);
-    const bool nlive = nrow < a.n;
-    const uint16_t* btrow = Bt + (int64_t)nrow * a.bt_sr + wave * kq + 8 * lg;
+    u32x4 cfr[pt][2];
+#pragma unroll
+    for (int t = 0; t < pt; ++t) {
+      const uint16_t* crow = ct + (int64_t)(wave * pq + 32 * t + perm_row(lq)) * ldct + n0 + 16 * lg;
+      cfr[t][0] = ldg16(crow);
+      cfr[t][1] = ldg16(crow + 8);
+    }
     f32x16 hp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) hp[r] = 0.f;
 #pragma unroll
-    for (int c = 0; c < kc; ++c)
-      hp = mfma32(nlive ? ldg16(btrow + 16 * c) : u32x4{0, 0, 0, 0}, af[c], hp);
-    const f32x16 h = reduce4(hp, red, wave, lane);
-    // slot r of lane l: row `row`, column n0 + 16 lg + r
-    float g[16];
+    for (int c = 0; c < kc; ++c) hp = mfma32(bfr[c], af[c], hp);
+    if (jt + 1 < jt1) load_bt(jt + 1);
+    // Sum the waves' partial tiles and apply GeLU, each wave taking 16 / NW of
+    // the 16 slots of every lane (slot r of lane l: row `row`, column
+    // n0 + 16 lg + r), then share G in bf16 through LDS.
+    {
+      f32x4* mine = reinterpret_cast<f32x4*>(red + (wave * 64 + lane) * 16);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) g[r] = gelu_f(a.scale * h[r]);
+      for (int i = 0; i < 4; ++i) mine[i] = f32x4{hp[4 * i], hp[4 * i + 1], hp[4 * i + 2], hp[4 * i + 3]};
+    }
+    __syncthreads();
+    {
+      constexpr int SPW = 16 / NW;  // slots per wave
+      float h[SPW];
+#pragma unroll
+      for (int j = 0; j < SPW; ++j) h[j] = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) h[j] += red[(w * 64 + lane) * 16 + wave * SPW + j];
+#pragma unroll
+      for (int j = 0; j < SPW; j += 2)
+        gsh[lane * 8 + (wave * SPW + j) / 2] = pack_bf16(gelu_f(a.scale * h[j]), gelu_f(a.scale * h[j + 1]));
+    }
+    __syncthreads();
     u32x4 gb[2];
-    pack16(g, gb);
+    gb[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
+    gb[1] = *reinterpret_cast<const u32x4*>(gsh + lane * 8 + 4);
 #pragma unroll
     for (int t = 0; t < pt; ++t) {
-      const uint16_t* crow = ct + (int64_t)(wave * pq + 32 * t + perm_row(lq)) * ldct + n0 + 16 * lg;
-      o[t] = mfma32(ldg16(crow), gb[0], o[t]);
-      o[t] = mfma32(ldg16(crow + 8), gb[1], o[t]);
+      o[t] = mfma32(cfr[t][0], gb[0], o[t]);
+      o[t] = mfma32(cfr[t][1], gb[1], o[t]);
     }
-    __syncthreads();  // LDS partials are reused by the next tile
   }
   if (!rlive) return;
   float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.p + wave * pq + 16 * lg;
@@ -444,7 +489,8 @@ template <int K, int P>
 hipError_t fwd_kp(const MlpArgs& a, const MlpLayout& L, uint16_t* ct, float* part, hipStream_t s) {
   const int ntiles = (a.n + 31) / 32;
   const int per = (ntiles + L.split_rows - 1) / L.split_rows;
-  const dim3 grid((unsigned)((a.m + 31) / 32), (unsigned)L.split_rows), block(256);
+  const dim3 grid((unsigned)((a.m + 31) / 32), (unsigned)L.split_rows),
+      block(64 * mlp_fwd_waves<K, P>());
   FAB_TIMED("mlp_fwd", s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, ct, L.n_pad, per, part));
   return hipGetLastError();
 }
