@@ -10,12 +10,14 @@
 // ("AutoSP" 2.B):
 //   dH = dG * GeLU'(H), dA = scale dH Bt, dBt = scale dH^T A, dC = GeLU(H)^T dO.
 //
-// Schedule ("lanes = rows" as in the attention kernels): a workgroup of 4
-// waves owns 32 rows (or 32 columns of n for the dBt/dC kernel).  The long
-// contractions of the first products (k, p <= 1024) are split across the 4
-// waves, each keeping its quarter of the resident operand in registers, and
-// the partial 32 x 32 tiles are summed through LDS.  Each wave then owns a
-// quarter of the output columns for the second product.  Operands whose
+// Schedule ("lanes = rows" as in the attention kernels): a workgroup of NW
+// waves (8, or 4 for the smallest k and p) owns 32 rows (or 32 columns of n
+// for the dBt/dC kernel).  The long contractions of the first products
+// (k, p <= 1024) are split across the NW waves, each keeping its 1 / NW of
+// the resident operand in registers; the partial 32 x 32 tiles are summed
+// through LDS and each wave finishes 16 / NW of every lane's tile entries
+// (GeLU or GeLU'), so each erf is evaluated once.  Each wave then owns 1 / NW
+// of the output columns for the second product.  Operands whose
 // contraction runs along their non-contiguous axis are read from transposed
 // copies that a small kernel writes into the workspace first (copies of the
 // inputs, not of the intermediate).  The n (or m) loop is split across
@@ -99,46 +101,50 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* part, in
   stg16(out + r * ld_out + c, v);
 }
 
-// Sum the NW waves' partial tiles through LDS (NW * 4 KiB); returns the full
-// tile in the calling lane's accumulator layout.
-template <int NW>
-__device__ __forceinline__ f32x16 reduce_waves(f32x16 v, float* lds, int wave, int lane) {
-  f32x4* mine = reinterpret_cast<f32x4*>(lds + (wave * 64 + lane) * 16);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) mine[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-  __syncthreads();
-  f32x16 s;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(lds + (w * 64 + lane) * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 x = src[i];
-      s[4 * i] += x[0];
-      s[4 * i + 1] += x[1];
-      s[4 * i + 2] += x[2];
-      s[4 * i + 3] += x[3];
-    }
-  }
-  return s;
-}
-__device__ __forceinline__ f32x16 reduce4(f32x16 v, float* lds, int wave, int lane) {
-  return reduce_waves<4>(v, lds, wave, lane);
-}
-
-__device__ __forceinline__ void pack16(const float* x, u32x4 out[2]) {
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) out[c][w] = pack_bf16(x[8 * c + 2 * w], x[8 * c + 2 * w + 1]);
+// 16 bytes at p, or zeros when !live.  Callers clamp the row so p is valid
+// either way: the load is unconditional (no branch) and a select zeroes it.
+__device__ __forceinline__ u32x4 ldg16_live(const uint16_t* p, bool live) {
+  const u32x4 v = ldg16(p);
+  return live ? v : u32x4{0, 0, 0, 0};
 }
 
 __device__ __forceinline__ void store_tile_f32(float* dst, const f32x16& v) {
   f32x4* d = reinterpret_cast<f32x4*>(dst);
 #pragma unroll
   for (int i = 0; i < 4; ++i) d[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+}
+
+// Sums the NW partial tiles of H (and of dG when GRAD) held in LDS and writes
+// GeLU(scale H) (or dG * GeLU'(scale H) when GRAD) as bf16 pairs to gsh; wave
+// w takes slots [16 w / NW, 16 (w + 1) / NW) of every lane, so each erf is
+// evaluated once.  Caller: barrier before (partials written) and after (gsh
+// complete).
+template <int NW, bool GRAD>
+__device__ __forceinline__ void finish_tile(const float* red_h, const float* red_g, uint32_t* gsh,
+                                            int wave, int lane, float scale) {
+  constexpr int SPW = 16 / NW;
+  static_assert(SPW % 2 == 0, "slots are packed in pairs");
+  float h[SPW], g[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) h[j] = g[j] = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+      h[j] += red_h[(w * 64 + lane) * 16 + wave * SPW + j];
+      if constexpr (GRAD) g[j] += red_g[(w * 64 + lane) * 16 + wave * SPW + j];
+    }
+  float x[SPW];
+#pragma unroll
+  for (int j = 0; j < SPW; ++j) x[j] = GRAD ? g[j] * gelu_grad_f(scale * h[j]) : gelu_f(scale * h[j]);
+#pragma unroll
+  for (int j = 0; j < SPW; j += 2) gsh[lane * 8 + (wave * SPW + j) / 2] = pack_bf16(x[j], x[j + 1]);
+}
+
+__device__ __forceinline__ void stash_tile(float* red, int wave, int lane, const f32x16& v) {
+  f32x4* mine = reinterpret_cast<f32x4*>(red + (wave * 64 + lane) * 16);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mine[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -156,7 +162,7 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
   constexpr int NW = mlp_fwd_waves<K, P>();
   __shared__ __attribute__((aligned(16))) float red[NW * 64 * 16];  // partial H tiles
   __shared__ __attribute__((aligned(16))) uint32_t gsh[64 * 8];     // G tile, bf16 pairs
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
   const int row = blockIdx.x * 32 + lq;
   const bool rlive = row < a.m;
@@ -187,9 +193,10 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
   u32x4 bfr[kc];
   auto load_bt = [&](int jt) {
     const int nrow = jt * 32 + perm_row(lq);
-    const uint16_t* btrow = Bt + (int64_t)nrow * a.bt_sr + wave * kq + 8 * lg;
+    const bool nlive = nrow < a.n;
+    const uint16_t* btrow = Bt + (int64_t)min(nrow, a.n - 1) * a.bt_sr + wave * kq + 8 * lg;
 #pragma unroll
-    for (int c = 0; c < kc; ++c) bfr[c] = nrow < a.n ? ldg16(btrow + 16 * c) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < kc; ++c) bfr[c] = ldg16_live(btrow + 16 * c, nlive);
   };
   if (jt0 < jt1) load_bt(jt0);
   for (int jt = jt0; jt < jt1; ++jt) {
@@ -206,29 +213,11 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
     for (int r = 0; r < 16; ++r) hp[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < kc; ++c) hp = mfma32(bfr[c], af[c], hp);
-    if (jt + 1 < jt1) load_bt(jt + 1);
-    // Sum the waves' partial tiles and apply GeLU, each wave taking 16 / NW of
-    // the 16 slots of every lane (slot r of lane l: row `row`, column
-    // n0 + 16 lg + r), then share G in bf16 through LDS.
-    {
-      f32x4* mine = reinterpret_cast<f32x4*>(red + (wave * 64 + lane) * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mine[i] = f32x4{hp[4 * i], hp[4 * i + 1], hp[4 * i + 2], hp[4 * i + 3]};
-    }
+    load_bt(min(jt + 1, jt1 - 1));  // unconditional: a branch here costs register copies
+    stash_tile(red, wave, lane, hp);
     __syncthreads();
-    {
-      constexpr int SPW = 16 / NW;  // slots per wave
-      float h[SPW];
-#pragma unroll
-      for (int j = 0; j < SPW; ++j) h[j] = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w)
-#pragma unroll
-        for (int j = 0; j < SPW; ++j) h[j] += red[(w * 64 + lane) * 16 + wave * SPW + j];
-#pragma unroll
-      for (int j = 0; j < SPW; j += 2)
-        gsh[lane * 8 + (wave * SPW + j) / 2] = pack_bf16(gelu_f(a.scale * h[j]), gelu_f(a.scale * h[j + 1]));
-    }
+    // slot r of lane l: row `row`, column n0 + 16 lg + r
+    finish_tile<NW, false>(red, nullptr, gsh, wave, lane, a.scale);
     __syncthreads();
     u32x4 gb[2];
     gb[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
@@ -246,19 +235,60 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
 }
 
 // ---------------------------------------------------------------------------
-// backward, dA: workgroup = 32 rows of A, one split of the n tiles
+// backward.  Both kernels below recompute one 32 x 32 tile of H (and of dG for
+// the gradient of the first product) per step, split over NW waves along the
+// contraction, then finish it with finish_tile and feed it to the second
+// product.  After this tile's first-product MFMAs, the tile's transposed
+// second-product operand is copied asynchronously into LDS and the rows of
+// the next tile's first-product operands are loaded into registers, so both
+// overlap the barriers and GeLU', and the second operand holds no registers
+// while the partial tiles do.
 // ---------------------------------------------------------------------------
+
+// The backward kernels stage their transposed second-product operand in LDS
+// with asynchronous global -> LDS copies (each lane reads back exactly the 16
+// byte pieces it copied, so only a wave-local wait is needed).  These waits
+// are assembly with a memory clobber so LDS accesses stay on their side.
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Copies the kt x 2 16-byte pieces of this lane's second-product operand
+// (rows row0 + 32 t + perm_row(lq) of the transposed copy xt, 16 columns from
+// col0 + 16 lg) into the wave's LDS region: piece (t, h) of lane l lands at
+// region + (2 t + h) * 1024 + 16 l.
+template <int kt>
+__device__ __forceinline__ void copy_second_operand(const uint16_t* xt, int64_t ldxt, int row0,
+                                                    int col0, int lq, int lg, char* region) {
+#pragma unroll
+  for (int t = 0; t < kt; ++t) {
+    const uint16_t* trow = xt + (int64_t)(row0 + 32 * t + perm_row(lq)) * ldxt + col0 + 16 * lg;
+    dma16_at(trow, region + (2 * t) * 1024);
+    dma16_at(trow + 8, region + (2 * t + 1) * 1024);
+  }
+}
+
+// Wave count of a backward kernel whose first product contracts over K (and P
+// for dG) and whose output has OUT columns: each wave needs a 16-deep slice
+// of each contraction and 32 output columns.
+template <int K, int P, int OUT>
+constexpr int mlp_bwd_waves() { return (K >= 128 && P >= 128 && OUT >= 256) ? 8 : 4; }
+
+// dA: workgroup = 32 rows of A, one split of the n tiles.
 template <int K, int P>
-__global__ __launch_bounds__(256, 1) void mlp_bwd_da_kernel(MlpArgs a, const uint16_t* btt,
-                                                            int64_t ldbtt, int tiles_per_split,
-                                                            float* part) {
-  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+__global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_kernel(
+    MlpArgs a, const uint16_t* btt, int64_t ldbtt, int tiles_per_split, float* part) {
+  constexpr int NW = mlp_bwd_waves<K, P, K>();
+  __shared__ __attribute__((aligned(16))) float red[2 * NW * 64 * 16];  // partial H, dG tiles
+  constexpr int kq = K / NW, kc = kq / 16, kt = kq / 32;
+  __shared__ __attribute__((aligned(16))) uint32_t gsh[64 * 8];         // dH tile, bf16 pairs
+  __shared__ __attribute__((aligned(16))) char tsh[NW * kt * 2048];     // Bt^T pieces, per wave
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
   const int row = blockIdx.x * 32 + lq;
   const bool rlive = row < a.m;
-  constexpr int kq = K / 4, kc = kq / 16, kt = kq / 32;
-  constexpr int pq = P / 4, pc = pq / 16;
+  char* const tmine = tsh + wave * kt * 2048;
+  constexpr int pq = P / NW, pc = pq / 16;
+  static_assert(kt >= 1 && pc >= 1, "each wave needs 32 columns of k and a 16-deep slice of p");
   const uint16_t* A = static_cast<const uint16_t*>(a.a);
   const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
   const uint16_t* Cm = static_cast<const uint16_t*>(a.c);
@@ -282,37 +312,46 @@ __global__ __launch_bounds__(256, 1) void mlp_bwd_da_kernel(MlpArgs a, const uin
   const int ntiles = (a.n + 31) / 32;
   const int jt0 = blockIdx.y * tiles_per_split;
   const int jt1 = min(ntiles, jt0 + tiles_per_split);
+  u32x4 bfr[kc], cfr[pc];
+  auto load_rows = [&](int jt) {
+    const int nrow = jt * 32 + perm_row(lq);
+    const bool nlive = nrow < a.n;
+    const int nc = min(nrow, a.n - 1);
+    const uint16_t* btrow = Bt + (int64_t)nc * a.bt_sr + wave * kq + 8 * lg;
+    const uint16_t* crow = Cm + (int64_t)nc * a.c_sr + wave * pq + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < kc; ++c) bfr[c] = ldg16_live(btrow + 16 * c, nlive);
+#pragma unroll
+    for (int c = 0; c < pc; ++c) cfr[c] = ldg16_live(crow + 16 * c, nlive);
+  };
+  if (jt0 < jt1) load_rows(jt0);
   for (int jt = jt0; jt < jt1; ++jt) {
     const int n0 = jt * 32;
-    const int nrow = n0 + perm_row(lq);
-    const bool nlive = nrow < a.n;
-    const uint16_t* btrow = Bt + (int64_t)nrow * a.bt_sr + wave * kq + 8 * lg;
-    const uint16_t* crow = Cm + (int64_t)nrow * a.c_sr + wave * pq + 8 * lg;
     f32x16 hp, gp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) hp[r] = gp[r] = 0.f;
 #pragma unroll
-    for (int c = 0; c < kc; ++c)
-      hp = mfma32(nlive ? ldg16(btrow + 16 * c) : u32x4{0, 0, 0, 0}, af[c], hp);
+    for (int c = 0; c < kc; ++c) hp = mfma32(bfr[c], af[c], hp);
 #pragma unroll
-    for (int c = 0; c < pc; ++c)
-      gp = mfma32(nlive ? ldg16(crow + 16 * c) : u32x4{0, 0, 0, 0}, df[c], gp);
-    const f32x16 h = reduce4(hp, red, wave, lane);
+    for (int c = 0; c < pc; ++c) gp = mfma32(cfr[c], df[c], gp);
+    wait_lds_reads();  // the previous tile's reads of tmine are done
+    copy_second_operand<kt>(btt, ldbtt, wave * kq, n0, lq, lg, tmine);
+    load_rows(min(jt + 1, jt1 - 1));  // unconditional: a branch here costs register copies
+    stash_tile(red, wave, lane, hp);
+    stash_tile(red + NW * 64 * 16, wave, lane, gp);
     __syncthreads();
-    const f32x16 dg = reduce4(gp, red, wave, lane);
     // slot r of lane l: row `row`, column n0 + 16 lg + r
-    float dh[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dh[r] = dg[r] * gelu_grad_f(a.scale * h[r]);
+    finish_tile<NW, true>(red, red + NW * 64 * 16, gsh, wave, lane, a.scale);
+    __syncthreads();
     u32x4 db[2];
-    pack16(dh, db);
+    db[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
+    db[1] = *reinterpret_cast<const u32x4*>(gsh + lane * 8 + 4);
+    wait_copies();
 #pragma unroll
     for (int t = 0; t < kt; ++t) {
-      const uint16_t* trow = btt + (int64_t)(wave * kq + 32 * t + perm_row(lq)) * ldbtt + n0 + 16 * lg;
-      acc[t] = mfma32(ldg16(trow), db[0], acc[t]);
-      acc[t] = mfma32(ldg16(trow + 8), db[1], acc[t]);
+      acc[t] = mfma32(lds16(tmine + (2 * t) * 1024 + 16 * lane), db[0], acc[t]);
+      acc[t] = mfma32(lds16(tmine + (2 * t + 1) * 1024 + 16 * lane), db[1], acc[t]);
     }
-    __syncthreads();
   }
   if (!rlive) return;
   float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.k + wave * kq + 16 * lg;
@@ -320,23 +359,28 @@ __global__ __launch_bounds__(256, 1) void mlp_bwd_da_kernel(MlpArgs a, const uin
   for (int t = 0; t < kt; ++t) store_tile_f32(dst + 32 * t, acc[t]);
 }
 
-// ---------------------------------------------------------------------------
-// backward, dBt (WANT_DB) or dC (!WANT_DB): workgroup = 32 columns of n, one
-// split of the m tiles.  dBt needs H and dG; dC needs only G = GeLU(H).
-// ---------------------------------------------------------------------------
+// dBt (WANT_DB) or dC (!WANT_DB): workgroup = 32 columns of n, one split of
+// the m tiles.  dBt needs H and dG; dC needs only G = GeLU(H).
 template <int K, int P, bool WANT_DB>
-__global__ __launch_bounds__(256, 1) void mlp_bwd_col_kernel(MlpArgs a, const uint16_t* xt,
-                                                             int64_t ldxt, int tiles_per_split,
-                                                             float* part) {
-  __shared__ __attribute__((aligned(16))) float red[4 * 64 * 16];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+constexpr int mlp_bwd_col_waves() { return mlp_bwd_waves<K, (WANT_DB ? P : 128), (WANT_DB ? K : P)>(); }
+
+template <int K, int P, bool WANT_DB>
+__global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp_bwd_col_kernel(
+    MlpArgs a, const uint16_t* xt, int64_t ldxt, int tiles_per_split, float* part) {
+  constexpr int NW = mlp_bwd_col_waves<K, P, WANT_DB>();
+  __shared__ __attribute__((aligned(16))) float red[(WANT_DB ? 2 : 1) * NW * 64 * 16];
+  constexpr int kq = K / NW, kc = kq / 16;
+  constexpr int pq = P / NW, pc = WANT_DB ? pq / 16 : 1;
+  // output columns of this kernel: k (dBt) or p (dC), 1 / NW per wave
+  constexpr int oq = WANT_DB ? kq : pq, ot = oq / 32;
+  __shared__ __attribute__((aligned(16))) uint32_t gsh[64 * 8];
+  __shared__ __attribute__((aligned(16))) char tsh[NW * ot * 2048];  // xt pieces, per wave
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
   const int col = blockIdx.x * 32 + lq;  // index along n
   const bool clive = col < a.n;
-  constexpr int kq = K / 4, kc = kq / 16;
-  constexpr int pq = P / 4, pc = WANT_DB ? pq / 16 : 1;
-  // output columns of this kernel: k (dBt) or p (dC), a quarter per wave
-  constexpr int oq = WANT_DB ? kq : pq, ot = oq / 32;
+  char* const tmine = tsh + wave * ot * 2048;
+  static_assert(kc >= 1 && pc >= 1 && ot >= 1, "slice too small for the wave count");
   const uint16_t* A = static_cast<const uint16_t*>(a.a);
   const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
   const uint16_t* Cm = static_cast<const uint16_t*>(a.c);
@@ -362,45 +406,50 @@ __global__ __launch_bounds__(256, 1) void mlp_bwd_col_kernel(MlpArgs a, const ui
   const int mtiles = (a.m + 31) / 32;
   const int it0 = blockIdx.y * tiles_per_split;
   const int it1 = min(mtiles, it0 + tiles_per_split);
+  u32x4 afr[kc], ofr[pc];
+  auto load_rows = [&](int it) {
+    const int arow = it * 32 + perm_row(lq);
+    const bool alive = arow < a.m;
+    const int ac = min(arow, a.m - 1);
+    const uint16_t* ap = A + (int64_t)ac * a.a_sr + wave * kq + 8 * lg;
+#pragma unroll
+    for (int c = 0; c < kc; ++c) afr[c] = ldg16_live(ap + 16 * c, alive);
+    if constexpr (WANT_DB) {
+      const uint16_t* op = dO + (int64_t)ac * a.o_sr + wave * pq + 8 * lg;
+#pragma unroll
+      for (int c = 0; c < pc; ++c) ofr[c] = ldg16_live(op + 16 * c, alive);
+    }
+  };
+  if (it0 < it1) load_rows(it0);
   for (int it = it0; it < it1; ++it) {
     const int r0 = it * 32;
-    const int arow = r0 + perm_row(lq);
-    const bool alive = arow < a.m;
-    const uint16_t* ap = A + (int64_t)arow * a.a_sr + wave * kq + 8 * lg;
-    f32x16 hp;
+    f32x16 hp, gp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) hp[r] = 0.f;
+    for (int r = 0; r < 16; ++r) hp[r] = gp[r] = 0.f;
 #pragma unroll
-    for (int c = 0; c < kc; ++c)
-      hp = mfma32(alive ? ldg16(ap + 16 * c) : u32x4{0, 0, 0, 0}, bf[c], hp);
-    const f32x16 h = reduce4(hp, red, wave, lane);
-    // slot r of lane l: column `col`, row r0 + 16 lg + r
-    float x[16];
+    for (int c = 0; c < kc; ++c) hp = mfma32(afr[c], bf[c], hp);
     if constexpr (WANT_DB) {
-      const uint16_t* op = dO + (int64_t)arow * a.o_sr + wave * pq + 8 * lg;
-      f32x16 gp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) gp[r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < pc; ++c)
-        gp = mfma32(alive ? ldg16(op + 16 * c) : u32x4{0, 0, 0, 0}, cf[c], gp);
-      __syncthreads();
-      const f32x16 dg = reduce4(gp, red, wave, lane);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = dg[r] * gelu_grad_f(a.scale * h[r]);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = gelu_f(a.scale * h[r]);
+      for (int c = 0; c < pc; ++c) gp = mfma32(ofr[c], cf[c], gp);
     }
+    wait_lds_reads();  // the previous tile's reads of tmine are done
+    copy_second_operand<ot>(xt, ldxt, wave * oq, r0, lq, lg, tmine);
+    load_rows(min(it + 1, it1 - 1));  // unconditional: a branch here costs register copies
+    stash_tile(red, wave, lane, hp);
+    if constexpr (WANT_DB) stash_tile(red + NW * 64 * 16, wave, lane, gp);
+    __syncthreads();
+    // slot r of lane l: column `col`, row r0 + 16 lg + r
+    finish_tile<NW, WANT_DB>(red, red + NW * 64 * 16, gsh, wave, lane, a.scale);
+    __syncthreads();
     u32x4 xb[2];
-    pack16(x, xb);
+    xb[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
+    xb[1] = *reinterpret_cast<const u32x4*>(gsh + lane * 8 + 4);
+    wait_copies();
 #pragma unroll
     for (int t = 0; t < ot; ++t) {
-      const uint16_t* trow = xt + (int64_t)(wave * oq + 32 * t + perm_row(lq)) * ldxt + r0 + 16 * lg;
-      acc[t] = mfma32(ldg16(trow), xb[0], acc[t]);
-      acc[t] = mfma32(ldg16(trow + 8), xb[1], acc[t]);
+      acc[t] = mfma32(lds16(tmine + (2 * t) * 1024 + 16 * lane), xb[0], acc[t]);
+      acc[t] = mfma32(lds16(tmine + (2 * t + 1) * 1024 + 16 * lane), xb[1], acc[t]);
     }
-    __syncthreads();
   }
   if (!clive) return;
   const int ocols = WANT_DB ? a.k : a.p;
@@ -501,15 +550,14 @@ hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const uint16_t* btt, con
   const int ntiles = (a.n + 31) / 32, mtiles = (a.m + 31) / 32;
   const int per_n = (ntiles + L.split_rows - 1) / L.split_rows;
   const int per_m = (mtiles + L.split_cols - 1) / L.split_cols;
-  const dim3 block(256);
   FAB_TIMED("mlp_bwd_da", s, hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)mtiles, (unsigned)L.split_rows),
-                     block, 0, s, a, btt, L.n_pad, per_n, pa));
+                     dim3(64 * mlp_bwd_waves<K, P, K>()), 0, s, a, btt, L.n_pad, per_n, pa));
   FAB_TIMED("mlp_bwd_dbt", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, true>),
-                     dim3((unsigned)ntiles, (unsigned)L.split_cols), block, 0, s, a, at, L.m_pad,
-                     per_m, pb));
+                     dim3((unsigned)ntiles, (unsigned)L.split_cols),
+                     dim3(64 * mlp_bwd_col_waves<K, P, true>()), 0, s, a, at, L.m_pad, per_m, pb));
   FAB_TIMED("mlp_bwd_dc", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, false>),
-                     dim3((unsigned)ntiles, (unsigned)L.split_cols), block, 0, s, a, dot, L.m_pad,
-                     per_m, pc));
+                     dim3((unsigned)ntiles, (unsigned)L.split_cols),
+                     dim3(64 * mlp_bwd_col_waves<K, P, false>()), 0, s, a, dot, L.m_pad, per_m, pc));
   return hipGetLastError();
 }
 
