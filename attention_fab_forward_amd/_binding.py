@@ -13,7 +13,7 @@ import torch
 
 LIB_PATH = os.environ.get("FAB_LIBRARY") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libfab.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 SOFTMAX, GELU_ERF = 0, 1
 MASK_NONE, MASK_CAUSAL = 0, 1
@@ -29,7 +29,8 @@ STATUS = {
 EXPORTS = ("fab_plan", "fab_forward", "fab_backward", "fab_plan_destroy",
            "fab_status_string", "fab_last_error", "fab_abi_version",
            "fab_problem_size", "fab_plan_describe", "fab_plan_set_timing",
-           "fab_plan_kernel_times", "fab_plan_reset_kernel_times", "fab_merge")
+           "fab_plan_kernel_times", "fab_plan_reset_kernel_times", "fab_merge",
+           "fab_ulysses_sizes", "fab_ulysses_pack", "fab_ulysses_unpack")
 
 
 class FabProblem(ctypes.Structure):
@@ -42,6 +43,14 @@ class FabProblem(ctypes.Structure):
         ("bt_stride", ctypes.c_int64 * 3), ("c_stride", ctypes.c_int64 * 3),
         ("o_stride", ctypes.c_int64 * 3), ("q_offset", ctypes.c_int64),
         ("k_offset", ctypes.c_int64),
+    ]
+
+
+class FabUlyssesLayout(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32), ("dtype", ctypes.c_int32), ("batch", ctypes.c_int64),
+        ("n_local", ctypes.c_int64), ("heads", ctypes.c_int64), ("head_dim", ctypes.c_int64),
+        ("ranks", ctypes.c_int64), ("x_stride", ctypes.c_int64 * 3),
     ]
 
 
@@ -98,6 +107,14 @@ def lib():
         L.fab_plan_reset_kernel_times.restype = ctypes.c_int
         L.fab_merge.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.fab_merge.restype = ctypes.c_int
+        lp = ctypes.POINTER(FabUlyssesLayout)
+        L.fab_ulysses_sizes.argtypes = [lp, ctypes.POINTER(ctypes.c_int64),
+                                        ctypes.POINTER(ctypes.c_int64)]
+        L.fab_ulysses_sizes.restype = ctypes.c_int
+        L.fab_ulysses_pack.argtypes = [lp, vp, vp, vp]
+        L.fab_ulysses_pack.restype = ctypes.c_int
+        L.fab_ulysses_unpack.argtypes = [lp, vp, vp, vp]
+        L.fab_ulysses_unpack.restype = ctypes.c_int
         if L.fab_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libfab.so ABI {L.fab_abi_version()} != binding {ABI_VERSION}")
         if L.fab_problem_size() != ctypes.sizeof(FabProblem):
@@ -218,11 +235,15 @@ def _get_plan(key, build):
     return plan
 
 
-def attention_plan(q, k, v, causal, scale, q_offset=0, k_offset=0):
+def attention_plan(q, k, v, causal, scale, q_offset=0, k_offset=0, o=None):
+    """Plan for these tensors' shapes and strides; O packed [b, m, hq, d]
+    unless `o` gives its layout."""
     b, m, hq, d = q.shape
     n, hkv = k.shape[1], k.shape[2]
+    o_stride = (_strides4(o) if o is not None
+                else (m * hq * v.shape[3], v.shape[3], hq * v.shape[3]))
     strides = {"a_stride": _strides4(q), "bt_stride": _strides4(k), "c_stride": _strides4(v),
-               "o_stride": (m * hq * v.shape[3], v.shape[3], hq * v.shape[3])}
+               "o_stride": o_stride}
     key = ("softmax", q.dtype, b, hq, hkv, m, n, d, v.shape[3], float(scale), bool(causal),
            tuple(sorted(strides.items())), int(q_offset), int(k_offset))
     return _get_plan(key, lambda: make_problem(SOFTMAX, _dtype_code(q), b, hq, hkv, m, n, d,
@@ -246,13 +267,15 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offset=0):
+def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offset=0,
+            out=None):
     """O = f(scale * A Bt^T) C on the GPU.
 
     softmax: a = Q [b, m, hq, d], bt = K [b, n, hkv, d], c = V [b, n, hkv, d];
     returns (O [b, m, hq, d], LSE float32 [b, hq, m]).  Default scale 1/sqrt(d).
     causal: key j is visible to query i iff k_offset + j <= q_offset + i; rows
-    that see no key get O = 0, LSE = -inf.
+    that see no key get O = 0, LSE = -inf.  out=(o, lse) writes there; o may
+    have any layout with a contiguous last dimension (e.g. an exchange buffer).
     gelu: a [m, k], bt [n, k], c [n, p]; returns (O [m, p], None).  Default scale 1.
     """
     dev, dt = a.device, a.dtype
@@ -261,13 +284,25 @@ def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offse
             _check_tensor(name, t, 4, dev, dt)
         if scale is None:
             scale = 1.0 / float(a.shape[3]) ** 0.5
-        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset)
         b, m, hq, _ = a.shape
-        o = torch.empty((b, m, hq, c.shape[3]), dtype=dt, device=dev)
-        lse = torch.empty((b, hq, m), dtype=torch.float32, device=dev)
+        if out is not None:
+            o, lse = out
+            _check_tensor("out o", o, 4, dev, dt)
+            if tuple(o.shape) != (b, m, hq, c.shape[3]):
+                raise ValueError(f"out o has shape {tuple(o.shape)}, expected "
+                                 f"{(b, m, hq, c.shape[3])}")
+            if (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != dev
+                    or tuple(lse.shape) != (b, hq, m)):
+                raise ValueError(f"out lse must be contiguous float32 {(b, hq, m)} on {dev}")
+        else:
+            o = torch.empty((b, m, hq, c.shape[3]), dtype=dt, device=dev)
+            lse = torch.empty((b, hq, m), dtype=torch.float32, device=dev)
+        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset, o)
     elif f == "gelu":
         if causal:
             raise ValueError("GeLU takes no causal mask")
+        if out is not None:
+            raise ValueError("out= is for softmax only")
         for name, t in (("a", a), ("bt", bt), ("c", c)):
             _check_tensor(name, t, 2, dev, dt)
         scale = 1.0 if scale is None else scale
@@ -286,7 +321,8 @@ def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None, q_offs
              k_offset=0):
     """Gradients (dA, dBt, dC) of <dO, O> for the forward above.  Over a key
     range (offsets) pass the merged O and LSE of all keys: dA is then the
-    range's contribution to dQ."""
+    range's contribution to dQ.  O may have any layout (dO must share it);
+    the gradients take the layouts of A, Bt and C."""
     dev, dt = a.device, a.dtype
     if f == "softmax":
         for name, t in (("q", a), ("k", bt), ("v", c), ("o", o), ("do", do)):
@@ -297,10 +333,9 @@ def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None, q_offs
             raise ValueError("dO must have the layout of O")
         if scale is None:
             scale = 1.0 / float(a.shape[3]) ** 0.5
-        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset)
-        if o.stride() != (a.shape[1] * a.shape[2] * c.shape[3], a.shape[2] * c.shape[3],
-                          c.shape[3], 1):
-            raise ValueError("O must be packed [b, m, hq, d]")
+        if tuple(o.shape) != (a.shape[0], a.shape[1], a.shape[2], c.shape[3]):
+            raise ValueError("O must have shape [b, m, hq, d]")
+        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset, o)
     elif f == "gelu":
         for name, t in (("a", a), ("bt", bt), ("c", c), ("do", do)):
             _check_tensor(name, t, 2, dev, dt)
@@ -338,3 +373,66 @@ def merge(o_a, lse_a, o_b, lse_b, out=None):
                                                1.0, False, None))
     plan.merge_raw(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse), _stream())
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Ulysses exchange layout (fab_ulysses_pack / fab_ulysses_unpack)
+# ---------------------------------------------------------------------------
+
+def _ulysses_layout(dtype, b, n_local, heads, d, ranks, x_stride=(0, 0, 0)):
+    lay = FabUlyssesLayout()
+    lay.abi_version = ABI_VERSION
+    lay.dtype = _dtype_code(torch.empty(0, dtype=dtype))
+    lay.batch, lay.n_local, lay.heads, lay.head_dim, lay.ranks = b, n_local, heads, d, ranks
+    lay.x_stride[:] = list(x_stride)
+    return lay
+
+
+def ulysses_sizes(b, n_local, heads, d, ranks, dtype=torch.bfloat16):
+    """(heads per rank Hl, elements of one exchange buffer); host only."""
+    lay = _ulysses_layout(dtype, b, n_local, heads, d, ranks)
+    hl, elems = ctypes.c_int64(), ctypes.c_int64()
+    check(lib().fab_ulysses_sizes(ctypes.byref(lay), ctypes.byref(hl), ctypes.byref(elems)))
+    return hl.value, elems.value
+
+
+def ulysses_pack(x, ranks, out=None):
+    """Send buffer [p, n_local, b, Hl, d] (block j for rank j) from this rank's
+    tokens x [b, n_local, H, d] (any strides, contiguous last dimension)."""
+    _check_tensor("x", x, 4, x.device, x.dtype)
+    b, nl, heads, d = x.shape
+    lay = _ulysses_layout(x.dtype, b, nl, heads, d, ranks, _strides4(x))
+    hl, _ = ulysses_sizes(b, nl, heads, d, ranks, x.dtype)
+    shape = (ranks, nl, b, hl, d)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape or not out.is_contiguous() or out.dtype != x.dtype:
+        raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape}")
+    check(lib().fab_ulysses_pack(ctypes.byref(lay), _ptr(x), _ptr(out), _stream()))
+    return out
+
+
+def ulysses_unpack(recv, heads, out=None):
+    """x [b, n_local, H, d] from the return exchange's receive buffer
+    [p, n_local, b, Hl, d]; a head held by several ranks gets their sum.
+    out: a tensor of that shape, any strides with a contiguous last dimension."""
+    if not recv.is_contiguous() or recv.dim() != 5:
+        raise ValueError("recv must be a contiguous [p, n_local, b, Hl, d] tensor")
+    p, nl, b, hl, d = recv.shape
+    if out is None:
+        out = torch.empty((b, nl, heads, d), dtype=recv.dtype, device=recv.device)
+    _check_tensor("out", out, 4, recv.device, recv.dtype)
+    if tuple(out.shape) != (b, nl, heads, d):
+        raise ValueError(f"out must have shape {(b, nl, heads, d)}")
+    lay = _ulysses_layout(recv.dtype, b, nl, heads, d, p, _strides4(out))
+    if ulysses_sizes(b, nl, heads, d, p, recv.dtype)[0] != hl:
+        raise ValueError("recv's head count does not match heads / ranks")
+    check(lib().fab_ulysses_unpack(ctypes.byref(lay), _ptr(recv), _ptr(out), _stream()))
+    return out
+
+
+def ulysses_sequence_view(recv):
+    """A receive buffer [p, n_local, b, Hl, d] of the first exchange seen as
+    [b, n, Hl, d] (no copy): the layout attention reads and writes in place."""
+    p, nl, b, hl, d = recv.shape
+    return recv.view(p * nl, b, hl, d).permute(1, 0, 2, 3)

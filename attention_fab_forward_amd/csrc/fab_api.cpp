@@ -192,6 +192,62 @@ fab::AttnArgs attn_args(const fab_plan_s* p) {
   return a;
 }
 
+
+// Validates a Ulysses exchange layout and fills the launch sizes; *hl and
+// *elems receive the heads per rank and the exchange buffer's elements.
+fab_status ulysses_setup(const fab_ulysses_layout* l, const char* who, bool pack,
+                         fab::UlyssesArgs* a, int64_t* hl, int64_t* elems) {
+  if (!l) return fail(FAB_ERR_NULL_ARG, "%s: layout is NULL", who);
+  if (l->abi_version != FAB_ABI_VERSION)
+    return fail(FAB_ERR_ABI_VERSION, "%s: abi_version %d, library has %d", who, l->abi_version,
+                FAB_ABI_VERSION);
+  if (l->dtype != FAB_BF16 && l->dtype != FAB_F32)
+    return fail(FAB_ERR_UNSUPPORTED, "%s: unknown dtype %d", who, l->dtype);
+  if (l->batch < 1 || l->n_local < 1 || l->heads < 1 || l->head_dim < 1 || l->ranks < 1)
+    return fail(FAB_ERR_BAD_SHAPE, "%s: sizes must be >= 1 (batch %lld n_local %lld heads %lld "
+                "head_dim %lld ranks %lld)", who, (long long)l->batch, (long long)l->n_local,
+                (long long)l->heads, (long long)l->head_dim, (long long)l->ranks);
+  if (l->heads % l->ranks != 0 && l->ranks % l->heads != 0)
+    return fail(FAB_ERR_BAD_SHAPE, "%s: heads %lld and ranks %lld: one must divide the other", who,
+                (long long)l->heads, (long long)l->ranks);
+  const int64_t esize = l->dtype == FAB_BF16 ? 2 : 4;
+  if ((l->head_dim * esize) % 16 != 0)
+    return fail(FAB_ERR_ALIGNMENT, "%s: a head row (%lld elements) must be a multiple of 16 bytes",
+                who, (long long)l->head_dim);
+  int64_t xs[3];
+  resolve(l->x_stride, l->n_local, l->heads, l->head_dim, xs);
+  const fab_status st = check_strides("x", xs, l->head_dim, 16 / esize);
+  if (st != FAB_OK) return st;
+  const int64_t h_loc = l->heads >= l->ranks ? l->heads / l->ranks : 1;
+  const int64_t cpr = l->head_dim * esize / 16;
+  const int64_t rows_buf = l->ranks * l->n_local * l->batch * h_loc;
+  const int64_t rows_x = l->batch * l->n_local * l->heads;
+  const int64_t limit = (int64_t)1 << 31;
+  if (l->ranks * l->heads >= limit || rows_buf > limit / cpr || rows_x > limit / cpr)
+    return fail(FAB_ERR_UNSUPPORTED, "%s: more than 2^31 16-byte chunks (or heads * ranks >= "
+                "2^31) is beyond this build's limits", who);
+  *hl = h_loc;
+  *elems = rows_buf * l->head_dim;
+  a->total = (uint32_t)((pack ? rows_buf : rows_x) * cpr);
+  a->cpr = (uint32_t)cpr;
+  a->hl = (uint32_t)h_loc;
+  a->b = (uint32_t)l->batch;
+  a->n_local = (uint32_t)l->n_local;
+  a->heads = (uint32_t)l->heads;
+  a->p = (uint32_t)l->ranks;
+  a->replicas = (uint32_t)(l->ranks > l->heads ? l->ranks / l->heads : 1);
+  a->esize = (uint32_t)esize;
+  a->row_bytes = l->head_dim * esize;
+  a->x_sb = xs[0], a->x_sh = xs[1], a->x_sr = xs[2];
+  a->div_cpr = fab::make_fastdiv(a->cpr);
+  a->div_hl = fab::make_fastdiv(a->hl);
+  a->div_b = fab::make_fastdiv(a->b);
+  a->div_nl = fab::make_fastdiv(a->n_local);
+  a->div_p = fab::make_fastdiv(a->p);
+  a->div_h = fab::make_fastdiv(a->heads);
+  return FAB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -477,6 +533,48 @@ fab_status fab_merge(const fab_plan_t* plan, const void* O_a, const float* lse_a
   TimerScope scope(plan->timer);
   const hipError_t e = fab::launch_attn_merge(a, (int)q.p, q.dtype == FAB_BF16, s);
   if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_merge: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fab_status fab_ulysses_sizes(const fab_ulysses_layout* l, int64_t* heads_per_rank,
+                             int64_t* buffer_elems) {
+  fab::UlyssesArgs a{};
+  int64_t hl = 0, elems = 0;
+  const fab_status st = ulysses_setup(l, "fab_ulysses_sizes", true, &a, &hl, &elems);
+  if (st != FAB_OK) return st;
+  if (heads_per_rank) *heads_per_rank = hl;
+  if (buffer_elems) *buffer_elems = elems;
+  return ok();
+}
+
+fab_status fab_ulysses_pack(const fab_ulysses_layout* l, const void* x, void* send, void* stream) {
+  if (!x || !send) return fail(FAB_ERR_NULL_ARG, "fab_ulysses_pack: null argument");
+  if (!aligned16(x) || !aligned16(send))
+    return fail(FAB_ERR_ALIGNMENT, "fab_ulysses_pack: pointers must be 16-byte aligned");
+  fab::UlyssesArgs a{};
+  int64_t hl = 0, elems = 0;
+  const fab_status st = ulysses_setup(l, "fab_ulysses_pack", true, &a, &hl, &elems);
+  if (st != FAB_OK) return st;
+  a.src = x;
+  a.dst = send;
+  const hipError_t e = fab::launch_ulysses(a, true, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_ulysses_pack: %s", hipGetErrorString(e));
+  return ok();
+}
+
+fab_status fab_ulysses_unpack(const fab_ulysses_layout* l, const void* recv, void* x,
+                              void* stream) {
+  if (!recv || !x) return fail(FAB_ERR_NULL_ARG, "fab_ulysses_unpack: null argument");
+  if (!aligned16(recv) || !aligned16(x))
+    return fail(FAB_ERR_ALIGNMENT, "fab_ulysses_unpack: pointers must be 16-byte aligned");
+  fab::UlyssesArgs a{};
+  int64_t hl = 0, elems = 0;
+  const fab_status st = ulysses_setup(l, "fab_ulysses_unpack", false, &a, &hl, &elems);
+  if (st != FAB_OK) return st;
+  a.src = recv;
+  a.dst = x;
+  const hipError_t e = fab::launch_ulysses(a, false, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_ulysses_unpack: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -51,6 +51,26 @@ struct MergeArgs {
   int32_t b, hq, m;
 };
 
+// Quotient by a divisor fixed at launch: (umulhi(n, m) + n) >> s, n < 2^31.
+struct FastDiv {
+  uint32_t m, s;
+};
+FastDiv make_fastdiv(uint32_t d);
+
+// Ulysses exchange layout (fab_ulysses_pack / _unpack).  x [b, n_local, H, d]
+// with element strides; exchange buffer [p][n_local][b][Hl][d] packed.
+// pack: src = x, dst = buffer; unpack: src = buffer, dst = x.
+struct UlyssesArgs {
+  const void* src;
+  void* dst;
+  uint32_t total;      // 16-byte chunks written
+  uint32_t cpr;        // chunks per head row (d * esize / 16)
+  uint32_t hl, b, n_local, heads, p, replicas, esize;
+  int64_t row_bytes;   // d * esize
+  int64_t x_sb, x_sr, x_sh;
+  FastDiv div_cpr, div_hl, div_b, div_nl, div_p, div_h;
+};
+
 // GeLU MLP: A [m, k], Bt [n, k], C [n, p], O [m, p] (row strides in elements).
 struct MlpArgs {
   const void* a;
@@ -112,6 +132,8 @@ hipError_t launch_attn_merge(const MergeArgs& a, int d, bool bf16, hipStream_t s
 hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_bwd_f32(const AttnArgs& a, int d, hipStream_t s);
+
+hipError_t launch_ulysses(const UlyssesArgs& a, bool pack, hipStream_t s);
 
 bool mlp_available();
 size_t mlp_fwd_workspace(int m, int n, int k, int p, int* splits);

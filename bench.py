@@ -274,6 +274,39 @@ def time_merge(w, reps, torch, fab):
             "shape": f"O {list(shape)} bf16, LSE {[w.batch, w.heads_q, w.seq]} fp32"}
 
 
+def time_ulysses(w, reps, torch, fab, ranks=8):
+    """HBM rate of the two layout kernels around the Ulysses exchanges, for a
+    rank of a `ranks`-way group whose share after the exchange is the
+    benchmarked attention workload: pack reads this rank's n / ranks tokens
+    of all heads and writes the send buffer; unpack reads the return
+    buffer and writes the tokens back (each byte read once, written once)."""
+    heads = w.heads_q * ranks
+    nl = w.seq // ranks
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(78)
+    x = torch.randn((w.batch, nl, heads, w.d), device="cuda", generator=gen).to(torch.bfloat16)
+    send = fab.ulysses_pack(x, ranks)
+    back = torch.empty_like(x)
+    out = {}
+    for name, fn in (("pack", lambda: fab.ulysses_pack(x, ranks, out=send)),
+                     ("unpack", lambda: fab.ulysses_unpack(send, heads, out=back))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = 2 * x.numel() * 2
+        out[name] = {"ms": ms, "bytes": nbytes, "gbs": nbytes / ms / 1e6,
+                     "frac_hbm_peak": nbytes / ms / 1e6 / HBM_PEAK_GBS}
+    out["shape"] = (f"x {[w.batch, nl, heads, w.d]} bf16 over {ranks} ranks "
+                    f"(exchange buffer {list(send.shape)})")
+    return out
+
+
 def time_mlp(steps, warmup, torch, fab_binding):
     from attention_fab_forward_amd.inputs import WORKLOADS, mlp_inputs
     w = WORKLOADS[MLP_WORKLOAD]
@@ -456,6 +489,9 @@ def main():
         }
         log("merge ...")
         extras["merge"] = time_merge(w, 20, torch, fab)
+        from attention_fab_forward_amd.inputs import WORKLOADS
+        extras["ulysses_layout"] = time_ulysses(
+            WORKLOADS["attn_causal_bf16_h4_n131072_d128"], 20, torch, fab)
         log("mlp ...")
         extras["mlp"] = time_mlp(max(3, args.steps), args.warmup, torch, fab_binding)
     cpu = None

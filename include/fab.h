@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FAB_ABI_VERSION 2
+#define FAB_ABI_VERSION 3
 
 typedef enum {
   FAB_OK = 0,
@@ -154,6 +154,67 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt,
 fab_status fab_merge(const fab_plan_t* plan, const void* O_a, const float* lse_a,
                      const void* O_b, const float* lse_b, void* O_out, float* lse_out,
                      void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Layout steps around the two all-to-all exchanges of Ulysses sequence
+ * parallelism ("Ulysses Sequence Parallelism", sections "Contexte Technique"
+ * and "Analyse"; "AutoSP" section 2: exchanges inserted at the attention
+ * boundaries, attention on the full sequence for a subset of heads).  Before
+ * the first exchange each of the p ranks holds n_local consecutive tokens of
+ * all H heads (x [b, n_local, H, d], rank j's tokens being j n_local ..
+ * j n_local + n_local - 1); afterwards each rank holds all n = p n_local
+ * tokens of Hl heads.  The exchanges themselves are the caller's (one
+ * all-to-all with equal splits of a buffer of fab_ulysses_sizes' elements).
+ *
+ * Exchange buffer: [p][n_local][b][Hl][d], packed.  Block j of a rank's send
+ * buffer goes to rank j; block s of its receive buffer came from rank s.  A
+ * receive buffer therefore reads as [n][b][Hl][d]: pass it to fab_plan /
+ * fab_forward directly with element strides {batch Hl d, head d, row b Hl d},
+ * and give O (and dQ, dK, dV) the same strides: that output is the send
+ * buffer of the return exchange, whose receive buffer fab_ulysses_unpack
+ * turns back into x's layout.
+ *
+ * Heads: with head0(j) = floor(j H / p), rank j receives heads head0(j) ..
+ * head0(j) + Hl - 1.  H % p == 0 gives Hl = H / p (disjoint head groups).
+ * p % H == 0 (fewer key/value heads than ranks under grouped-query attention)
+ * gives Hl = 1: head h goes to the p / H consecutive ranks whose query heads
+ * read it, and fab_ulysses_unpack sums what those ranks return (the gradient
+ * of a replicated head), in fp32, in rank order, rounded once to the dtype.
+ * Any other H, p pair is FAB_ERR_BAD_SHAPE.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t abi_version; /* must be FAB_ABI_VERSION                               */
+  int32_t dtype;       /* fab_dtype of x and of the exchange buffer              */
+  int64_t batch;       /* b >= 1                                                */
+  int64_t n_local;     /* tokens per rank before the exchange, >= 1             */
+  int64_t heads;       /* H, heads of x, >= 1                                   */
+  int64_t head_dim;    /* d; d * element size must be a multiple of 16 bytes    */
+  int64_t ranks;       /* p >= 1                                                */
+  /* element strides {batch, head, row} of x; all-zero = packed [b, n_local, H, d];
+   * multiples of 16 bytes, last dimension contiguous */
+  int64_t x_stride[3];
+} fab_ulysses_layout;
+
+/* Validates the layout; *heads_per_rank receives Hl and *buffer_elems the
+ * elements of one exchange buffer (p n_local b Hl d).  Either output may be
+ * NULL.  Host only. */
+fab_status fab_ulysses_sizes(const fab_ulysses_layout* layout, int64_t* heads_per_rank,
+                             int64_t* buffer_elems);
+
+/* send[j][t][bi][hl][:] = x[bi][t][head0(j) + hl][:] for every rank j (a
+ * pure copy, bit-exact).  x: device, the layout's strides; send: device,
+ * buffer_elems elements, must not overlap x.  Both 16-byte aligned.  Enqueued
+ * on `stream` (a hipStream_t; NULL = default). */
+fab_status fab_ulysses_pack(const fab_ulysses_layout* layout, const void* x, void* send,
+                            void* stream);
+
+/* x[bi][t][h][:] = sum over the ranks j holding head h of
+ * recv[j][t][bi][h - head0(j)][:]; one term (a bit-exact copy) unless H < p.
+ * recv: device, buffer_elems elements; x: device, the layout's strides,
+ * overwritten, must not overlap recv.  Both 16-byte aligned.  Enqueued on
+ * `stream`. */
+fab_status fab_ulysses_unpack(const fab_ulysses_layout* layout, const void* recv, void* x,
+                              void* stream);
 
 /* Release a plan (NULL is ignored). */
 void fab_plan_destroy(fab_plan_t* plan);

@@ -20,4 +20,9 @@ from .fab_oracle import (  # noqa: F401
     brute_attention_forward,
     brute_attention_backward,
     brute_mlp_forward,
+    ulysses_heads_per_rank,
+    ulysses_pack,
+    ulysses_unpack,
+    ulysses_sequence_view,
+    all_to_all,
 )

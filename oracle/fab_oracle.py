@@ -33,6 +33,9 @@ What it computes (the plain definition, not the tiled algorithm):
   and 2.B).  Phi is the standard normal CDF.
 * Backward passes are the derivative of the same definitions; recomputing the
   intermediate instead of storing it (AutoSP 2.B) does not change them.
+* The Ulysses exchange layout (pack before and unpack after the all-to-all
+  exchanges): plain index copies, and for a head held by several ranks the
+  sum of their blocks (see the section below).
 
 Layouts: attention tensors are [batch, seq, heads, dim] ("BSHD"); query head h
 uses key/value head h // (Hq // Hkv).  LSE is [batch, Hq, m], natural log.
@@ -336,6 +339,70 @@ def mlp_backward(a, bt, c, do, scale=1.0, workers=None, block_rows=None):
 # ---------------------------------------------------------------------------
 # brute-force scalar loops (tiny shapes only)
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# Ulysses sequence parallelism: the exchange layout
+# ---------------------------------------------------------------------------
+# "Ulysses Sequence Parallelism", sections "Contexte Technique" and "Analyse":
+# the sequence is split into p chunks, one per rank; an all-to-all then gives
+# every rank all positions for a subset of the heads, and a second all-to-all
+# after attention returns to the sequence split ("AutoSP" section 2 inserts
+# these exchanges at the attention boundaries).  Readings taken: rank j owns
+# tokens j n_local .. j n_local + n_local - 1 and heads
+# floor(j H / p) .. floor(j H / p) + Hl - 1 with Hl = H / p when p divides H;
+# when H < p (grouped-query key/value heads) a head goes to the p / H ranks
+# whose query heads read it, and the gradients those ranks return for it are
+# summed.  One rank's exchange buffer is [p, n_local, b, Hl, d]: block j goes
+# to (or came from) rank j.
+
+
+def ulysses_heads_per_rank(heads, ranks):
+    """Hl, the heads each rank holds after the exchange."""
+    if heads % ranks and ranks % heads:
+        raise ValueError(f"heads {heads} and ranks {ranks}: one must divide the other")
+    return heads // ranks if heads >= ranks else 1
+
+
+def ulysses_pack(x, ranks):
+    """Send buffer [p, n_local, b, Hl, d] of one rank whose tokens are
+    x [b, n_local, H, d]: block j holds, for every local token, the heads
+    rank j computes attention for."""
+    b, nl, heads, d = x.shape
+    hl = ulysses_heads_per_rank(heads, ranks)
+    out = np.empty((ranks, nl, b, hl, d), dtype=x.dtype)
+    for j in range(ranks):
+        h0 = (j * heads) // ranks
+        out[j] = np.transpose(x[:, :, h0:h0 + hl, :], (1, 0, 2, 3))
+    return out
+
+
+def all_to_all(sends):
+    """The exchange itself (equal splits): sends[s][j] goes to rank j, and
+    rank j's receive buffer holds, as block s, what rank s sent it."""
+    p = len(sends)
+    return [np.stack([sends[s][j] for s in range(p)]) for j in range(p)]
+
+
+def ulysses_unpack(recv, heads):
+    """x [b, n_local, H, d] (float64) from a receive buffer [p, n_local, b,
+    Hl, d] of the return exchange: block j carries rank j's result for its
+    heads; heads held by several ranks get the sum of their blocks."""
+    p, nl, b, hl, d = recv.shape
+    if ulysses_heads_per_rank(heads, p) != hl:
+        raise ValueError("buffer does not match heads / ranks")
+    out = np.zeros((b, nl, heads, d), dtype=np.float64)
+    for j in range(p):
+        h0 = (j * heads) // p
+        out[:, :, h0:h0 + hl, :] += np.transpose(_f64(recv[j]), (1, 0, 2, 3))
+    return out
+
+
+def ulysses_sequence_view(recv):
+    """A receive buffer of the first exchange read as [b, n, Hl, d]: block s
+    holds tokens s n_local .. s n_local + n_local - 1."""
+    p, nl, b, hl, d = recv.shape
+    return np.transpose(recv.reshape(p * nl, b, hl, d), (1, 0, 2, 3))
+
 
 def brute_attention_forward(q, k, v, scale, causal=False, q_offset=0, k_offset=0):
     """Scalar-loop attention with math.exp; same layouts as attention_forward."""

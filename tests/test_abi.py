@@ -28,8 +28,9 @@ def test_exports_every_declared_symbol():
 def test_abi_version_and_struct_size():
     L = B.lib()
     assert L.fab_abi_version() == B.ABI_VERSION
-    assert L.fab_abi_version() == 2
+    assert L.fab_abi_version() == 3
     assert L.fab_problem_size() == ctypes.sizeof(B.FabProblem) == 192
+    assert ctypes.sizeof(B.FabUlyssesLayout) == 72
 
 
 def attn(**kw):
@@ -128,3 +129,58 @@ def test_merge_argument_errors_before_any_launch():
                     p=128, scale=1.0))
     st = L.fab_merge(g._ptr, good, good, good, good, good, good, None)
     assert B.STATUS[st] == "FAB_ERR_UNSUPPORTED"
+
+
+def ulysses_status(lay):
+    L = B.lib()
+    hl, elems = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    st = L.fab_ulysses_sizes(ctypes.byref(lay), ctypes.byref(hl), ctypes.byref(elems))
+    return B.STATUS[st], hl.value, elems.value
+
+
+@pytest.mark.parametrize("b,nl,heads,d,p,hl", [
+    (1, 4096, 32, 128, 8, 4), (2, 100, 8, 64, 8, 1), (1, 16, 2, 128, 8, 1), (3, 7, 6, 64, 3, 2),
+    (1, 1, 1, 8, 1, 1)])
+def test_ulysses_sizes(b, nl, heads, d, p, hl):
+    import torch
+    st, got_hl, elems = ulysses_status(B._ulysses_layout(torch.bfloat16, b, nl, heads, d, p))
+    assert (st, got_hl, elems) == ("FAB_OK", hl, p * nl * b * hl * d)
+
+
+@pytest.mark.parametrize("change,expect", [
+    ({"heads": 6, "ranks": 4}, "FAB_ERR_BAD_SHAPE"),
+    ({"ranks": 0}, "FAB_ERR_BAD_SHAPE"),
+    ({"n_local": 0}, "FAB_ERR_BAD_SHAPE"),
+    ({"head_dim": 12}, "FAB_ERR_ALIGNMENT"),          # 24 bytes per bf16 row
+    ({"abi_version": 2}, "FAB_ERR_ABI_VERSION"),
+    ({"dtype": 7}, "FAB_ERR_UNSUPPORTED"),
+    ({"x_stride": (4096, 128, -1)}, "FAB_ERR_BAD_SHAPE"),
+    ({"x_stride": (4096, 132, 512)}, "FAB_ERR_ALIGNMENT"),
+    ({"x_stride": (4096, 128, 64)}, "FAB_ERR_BAD_SHAPE"),  # row shorter than a head row
+    ({"n_local": 1 << 28}, "FAB_ERR_UNSUPPORTED"),     # beyond 2^31 16-byte chunks
+])
+def test_ulysses_layout_validation(change, expect):
+    import torch
+    lay = B._ulysses_layout(torch.bfloat16, 1, 64, 8, 128, 4)
+    for k, v in change.items():
+        if k == "x_stride":
+            lay.x_stride[:] = list(v)
+        else:
+            setattr(lay, k, v)
+    assert ulysses_status(lay)[0] == expect
+
+
+def test_ulysses_argument_errors_before_any_launch():
+    import torch
+    L = B.lib()
+    vp = ctypes.c_void_p
+    good = vp(0x10000)
+    lay = B._ulysses_layout(torch.bfloat16, 1, 64, 8, 128, 4)
+    for fn in (L.fab_ulysses_pack, L.fab_ulysses_unpack):
+        assert B.STATUS[fn(None, good, good, None)] == "FAB_ERR_NULL_ARG"
+        assert B.STATUS[fn(ctypes.byref(lay), None, good, None)] == "FAB_ERR_NULL_ARG"
+        assert B.STATUS[fn(ctypes.byref(lay), good, None, None)] == "FAB_ERR_NULL_ARG"
+        assert B.STATUS[fn(ctypes.byref(lay), vp(0x10008), good, None)] == "FAB_ERR_ALIGNMENT"
+        assert B.STATUS[fn(ctypes.byref(lay), good, vp(0x10004), None)] == "FAB_ERR_ALIGNMENT"
+        bad = B._ulysses_layout(torch.bfloat16, 1, 64, 6, 128, 4)
+        assert B.STATUS[fn(ctypes.byref(bad), good, good, None)] == "FAB_ERR_BAD_SHAPE"
