@@ -11,9 +11,12 @@
 namespace fab {
 namespace {
 
-// One query row (b, h, i) per LPR lanes, each lane 16 bytes of the row; the
-// lanes of a row sit in one wave, so an in-place merge (O_out = O_a,
-// lse_out = lse_a) reads every input before any lane writes.
+// One query row (b, i, h) per LPR lanes, each lane 16 bytes of the row; rows
+// are taken in O's [b, m, hq] order, so for the packed layout a workgroup
+// streams one contiguous stretch of O (the LSE reads, 4 bytes per row, are
+// the scattered ones).  The lanes of a row sit in one wave, so an in-place
+// merge (O_out = O_a, lse_out = lse_a) reads every input before any lane
+// writes.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   constexpr int ES = BF16 ? 2 : 4;
@@ -22,12 +25,24 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   constexpr int RPB = 256 / LPR;
   static_assert(64 % LPR == 0, "a row's lanes must share a wave");
   const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // LSE order [b, hq, m]
+  const int64_t orow = (int64_t)blockIdx.x * RPB + tid / LPR;  // O order [b, m, hq]
   const int part = tid % LPR;
   const int64_t total = (int64_t)a.b * a.hq * a.m;
-  if (row >= total) return;
-  const int64_t i = row % a.m, bh = row / a.m;
-  const int h = (int)(bh % a.hq), bi = (int)(bh / a.hq);
+  if (orow >= total) return;
+  int64_t i, h, bi;
+  if (a.small) {  // every index below 2^31: division by multiplication
+    const uint32_t r32 = (uint32_t)orow;
+    const uint32_t bm = (__umulhi(r32, a.div_hq.m) + r32) >> a.div_hq.s;
+    h = r32 - bm * (uint32_t)a.hq;
+    bi = (__umulhi(bm, a.div_m.m) + bm) >> a.div_m.s;
+    i = bm - (uint32_t)bi * (uint32_t)a.m;
+  } else {
+    const int64_t bm = orow / a.hq;
+    h = orow - bm * a.hq;
+    bi = bm / a.m;
+    i = bm - bi * a.m;
+  }
+  const int64_t row = (bi * a.hq + h) * a.m + i;  // LSE order [b, hq, m]
   const float la = a.la[row], lb = a.lb[row];
   const float mx = fmaxf(la, lb);
   float wa = 0.f, wb = 0.f, lse = -INFINITY;

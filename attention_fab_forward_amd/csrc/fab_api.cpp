@@ -529,6 +529,9 @@ fab_status fab_merge(const fab_plan_t* plan, const void* O_a, const float* lse_a
   a.oa = O_a, a.ob = O_b, a.oo = O_out, a.la = lse_a, a.lb = lse_b, a.lo = lse_out;
   a.o_sb = plan->os[0], a.o_sh = plan->os[1], a.o_sr = plan->os[2];
   a.b = (int32_t)q.batch, a.hq = (int32_t)q.heads_a, a.m = (int32_t)q.m;
+  a.small = q.batch * q.heads_a * q.m < ((int64_t)1 << 31);
+  a.div_hq = fab::make_fastdiv((uint32_t)q.heads_a);
+  a.div_m = fab::make_fastdiv((uint32_t)q.m);
   hipStream_t s = static_cast<hipStream_t>(stream);
   TimerScope scope(plan->timer);
   const hipError_t e = fab::launch_attn_merge(a, (int)q.p, q.dtype == FAB_BF16, s);

@@ -39,6 +39,12 @@ struct AttnArgs {
   int32_t diag;
 };
 
+// Quotient by a divisor fixed at launch: (umulhi(n, m) + n) >> s, n < 2^31.
+struct FastDiv {
+  uint32_t m, s;
+};
+FastDiv make_fastdiv(uint32_t d);
+
 // Merge of two partial softmax results (fab_merge): packed LSE [b, hq, m].
 struct MergeArgs {
   const void* oa;
@@ -49,13 +55,9 @@ struct MergeArgs {
   float* lo;
   int64_t o_sb, o_sh, o_sr;
   int32_t b, hq, m;
+  int32_t small;          // b * hq * m < 2^31: the divisions below apply
+  FastDiv div_hq, div_m;
 };
-
-// Quotient by a divisor fixed at launch: (umulhi(n, m) + n) >> s, n < 2^31.
-struct FastDiv {
-  uint32_t m, s;
-};
-FastDiv make_fastdiv(uint32_t d);
 
 // Ulysses exchange layout (fab_ulysses_pack / _unpack).  x [b, n_local, H, d]
 // with element strides; exchange buffer [p][n_local][b][Hl][d] packed.

@@ -95,3 +95,25 @@ def test_key_split_merge_and_range_backward(dtype, causal):
         assert_close(f"dK[{a}:{b}]", to_host(dk), rdk[:, a:b], dtype)
         assert_close(f"dV[{a}:{b}]", to_host(dv), rdv[:, a:b], dtype)
     assert_close("dQ (sum of ranges)", to_host(dq_sum), rdq, dtype)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_merge_direct(dtype, d):
+    """fab_merge on random parts (batch 2, 3 heads, ragged rows; some rows with
+    one or both LSE = -inf) against the merge formula."""
+    import attention_fab_forward_amd as fab
+    b, m, hq = 2, 77, 3
+    oa = random_array(900 + d, (b, m, hq, d), 1.0, dtype)
+    ob = random_array(901 + d, (b, m, hq, d), 1.0, dtype)
+    la = 3.0 * np.random.default_rng(902).standard_normal((b, hq, m)).astype(np.float32)
+    lb = 3.0 * np.random.default_rng(903).standard_normal((b, hq, m)).astype(np.float32)
+    la[0, 1, :5] = -np.inf
+    lb[1, 2, 3:9] = -np.inf
+    la[1, 2, 5:7] = -np.inf          # rows 5, 6 of (1, 2): both sides empty
+    import torch
+    o, lse = fab.merge(to_device(oa, dtype), torch.from_numpy(la).cuda(),
+                       to_device(ob, dtype), torch.from_numpy(lb).cuda())
+    ro, rl = attention_merge(oa, la, ob, lb)
+    assert_close("O merge", to_host(o), ro, dtype, zero_scale=1.0)
+    check_lse(lse.cpu().numpy(), rl, dtype)
+    assert np.all(to_host(o)[1, 5:7, 2] == 0.0)
