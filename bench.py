@@ -307,6 +307,68 @@ def time_ulysses(w, reps, torch, fab, ranks=8):
     return out
 
 
+def eager_attention_mlp(torch, q, k, v, w1t, w2, causal, scale, part="both", a_in=None):
+    """The same attention + GeLU MLP block composed from plain PyTorch ops,
+    used only to count the activations autograd keeps when nothing is
+    recomputed (scores, probabilities, H, GeLU(H)).  Forward only; every
+    batched bf16 product gets contiguous operands, the softmax runs in fp32.
+    part: "attention" (returns O), "mlp" (applies the MLP to a_in) or "both"."""
+    import torch.nn.functional as F
+    if part in ("attention", "both"):
+        b, n, hq, d = q.shape
+        qh = q.permute(0, 2, 1, 3).contiguous()
+        kt = k.permute(0, 2, 3, 1).contiguous()
+        vh = v.permute(0, 2, 1, 3).contiguous()
+        sc = torch.matmul(qh, kt).float() * scale
+        if causal:
+            mask = torch.triu(torch.ones(n, n, dtype=torch.bool, device=q.device), 1)
+            sc = sc.masked_fill(mask, float("-inf"))
+        pr = torch.softmax(sc, dim=-1).to(q.dtype)
+        o = torch.matmul(pr, vh).permute(0, 2, 1, 3)
+        if part == "attention":
+            return o
+        a_in = o.reshape(b * n, hq * d)
+    return torch.matmul(F.gelu(torch.matmul(a_in, w1t)), w2)
+
+
+def activation_memory(torch, fab_pkg):
+    """Bytes autograd keeps between forward and backward for the attention +
+    GeLU MLP block (attention over 8 heads of d = 128 on 4096 tokens, then
+    the MLP 1024 -> 4096 -> 1024 on its rows), the fused kernels' path vs the
+    plain composition; weights are not counted."""
+    from attention_fab_forward_amd import autograd as AG
+    b, n, hq, d, ffn, out = 1, 4096, 8, 128, 4096, 1024
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(79)
+    mk = lambda *sh: (torch.randn(sh, device="cuda", generator=gen) * 0.5).to(
+        torch.bfloat16).requires_grad_(True)
+    q, k, v = mk(b, n, hq, d), mk(b, n, hq, d), mk(b, n, hq, d)
+    blk = AG.AttentionMlpBlock(hq * d, ffn, out)
+    w1t = blk.w1.detach().t().contiguous().requires_grad_(True)
+    w2 = blk.w2.detach().clone().requires_grad_(True)
+    scale = d ** -0.5
+    a = mk(b * n, hq * d)
+    params = (blk.w1, blk.w2, w1t, w2)
+    res = {}
+    _, res["fab_attention"] = AG.saved_activation_bytes(AG.attention, q, k, v, True, scale)
+    _, res["fab_mlp"] = AG.saved_activation_bytes(AG.gelu_mlp, a, blk.w1, blk.w2,
+                                                  exclude=params)
+    _, res["fab_block"] = AG.saved_activation_bytes(blk, q, k, v, exclude=params)
+    _, res["eager_attention"] = AG.saved_activation_bytes(
+        lambda: eager_attention_mlp(torch, q, k, v, w1t, w2, True, scale, "attention"))
+    _, res["eager_mlp"] = AG.saved_activation_bytes(
+        lambda: eager_attention_mlp(torch, q, k, v, w1t, w2, True, scale, "mlp", a),
+        exclude=params)
+    _, res["eager_block"] = AG.saved_activation_bytes(
+        lambda: eager_attention_mlp(torch, q, k, v, w1t, w2, True, scale), exclude=params)
+    torch.cuda.synchronize()
+    res["ratio_attention"] = res["eager_attention"] / res["fab_attention"]
+    res["ratio_mlp"] = res["eager_mlp"] / res["fab_mlp"]
+    res["ratio_block"] = res["eager_block"] / res["fab_block"]
+    res["shape"] = (f"b {b} n {n} heads {hq} d {d} causal bf16; MLP {hq * d} -> {ffn} -> {out}")
+    return res
+
+
 def time_mlp(steps, warmup, torch, fab_binding):
     from attention_fab_forward_amd.inputs import WORKLOADS, mlp_inputs
     w = WORKLOADS[MLP_WORKLOAD]
@@ -492,6 +554,8 @@ def main():
         from attention_fab_forward_amd.inputs import WORKLOADS
         extras["ulysses_layout"] = time_ulysses(
             WORKLOADS["attn_causal_bf16_h4_n131072_d128"], 20, torch, fab)
+        log("activation memory ...")
+        extras["activation_memory"] = activation_memory(torch, fab)
         log("mlp ...")
         extras["mlp"] = time_mlp(max(3, args.steps), args.warmup, torch, fab_binding)
     cpu = None
