@@ -208,11 +208,15 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
       cfr[t][0] = ldg16(crow);
       cfr[t][1] = ldg16(crow + 8);
     }
+    // keep these loads ahead of the next tile's: the wait for C^T before the
+    // second product then leaves the Bt prefetch in flight
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 hp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) hp[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < kc; ++c) hp = mfma32(bfr[c], af[c], hp);
+    __builtin_amdgcn_sched_barrier(0);
     load_bt(min(jt + 1, jt1 - 1));  // unconditional: a branch here costs register copies
     stash_tile(red, wave, lane, hp);
     __syncthreads();
@@ -247,9 +251,17 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
 
 // The backward kernels stage their transposed second-product operand in LDS
 // with asynchronous global -> LDS copies (each lane reads back exactly the 16
-// byte pieces it copied, so only a wave-local wait is needed).  These waits
-// are assembly with a memory clobber so LDS accesses stay on their side.
-__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// byte pieces it copied, so only a wave-local wait is needed).  The copies are
+// issued right before the next tile's row loads, and vector memory operations
+// complete in issue order, so waiting until only those N loads remain
+// outstanding waits for exactly the copies.  These waits are assembly with a
+// memory clobber so LDS accesses stay on their side.
+// Waits for the copies while the N loads issued after them stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Copies the kt x 2 16-byte pieces of this lane's second-product operand
@@ -346,7 +358,7 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
     u32x4 db[2];
     db[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
     db[1] = *reinterpret_cast<const u32x4*>(gsh + lane * 8 + 4);
-    wait_copies();
+    wait_copies<kc + pc>();  // the next tile's row loads stay in flight
 #pragma unroll
     for (int t = 0; t < kt; ++t) {
       acc[t] = mfma32(lds16(tmine + (2 * t) * 1024 + 16 * lane), db[0], acc[t]);
@@ -444,7 +456,7 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
     u32x4 xb[2];
     xb[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
     xb[1] = *reinterpret_cast<const u32x4*>(gsh + lane * 8 + 4);
-    wait_copies();
+    wait_copies<kc + (WANT_DB ? pc : 0)>();  // the next tile's row loads stay in flight
 #pragma unroll
     for (int t = 0; t < ot; ++t) {
       acc[t] = mfma32(lds16(tmine + (2 * t) * 1024 + 16 * lane), xb[0], acc[t]);
