@@ -478,7 +478,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the memory sweep and the MLP measurement")
+                    help="skip every measurement besides the benchmarked workload")
+    ap.add_argument("--extras", default="all",
+                    help="comma list of extra measurements: sweep, workloads, merge, ulysses, "
+                         "activation, mlp (default all)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
                          "three times (reference reading for hardware byte counters)")
@@ -539,9 +542,13 @@ def main():
         del src, dst
 
     extras = {}
-    if not args.no_extras:
+    want = set() if args.no_extras else (
+        {"sweep", "workloads", "merge", "ulysses", "activation", "mlp"} if args.extras == "all"
+        else set(args.extras.split(",")))
+    if "sweep" in want:
         log("peak-memory sweep ...")
         extras["peak_hbm_vs_seq"] = peak_hbm_sweep(torch, fab)
+    if "workloads" in want:
         log("other workloads ...")
         extras["workloads"] = {
             "attn_causal_bf16_h4_n131072_d128": time_workload(
@@ -549,13 +556,17 @@ def main():
             "attn_causal_bf16_gqa2_n1048576_d128": time_workload(
                 "attn_causal_bf16_gqa2_n1048576_d128", 1, torch, fab),
         }
+    if "merge" in want:
         log("merge ...")
         extras["merge"] = time_merge(w, 20, torch, fab)
-        from attention_fab_forward_amd.inputs import WORKLOADS
+    if "ulysses" in want:
+        log("ulysses layout ...")
         extras["ulysses_layout"] = time_ulysses(
             WORKLOADS["attn_causal_bf16_h4_n131072_d128"], 20, torch, fab)
+    if "activation" in want:
         log("activation memory ...")
         extras["activation_memory"] = activation_memory(torch, fab)
+    if "mlp" in want:
         log("mlp ...")
         extras["mlp"] = time_mlp(max(3, args.steps), args.warmup, torch, fab_binding)
     cpu = None
