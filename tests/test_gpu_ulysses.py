@@ -156,3 +156,18 @@ def test_ulysses_attention_backward(b, n, hq, hkv, d, p):
     assert_close("dQ (Ulysses)", to_host(g["dq"]), rdq, dtype, zero_scale=1.0)
     assert_close("dK (Ulysses)", to_host(g["dk"]), rdk, dtype, zero_scale=1.0)
     assert_close("dV (Ulysses)", to_host(g["dv"]), rdv, dtype, zero_scale=1.0)
+
+
+def test_full_size_rank_share_bit_exact():
+    """The size the benchmark times (x 1 x 16384 x 32 x 128 bf16, 8 ranks: one
+    rank of the 4-head, 131072-token share): every element of pack and of
+    unpack against the oracle."""
+    import attention_fab_forward_amd as fab
+    b, nl, h, d, p = 1, 16384, 32, 128, 8
+    x = random_array(7500, (b, nl, h, d), 1.0, "bf16")
+    print(f"full-size pack / unpack b={b} n_local={nl} H={h} d={d} p={p}", flush=True)
+    send = fab.ulysses_pack(to_device(x, "bf16"), p)
+    ref = ulysses_pack(x, p)
+    assert np.array_equal(send.float().cpu().numpy(), ref)
+    back = fab.ulysses_unpack(send, h)
+    assert np.array_equal(back.float().cpu().numpy(), ulysses_unpack(ref, h))
