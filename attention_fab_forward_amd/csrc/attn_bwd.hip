@@ -267,19 +267,25 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
       u32x4 pb[2][2];
       if (work) {
         const bool need_mask = (CAUSAL && q0 + a.diag < k0w + 31) || q0 + C::TILE > a.m;
+        // S for both query sub-blocks first, at raised wave priority, so the
+        // exponentials below overlap the partner wave's dP products on this SIMD
+        f32x16 s[2];
+#pragma unroll
+        for (int sq = 0; sq < 2; ++sq)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[sq][r] = 0.f;
+        __builtin_amdgcn_s_setprio(2);
+        lds_mfma_pipeline<2 * C::DC, 4>(
+            [&](int i) { return read_nat<D>(st + L::Q, i / C::DC, i % C::DC, lq, lg); },
+            [&](int i, const u32x4& x) { s[i / C::DC] = mfma32(x, kv[i % C::DC], s[i / C::DC]); });
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int sq = 0; sq < 2; ++sq) {
-          f32x16 s;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = 0.f;
-          lds_mfma_pipeline<C::DC, 4>(
-              [&](int c) { return read_nat<D>(st + L::Q, sq, c, lq, lg); },
-              [&](int c, const u32x4& x) { s = mfma32(x, kv[c], s); });
           if (need_mask) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int q = q0 + 32 * sq + 16 * lg + r;
-              if ((CAUSAL && q + a.diag < mykey) || q >= a.m) s[r] = -INFINITY;
+              if ((CAUSAL && q + a.diag < mykey) || q >= a.m) s[sq][r] = -INFINITY;
             }
           }
           const f32x4* l2 = reinterpret_cast<const f32x4*>(st + L::LSE) + 8 * sq + 4 * lg;
@@ -288,7 +294,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
             const f32x4 lse2 = l2[j];
             f32x4 p;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[4 * j + e], cs, -lse2[e]));
+            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[sq][4 * j + e], cs, -lse2[e]));
             px[(4 * sq + j) * 64] = p;
             pb[sq][j >> 1][2 * (j & 1)] = pack_bf16(p[0], p[1]);
             pb[sq][j >> 1][2 * (j & 1) + 1] = pack_bf16(p[2], p[3]);
