@@ -456,9 +456,14 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
     // operand i: output tile t = i % DT, key chunk c = i / DT
     auto kt_read = [&](int i) { return read_tr<D>(st + S::K, i % C::DT, sb, i / C::DT, lg, tr_d, tr_row); };
     if constexpr (QT == 1) {
+      // raised wave priority while issuing dQ: the wave that has finished its
+      // dS gets the MFMA pipe first, so the two waves of a SIMD drift out of
+      // phase and one's dS work overlaps the other's products
+      __builtin_amdgcn_s_setprio(2);
       lds_mfma_pipeline<2 * C::DT, 4>(kt_read, [&](int i, const u32x4& x) {
         dq[0][i % C::DT] = mfma32(x, db[0][i / C::DT], dq[0][i % C::DT]);
       });
+      __builtin_amdgcn_s_setprio(0);
     } else {
 #pragma unroll
       for (int i = 0; i < 2 * C::DT; ++i) {

@@ -261,6 +261,9 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   // two 4-key groups.
   auto pv = [&](int j) {
     const char* vt = vbuf(j);
+    // raised wave priority while issuing PV: the group that has finished its
+    // softmax gets the MFMA pipe before the other group's S products
+    __builtin_amdgcn_s_setprio(2);
     lds_mfma_pipeline<4 * C::DT, 4>(
         [&](int i) {
           const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
@@ -276,6 +279,7 @@ attn_fwd_bf16_kernel(AttnArgs a) {
           const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
           o[t] = mfma32(x, pb[sb][c], o[t]);
         });
+    __builtin_amdgcn_s_setprio(0);
   };
   // copies issued in iteration j: K[j + 1] and V[j] (their buffers held
   // K[j - 1] and V[j - 2], read by both groups before the previous barrier)
