@@ -353,9 +353,13 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
             db[j >> 1][2 * (j & 1) + 1] =
                 pack_bf16(p[2] * dp[sq][4 * j + 2], p[3] * dp[sq][4 * j + 3]);
           }
+          // raised priority while issuing dK, as for dQ (the dS wave has just
+          // finished its VALU work; its partner's dV products wait)
+          __builtin_amdgcn_s_setprio(2);
           lds_mfma_pipeline<2 * C::DT, 4>(
               [&](int i) { return read_tr<D>(st + L::Q, i / 2, sq, i % 2, lg, tr_d, tr_row); },
               [&](int i, const u32x4& x) { acc[i / 2] = mfma32(x, db[i % 2], acc[i / 2]); });
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       wait_vmem();
