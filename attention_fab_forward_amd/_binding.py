@@ -30,7 +30,7 @@ EXPORTS = ("fab_plan", "fab_forward", "fab_backward", "fab_plan_destroy",
            "fab_status_string", "fab_last_error", "fab_abi_version",
            "fab_problem_size", "fab_plan_describe", "fab_plan_set_timing",
            "fab_plan_kernel_times", "fab_plan_reset_kernel_times", "fab_merge",
-           "fab_ulysses_sizes", "fab_ulysses_pack", "fab_ulysses_unpack")
+           "fab_ulysses_sizes", "fab_ulysses_pack", "fab_ulysses_unpack", "fab_exp_probe")
 
 
 class FabProblem(ctypes.Structure):
@@ -115,6 +115,8 @@ def lib():
         L.fab_ulysses_pack.restype = ctypes.c_int
         L.fab_ulysses_unpack.argtypes = [lp, vp, vp, vp]
         L.fab_ulysses_unpack.restype = ctypes.c_int
+        L.fab_exp_probe.argtypes = [ctypes.c_int, ctypes.c_int, vp, ctypes.POINTER(ctypes.c_int64), vp]
+        L.fab_exp_probe.restype = ctypes.c_int
         if L.fab_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libfab.so ABI {L.fab_abi_version()} != binding {ABI_VERSION}")
         if L.fab_problem_size() != ctypes.sizeof(FabProblem):
@@ -436,3 +438,14 @@ def ulysses_sequence_view(recv):
     [b, n, Hl, d] (no copy): the layout attention reads and writes in place."""
     p, nl, b, hl, d = recv.shape
     return recv.view(p * nl, b, hl, d).permute(1, 0, 2, 3)
+
+
+def exp_probe(blocks, iters, sink):
+    """Enqueue the exp2(fma) rate probe (fab_exp_probe) on torch's current
+    stream; sink: float32 CUDA tensor of at least blocks * 256 elements.
+    Returns the number of exponentials enqueued."""
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256 or sink.device.type != "cuda":
+        raise ValueError("sink must be a float32 CUDA tensor of blocks * 256 elements")
+    count = ctypes.c_int64()
+    check(lib().fab_exp_probe(blocks, iters, _ptr(sink), ctypes.byref(count), _stream()))
+    return count.value

@@ -581,4 +581,16 @@ fab_status fab_ulysses_unpack(const fab_ulysses_layout* l, const void* recv, voi
   return ok();
 }
 
+fab_status fab_exp_probe(int blocks, int iters, float* sink, int64_t* exp_count, void* stream) {
+  if (blocks < 1 || iters < 1 || blocks > (1 << 20) || iters > (1 << 24))
+    return fail(FAB_ERR_BAD_SHAPE, "fab_exp_probe: blocks in [1, 2^20], iters in [1, 2^24]");
+  if (exp_count) *exp_count = (int64_t)blocks * 256 * iters * fab::exp_probe_chains();
+  if (!sink) return ok();  // count only
+  if (reinterpret_cast<uintptr_t>(sink) & 3u)
+    return fail(FAB_ERR_ALIGNMENT, "fab_exp_probe: sink must be 4-byte aligned");
+  const hipError_t e = fab::launch_exp_probe(blocks, iters, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_exp_probe: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

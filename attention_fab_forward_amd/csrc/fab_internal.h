@@ -137,6 +137,9 @@ hipError_t launch_attn_bwd_f32(const AttnArgs& a, int d, hipStream_t s);
 
 hipError_t launch_ulysses(const UlyssesArgs& a, bool pack, hipStream_t s);
 
+int exp_probe_chains();
+hipError_t launch_exp_probe(int blocks, int iters, float* sink, hipStream_t s);
+
 bool mlp_available();
 size_t mlp_fwd_workspace(int m, int n, int k, int p, int* splits);
 size_t mlp_bwd_workspace(int m, int n, int k, int p);

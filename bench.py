@@ -274,6 +274,29 @@ def time_merge(w, reps, torch, fab):
             "shape": f"O {list(shape)} bf16, LSE {[w.batch, w.heads_q, w.seq]} fp32"}
 
 
+def exp_bound(torch, fab_binding, pairs_fwd):
+    """Secondary bound of the softmax: the rate of exp2(fma(x, a, b)) (one per
+    probability) from the library's probe, timed with events on torch's
+    stream, and the time the benchmarked step's exponentials would take at
+    that rate (forward: one per unmasked pair and head; backward: two, the dK/dV
+    and dQ kernels each rebuilding P)."""
+    blocks, iters = 2048, 2048
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    fab_binding.exp_probe(blocks, iters, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    count = 0
+    for _ in range(5):
+        count += fab_binding.exp_probe(blocks, iters, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = count / (e0.elapsed_time(e1) / 1e3)
+    return {"exp_per_s": rate, "exp_bound_ms_fwd": pairs_fwd / rate * 1e3,
+            "exp_bound_ms_fwd_bwd": 3 * pairs_fwd / rate * 1e3,
+            "probe": f"{blocks} x 256 lanes x {iters} steps x 8 chains of exp2(fma)"}
+
+
 def time_ulysses(w, reps, torch, fab, ranks=8):
     """HBM rate of the two layout kernels around the Ulysses exchanges, for a
     rank of a `ranks`-way group whose share after the exchange is the
@@ -530,6 +553,10 @@ def main():
                 "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "kernel": dom}
     log(f"step {step_ms:.3f} ms ({value:.1f} TFLOP/s), fwd {fwd_ms:.3f} ms; kernels: "
         + ", ".join(f"{k_} {v['avg_ms']:.3f} ms" for k_, v in kern.items()))
+    secondary = exp_bound(torch, fab_binding, unit)
+    secondary["exp_bound_frac_of_step"] = secondary["exp_bound_ms_fwd_bwd"] / step_ms
+    log(f"exp2(fma) rate {secondary['exp_per_s']:.3e}/s -> exp-bound {secondary['exp_bound_ms_fwd_bwd']:.3f} ms "
+        f"of the {step_ms:.3f} ms step")
 
     if args.copy_probe_mib:
         nbytes = args.copy_probe_mib << 20
@@ -599,6 +626,7 @@ def main():
         "kernels": kern,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "secondary_bound": secondary,
     }
     line.update(extras)
     print(json.dumps(line), flush=True)

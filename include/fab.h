@@ -255,6 +255,16 @@ int fab_plan_kernel_times(fab_plan_t* plan, const char** names, int* counts,
 /* Waits for pending events and clears the per-kernel totals. */
 fab_status fab_plan_reset_kernel_times(fab_plan_t* plan);
 
+/* Rate probe of the softmax's per-element transcendental work (a secondary
+ * bound of the attention kernels beside the MFMA rate): enqueues `blocks`
+ * workgroups of 256 lanes, each lane running `iters` steps of 8 independent
+ * chains x <- exp2(fma(x, a, b)) -- the form every probability takes -- and
+ * writing one float to sink[lane index] (sink: device, blocks * 256 floats).
+ * *exp_count receives the number of exponentials enqueued (may be NULL).
+ * With sink NULL nothing is launched (count only).  The caller times the
+ * stream; blocks in [1, 2^20], iters in [1, 2^24]. */
+fab_status fab_exp_probe(int blocks, int iters, float* sink, int64_t* exp_count, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

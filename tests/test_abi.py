@@ -184,3 +184,15 @@ def test_ulysses_argument_errors_before_any_launch():
         assert B.STATUS[fn(ctypes.byref(lay), good, vp(0x10004), None)] == "FAB_ERR_ALIGNMENT"
         bad = B._ulysses_layout(torch.bfloat16, 1, 64, 6, 128, 4)
         assert B.STATUS[fn(ctypes.byref(bad), good, good, None)] == "FAB_ERR_BAD_SHAPE"
+
+
+def test_exp_probe_count_and_argument_errors():
+    L = B.lib()
+    count = ctypes.c_int64(-1)
+    # count only: a NULL sink launches nothing
+    assert B.STATUS[L.fab_exp_probe(10, 100, None, ctypes.byref(count), None)] == "FAB_OK"
+    assert count.value == 10 * 256 * 100 * 8
+    assert B.STATUS[L.fab_exp_probe(0, 100, None, None, None)] == "FAB_ERR_BAD_SHAPE"
+    assert B.STATUS[L.fab_exp_probe(10, 0, None, None, None)] == "FAB_ERR_BAD_SHAPE"
+    assert B.STATUS[L.fab_exp_probe(10, 100, ctypes.c_void_p(0x10002), None, None)] == \
+        "FAB_ERR_ALIGNMENT"
