@@ -122,12 +122,12 @@ def time_workload(key, reps, torch, fab):
     from attention_fab_forward_amd.inputs import WORKLOADS
     w = WORKLOADS[key]
     gen = torch.Generator(device="cuda")
-    c = {"attn_causal_bf16_h4_n131072_d128": 4, "attn_causal_bf16_gqa2_n1048576_d128": 5}.get(key, 9)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     def draw(t, heads):
-        gen.manual_seed(1000 * c + t)
+        gen.manual_seed(1000 * w.number + t)
         return torch.randn(w.batch, w.seq, heads, w.d, device="cuda", dtype=torch.float32,
-                           generator=gen).to(torch.bfloat16)
+                           generator=gen).to(dt)
 
     q, k, v, do = draw(1, w.heads_q), draw(2, w.heads_kv), draw(3, w.heads_kv), draw(4, w.heads_q)
     o, lse = fab.forward(q, k, v, "softmax", w.causal, w.scale())
@@ -150,7 +150,8 @@ def time_workload(key, reps, torch, fab):
     fm, bm = sorted(fms)[len(fms) // 2], sorted(bms)[len(bms) // 2]
     del q, k, v, do, o, lse
     torch.cuda.empty_cache()
-    return {"fwd_ms": fm, "bwd_ms": bm, "fwd_tflops": fwd_fl / fm / 1e9,
+    return {"fwd_ms": fm, "bwd_ms": bm, "fwd_us": 1e3 * fm, "bwd_us": 1e3 * bm,
+            "dtype": w.dtype, "fwd_tflops": fwd_fl / fm / 1e9,
             "fwd_bwd_tflops": (fwd_fl + bwd_fl) / (fm + bm) / 1e9,
             "fwd_bwd_pct_bf16_peak": 100.0 * (fwd_fl + bwd_fl) / (fm + bm) / 1e9 / BF16_PEAK_TFLOPS,
             "reps": reps, "inputs": "N(0,1) drawn on the device, seeded per tensor"}
@@ -578,6 +579,8 @@ def main():
     if "workloads" in want:
         log("other workloads ...")
         extras["workloads"] = {
+            # latency-bound (microseconds of work): reported in us
+            "attn_f32_h1_n256_d64": time_workload("attn_f32_h1_n256_d64", 51, torch, fab),
             "attn_causal_bf16_h4_n131072_d128": time_workload(
                 "attn_causal_bf16_h4_n131072_d128", 3, torch, fab),
             "attn_causal_bf16_gqa2_n1048576_d128": time_workload(
