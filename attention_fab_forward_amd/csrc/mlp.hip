@@ -147,6 +147,21 @@ __device__ __forceinline__ void stash_tile(float* red, int wave, int lane, const
   for (int i = 0; i < 4; ++i) mine[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
 }
 
+// The backward kernels stage their transposed second-product operand in LDS
+// with asynchronous global -> LDS copies (each lane reads back exactly the 16
+// byte pieces it copied, so only a wave-local wait is needed).  The copies are
+// issued right before the next tile's row loads, and vector memory operations
+// complete in issue order, so waiting until only those N loads remain
+// outstanding waits for exactly the copies.  These waits are assembly with a
+// memory clobber so LDS accesses stay on their side.
+// Waits for the copies while the N loads issued after them stay in flight.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // forward: workgroup = 32 rows of A, one split of the n tiles
 // ---------------------------------------------------------------------------
@@ -160,17 +175,25 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
                                                          int64_t ldct, int tiles_per_split,
                                                          float* part) {
   constexpr int NW = mlp_fwd_waves<K, P>();
+  constexpr int kq = K / NW, kc = kq / 16;
+  constexpr int pq = P / NW, pt = pq / 32;
+  static_assert(kc >= 1 && pt >= 1, "each wave needs a 16-deep slice of k and 32 columns of p");
+  // Bt tile slices: wave w holds rows n0 .. n0 + 31, columns w kq .. w kq + kq - 1,
+  // LDS row r = tile row perm_row(r), 16-byte chunk c at physical chunk c ^ (r % LPR)
+  constexpr int RB = 2 * kq;        // bytes of one slice row
+  constexpr int LPR = kq / 8;       // 16-byte chunks (copy lanes) per row
+  constexpr int RPI = 64 / LPR;     // rows per 1 KiB copy
+  static_assert(kc * 1024 == 32 * RB, "a slice is kc 1 KiB copies");
+  __shared__ __attribute__((aligned(1024))) char bsh[NW * 32 * RB];
   __shared__ __attribute__((aligned(16))) float red[NW * 64 * 16];  // partial H tiles
   __shared__ __attribute__((aligned(16))) uint32_t gsh[64 * 8];     // G tile, bf16 pairs
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, lg = lane >> 5;
   const int row = blockIdx.x * 32 + lq;
   const bool rlive = row < a.m;
-  constexpr int kq = K / NW, kc = kq / 16;
-  constexpr int pq = P / NW, pt = pq / 32;
-  static_assert(kc >= 1 && pt >= 1, "each wave needs a 16-deep slice of k and 32 columns of p");
   const uint16_t* A = static_cast<const uint16_t*>(a.a);
   const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
+  char* const mybt = bsh + wave * 32 * RB;
 
   u32x4 af[kc];
 #pragma unroll
@@ -186,19 +209,32 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
   const int ntiles = (a.n + 31) / 32;
   const int jt0 = blockIdx.y * tiles_per_split;
   const int jt1 = min(ntiles, jt0 + tiles_per_split);
-  // Operands are loaded one phase ahead of their use: the Bt fragments of
-  // tile jt + 1 right after the first product of tile jt, and the C^T
-  // fragments of tile jt at its top, so both loads overlap the barriers, the
-  // reduction and the GeLU instead of stalling the MFMAs.
-  u32x4 bfr[kc];
-  auto load_bt = [&](int jt) {
-    const int nrow = jt * 32 + perm_row(lq);
-    const bool nlive = nrow < a.n;
-    const uint16_t* btrow = Bt + (int64_t)min(nrow, a.n - 1) * a.bt_sr + wave * kq + 8 * lg;
+  // Copy i of lane l fills LDS row r = RPI i + l / LPR, physical chunk l % LPR,
+  // from the 256-byte-or-less row segment of tile row perm_row(r): each copy
+  // instruction reads RPI whole row segments (coalesced), unlike register
+  // loads in MFMA operand order (32 rows x 32 bytes each).
+  uint32_t boff[kc];
 #pragma unroll
-    for (int c = 0; c < kc; ++c) bfr[c] = ldg16_live(btrow + 16 * c, nlive);
+  for (int i = 0; i < kc; ++i) {
+    const int r = RPI * i + lane / LPR, pc = lane % LPR;
+    boff[i] = (uint32_t)(2 * ((int64_t)perm_row(r) * a.bt_sr + 8 * (pc ^ (r % LPR))));
+  }
+  auto copy_bt = [&](int jt) {
+    const int n0 = jt * 32;
+    const uint16_t* base = Bt + (int64_t)n0 * a.bt_sr + wave * kq;
+    if (n0 + 32 <= a.n) {
+#pragma unroll
+      for (int i = 0; i < kc; ++i) dma16(base, boff[i], mybt + i * 1024);
+    } else {  // ragged last tile: rows past n read row n - 1 (their C^T rows are zero)
+#pragma unroll
+      for (int i = 0; i < kc; ++i) {
+        const int r = RPI * i + lane / LPR, pc = lane % LPR;
+        const int tr = min(perm_row(r), a.n - 1 - n0);
+        dma16_at(base + (int64_t)tr * a.bt_sr + 8 * (pc ^ (r % LPR)), mybt + i * 1024);
+      }
+    }
   };
-  if (jt0 < jt1) load_bt(jt0);
+  if (jt0 < jt1) copy_bt(jt0);
   for (int jt = jt0; jt < jt1; ++jt) {
     const int n0 = jt * 32;
     u32x4 cfr[pt][2];
@@ -208,18 +244,21 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
       cfr[t][0] = ldg16(crow);
       cfr[t][1] = ldg16(crow + 8);
     }
-    // keep these loads ahead of the next tile's: the wait for C^T before the
-    // second product then leaves the Bt prefetch in flight
-    __builtin_amdgcn_sched_barrier(0);
+    wait_copies<2 * pt>();  // this tile's Bt slice; the C^T loads above stay in flight
     f32x16 hp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) hp[r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < kc; ++c) hp = mfma32(bfr[c], af[c], hp);
-    __builtin_amdgcn_sched_barrier(0);
-    load_bt(min(jt + 1, jt1 - 1));  // unconditional: a branch here costs register copies
+    lds_mfma_pipeline<kc, 4>(
+        [&](int c) { return lds16(mybt + lq * RB + 16 * ((2 * c + lg) ^ (lq % LPR))); },
+        [&](int c, const u32x4& x) { hp = mfma32(x, af[c], hp); });
     stash_tile(red, wave, lane, hp);
     __syncthreads();
+    // C^T of this tile has had the first product and the barrier to arrive;
+    // waiting here (a wait the compiler sees) keeps its own wait before the
+    // second product from also covering the next tile's Bt copy issued below
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    wait_lds_reads();  // this wave's reads of its Bt slice are done
+    if (jt + 1 < jt1) copy_bt(jt + 1);
     // slot r of lane l: row `row`, column n0 + 16 lg + r
     finish_tile<NW, false>(red, nullptr, gsh, wave, lane, a.scale);
     __syncthreads();
@@ -232,6 +271,7 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
       o[t] = mfma32(cfr[t][1], gb[1], o[t]);
     }
   }
+  wait_copies<0>();
   if (!rlive) return;
   float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.p + wave * pq + 16 * lg;
 #pragma unroll
@@ -248,21 +288,6 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
 // overlap the barriers and GeLU', and the second operand holds no registers
 // while the partial tiles do.
 // ---------------------------------------------------------------------------
-
-// The backward kernels stage their transposed second-product operand in LDS
-// with asynchronous global -> LDS copies (each lane reads back exactly the 16
-// byte pieces it copied, so only a wave-local wait is needed).  The copies are
-// issued right before the next tile's row loads, and vector memory operations
-// complete in issue order, so waiting until only those N loads remain
-// outstanding waits for exactly the copies.  These waits are assembly with a
-// memory clobber so LDS accesses stay on their side.
-// Waits for the copies while the N loads issued after them stay in flight.
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Copies the kt x 2 16-byte pieces of this lane's second-product operand
 // (rows row0 + 32 t + perm_row(lq) of the transposed copy xt, 16 columns from
