@@ -40,22 +40,45 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
   return cdf + x * 0.3989422804014327f * expf(-0.5f * x * x);
 }
 
-// out[c][r] = in[r][c] for r < rows, c < cols; zero for r in [rows, ld_out).
-// in: row stride ld_in (elements); out: [cols][ld_out], ld_out % 64 == 0.
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* in, int64_t ld_in,
-                                                             int rows, int cols, uint16_t* out,
-                                                             int64_t ld_out) {
+// Operands are streamed from copies packed in MFMA operand order, so that
+// every load (or async copy) of a wave reads 1 KiB of contiguous memory: a
+// fragment is the 64 lanes x 16 bytes one MFMA takes as its A operand, lane
+// l holding 8 consecutive values of row perm_row(l % 32) of a 32-row tile.
+//  * "row" fragments (first-product operands, X [rows][cols] as stored):
+//    fragment (R, j), j = cols / 16 chunk, lane l: X[32 R + perm_row(l % 32)]
+//    [16 j + 8 (l / 32) + e]; stored at ((R * cols / 16) + j) * 512.
+//  * "column" fragments (second-product operands, X transposed): fragment
+//    (R, T, c), R over cols / 32, T over rows_pad / 32, c in {0, 1}, lane l:
+//    X[32 T + 16 (l / 32) + 8 c + e][32 R + perm_row(l % 32)]; stored at
+//    ((R * rows_pad / 32 + T) * 2 + c) * 512.
+// Rows of X at or past `rows` read as zero.  rows_pad % 64 == 0, cols % 64 == 0.
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* x, int64_t ld, int rows,
+                                                        int cols, int64_t pieces, uint16_t* out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte piece
+  if (i >= pieces) return;
+  const int l = (int)(i & 63);
+  const int64_t f = i >> 6;
+  const int nj = cols / 16;
+  const int j = (int)(f % nj);
+  const int64_t R = f / nj;
+  const int64_t row = 32 * R + perm_row(l & 31);
+  const u32x4 v = row < rows ? ldg16(x + row * ld + 16 * j + 8 * (l >> 5)) : u32x4{0, 0, 0, 0};
+  stg16(out + i * 8, v);
+}
+
+__global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64_t ld, int rows,
+                                                        int cols, int rows_pad, uint16_t* out) {
   __shared__ uint16_t tile[64][64 + 2];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
-  // load 64 x 64: 512 chunks of 8 elements, 2 per thread
+  // load 64 x 64 of X: 512 chunks of 8 elements, 2 per thread
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int i = tid + 256 * u;
     const int r = i / 8, ch = i % 8;
     const int gr = r0 + r, gc = c0 + ch * 8;
     u32x4 v = {0, 0, 0, 0};
-    if (gr < rows && gc < cols) v = ldg16(in + (int64_t)gr * ld_in + gc);
+    if (gr < rows && gc < cols) v = ldg16(x + (int64_t)gr * ld + gc);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       tile[r][ch * 8 + 2 * w] = (uint16_t)(v[w] & 0xffff);
@@ -63,17 +86,20 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* in,
     }
   }
   __syncthreads();
+  // write the 2 (R) x 2 (T) x 2 (c) fragments of this 64 x 64 block
+  const int tt = rows_pad / 32;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int i = tid + 256 * u;
-    const int c = i / 8, ch = i % 8;  // output row c0 + c, columns r0 + 8 ch ..
-    const int gc = c0 + c;
-    if (gc >= cols) continue;
+    const int piece = tid + 256 * u;
+    const int l = piece & 63, c = (piece >> 6) & 1, tl = (piece >> 7) & 1, rl = piece >> 8;
+    const int xc = 32 * rl + perm_row(l & 31);
+    const int xr = 32 * tl + 16 * (l >> 5) + 8 * c;
     u32x4 v;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-      v[w] = (uint32_t)tile[ch * 8 + 2 * w][c] | ((uint32_t)tile[ch * 8 + 2 * w + 1][c] << 16);
-    if (r0 + ch * 8 < ld_out) stg16(out + (int64_t)gc * ld_out + r0 + ch * 8, v);
+      v[w] = (uint32_t)tile[xr + 2 * w][xc] | ((uint32_t)tile[xr + 2 * w + 1][xc] << 16);
+    const int64_t frag = ((int64_t)(c0 / 32 + rl) * tt + (r0 / 32 + tl)) * 2 + c;
+    stg16(out + frag * 512 + l * 8, v);
   }
 }
 
@@ -99,13 +125,6 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* part, in
 #pragma unroll
   for (int w = 0; w < 4; ++w) v[w] = pack_bf16(acc[2 * w] * scale, acc[2 * w + 1] * scale);
   stg16(out + r * ld_out + c, v);
-}
-
-// 16 bytes at p, or zeros when !live.  Callers clamp the row so p is valid
-// either way: the load is unconditional (no branch) and a select zeroes it.
-__device__ __forceinline__ u32x4 ldg16_live(const uint16_t* p, bool live) {
-  const u32x4 v = ldg16(p);
-  return live ? v : u32x4{0, 0, 0, 0};
 }
 
 __device__ __forceinline__ void store_tile_f32(float* dst, const f32x16& v) {
@@ -171,8 +190,8 @@ template <int K, int P>
 constexpr int mlp_fwd_waves() { return (K >= 128 && P >= 256) ? 8 : 4; }
 
 template <int K, int P>
-__global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(MlpArgs a, const uint16_t* ct,
-                                                         int64_t ldct, int tiles_per_split,
+__global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(MlpArgs a, const uint16_t* ctf,
+                                                         int tt, int tiles_per_split,
                                                          float* part) {
   constexpr int NW = mlp_fwd_waves<K, P>();
   constexpr int kq = K / NW, kc = kq / 16;
@@ -240,9 +259,10 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
     u32x4 cfr[pt][2];
 #pragma unroll
     for (int t = 0; t < pt; ++t) {
-      const uint16_t* crow = ct + (int64_t)(wave * pq + 32 * t + perm_row(lq)) * ldct + n0 + 16 * lg;
-      cfr[t][0] = ldg16(crow);
-      cfr[t][1] = ldg16(crow + 8);
+      // column fragments (wave pq / 32 + t, jt, c) of C: 1 KiB each
+      const uint16_t* cf = ctf + (((int64_t)(wave * pq / 32 + t) * tt + jt) * 2) * 512 + lane * 8;
+      cfr[t][0] = ldg16(cf);
+      cfr[t][1] = ldg16(cf + 512);
     }
     wait_copies<2 * pt>();  // this tile's Bt slice; the C^T loads above stay in flight
     f32x16 hp;
@@ -289,19 +309,18 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
 // while the partial tiles do.
 // ---------------------------------------------------------------------------
 
-// Copies the kt x 2 16-byte pieces of this lane's second-product operand
-// (rows row0 + 32 t + perm_row(lq) of the transposed copy xt, 16 columns from
-// col0 + 16 lg) into the wave's LDS region: piece (t, h) of lane l lands at
-// region + (2 t + h) * 1024 + 16 l.
+// Copies this wave's kt x 2 column fragments (32 R0 + 32 t rows of the
+// transposed operand, tile T, halves c) into its LDS region: fragment (t, c)
+// lands at region + (2 t + c) * 1024, lane l's 16 bytes at + 16 l, which is
+// where that lane reads them back.  Each copy reads 1 KiB of contiguous memory.
 template <int kt>
-__device__ __forceinline__ void copy_second_operand(const uint16_t* xt, int64_t ldxt, int row0,
-                                                    int col0, int lq, int lg, char* region) {
+__device__ __forceinline__ void copy_second_operand(const uint16_t* xf, int tt, int r0, int T,
+                                                    int lane, char* region) {
 #pragma unroll
-  for (int t = 0; t < kt; ++t) {
-    const uint16_t* trow = xt + (int64_t)(row0 + 32 * t + perm_row(lq)) * ldxt + col0 + 16 * lg;
-    dma16_at(trow, region + (2 * t) * 1024);
-    dma16_at(trow + 8, region + (2 * t + 1) * 1024);
-  }
+  for (int t = 0; t < kt; ++t)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      dma16(xf + (((int64_t)(r0 + t) * tt + T) * 2 + c) * 512, 16 * lane, region + (2 * t + c) * 1024);
 }
 
 // Wave count of a backward kernel whose first product contracts over K (and P
@@ -313,7 +332,8 @@ constexpr int mlp_bwd_waves() { return (K >= 128 && P >= 128 && OUT >= 256) ? 8 
 // dA: workgroup = 32 rows of A, one split of the n tiles.
 template <int K, int P>
 __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_kernel(
-    MlpArgs a, const uint16_t* btt, int64_t ldbtt, int tiles_per_split, float* part) {
+    MlpArgs a, const uint16_t* btr, const uint16_t* cr, const uint16_t* btc, int tt,
+    int tiles_per_split, float* part) {
   constexpr int NW = mlp_bwd_waves<K, P, K>();
   __shared__ __attribute__((aligned(16))) float red[2 * NW * 64 * 16];  // partial H, dG tiles
   constexpr int kq = K / NW, kc = kq / 16, kt = kq / 32;
@@ -327,9 +347,7 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
   constexpr int pq = P / NW, pc = pq / 16;
   static_assert(kt >= 1 && pc >= 1, "each wave needs 32 columns of k and a 16-deep slice of p");
   const uint16_t* A = static_cast<const uint16_t*>(a.a);
-  const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
-  const uint16_t* Cm = static_cast<const uint16_t*>(a.c);
-  const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
+    const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
 
   u32x4 af[kc], df[pc];
 #pragma unroll
@@ -350,16 +368,14 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
   const int jt0 = blockIdx.y * tiles_per_split;
   const int jt1 = min(ntiles, jt0 + tiles_per_split);
   u32x4 bfr[kc], cfr[pc];
+  // row fragments (jt, wave kc + c) of Bt and (jt, wave pc + c) of C
   auto load_rows = [&](int jt) {
-    const int nrow = jt * 32 + perm_row(lq);
-    const bool nlive = nrow < a.n;
-    const int nc = min(nrow, a.n - 1);
-    const uint16_t* btrow = Bt + (int64_t)nc * a.bt_sr + wave * kq + 8 * lg;
-    const uint16_t* crow = Cm + (int64_t)nc * a.c_sr + wave * pq + 8 * lg;
+    const uint16_t* bp = btr + ((int64_t)jt * (K / 16) + wave * kc) * 512 + lane * 8;
+    const uint16_t* cp = cr + ((int64_t)jt * (P / 16) + wave * pc) * 512 + lane * 8;
 #pragma unroll
-    for (int c = 0; c < kc; ++c) bfr[c] = ldg16_live(btrow + 16 * c, nlive);
+    for (int c = 0; c < kc; ++c) bfr[c] = ldg16(bp + c * 512);
 #pragma unroll
-    for (int c = 0; c < pc; ++c) cfr[c] = ldg16_live(crow + 16 * c, nlive);
+    for (int c = 0; c < pc; ++c) cfr[c] = ldg16(cp + c * 512);
   };
   if (jt0 < jt1) load_rows(jt0);
   for (int jt = jt0; jt < jt1; ++jt) {
@@ -372,7 +388,7 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
 #pragma unroll
     for (int c = 0; c < pc; ++c) gp = mfma32(cfr[c], df[c], gp);
     wait_lds_reads();  // the previous tile's reads of tmine are done
-    copy_second_operand<kt>(btt, ldbtt, wave * kq, n0, lq, lg, tmine);
+    copy_second_operand<kt>(btc, tt, wave * kq / 32, jt, lane, tmine);
     load_rows(min(jt + 1, jt1 - 1));  // unconditional: a branch here costs register copies
     stash_tile(red, wave, lane, hp);
     stash_tile(red + NW * 64 * 16, wave, lane, gp);
@@ -403,7 +419,8 @@ constexpr int mlp_bwd_col_waves() { return mlp_bwd_waves<K, (WANT_DB ? P : 128),
 
 template <int K, int P, bool WANT_DB>
 __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp_bwd_col_kernel(
-    MlpArgs a, const uint16_t* xt, int64_t ldxt, int tiles_per_split, float* part) {
+    MlpArgs a, const uint16_t* ar, const uint16_t* dor, const uint16_t* xc, int tt,
+    int tiles_per_split, float* part) {
   constexpr int NW = mlp_bwd_col_waves<K, P, WANT_DB>();
   __shared__ __attribute__((aligned(16))) float red[(WANT_DB ? 2 : 1) * NW * 64 * 16];
   constexpr int kq = K / NW, kc = kq / 16;
@@ -418,10 +435,8 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
   const bool clive = col < a.n;
   char* const tmine = tsh + wave * ot * 2048;
   static_assert(kc >= 1 && pc >= 1 && ot >= 1, "slice too small for the wave count");
-  const uint16_t* A = static_cast<const uint16_t*>(a.a);
   const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
   const uint16_t* Cm = static_cast<const uint16_t*>(a.c);
-  const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
 
   u32x4 bf[kc], cf[pc];
 #pragma unroll
@@ -444,17 +459,15 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
   const int it0 = blockIdx.y * tiles_per_split;
   const int it1 = min(mtiles, it0 + tiles_per_split);
   u32x4 afr[kc], ofr[pc];
+  // row fragments (it, wave kc + c) of A and (it, wave pc + c) of dO
   auto load_rows = [&](int it) {
-    const int arow = it * 32 + perm_row(lq);
-    const bool alive = arow < a.m;
-    const int ac = min(arow, a.m - 1);
-    const uint16_t* ap = A + (int64_t)ac * a.a_sr + wave * kq + 8 * lg;
+    const uint16_t* ap = ar + ((int64_t)it * (K / 16) + wave * kc) * 512 + lane * 8;
 #pragma unroll
-    for (int c = 0; c < kc; ++c) afr[c] = ldg16_live(ap + 16 * c, alive);
+    for (int c = 0; c < kc; ++c) afr[c] = ldg16(ap + c * 512);
     if constexpr (WANT_DB) {
-      const uint16_t* op = dO + (int64_t)ac * a.o_sr + wave * pq + 8 * lg;
+      const uint16_t* op = dor + ((int64_t)it * (P / 16) + wave * pc) * 512 + lane * 8;
 #pragma unroll
-      for (int c = 0; c < pc; ++c) ofr[c] = ldg16_live(op + 16 * c, alive);
+      for (int c = 0; c < pc; ++c) ofr[c] = ldg16(op + c * 512);
     }
   };
   if (it0 < it1) load_rows(it0);
@@ -470,7 +483,7 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
       for (int c = 0; c < pc; ++c) gp = mfma32(ofr[c], cf[c], gp);
     }
     wait_lds_reads();  // the previous tile's reads of tmine are done
-    copy_second_operand<ot>(xt, ldxt, wave * oq, r0, lq, lg, tmine);
+    copy_second_operand<ot>(xc, tt, wave * oq / 32, it, lane, tmine);
     load_rows(min(it + 1, it1 - 1));  // unconditional: a branch here costs register copies
     stash_tile(red, wave, lane, hp);
     if constexpr (WANT_DB) stash_tile(red + NW * 64 * 16, wave, lane, gp);
@@ -500,7 +513,8 @@ struct MlpLayout {
   int split_cols;   // splits of the m loop for the column-block kernel
   int64_t m_pad, n_pad;
   size_t fwd_ct, fwd_part, fwd_total;
-  size_t bwd_btt, bwd_at, bwd_dot, bwd_pa, bwd_pb, bwd_pc, bwd_total;
+  // row fragments of Bt, C, A, dO; column fragments of Bt, A, dO; partials
+  size_t bwd_btr, bwd_cr, bwd_ar, bwd_dor, bwd_btc, bwd_ac, bwd_doc, bwd_pa, bwd_pb, bwd_pc, bwd_total;
 };
 
 int pick_splits(int blocks, int tiles) {
@@ -523,12 +537,20 @@ MlpLayout layout(int m, int n, int k, int p) {
   off = round_up(off + (size_t)L.split_rows * m * p * 4, 256);
   L.fwd_total = off;
   off = 0;
-  L.bwd_btt = off;
-  off = round_up(off + (size_t)k * L.n_pad * 2, 256);
-  L.bwd_at = off;
-  off = round_up(off + (size_t)k * L.m_pad * 2, 256);
-  L.bwd_dot = off;
-  off = round_up(off + (size_t)p * L.m_pad * 2, 256);
+  for (size_t* slot : {&L.bwd_btr, &L.bwd_btc}) {
+    *slot = off;
+    off = round_up(off + (size_t)k * L.n_pad * 2, 256);
+  }
+  L.bwd_cr = off;
+  off = round_up(off + (size_t)p * L.n_pad * 2, 256);
+  for (size_t* slot : {&L.bwd_ar, &L.bwd_ac}) {
+    *slot = off;
+    off = round_up(off + (size_t)k * L.m_pad * 2, 256);
+  }
+  for (size_t* slot : {&L.bwd_dor, &L.bwd_doc}) {
+    *slot = off;
+    off = round_up(off + (size_t)p * L.m_pad * 2, 256);
+  }
   L.bwd_pa = off;
   off = round_up(off + (size_t)L.split_rows * m * k * 4, 256);
   L.bwd_pb = off;
@@ -539,12 +561,24 @@ MlpLayout layout(int m, int n, int k, int p) {
   return L;
 }
 
-hipError_t transpose(const void* in, int64_t ld_in, int rows, int cols, void* out, int64_t ld_out,
+// Row fragments of X [rows][cols] (rows padded to rows_pad with zeros).
+hipError_t pack_rows(const void* x, int64_t ld, int rows, int cols, int64_t rows_pad, void* out,
                      hipStream_t s) {
-  const dim3 grid((unsigned)((ld_out + 63) / 64), (unsigned)((cols + 63) / 64)), block(256);
-  FAB_TIMED("mlp_transpose", s, hipLaunchKernelGGL(transpose_bf16_kernel, grid, block, 0, s,
-                     static_cast<const uint16_t*>(in), ld_in, rows, cols,
-                     static_cast<uint16_t*>(out), ld_out));
+  const int64_t pieces = rows_pad * cols / 8;
+  const dim3 grid((unsigned)((pieces + 255) / 256)), block(256);
+  FAB_TIMED("mlp_pack", s, hipLaunchKernelGGL(pack_rows_kernel, grid, block, 0, s,
+                     static_cast<const uint16_t*>(x), ld, rows, cols, pieces,
+                     static_cast<uint16_t*>(out)));
+  return hipGetLastError();
+}
+
+// Column fragments of X [rows][cols], i.e. row fragments of X^T.
+hipError_t pack_cols(const void* x, int64_t ld, int rows, int cols, int64_t rows_pad, void* out,
+                     hipStream_t s) {
+  const dim3 grid((unsigned)(rows_pad / 64), (unsigned)(cols / 64)), block(256);
+  FAB_TIMED("mlp_pack", s, hipLaunchKernelGGL(pack_cols_kernel, grid, block, 0, s,
+                     static_cast<const uint16_t*>(x), ld, rows, cols, (int)rows_pad,
+                     static_cast<uint16_t*>(out)));
   return hipGetLastError();
 }
 
@@ -572,29 +606,34 @@ size_t mlp_bwd_workspace(int m, int n, int k, int p) { return layout(m, n, k, p)
 namespace {
 
 template <int K, int P>
-hipError_t fwd_kp(const MlpArgs& a, const MlpLayout& L, uint16_t* ct, float* part, hipStream_t s) {
+hipError_t fwd_kp(const MlpArgs& a, const MlpLayout& L, const uint16_t* ctf, float* part, hipStream_t s) {
   const int ntiles = (a.n + 31) / 32;
   const int per = (ntiles + L.split_rows - 1) / L.split_rows;
   const dim3 grid((unsigned)((a.m + 31) / 32), (unsigned)L.split_rows),
       block(64 * mlp_fwd_waves<K, P>());
-  FAB_TIMED("mlp_fwd", s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, ct, L.n_pad, per, part));
+  FAB_TIMED("mlp_fwd", s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, ctf, (int)(L.n_pad / 32), per, part));
   return hipGetLastError();
 }
 
 template <int K, int P>
-hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const uint16_t* btt, const uint16_t* at,
-                  const uint16_t* dot, float* pa, float* pb, float* pc, hipStream_t s) {
+hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const char* ws, float* pa, float* pb,
+                  float* pc, hipStream_t s) {
+  auto frag = [&](size_t off) { return reinterpret_cast<const uint16_t*>(ws + off); };
+  const int ttn = (int)(L.n_pad / 32), ttm = (int)(L.m_pad / 32);
   const int ntiles = (a.n + 31) / 32, mtiles = (a.m + 31) / 32;
   const int per_n = (ntiles + L.split_rows - 1) / L.split_rows;
   const int per_m = (mtiles + L.split_cols - 1) / L.split_cols;
   FAB_TIMED("mlp_bwd_da", s, hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)mtiles, (unsigned)L.split_rows),
-                     dim3(64 * mlp_bwd_waves<K, P, K>()), 0, s, a, btt, L.n_pad, per_n, pa));
+                     dim3(64 * mlp_bwd_waves<K, P, K>()), 0, s, a, frag(L.bwd_btr), frag(L.bwd_cr),
+                     frag(L.bwd_btc), ttn, per_n, pa));
   FAB_TIMED("mlp_bwd_dbt", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, true>),
                      dim3((unsigned)ntiles, (unsigned)L.split_cols),
-                     dim3(64 * mlp_bwd_col_waves<K, P, true>()), 0, s, a, at, L.m_pad, per_m, pb));
+                     dim3(64 * mlp_bwd_col_waves<K, P, true>()), 0, s, a, frag(L.bwd_ar), frag(L.bwd_dor),
+                     frag(L.bwd_ac), ttm, per_m, pb));
   FAB_TIMED("mlp_bwd_dc", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, false>),
                      dim3((unsigned)ntiles, (unsigned)L.split_cols),
-                     dim3(64 * mlp_bwd_col_waves<K, P, false>()), 0, s, a, dot, L.m_pad, per_m, pc));
+                     dim3(64 * mlp_bwd_col_waves<K, P, false>()), 0, s, a, frag(L.bwd_ar), frag(L.bwd_dor),
+                     frag(L.bwd_doc), ttm, per_m, pc));
   return hipGetLastError();
 }
 
@@ -630,11 +669,11 @@ hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s) {
   if (!mlp_shape_supported(a.k, a.p)) return hipErrorInvalidValue;
   const MlpLayout L = layout(a.m, a.n, a.k, a.p);
   char* ws = reinterpret_cast<char*>(a.ws);
-  uint16_t* ct = reinterpret_cast<uint16_t*>(ws + L.fwd_ct);
+  uint16_t* ctf = reinterpret_cast<uint16_t*>(ws + L.fwd_ct);
   float* part = reinterpret_cast<float*>(ws + L.fwd_part);
-  hipError_t e = transpose(a.c, a.c_sr, a.n, a.p, ct, L.n_pad, s);
+  hipError_t e = pack_cols(a.c, a.c_sr, a.n, a.p, L.n_pad, ctf, s);
   if (e != hipSuccess) return e;
-  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() { return fwd_kp<K, P>(a, L, ct, part, s); });
+  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() { return fwd_kp<K, P>(a, L, ctf, part, s); });
   if (e != hipSuccess) return e;
   return reduce(part, L.split_rows, a.m, a.p, 1.f, a.o, a.o_sr, s);
 }
@@ -643,19 +682,18 @@ hipError_t launch_mlp_bwd_bf16(const MlpArgs& a, hipStream_t s) {
   if (!mlp_shape_supported(a.k, a.p)) return hipErrorInvalidValue;
   const MlpLayout L = layout(a.m, a.n, a.k, a.p);
   char* ws = reinterpret_cast<char*>(a.ws);
-  uint16_t* btt = reinterpret_cast<uint16_t*>(ws + L.bwd_btt);
-  uint16_t* at = reinterpret_cast<uint16_t*>(ws + L.bwd_at);
-  uint16_t* dot = reinterpret_cast<uint16_t*>(ws + L.bwd_dot);
   float* pa = reinterpret_cast<float*>(ws + L.bwd_pa);
   float* pb = reinterpret_cast<float*>(ws + L.bwd_pb);
   float* pc = reinterpret_cast<float*>(ws + L.bwd_pc);
   hipError_t e;
-  if ((e = transpose(a.bt, a.bt_sr, a.n, a.k, btt, L.n_pad, s)) != hipSuccess) return e;
-  if ((e = transpose(a.a, a.a_sr, a.m, a.k, at, L.m_pad, s)) != hipSuccess) return e;
-  if ((e = transpose(a.dout, a.o_sr, a.m, a.p, dot, L.m_pad, s)) != hipSuccess) return e;
-  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() {
-    return bwd_kp<K, P>(a, L, btt, at, dot, pa, pb, pc, s);
-  });
+  if ((e = pack_rows(a.bt, a.bt_sr, a.n, a.k, L.n_pad, ws + L.bwd_btr, s)) != hipSuccess) return e;
+  if ((e = pack_rows(a.c, a.c_sr, a.n, a.p, L.n_pad, ws + L.bwd_cr, s)) != hipSuccess) return e;
+  if ((e = pack_rows(a.a, a.a_sr, a.m, a.k, L.m_pad, ws + L.bwd_ar, s)) != hipSuccess) return e;
+  if ((e = pack_rows(a.dout, a.o_sr, a.m, a.p, L.m_pad, ws + L.bwd_dor, s)) != hipSuccess) return e;
+  if ((e = pack_cols(a.bt, a.bt_sr, a.n, a.k, L.n_pad, ws + L.bwd_btc, s)) != hipSuccess) return e;
+  if ((e = pack_cols(a.a, a.a_sr, a.m, a.k, L.m_pad, ws + L.bwd_ac, s)) != hipSuccess) return e;
+  if ((e = pack_cols(a.dout, a.o_sr, a.m, a.p, L.m_pad, ws + L.bwd_doc, s)) != hipSuccess) return e;
+  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() { return bwd_kp<K, P>(a, L, ws, pa, pb, pc, s); });
   if (e != hipSuccess) return e;
   if ((e = reduce(pa, L.split_rows, a.m, a.k, a.scale, a.da, a.a_sr, s)) != hipSuccess) return e;
   if ((e = reduce(pb, L.split_cols, a.n, a.k, a.scale, a.dbt, a.bt_sr, s)) != hipSuccess) return e;
