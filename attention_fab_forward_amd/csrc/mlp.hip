@@ -133,7 +133,12 @@ __device__ __forceinline__ void store_tile_f32(float* dst, const f32x16& v) {
   for (int i = 0; i < 4; ++i) d[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
 }
 
-// Sums the NW partial tiles of H (and of dG when GRAD) held in LDS and writes
+// Partial tiles live in LDS as float pairs, slot-pair major: pair q (slots
+// 2q, 2q + 1) of wave w's partial for lane l at float2 index (8 w + q) 64 + l,
+// so every 8-byte write or read of a wave covers 512 contiguous bytes (no bank
+// conflicts; a lane-major layout puts a wave's reads 64 bytes apart).
+//
+// finish_tile sums the NW partial tiles of H (and of dG when GRAD) and writes
 // GeLU(scale H) (or dG * GeLU'(scale H) when GRAD) as bf16 pairs to gsh; wave
 // w takes slots [16 w / NW, 16 (w + 1) / NW) of every lane, so each erf is
 // evaluated once.  Caller: barrier before (partials written) and after (gsh
@@ -146,12 +151,21 @@ __device__ __forceinline__ void finish_tile(const float* red_h, const float* red
   float h[SPW], g[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) h[j] = g[j] = 0.f;
+  const f32x2* rh = reinterpret_cast<const f32x2*>(red_h);
+  const f32x2* rg = reinterpret_cast<const f32x2*>(red_g);
 #pragma unroll
   for (int w = 0; w < NW; ++w)
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      h[j] += red_h[(w * 64 + lane) * 16 + wave * SPW + j];
-      if constexpr (GRAD) g[j] += red_g[(w * 64 + lane) * 16 + wave * SPW + j];
+    for (int j = 0; j < SPW; j += 2) {
+      const int idx = (8 * w + (wave * SPW + j) / 2) * 64 + lane;
+      const f32x2 x = rh[idx];
+      h[j] += x[0];
+      h[j + 1] += x[1];
+      if constexpr (GRAD) {
+        const f32x2 y = rg[idx];
+        g[j] += y[0];
+        g[j + 1] += y[1];
+      }
     }
   float x[SPW];
 #pragma unroll
@@ -161,9 +175,9 @@ __device__ __forceinline__ void finish_tile(const float* red_h, const float* red
 }
 
 __device__ __forceinline__ void stash_tile(float* red, int wave, int lane, const f32x16& v) {
-  f32x4* mine = reinterpret_cast<f32x4*>(red + (wave * 64 + lane) * 16);
+  f32x2* mine = reinterpret_cast<f32x2*>(red) + wave * 8 * 64 + lane;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) mine[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+  for (int q = 0; q < 8; ++q) mine[q * 64] = f32x2{v[2 * q], v[2 * q + 1]};
 }
 
 // The backward kernels stage their transposed second-product operand in LDS
