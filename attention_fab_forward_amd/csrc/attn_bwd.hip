@@ -592,13 +592,28 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(AttnArgs a) {
   constexpr int LPR = D * 2 / 16;
   constexpr int RPB = 256 / LPR;
   const int tid = threadIdx.x;
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;  // over b * hq * m
+  // rows taken in O's [b, m, hq] order, so a workgroup streams contiguous O
+  // and dO (the 4-byte results, in [b, hq, m] order, are the scattered part)
+  const int64_t orow = (int64_t)blockIdx.x * RPB + tid / LPR;
   const int part = tid % LPR;
   const int64_t total = (int64_t)a.b * a.hq * a.m;
   float acc = 0.f;
-  if (row < total) {
-    const int64_t i = row % a.m, bh = row / a.m;
-    const int h = (int)(bh % a.hq), bi = (int)(bh / a.hq);
+  int64_t row = 0;  // [b, hq, m] index of the result
+  if (orow < total) {
+    int64_t i, h, bi;
+    if (a.rows_small) {
+      const uint32_t r32 = (uint32_t)orow;
+      const uint32_t bm = (__umulhi(r32, a.div_hq.m) + r32) >> a.div_hq.s;
+      h = r32 - bm * (uint32_t)a.hq;
+      bi = (__umulhi(bm, a.div_m.m) + bm) >> a.div_m.s;
+      i = bm - (uint32_t)bi * (uint32_t)a.m;
+    } else {
+      const int64_t bm = orow / a.hq;
+      h = orow - bm * a.hq;
+      bi = bm / a.m;
+      i = bm - bi * a.m;
+    }
+    row = (bi * a.hq + h) * a.m + i;
     const int64_t off = bi * a.o_sb + h * a.o_sh + i * a.o_sr + part * 8;
     const u32x4 x = ldg16(static_cast<const uint16_t*>(a.o) + off);
     const u32x4 y = ldg16(static_cast<const uint16_t*>(a.dout) + off);
@@ -608,7 +623,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int sft = 1; sft < LPR; sft <<= 1) acc += __shfl_xor(acc, sft, 64);
-  if (row < total && part == 0) {
+  if (orow < total && part == 0) {
     a.delta[row] = -acc;
     // a row without keys (LSE = -inf) gets +inf, so its P = exp2(S - inf) = 0
     const float l = a.lse_in[row];

@@ -189,6 +189,9 @@ fab::AttnArgs attn_args(const fab_plan_s* p) {
   a.causal = q.mask == FAB_MASK_CAUSAL;
   const int64_t diag = q.q_offset - q.k_offset;
   a.diag = (int32_t)std::min<int64_t>(std::max<int64_t>(diag, -q.m - 1), q.n);
+  a.rows_small = q.batch * q.heads_a * q.m < ((int64_t)1 << 31);
+  a.div_hq = fab::make_fastdiv((uint32_t)q.heads_a);
+  a.div_m = fab::make_fastdiv((uint32_t)q.m);
   return a;
 }
 

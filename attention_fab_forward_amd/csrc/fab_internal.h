@@ -9,6 +9,12 @@
 
 namespace fab {
 
+// Quotient by a divisor fixed at launch: (umulhi(n, m) + n) >> s, n < 2^31.
+struct FastDiv {
+  uint32_t m, s;
+};
+FastDiv make_fastdiv(uint32_t d);
+
 // Softmax attention: A = Q [b, m, hq, d], Bt = K [b, n, hkv, d], C = V [b, n, hkv, d].
 struct AttnArgs {
   const void* q;
@@ -37,13 +43,10 @@ struct AttnArgs {
   // query offset - key offset, clamped to [-m - 1, n]: beyond that range every
   // row sees all keys or none)
   int32_t diag;
+  // row index splits of [b, m, hq] by multiplication (when b hq m < 2^31)
+  int32_t rows_small;
+  FastDiv div_hq, div_m;
 };
-
-// Quotient by a divisor fixed at launch: (umulhi(n, m) + n) >> s, n < 2^31.
-struct FastDiv {
-  uint32_t m, s;
-};
-FastDiv make_fastdiv(uint32_t d);
 
 // Merge of two partial softmax results (fab_merge): packed LSE [b, hq, m].
 struct MergeArgs {
