@@ -17,18 +17,19 @@
 // the resident operand in registers; the partial 32 x 32 tiles are summed
 // through LDS and each wave finishes 16 / NW of every lane's tile entries
 // (GeLU or GeLU'), so each erf is evaluated once.  Each wave then owns 1 / NW
-// of the output columns for the second product.  Operands whose
-// contraction runs along their non-contiguous axis are read from transposed
-// copies that a small kernel writes into the workspace first (copies of the
-// inputs, not of the intermediate).  The n (or m) loop is split across
-// workgroups; the fp32 partial sums are added by a final elementwise kernel.
+// of the output columns for the second product.  Streamed operands are read
+// from copies of the inputs (never of the intermediate) that small kernels
+// pack into the workspace first, in MFMA operand order, so each load reads
+// 1 KiB of contiguous memory (see the packing kernels below).  The n (or m)
+// loop is split across workgroups; the fp32 partial sums are added by a final
+// elementwise kernel.
 #include "fab_device.h"
 #include "fab_internal.h"
 
 namespace fab {
 namespace {
 
-constexpr int kPad = 64;        // padding of transposed copies' leading dimension
+constexpr int kPad = 64;        // padding of the packed copies' row count
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
