@@ -3,10 +3,11 @@
 //
 // The fp32 path keeps every operation in fp32 FMA arithmetic (no reduced
 // precision step anywhere), as the fp32 workload asks.  Its intended sizes are
-// small and latency-bound, so it uses plain VALU FMA: T = D/32 lanes share one
-// row (query or key), each owning 32 of its D columns, and dot products are
-// finished with lane exchanges.  Key/value (or query/dO) tiles are staged in
-// LDS and read by broadcast.
+// small and latency-bound, so it uses plain VALU FMA: T = D/16 lanes share one
+// row (query or key), each owning 16 of its D columns, and dot products are
+// finished with lane exchanges.  Key/value (or query/dO) stages are staged in
+// LDS and read by broadcast; the loop over them is split across the waves of
+// a workgroup (see below), which keeps the serial chain per lane short.
 //
 // Definitions follow the softmax attention block O = softmax(scale Q K^T) V
 // (the block O = f(A B) C of the "Memory-efficient tensor parallelism"
@@ -22,22 +23,35 @@
 namespace fab {
 namespace {
 
-constexpr int kTile = 32;  // rows of a staged tile
+// Lane layout: T = D / kCols lanes share one row (query, or key in the dK/dV
+// kernel), each owning kCols of its D columns; a wave holds RW = 64 / T rows and
+// a workgroup is one wave-width of rows served by NW waves.  The loop over the
+// other side (keys, or queries) runs in stages of SUP = NW * KS rows staged
+// in LDS by the whole workgroup; wave w takes rows w KS .. w KS + KS - 1 of
+// each stage, so the serial work per lane is 1 / NW of the loop.  The waves'
+// partial results are combined through LDS at the end (softmax states merged
+// by their maxima, gradients summed).
+constexpr int kCols = 8;    // columns of a row per lane
+constexpr int kWaves = 8;   // NW
+constexpr int kSlice = 16;  // KS: rows of a stage per wave
+constexpr int kStage = kWaves * kSlice;
 
 template <int T>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (T >= 2) v += __shfl_xor(v, 1, 64);
   if constexpr (T >= 4) v += __shfl_xor(v, 2, 64);
+  if constexpr (T >= 8) v += __shfl_xor(v, 4, 64);
+  if constexpr (T >= 16) v += __shfl_xor(v, 8, 64);
   return v;
 }
 
-// Stage rows [r0, r0 + kTile) of a [rows, D] fp32 matrix (row stride sr) into
+// Stage rows [r0, r0 + kStage) of a [rows, D] fp32 matrix (row stride sr) into
 // LDS (packed rows of D floats); rows >= nrows are zero.
 template <int D>
 __device__ __forceinline__ void stage_f32(float* dst, const float* src, int64_t sr, int r0,
-                                          int nrows, int tid, int nthreads) {
+                                          int nrows, int tid) {
   constexpr int V4 = D / 4;
-  for (int i = tid; i < kTile * V4; i += nthreads) {
+  for (int i = tid; i < kStage * V4; i += 64 * kWaves) {
     const int r = i / V4, c = i % V4;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (r0 + r < nrows) v = *reinterpret_cast<const f32x4*>(src + (int64_t)(r0 + r) * sr + 4 * c);
@@ -45,52 +59,91 @@ __device__ __forceinline__ void stage_f32(float* dst, const float* src, int64_t 
   }
 }
 
+// LDS floats: a stage of two [kStage, D] matrices (+ two kStage vectors), or
+// the cross-wave combination area (NW x RW x D partial rows + 2 NW RW scalars).
+template <int D>
+struct F32Lds {
+  static constexpr int T = D / kCols;
+  static constexpr int RW = 64 / T;
+  static constexpr int CHUNKS = RW * D / 4;  // float4 chunks of an RW x D block
+  static constexpr int STAGE = 2 * kStage * D + 2 * kStage;
+  static constexpr int PART = kWaves * RW * D;
+  static constexpr int FLOATS = STAGE > PART + 2 * kWaves * RW ? STAGE : PART + 2 * kWaves * RW;
+};
+
+// Sum of the NW waves' partial rows part[w][r][:] (r < RW) for float4 chunk
+// `tid` (< CHUNKS) of the RW x D block: returns the chunk, row r = tid / (D / 4).
+template <int D>
+__device__ __forceinline__ f32x4 sum_parts(const float* part, int tid) {
+  constexpr int RW = F32Lds<D>::RW;
+  const int r = tid / (D / 4), c = tid % (D / 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) acc += *reinterpret_cast<const f32x4*>(part + (w * RW + r) * D + 4 * c);
+  return acc;
+}
+
+// Writes this lane's kCols partial columns of row `row` (0..RW-1) for wave w.
+__device__ __forceinline__ void put_part(float* part, int D, int RW, int w, int row, int col0,
+                                         const float (&x)[kCols]) {
+  float* dst = part + (w * RW + row) * D + col0;
+#pragma unroll
+  for (int i = 0; i < kCols; i += 4)
+    *reinterpret_cast<f32x4*>(dst + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+}
+
 // ---------------------------------------------------------------------------
-// forward: one row group of T lanes per query, 256 threads = 256/T queries
+// forward: workgroup = RW queries of one head, keys split over the waves
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
-  constexpr int T = D / 32, QPB = 256 / T;
-  __shared__ float ks[kTile * D];
-  __shared__ float vs[kTile * D];
+__global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
+  constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  static_assert(F32Lds<D>::CHUNKS <= 64 * kWaves, "one float4 of the output block per thread");
+  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
+  float* ks = sm;
+  float* vs = sm + kStage * D;
   const int tid = threadIdx.x;
-  const int part = tid % T;
-  const int nqb = (a.m + QPB - 1) / QPB;
+  const int wave = tid / 64, lane = tid % 64, part = lane % T;
+  const int nqb = (a.m + RW - 1) / RW;
   int id = blockIdx.x;
   const int h = id % a.hq;
   id /= a.hq;
   const int bi = id % a.b;
   id /= a.b;
-  const int qb = CAUSAL ? nqb - 1 - id : id;
+  const int qb = CAUSAL ? nqb - 1 - id : id;  // causal: longest blocks first
   const int g = h / a.group;
-  const int q = qb * QPB + tid / T;
+  const int q = qb * RW + lane / T;
   const float* qbase = static_cast<const float*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const float* kbase = static_cast<const float*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const float* vbase = static_cast<const float*>(a.v) + bi * a.v_sb + g * a.v_sh;
 
-  float qr[32], o[32];
+  float qr[kCols], o[kCols];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    qr[i] = q < a.m ? qbase[(int64_t)q * a.q_sr + part * 32 + i] : 0.f;
+  for (int i = 0; i < kCols; ++i) {
+    qr[i] = q < a.m ? qbase[(int64_t)q * a.q_sr + part * kCols + i] : 0.f;
     o[i] = 0.f;
   }
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // scores in scale * log2(e) units
   const float cs = a.scale_log2;
-  const int kend = CAUSAL ? min(a.n, max(0, qb * QPB + QPB + a.diag)) : a.n;
-  for (int k0 = 0; k0 < kend; k0 += kTile) {
+  const int kend = CAUSAL ? min(a.n, max(0, qb * RW + RW + a.diag)) : a.n;
+  for (int k0 = 0; k0 < kend; k0 += kStage) {
     __syncthreads();
-    stage_f32<D>(ks, kbase, a.k_sr, k0, a.n, tid, 256);
-    stage_f32<D>(vs, vbase, a.v_sr, k0, a.n, tid, 256);
+    stage_f32<D>(ks, kbase, a.k_sr, k0, a.n, tid);
+    stage_f32<D>(vs, vbase, a.v_sr, k0, a.n, tid);
     __syncthreads();
-    float s[kTile];
+    const int kw = k0 + wave * kSlice;
+    if (kw >= kend) continue;  // wave-uniform
+    const float* kt = ks + wave * kSlice * D + part * kCols;
+    const float* vt = vs + wave * kSlice * D + part * kCols;
+    float s[kSlice];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
+    for (int j = 0; j < kSlice; ++j) {
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) acc = fmaf(qr[i], ks[j * D + part * 32 + i], acc);
+      for (int i = 0; i < kCols; ++i) acc = fmaf(qr[i], kt[j * D + i], acc);
       acc = group_sum<T>(acc);
-      const int key = k0 + j;
+      const int key = kw + j;
       const bool dead = key >= a.n || (CAUSAL && key > q + a.diag);
       s[j] = dead ? -INFINITY : acc * cs;
       mx = fmaxf(mx, s[j]);
@@ -99,42 +152,66 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(AttnArgs a) {
     const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
     float lsum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] *= alpha;
+    for (int i = 0; i < kCols; ++i) o[i] *= alpha;
 #pragma unroll
-    for (int j = 0; j < kTile; ++j) {
+    for (int j = 0; j < kSlice; ++j) {
       const float p = s[j] == -INFINITY ? 0.f : exp2f(s[j] - m_new);
       lsum += p;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] = fmaf(p, vs[j * D + part * 32 + i], o[i]);
+      for (int i = 0; i < kCols; ++i) o[i] = fmaf(p, vt[j * D + i], o[i]);
     }
     l_run = l_run * alpha + lsum;
     m_run = m_new;
   }
-  if (q >= a.m) return;
-  // a row that saw no key (offset causal masks): O = 0, LSE = -inf
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  float* orow = static_cast<float*>(a.o_out) + bi * a.o_sb + h * a.o_sh + (int64_t)q * a.o_sr +
-                part * 32;
-#pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    f32x4 v = {o[i] * inv, o[i + 1] * inv, o[i + 2] * inv, o[i + 3] * inv};
-    *reinterpret_cast<f32x4*>(orow + i) = v;
+
+  // merge the waves' states: M = max_w m_w, L = sum_w l_w 2^(m_w - M),
+  // O = sum_w o_w 2^(m_w - M) / L
+  __syncthreads();
+  float* po = sm;
+  float* pm = sm + F32Lds<D>::PART;
+  float* pl = pm + kWaves * RW;
+  put_part(po, D, RW, wave, lane / T, part * kCols, o);
+  if (part == 0) {
+    pm[wave * RW + lane / T] = m_run;
+    pl[wave * RW + lane / T] = l_run;
   }
-  if (part == 0)
-    a.lse[((int64_t)bi * a.hq + h) * a.m + q] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  __syncthreads();
+  const int r = tid / (D / 4), c = tid % (D / 4);
+  const int qo = qb * RW + r;
+  if (tid >= F32Lds<D>::CHUNKS || qo >= a.m) return;
+  float mm = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, pm[w * RW + r]);
+  float ll = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (mm != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float e = exp2f(pm[w * RW + r] - mm);  // 0 for a wave that saw no key
+      ll = fmaf(pl[w * RW + r], e, ll);
+      acc += e * *reinterpret_cast<const f32x4*>(po + (w * RW + r) * D + 4 * c);
+    }
+  }
+  // a row that saw no key (offset causal masks): O = 0, LSE = -inf
+  const float inv = ll > 0.f ? 1.f / ll : 0.f;
+  float* orow = static_cast<float*>(a.o_out) + bi * a.o_sb + h * a.o_sh + (int64_t)qo * a.o_sr;
+  *reinterpret_cast<f32x4*>(orow + 4 * c) = acc * inv;
+  if (c == 0)
+    a.lse[((int64_t)bi * a.hq + h) * a.m + qo] = ll > 0.f ? (mm + log2f(ll)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
-// dQ: one row group per query, loop over keys
+// dQ: workgroup = RW queries of one head, keys split over the waves
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_dq_f32_kernel(AttnArgs a) {
-  constexpr int T = D / 32, QPB = 256 / T;
-  __shared__ float ks[kTile * D];
-  __shared__ float vs[kTile * D];
+__global__ __launch_bounds__(64 * kWaves) void attn_dq_f32_kernel(AttnArgs a) {
+  constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
+  float* ks = sm;
+  float* vs = sm + kStage * D;
   const int tid = threadIdx.x;
-  const int part = tid % T;
-  const int nqb = (a.m + QPB - 1) / QPB;
+  const int wave = tid / 64, lane = tid % 64, part = lane % T;
+  const int nqb = (a.m + RW - 1) / RW;
   int id = blockIdx.x;
   const int h = id % a.hq;
   id /= a.hq;
@@ -142,15 +219,15 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(AttnArgs a) {
   id /= a.b;
   const int qb = CAUSAL ? nqb - 1 - id : id;
   const int g = h / a.group;
-  const int q = qb * QPB + tid / T;
-  const int64_t qoff = bi * a.q_sb + h * a.q_sh + (int64_t)q * a.q_sr + part * 32;
-  const int64_t ooff = bi * a.o_sb + h * a.o_sh + (int64_t)q * a.o_sr + part * 32;
+  const int q = qb * RW + lane / T;
+  const int64_t qoff = bi * a.q_sb + h * a.q_sh + (int64_t)q * a.q_sr + part * kCols;
+  const int64_t ooff = bi * a.o_sb + h * a.o_sh + (int64_t)q * a.o_sr + part * kCols;
   const float* kbase = static_cast<const float*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const float* vbase = static_cast<const float*>(a.v) + bi * a.v_sb + g * a.v_sh;
-  float qr[32], dor[32], dq[32];
+  float qr[kCols], dor[kCols], dq[kCols];
   const bool live = q < a.m;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
+  for (int i = 0; i < kCols; ++i) {
     qr[i] = live ? static_cast<const float*>(a.q)[qoff + i] : 0.f;
     dor[i] = live ? static_cast<const float*>(a.dout)[ooff + i] : 0.f;
     dq[i] = 0.f;
@@ -164,131 +241,153 @@ __global__ __launch_bounds__(256) void attn_dq_f32_kernel(AttnArgs a) {
   {
     const float* orow = static_cast<const float*>(a.o) + ooff;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) dlt = fmaf(dor[i], live ? orow[i] : 0.f, dlt);
+    for (int i = 0; i < kCols; ++i) dlt = fmaf(dor[i], live ? orow[i] : 0.f, dlt);
     dlt = group_sum<T>(dlt);
-    if (live && part == 0) a.delta[ridx] = dlt;
+    if (live && part == 0 && wave == 0) a.delta[ridx] = dlt;
   }
   const float cs = a.scale_log2;
-  const int kend = CAUSAL ? min(a.n, max(0, qb * QPB + QPB + a.diag)) : a.n;
-  for (int k0 = 0; k0 < kend; k0 += kTile) {
+  const int kend = CAUSAL ? min(a.n, max(0, qb * RW + RW + a.diag)) : a.n;
+  for (int k0 = 0; k0 < kend; k0 += kStage) {
     __syncthreads();
-    stage_f32<D>(ks, kbase, a.k_sr, k0, a.n, tid, 256);
-    stage_f32<D>(vs, vbase, a.v_sr, k0, a.n, tid, 256);
+    stage_f32<D>(ks, kbase, a.k_sr, k0, a.n, tid);
+    stage_f32<D>(vs, vbase, a.v_sr, k0, a.n, tid);
     __syncthreads();
+    const int kw = k0 + wave * kSlice;
+    if (kw >= kend) continue;  // wave-uniform
+    const float* kt = ks + wave * kSlice * D + part * kCols;
+    const float* vt = vs + wave * kSlice * D + part * kCols;
 #pragma unroll 4
-    for (int j = 0; j < kTile; ++j) {
+    for (int j = 0; j < kSlice; ++j) {
       float sacc = 0.f, dpacc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        sacc = fmaf(qr[i], ks[j * D + part * 32 + i], sacc);
-        dpacc = fmaf(dor[i], vs[j * D + part * 32 + i], dpacc);
+      for (int i = 0; i < kCols; ++i) {
+        sacc = fmaf(qr[i], kt[j * D + i], sacc);
+        dpacc = fmaf(dor[i], vt[j * D + i], dpacc);
       }
       sacc = group_sum<T>(sacc);
       dpacc = group_sum<T>(dpacc);
-      const int key = k0 + j;
+      const int key = kw + j;
       const bool dead = !live || key >= a.n || (CAUSAL && key > q + a.diag);
       const float p = dead ? 0.f : exp2f(sacc * cs - lse2);
       const float ds = p * (dpacc - dlt);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) dq[i] = fmaf(ds, ks[j * D + part * 32 + i], dq[i]);
+      for (int i = 0; i < kCols; ++i) dq[i] = fmaf(ds, kt[j * D + i], dq[i]);
     }
   }
-  if (!live) return;
-  float* out = static_cast<float*>(a.dq) + qoff;
-#pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    f32x4 v = {dq[i] * a.scale, dq[i + 1] * a.scale, dq[i + 2] * a.scale, dq[i + 3] * a.scale};
-    *reinterpret_cast<f32x4*>(out + i) = v;
-  }
+  __syncthreads();
+  put_part(sm, D, RW, wave, lane / T, part * kCols, dq);
+  __syncthreads();
+  const int r = tid / (D / 4), c = tid % (D / 4);
+  const int qo = qb * RW + r;
+  if (tid >= F32Lds<D>::CHUNKS || qo >= a.m) return;
+  const f32x4 x = sum_parts<D>(sm, tid) * a.scale;
+  *reinterpret_cast<f32x4*>(static_cast<float*>(a.dq) + bi * a.q_sb + h * a.q_sh +
+                            (int64_t)qo * a.q_sr + 4 * c) = x;
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one row group per key, loop over the group's query heads and rows
+// dK, dV: workgroup = RW keys of one kv head; the group's query heads and rows
+// split over the waves
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_dkdv_f32_kernel(AttnArgs a) {
-  constexpr int T = D / 32, KPB = 256 / T;
-  __shared__ float qs[kTile * D];
-  __shared__ float dos[kTile * D];
-  __shared__ float lses[kTile];
-  __shared__ float dls[kTile];
+__global__ __launch_bounds__(64 * kWaves) void attn_dkdv_f32_kernel(AttnArgs a) {
+  constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
+  float* qs = sm;
+  float* dos = sm + kStage * D;
+  float* lses = sm + 2 * kStage * D;
+  float* dls = lses + kStage;
   const int tid = threadIdx.x;
-  const int part = tid % T;
-  const int nkb = (a.n + KPB - 1) / KPB;
+  const int wave = tid / 64, lane = tid % 64, part = lane % T;
+  const int nkb = (a.n + RW - 1) / RW;
   int id = blockIdx.x;
   const int g = id % a.hkv;
   id /= a.hkv;
   const int bi = id % a.b;
   id /= a.b;
   const int kblk = CAUSAL ? id : nkb - 1 - id;  // causal: early keys see most queries
-  const int key = kblk * KPB + tid / T;
+  const int key = kblk * RW + lane / T;
   const bool live = key < a.n;
-  const int64_t koff = bi * a.k_sb + g * a.k_sh + (int64_t)key * a.k_sr + part * 32;
-  const int64_t voff = bi * a.v_sb + g * a.v_sh + (int64_t)key * a.v_sr + part * 32;
-  float kr[32], vr[32], dk[32], dv[32];
+  const int64_t koff = bi * a.k_sb + g * a.k_sh + (int64_t)key * a.k_sr + part * kCols;
+  const int64_t voff = bi * a.v_sb + g * a.v_sh + (int64_t)key * a.v_sr + part * kCols;
+  float kr[kCols], vr[kCols], dk[kCols], dv[kCols];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
+  for (int i = 0; i < kCols; ++i) {
     kr[i] = live ? static_cast<const float*>(a.k)[koff + i] : 0.f;
     vr[i] = live ? static_cast<const float*>(a.v)[voff + i] : 0.f;
     dk[i] = 0.f;
     dv[i] = 0.f;
   }
   const float cs = a.scale_log2;
-  // first query tile holding a query that sees the block's first key
-  const int qstart = CAUSAL ? (max(0, kblk * KPB - a.diag) / kTile) * kTile : 0;
+  // first query that sees the block's first key
+  const int qstart = CAUSAL ? max(0, kblk * RW - a.diag) : 0;
   for (int hh = 0; hh < a.group; ++hh) {
     const int h = g * a.group + hh;
     const float* qbase = static_cast<const float*>(a.q) + bi * a.q_sb + h * a.q_sh;
     const float* dobase = static_cast<const float*>(a.dout) + bi * a.o_sb + h * a.o_sh;
     const int64_t rbase = ((int64_t)bi * a.hq + h) * a.m;
-    for (int q0 = qstart; q0 < a.m; q0 += kTile) {
+    for (int q0 = qstart; q0 < a.m; q0 += kStage) {
       __syncthreads();
-      stage_f32<D>(qs, qbase, a.q_sr, q0, a.m, tid, 256);
-      stage_f32<D>(dos, dobase, a.o_sr, q0, a.m, tid, 256);
-      if (tid < kTile) {
+      stage_f32<D>(qs, qbase, a.q_sr, q0, a.m, tid);
+      stage_f32<D>(dos, dobase, a.o_sr, q0, a.m, tid);
+      if (tid < kStage) {
         const bool ok = q0 + tid < a.m;
         lses[tid] = ok ? a.lse_in[rbase + q0 + tid] * kLog2e : 0.f;
         dls[tid] = ok ? a.delta[rbase + q0 + tid] : 0.f;
       }
       __syncthreads();
-#pragma unroll 4
-      for (int j = 0; j < kTile; ++j) {
+      const int qw = q0 + wave * kSlice;
+      if (qw >= a.m) continue;  // wave-uniform
+      const float* qt = qs + wave * kSlice * D + part * kCols;
+      const float* dt = dos + wave * kSlice * D + part * kCols;
+#pragma unroll 1
+      for (int j = 0; j < kSlice; ++j) {
         float sacc = 0.f, dpacc = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          sacc = fmaf(kr[i], qs[j * D + part * 32 + i], sacc);
-          dpacc = fmaf(vr[i], dos[j * D + part * 32 + i], dpacc);
+        for (int i = 0; i < kCols; ++i) {
+          sacc = fmaf(kr[i], qt[j * D + i], sacc);
+          dpacc = fmaf(vr[i], dt[j * D + i], dpacc);
         }
         sacc = group_sum<T>(sacc);
         dpacc = group_sum<T>(dpacc);
-        const int qi = q0 + j;
+        const int qi = qw + j;
         const bool dead = !live || qi >= a.m || (CAUSAL && key > qi + a.diag);
-        const float p = dead ? 0.f : exp2f(sacc * cs - lses[j]);
-        const float ds = p * (dpacc - dls[j]);
+        const int js = wave * kSlice + j;
+        const float p = dead ? 0.f : exp2f(sacc * cs - lses[js]);
+        const float ds = p * (dpacc - dls[js]);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          dv[i] = fmaf(p, dos[j * D + part * 32 + i], dv[i]);
-          dk[i] = fmaf(ds, qs[j * D + part * 32 + i], dk[i]);
+        for (int i = 0; i < kCols; ++i) {
+          dv[i] = fmaf(p, dt[j * D + i], dv[i]);
+          dk[i] = fmaf(ds, qt[j * D + i], dk[i]);
         }
       }
     }
   }
-  if (!live) return;
-  float* dko = static_cast<float*>(a.dk) + koff;
-  float* dvo = static_cast<float*>(a.dv) + voff;
-#pragma unroll
-  for (int i = 0; i < 32; i += 4) {
-    f32x4 x = {dk[i] * a.scale, dk[i + 1] * a.scale, dk[i + 2] * a.scale, dk[i + 3] * a.scale};
-    f32x4 y = {dv[i], dv[i + 1], dv[i + 2], dv[i + 3]};
-    *reinterpret_cast<f32x4*>(dko + i) = x;
-    *reinterpret_cast<f32x4*>(dvo + i) = y;
+  const int r = tid / (D / 4), c = tid % (D / 4);
+  const int ko = kblk * RW + r;
+  const bool out_ok = tid < F32Lds<D>::CHUNKS && ko < a.n;
+  __syncthreads();
+  put_part(sm, D, RW, wave, lane / T, part * kCols, dk);
+  __syncthreads();
+  if (out_ok) {
+    const f32x4 x = sum_parts<D>(sm, tid) * a.scale;
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.dk) + bi * a.k_sb + g * a.k_sh +
+                              (int64_t)ko * a.k_sr + 4 * c) = x;
+  }
+  __syncthreads();
+  put_part(sm, D, RW, wave, lane / T, part * kCols, dv);
+  __syncthreads();
+  if (out_ok) {
+    const f32x4 y = sum_parts<D>(sm, tid);
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.dv) + bi * a.v_sb + g * a.v_sh +
+                              (int64_t)ko * a.v_sr + 4 * c) = y;
   }
 }
 
 template <int D>
 hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
-  constexpr int QPB = 256 / (D / 32);
-  const dim3 grid((unsigned)((a.m + QPB - 1) / QPB) * a.hq * a.b), block(256);
+  constexpr int RW = F32Lds<D>::RW;
+  const dim3 grid((unsigned)((a.m + RW - 1) / RW) * a.hq * a.b), block(64 * kWaves);
   if (a.causal)
     FAB_TIMED("attn_fwd_f32", s, hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), grid, block, 0, s, a));
   else
@@ -298,10 +397,10 @@ hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
 
 template <int D>
 hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
-  constexpr int T = D / 32, RPB = 256 / T;
-  const dim3 block(256);
-  const dim3 gq((unsigned)((a.m + RPB - 1) / RPB) * a.hq * a.b);
-  const dim3 gk((unsigned)((a.n + RPB - 1) / RPB) * a.hkv * a.b);
+  constexpr int RW = F32Lds<D>::RW;
+  const dim3 block(64 * kWaves);
+  const dim3 gq((unsigned)((a.m + RW - 1) / RW) * a.hq * a.b);
+  const dim3 gk((unsigned)((a.n + RW - 1) / RW) * a.hkv * a.b);
   if (a.causal) {
     FAB_TIMED("attn_bwd_dq_f32", s, hipLaunchKernelGGL((attn_dq_f32_kernel<D, true>), gq, block, 0, s, a));
     FAB_TIMED("attn_bwd_dkdv_f32", s, hipLaunchKernelGGL((attn_dkdv_f32_kernel<D, true>), gk, block, 0, s, a));

@@ -118,7 +118,13 @@ def time_attention(w, steps, warmup, torch, fab_binding):
 
 def time_workload(key, reps, torch, fab):
     """Forward and backward time of another attention configuration, on
-    N(0, 1) inputs drawn on the device (torch generator seeded per tensor)."""
+    N(0, 1) inputs drawn on the device (torch generator seeded per tensor).
+
+    Outputs and workspace are allocated once and the plan's raw calls are
+    enqueued `reps` times back to back between two events (device time per
+    call, host overhead hidden); a second pass records HIP events around
+    every kernel (kernel durations alone)."""
+    from attention_fab_forward_amd import _binding as B
     from attention_fab_forward_amd.inputs import WORKLOADS
     w = WORKLOADS[key]
     gen = torch.Generator(device="cuda")
@@ -130,31 +136,53 @@ def time_workload(key, reps, torch, fab):
                            generator=gen).to(dt)
 
     q, k, v, do = draw(1, w.heads_q), draw(2, w.heads_kv), draw(3, w.heads_kv), draw(4, w.heads_q)
-    o, lse = fab.forward(q, k, v, "softmax", w.causal, w.scale())
-    grads = fab.backward(q, k, v, o, lse, do, "softmax", w.causal, w.scale())
-    del grads
+    plan = B.attention_plan(q, k, v, w.causal, w.scale())
+    o, lse = torch.empty_like(q), torch.empty((w.batch, w.heads_q, w.seq), dtype=torch.float32,
+                                              device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(plan.bwd_workspace, plan.fwd_workspace, 1), dtype=torch.uint8,
+                     device="cuda")
+    P = B._ptr
+    stream = torch.cuda.current_stream()
+    sp = B.ctypes.c_void_p(stream.cuda_stream)
+
+    def fwd():
+        plan.forward_raw(P(q), P(k), P(v), P(o), P(lse), P(ws), plan.fwd_workspace, sp)
+
+    def bwd():
+        plan.backward_raw(P(q), P(k), P(v), P(o), P(lse), P(do), P(dq), P(dk), P(dv), P(ws),
+                          plan.bwd_workspace, sp)
+
+    fwd()
+    bwd()
     torch.cuda.synchronize()
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    fms, bms = [], []
+    e[0].record(stream)
     for _ in range(reps):
-        e[0].record()
-        o, lse = fab.forward(q, k, v, "softmax", w.causal, w.scale())
-        e[1].record()
-        grads = fab.backward(q, k, v, o, lse, do, "softmax", w.causal, w.scale())
-        e[2].record()
-        torch.cuda.synchronize()
-        fms.append(e[0].elapsed_time(e[1]))
-        bms.append(e[1].elapsed_time(e[2]))
-        del grads
+        fwd()
+    e[1].record(stream)
+    for _ in range(reps):
+        bwd()
+    e[2].record(stream)
+    torch.cuda.synchronize()
+    fm, bm = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+    plan.set_timing(True)
+    plan.reset_kernel_times()
+    for _ in range(reps):
+        fwd()
+        bwd()
+    kernels = {name: tot / cnt for name, (cnt, tot) in plan.kernel_times().items()}
+    plan.set_timing(False)
     fwd_fl, bwd_fl, _ = attention_flops(w)
-    fm, bm = sorted(fms)[len(fms) // 2], sorted(bms)[len(bms) // 2]
-    del q, k, v, do, o, lse
+    del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return {"fwd_ms": fm, "bwd_ms": bm, "fwd_us": 1e3 * fm, "bwd_us": 1e3 * bm,
             "dtype": w.dtype, "fwd_tflops": fwd_fl / fm / 1e9,
             "fwd_bwd_tflops": (fwd_fl + bwd_fl) / (fm + bm) / 1e9,
             "fwd_bwd_pct_bf16_peak": 100.0 * (fwd_fl + bwd_fl) / (fm + bm) / 1e9 / BF16_PEAK_TFLOPS,
-            "reps": reps, "inputs": "N(0,1) drawn on the device, seeded per tensor"}
+            "kernels_avg_ms": kernels, "reps": reps,
+            "timing": "device time per call, calls enqueued back to back",
+            "inputs": "N(0,1) drawn on the device, seeded per tensor"}
 
 
 def kernel_flops(w):
@@ -580,7 +608,7 @@ def main():
         log("other workloads ...")
         extras["workloads"] = {
             # latency-bound (microseconds of work): reported in us
-            "attn_f32_h1_n256_d64": time_workload("attn_f32_h1_n256_d64", 51, torch, fab),
+            "attn_f32_h1_n256_d64": time_workload("attn_f32_h1_n256_d64", 200, torch, fab),
             "attn_causal_bf16_h4_n131072_d128": time_workload(
                 "attn_causal_bf16_h4_n131072_d128", 3, torch, fab),
             "attn_causal_bf16_gqa2_n1048576_d128": time_workload(

@@ -109,7 +109,8 @@ def sampled(n, seed, count=16):
 
 
 @pytest.mark.parametrize("key", ["attn_causal_bf16_h32_n32768_d128",
-                                 "attn_causal_bf16_h4_n131072_d128"])
+                                 "attn_causal_bf16_h4_n131072_d128",
+                                 "attn_causal_bf16_gqa2_n1048576_d128"])
 def test_full_size_sampled_and_identities(key):
     """Full-size backward (the benchmarked launch): exact oracle rows of dQ,
     exact late-key rows of dK / dV, and the identities over every row."""

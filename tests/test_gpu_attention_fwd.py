@@ -115,7 +115,8 @@ def sampled_rows(n, seed):
 
 
 @pytest.mark.parametrize("key", ["attn_causal_bf16_h32_n32768_d128",
-                                 "attn_causal_bf16_h4_n131072_d128"])
+                                 "attn_causal_bf16_h4_n131072_d128",
+                                 "attn_causal_bf16_gqa2_n1048576_d128"])
 def test_full_size_sampled_rows(key):
     """Full-size forward (the benchmarked launch), checked on sampled rows."""
     w = WORKLOADS[key]
