@@ -241,6 +241,28 @@ def measured_traffic(kernel):
     return None
 
 
+def measured_mfma(kernel):
+    """MFMA counters of a kernel from the committed rocprofv3 summary (median
+    dispatch): share of SIMD cycles its MFMA unit was busy, the GPU-active
+    clock, and executed bf16 MFMA flops per dispatch; None when the summary is
+    missing or was taken from different kernel sources."""
+    if kernel not in ROCPROF_NAMES:
+        return None
+    rname, src = ROCPROF_NAMES[kernel]
+    path = os.path.join(ROOT, "profiles", "attn_mlp_bf16.mfma_counters.txt")
+    if not os.path.exists(path):
+        return None
+    want = f"{src}:{source_hash(src)}"
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith(rname) and line.rstrip().endswith(want):
+                f = line[len(rname):].split()
+                # columns: dispatches, avg_ms, bf16_flops, clock_ghz, mfma_busy, mfma_util, ...
+                return {"mfma_busy": float(f[4]) / 100.0, "clock_ghz": float(f[3]),
+                        "bf16_flops_executed": float(f[2])}
+    return None
+
+
 def peak_hbm_sweep(torch, fab, exps=range(12, 21)):
     """Peak device memory of forward + backward versus n (grouped-query geometry
     of the long-context workload: 2 query heads, 1 kv head, d = 128)."""
@@ -575,7 +597,8 @@ def main():
         ach = kflops[dom] / kern[dom]["avg_ms"] / 1e9
         roof = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": ach / BF16_PEAK_TFLOPS, "traffic": measured_traffic(dom), "kernel": dom,
-                "flops_per_launch": kflops[dom], "avg_launch_ms": kern[dom]["avg_ms"]}
+                "flops_per_launch": kflops[dom], "avg_launch_ms": kern[dom]["avg_ms"],
+                "mfma_counters": measured_mfma(dom)}
     else:
         ach = kbytes[dom] / kern[dom]["avg_ms"] / 1e6
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
