@@ -263,9 +263,10 @@ def measured_mfma(kernel):
     return None
 
 
-def peak_hbm_sweep(torch, fab, exps=range(12, 21)):
-    """Peak device memory of forward + backward versus n (grouped-query geometry
-    of the long-context workload: 2 query heads, 1 kv head, d = 128)."""
+def peak_hbm_sweep(torch, fab, exps=range(12, 21), hq=2, hkv=1):
+    """Peak device memory of forward + backward versus n, causal bf16, d = 128
+    (default: the long-context geometry, 2 query heads and 1 kv head).  The
+    library allocates nothing, so torch's peak counter sees every byte."""
     out = []
     for e in exps:
         n = 1 << e
@@ -273,9 +274,9 @@ def peak_hbm_sweep(torch, fab, exps=range(12, 21)):
         torch.cuda.empty_cache()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
-        q = torch.randn(1, n, 2, 128, device="cuda", dtype=torch.bfloat16)
-        k = torch.randn(1, n, 1, 128, device="cuda", dtype=torch.bfloat16)
-        v = torch.randn(1, n, 1, 128, device="cuda", dtype=torch.bfloat16)
+        q = torch.randn(1, n, hq, 128, device="cuda", dtype=torch.bfloat16)
+        k = torch.randn(1, n, hkv, 128, device="cuda", dtype=torch.bfloat16)
+        v = torch.randn(1, n, hkv, 128, device="cuda", dtype=torch.bfloat16)
         do = torch.randn_like(q)
         o, lse = fab.forward(q, k, v, "softmax", True)
         fwd_peak = torch.cuda.max_memory_allocated() - base
@@ -293,7 +294,7 @@ def peak_hbm_sweep(torch, fab, exps=range(12, 21)):
     a = my - b * mn
     resid = max(abs(y - (a + b * x)) / y for x, y in zip(ns, ys))
     ratios = [ys[i + 1] / ys[i] for i in range(len(ys) - 1)]
-    return {"geometry": "causal, 2 query heads / 1 kv head, d=128, bf16, fwd+bwd",
+    return {"geometry": f"causal, {hq} query heads / {hkv} kv heads, d=128, bf16, fwd+bwd",
             "points": out, "bytes_per_token": b, "max_rel_residual_linear_fit": resid,
             "doubling_ratios": ratios}
 
@@ -627,6 +628,9 @@ def main():
     if "sweep" in want:
         log("peak-memory sweep ...")
         extras["peak_hbm_vs_seq"] = peak_hbm_sweep(torch, fab)
+        # the sequence-parallel rank share's geometry (4 heads), up to its
+        # full n = 2^17
+        extras["peak_hbm_vs_seq_rank_share"] = peak_hbm_sweep(torch, fab, range(12, 18), 4, 4)
     if "workloads" in want:
         log("other workloads ...")
         extras["workloads"] = {
