@@ -301,6 +301,15 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
   if (q.m > kMaxRows || q.n > kMaxRows || q.batch * q.heads_a > (1 << 20))
     return fail(FAB_ERR_UNSUPPORTED, "sizes beyond this build's limits (rows <= 2^30, "
                 "batch*heads <= 2^20)");
+  if (q.f == FAB_F_SOFTMAX) {
+    // the largest grids (fp32 kernels: 4 rows per workgroup at d = 128;
+    // per-row kernels: 16 rows per workgroup) stay below 2^31 workgroups
+    const int64_t rows = std::max(q.m, q.n);
+    if (rows > ((((int64_t)1 << 33) - 1) / (q.batch * q.heads_a)))
+      return fail(FAB_ERR_UNSUPPORTED, "batch * heads_a * max(m, n) = %lld * %lld * %lld is beyond "
+                  "this build's limit of 2^33 rows (kernel grids would exceed 2^31 workgroups)",
+                  (long long)q.batch, (long long)q.heads_a, (long long)rows);
+  }
   if (!std::isfinite(q.scale)) return fail(FAB_ERR_BAD_SHAPE, "scale must be finite");
   if (q.q_offset < -((int64_t)1 << 40) || q.q_offset > ((int64_t)1 << 40) ||
       q.k_offset < -((int64_t)1 << 40) || q.k_offset > ((int64_t)1 << 40))

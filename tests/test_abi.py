@@ -59,6 +59,11 @@ def status_of(prob):
     ({"m": 100, "n": 300, "q_offset": 200}, "FAB_OK"),
     ({"k_offset": -5, "q_offset": 7}, "FAB_OK"),
     ({"q_offset": 1 << 41}, "FAB_ERR_BAD_SHAPE"),
+    # grids of 2^31 workgroups or more are refused at plan time
+    ({"batch": 1 << 10, "heads_a": 1 << 10, "heads_bc": 1 << 10, "m": 1 << 13, "n": 1 << 13},
+     "FAB_ERR_UNSUPPORTED"),
+    ({"batch": 1 << 10, "heads_a": 1 << 10, "heads_bc": 1 << 10, "m": (1 << 13) - 1,
+      "n": (1 << 13) - 1}, "FAB_OK"),
     ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "q_offset": 3},
      "FAB_ERR_UNSUPPORTED"),
     ({"k": 96, "p": 96}, "FAB_ERR_UNSUPPORTED"),
