@@ -210,6 +210,10 @@ ROCPROF_NAMES = {
     "attn_bwd_dkdv_bf16": ("attn_dkdv_bf16_kernel<128, true, true>", "attn_bwd.hip"),
     "attn_bwd_dq_bf16": ("attn_dq_bf16_kernel<128, true, 1, true>", "attn_bwd.hip"),
     "attn_bwd_prep": ("attn_bwd_prep_bf16_kernel<128>", "attn_bwd.hip"),
+    "mlp_fwd": ("mlp_fwd_kernel<1024, 1024>", "mlp.hip"),
+    "mlp_bwd_da": ("mlp_bwd_da_kernel<1024, 1024>", "mlp.hip"),
+    "mlp_bwd_dbt": ("mlp_bwd_col_kernel<1024, 1024, true>", "mlp.hip"),
+    "mlp_bwd_dc": ("mlp_bwd_col_kernel<1024, 1024, false>", "mlp.hip"),
 }
 
 
@@ -487,9 +491,13 @@ def time_mlp(steps, warmup, torch, fab_binding):
     step_ms = sum(v[1] for v in kernels.values()) / steps
     gemm = 2 * m * k * n
     fwd_fl, bwd_fl = 2 * gemm, 5 * gemm
+    fwd_tf, step_tf = fwd_fl / fwd_ms / 1e9, (fwd_fl + bwd_fl) / step_ms / 1e9
     return {"workload": MLP_WORKLOAD, "fwd_ms": fwd_ms, "fwd_bwd_ms": step_ms,
-            "fwd_tflops": fwd_fl / fwd_ms / 1e9, "fwd_bwd_tflops": (fwd_fl + bwd_fl) / step_ms / 1e9,
-            "kernels_avg_ms": {k_: v[1] / v[0] for k_, v in kernels.items()}}
+            "fwd_tflops": fwd_tf, "fwd_bwd_tflops": step_tf,
+            "fwd_pct_bf16_peak": 100.0 * fwd_tf / BF16_PEAK_TFLOPS,
+            "fwd_bwd_pct_bf16_peak": 100.0 * step_tf / BF16_PEAK_TFLOPS,
+            "kernels_avg_ms": {k_: v[1] / v[0] for k_, v in kernels.items()},
+            "mfma_counters": {k_: measured_mfma(k_) for k_ in kernels if measured_mfma(k_)}}
 
 
 def cpu_baseline(w, x, seconds):
