@@ -130,3 +130,48 @@ def test_full_size_sampled_and_identities(key):
                                          keys)
         assert_close(f"dK head {g}", dk[0, keys, g], rk, "bf16")
         assert_close(f"dV head {g}", dv[0, keys, g], rv, "bf16")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_strided_views_backward(dtype, d, causal):
+    """Q, K, V as views of one fused [b, n, h, 3, d] projection (row stride
+    3 h d, unlike O and dO, packed at h d), and a grouped-query case whose K and
+    V have different row strides (K contiguous, V a view of a [b, n, hkv, 2, d]
+    tensor): the kernel variants for unequal strides.  Gradients take the
+    layouts of their primal views."""
+    import attention_fab_forward_amd as fab
+    b, n, h = 2, 300, 3
+    big = random_array(101, (b, n, h, 3, d), 1.0, dtype)
+    do = random_array(102, (b, n, h, d), 1.0, dtype)
+    t = to_device(big, dtype)
+    q, k, v = t[:, :, :, 0], t[:, :, :, 1], t[:, :, :, 2]
+    assert q.stride(1) == 3 * h * d
+    sc = float(np.float32(d ** -0.5))
+    o, lse = fab.forward(q, k, v, "softmax", causal, sc)
+    dq, dk, dv = fab.backward(q, k, v, o, lse, to_device(do, dtype), "softmax", causal, sc)
+    assert dq.stride() == q.stride() and dk.stride() == k.stride()
+    rq, rk, rv = attention_backward(big[:, :, :, 0], big[:, :, :, 1], big[:, :, :, 2], do, sc,
+                                    causal)
+    zs = float(np.abs(rv).max())
+    assert_close("dQ", to_host(dq), rq, dtype, zero_scale=zs)
+    assert_close("dK", to_host(dk), rk, dtype, zero_scale=zs)
+    assert_close("dV", to_host(dv), rv, dtype)
+
+    hq, hkv = 4, 2
+    qg = random_array(103, (b, n, hq, d), 1.0, dtype)
+    kg = random_array(104, (b, n, hkv, d), 1.0, dtype)
+    kvbig = random_array(105, (b, n, hkv, 2, d), 1.0, dtype)
+    vg = kvbig[:, :, :, 1]
+    dog = random_array(106, (b, n, hq, d), 1.0, dtype)
+    vt = to_device(kvbig, dtype)[:, :, :, 1]
+    qt, kt = to_device(qg, dtype), to_device(kg, dtype)
+    assert vt.stride(1) != kt.stride(1)
+    o, lse = fab.forward(qt, kt, vt, "softmax", causal, sc)
+    dq, dk, dv = fab.backward(qt, kt, vt, o, lse, to_device(dog, dtype), "softmax", causal, sc)
+    assert dv.stride() == vt.stride()
+    rq, rk, rv = attention_backward(qg, kg, vg, dog, sc, causal)
+    zs = float(np.abs(rv).max())
+    assert_close("dQ (GQA, V strided)", to_host(dq), rq, dtype, zero_scale=zs)
+    assert_close("dK (GQA, V strided)", to_host(dk), rk, dtype, zero_scale=zs)
+    assert_close("dV (GQA, V strided)", to_host(dv), rv, dtype)
