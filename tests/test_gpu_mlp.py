@@ -78,3 +78,13 @@ def test_zero_weights_special_case():
     assert float(o.abs().max()) == 0 and float(da.abs().max()) == 0 and float(dc.abs().max()) == 0
     ref = 0.5 * 0.9 * (do.astype(np.float64) @ c.T.astype(np.float64)).T @ a.astype(np.float64)
     assert_close("dBt", to_host(dbt), ref, "bf16")
+
+
+@pytest.mark.parametrize("k", [128, 256, 512, 1024])
+@pytest.mark.parametrize("p", [128, 256, 512, 1024])
+def test_every_supported_width_pair(k, p):
+    """Each (k, p) pair the library instantiates, at small ragged m and n."""
+    m, n = 77, 45
+    x = {"a": random_array(111, (m, k), 0.1, "bf16"), "bt": random_array(112, (n, k), 0.1, "bf16"),
+         "c": random_array(113, (n, p), 0.1, "bf16"), "do": random_array(114, (m, p), 1.0, "bf16")}
+    check(x, 1.0)
