@@ -201,18 +201,18 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Backward: one launch holds the dQ workgroups and the dK/dV workgroups (they
+// are independent), so the two run side by side.
 // dQ: workgroup = RW queries of one head, keys split over the waves
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kWaves) void attn_dq_f32_kernel(AttnArgs a) {
+__device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm) {
   constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
-  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
   float* ks = sm;
   float* vs = sm + kStage * D;
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, part = lane % T;
   const int nqb = (a.m + RW - 1) / RW;
-  int id = blockIdx.x;
   const int h = id % a.hq;
   id /= a.hq;
   const int bi = id % a.b;
@@ -236,14 +236,14 @@ __global__ __launch_bounds__(64 * kWaves) void attn_dq_f32_kernel(AttnArgs a) {
   const float lse2 = live ? a.lse_in[ridx] * kLog2e : 0.f;
   // D = rowsum(dO * O), accumulated in the same lane split and order as the
   // dP dot products below, so that a row whose exact dS vanishes (a query that
-  // sees a single key) gets dP - D = 0 exactly.  Written for the dK/dV kernel.
+  // sees a single key) gets dP - D = 0 exactly.  The dK/dV workgroups form the
+  // same value the same way.
   float dlt = 0.f;
   {
     const float* orow = static_cast<const float*>(a.o) + ooff;
 #pragma unroll
     for (int i = 0; i < kCols; ++i) dlt = fmaf(dor[i], live ? orow[i] : 0.f, dlt);
     dlt = group_sum<T>(dlt);
-    if (live && part == 0 && wave == 0) a.delta[ridx] = dlt;
   }
   const float cs = a.scale_log2;
   const int kend = CAUSAL ? min(a.n, max(0, qb * RW + RW + a.diag)) : a.n;
@@ -290,9 +290,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_dq_f32_kernel(AttnArgs a) {
 // split over the waves
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kWaves) void attn_dkdv_f32_kernel(AttnArgs a) {
+__device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* sm) {
   constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
-  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
   float* qs = sm;
   float* dos = sm + kStage * D;
   float* lses = sm + 2 * kStage * D;
@@ -300,7 +299,6 @@ __global__ __launch_bounds__(64 * kWaves) void attn_dkdv_f32_kernel(AttnArgs a) 
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64, part = lane % T;
   const int nkb = (a.n + RW - 1) / RW;
-  int id = blockIdx.x;
   const int g = id % a.hkv;
   id /= a.hkv;
   const int bi = id % a.b;
@@ -325,6 +323,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_dkdv_f32_kernel(AttnArgs a) 
     const int h = g * a.group + hh;
     const float* qbase = static_cast<const float*>(a.q) + bi * a.q_sb + h * a.q_sh;
     const float* dobase = static_cast<const float*>(a.dout) + bi * a.o_sb + h * a.o_sh;
+    const float* obase = static_cast<const float*>(a.o) + bi * a.o_sb + h * a.o_sh;
     const int64_t rbase = ((int64_t)bi * a.hq + h) * a.m;
     for (int q0 = qstart; q0 < a.m; q0 += kStage) {
       __syncthreads();
@@ -333,7 +332,22 @@ __global__ __launch_bounds__(64 * kWaves) void attn_dkdv_f32_kernel(AttnArgs a) 
       if (tid < kStage) {
         const bool ok = q0 + tid < a.m;
         lses[tid] = ok ? a.lse_in[rbase + q0 + tid] * kLog2e : 0.f;
-        dls[tid] = ok ? a.delta[rbase + q0 + tid] : 0.f;
+      }
+      __syncthreads();
+      // D of the staged rows: T lanes per row, each summing dO * O over its
+      // kCols columns in order, then the lane exchange -- the dQ workgroups'
+      // split and order, so both get the same value
+#pragma unroll
+      for (int r0 = 0; r0 < kStage; r0 += 64 * kWaves / T) {
+        const int r = r0 + tid / T;
+        const bool ok = q0 + r < a.m;
+        const float* drow = dos + r * D + part * kCols;
+        const float* orow = obase + (int64_t)(q0 + r) * a.o_sr + part * kCols;
+        float dl = 0.f;
+#pragma unroll
+        for (int i = 0; i < kCols; ++i) dl = fmaf(drow[i], ok ? orow[i] : 0.f, dl);
+        dl = group_sum<T>(dl);
+        if (part == 0) dls[r] = dl;
       }
       __syncthreads();
       const int qw = q0 + wave * kSlice;
@@ -395,19 +409,26 @@ hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kWaves) void attn_bwd_f32_kernel(AttnArgs a, int nq) {
+  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
+  if ((int)blockIdx.x < nq)
+    dq_f32_body<D, CAUSAL>(a, (int)blockIdx.x, sm);
+  else
+    dkdv_f32_body<D, CAUSAL>(a, (int)blockIdx.x - nq, sm);
+}
+
 template <int D>
 hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   constexpr int RW = F32Lds<D>::RW;
   const dim3 block(64 * kWaves);
-  const dim3 gq((unsigned)((a.m + RW - 1) / RW) * a.hq * a.b);
-  const dim3 gk((unsigned)((a.n + RW - 1) / RW) * a.hkv * a.b);
-  if (a.causal) {
-    FAB_TIMED("attn_bwd_dq_f32", s, hipLaunchKernelGGL((attn_dq_f32_kernel<D, true>), gq, block, 0, s, a));
-    FAB_TIMED("attn_bwd_dkdv_f32", s, hipLaunchKernelGGL((attn_dkdv_f32_kernel<D, true>), gk, block, 0, s, a));
-  } else {
-    FAB_TIMED("attn_bwd_dq_f32", s, hipLaunchKernelGGL((attn_dq_f32_kernel<D, false>), gq, block, 0, s, a));
-    FAB_TIMED("attn_bwd_dkdv_f32", s, hipLaunchKernelGGL((attn_dkdv_f32_kernel<D, false>), gk, block, 0, s, a));
-  }
+  const int nq = (a.m + RW - 1) / RW * a.hq * a.b;
+  const int nk = (a.n + RW - 1) / RW * a.hkv * a.b;
+  const dim3 grid((unsigned)(nq + nk));
+  if (a.causal)
+    FAB_TIMED("attn_bwd_f32", s, hipLaunchKernelGGL((attn_bwd_f32_kernel<D, true>), grid, block, 0, s, a, nq));
+  else
+    FAB_TIMED("attn_bwd_f32", s, hipLaunchKernelGGL((attn_bwd_f32_kernel<D, false>), grid, block, 0, s, a, nq));
   return hipGetLastError();
 }
 

@@ -336,9 +336,10 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
       return fail(FAB_ERR_UNSUPPORTED, "softmax head dim %lld not in {64, 128}", (long long)q.k);
     if (!(q.scale > 0.f)) return fail(FAB_ERR_UNSUPPORTED, "softmax scale must be > 0");
     tmp.fwd_ws = 0;
-    // per query row: delta (both paths) and LSE * log2(e) (bf16 path)
+    // bf16 path: -D and LSE * log2(e) per query row; the fp32 path forms D
+    // inside its backward kernel and needs no workspace
     const size_t rows = (size_t)q.batch * q.heads_a * q.m;
-    tmp.bwd_ws = round_up(rows * sizeof(float) * (q.dtype == FAB_BF16 ? 2 : 1), 256);
+    tmp.bwd_ws = q.dtype == FAB_BF16 ? round_up(rows * sizeof(float) * 2, 256) : 0;
     if (q.dtype == FAB_BF16)
       snprintf(tmp.desc, sizeof tmp.desc,
                "attention %s d=%lld %s group=%lld fwd[BM=%d BN=%d grid=%lld] "
@@ -506,8 +507,11 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, c
       return fail(FAB_ERR_ALIGNMENT, "fab_backward: lse must be 4-byte aligned");
     fab::AttnArgs a = attn_args(plan);
     a.q = A, a.k = Bt, a.v = C, a.o = O, a.lse_in = lse, a.dout = dO;
-    a.dq = dA, a.dk = dBt, a.dv = dC, a.delta = static_cast<float*>(workspace);
-    a.lse2 = a.delta + (size_t)q.batch * q.heads_a * q.m;
+    a.dq = dA, a.dk = dBt, a.dv = dC;
+    if (q.dtype == FAB_BF16) {  // the fp32 path uses no workspace
+      a.delta = static_cast<float*>(workspace);
+      a.lse2 = a.delta + (size_t)q.batch * q.heads_a * q.m;
+    }
     e = q.dtype == FAB_BF16 ? fab::launch_attn_bwd_bf16(a, (int)q.k, s)
                             : fab::launch_attn_bwd_f32(a, (int)q.k, s);
   } else {

@@ -88,6 +88,8 @@ def test_plan_workspace_and_describe():
     assert p.fwd_workspace == 0
     assert p.bwd_workspace >= 4 * 256 * 4
     assert "attention bf16 d=128 causal" in p.describe()
+    # the fp32 backward forms D inside its kernel: no workspace
+    assert B.Plan(attn(dtype=B.F32, k=64, p=64)).bwd_workspace == 0
 
 
 def test_null_and_alignment_errors_before_any_launch():
