@@ -28,7 +28,7 @@ struct AttnArgs {
   void* dq;           // layout of Q
   void* dk;           // layout of K
   void* dv;           // layout of V
-  float* delta;       // workspace [b, hq, m] (bf16 path): -rowsum(dO * O)
+  float* delta;       // workspace [b, hq, m]: rowsum(dO * O); negated on the bf16 path
   float* lse2;        // workspace [b, hq, m] (bf16 path): LSE * log2(e)
   int64_t q_sb, q_sh, q_sr;
   int64_t k_sb, k_sh, k_sr;
