@@ -144,9 +144,10 @@ __device__ __forceinline__ void issue_vec64(const float* src, int i0, int count,
 // served by a pair of waves with split roles, so that each wave's registers
 // (one 32-key accumulator, one operand set) leave room for two waves per SIMD:
 //  * P wave (waves 0-3): holds K; S = Q K^T, P = exp2(S scale log2e - LSE
-//    log2e); hands P (fp32) to its partner through LDS; dV^T += dO^T P.
-//  * dS wave (waves 4-7): holds V; dP - D = dO V^T - D; dS = P (dP - D);
-//    dK^T += Q^T dS.
+//    log2e); hands P (bf16, as its dV products take it) to its partner
+//    through LDS; dV^T += dO^T P.
+//  * dS wave (waves 4-7): holds V; dP - D = dO V^T - D; dS = P (dP - D) with
+//    the bf16 P; dK^T += Q^T dS.
 // Query blocks of 64 (all query heads of the group) stream through two LDS
 // stages; each step has two barriers: P written -> P read, and end of step
 // (stage and P buffer released).
@@ -160,8 +161,8 @@ struct DkdvLds {
   static constexpr int LSE = 2 * BwdCfg<D>::TBYTES;    // LSE * log2(e), 64 floats
   static constexpr int DLT = LSE + 256;                // -D, 64 floats
   static constexpr int STAGE = DLT + 256;
-  static constexpr int PX = 2 * STAGE;                 // P exchange: [group][sq][j][lane] f32x4
-  static constexpr int PX_GROUP = 2 * 4 * 64 * 16;     // 8 KiB per 32-key group
+  static constexpr int PX = 2 * STAGE;                 // P exchange: [group][sq][c][lane] 8 x bf16
+  static constexpr int PX_GROUP = 2 * 2 * 64 * 16;     // 4 KiB per 32-key group
   static constexpr int BYTES = PX + 4 * PX_GROUP;
 };
 
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   for (int t = 0; t < C::DT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-  f32x4* px = reinterpret_cast<f32x4*>(smem + L::PX + kg * L::PX_GROUP) + lane;
+  u32x4* px = reinterpret_cast<u32x4*>(smem + L::PX + kg * L::PX_GROUP) + lane;
   wait_vmem();
   lds_barrier();
 
@@ -295,10 +296,12 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
             f32x4 p;
 #pragma unroll
             for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[sq][4 * j + e], cs, -lse2[e]));
-            px[(4 * sq + j) * 64] = p;
             pb[sq][j >> 1][2 * (j & 1)] = pack_bf16(p[0], p[1]);
             pb[sq][j >> 1][2 * (j & 1) + 1] = pack_bf16(p[2], p[3]);
           }
+          // P goes to the partner in the bf16 form the dV products use
+          px[(2 * sq) * 64] = pb[sq][0];
+          px[(2 * sq + 1) * 64] = pb[sq][1];
         }
       }
       lds_barrier();  // P visible to the dS waves
@@ -345,13 +348,16 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
       if (work) {
 #pragma unroll
         for (int sq = 0; sq < 2; ++sq) {
+          // dS = P (dP - D) with the partner's bf16 P; slot pair (8 c + 2 w,
+          // 8 c + 2 w + 1) in word w of chunk c
           u32x4 db[2];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 p = px[(4 * sq + j) * 64];
-            db[j >> 1][2 * (j & 1)] = pack_bf16(p[0] * dp[sq][4 * j], p[1] * dp[sq][4 * j + 1]);
-            db[j >> 1][2 * (j & 1) + 1] =
-                pack_bf16(p[2] * dp[sq][4 * j + 2], p[3] * dp[sq][4 * j + 3]);
+          for (int c = 0; c < 2; ++c) {
+            const u32x4 pv = px[(2 * sq + c) * 64];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              db[c][w] = pack_bf16(bf16_lo(pv[w]) * dp[sq][8 * c + 2 * w],
+                                   bf16_hi(pv[w]) * dp[sq][8 * c + 2 * w + 1]);
           }
           // raised priority while issuing dK, as for dQ (the dS wave has just
           // finished its VALU work; its partner's dV products wait)
