@@ -88,3 +88,26 @@ def test_every_supported_width_pair(k, p):
     x = {"a": random_array(111, (m, k), 0.1, "bf16"), "bt": random_array(112, (n, k), 0.1, "bf16"),
          "c": random_array(113, (n, p), 0.1, "bf16"), "do": random_array(114, (m, p), 1.0, "bf16")}
     check(x, 1.0)
+
+
+def mlp_cases(count=24, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        k = int(rng.choice([128, 256, 512, 1024]))
+        p = int(rng.choice([128, 256, 512, 1024]))
+        m = int(rng.integers(1, 1500))
+        n = int(rng.integers(1, 1500))
+        sigma = float(rng.choice([0.02, 0.1, 0.3]))
+        scale = float(np.float32(rng.uniform(0.25, 2.0)))
+        out.append((i, m, n, k, p, sigma, scale))
+    return out
+
+
+@pytest.mark.parametrize("i,m,n,k,p,sigma,scale", mlp_cases())
+def test_random_shape(i, m, n, k, p, sigma, scale):
+    x = {"a": random_array(2000 + 4 * i, (m, k), sigma, "bf16"),
+         "bt": random_array(2001 + 4 * i, (n, k), sigma, "bf16"),
+         "c": random_array(2002 + 4 * i, (n, p), sigma, "bf16"),
+         "do": random_array(2003 + 4 * i, (m, p), 1.0, "bf16")}
+    check(x, scale)
