@@ -196,7 +196,7 @@ attn_fwd_bf16_kernel(AttnArgs a) {
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-    lds_mfma_pipeline<2 * C::DC, 4>(
+    lds_mfma_pipeline<2 * C::DC, 6>(
         [&](int i) {
           const int row = 32 * (i % 2) + lq;
           return lds16(kt + row * C::RB + 16 * k_swz<D>(row, 2 * (i / 2) + lg));
@@ -264,7 +264,7 @@ attn_fwd_bf16_kernel(AttnArgs a) {
     // raised wave priority while issuing PV: the group that has finished its
     // softmax gets the MFMA pipe before the other group's S products
     __builtin_amdgcn_s_setprio(2);
-    lds_mfma_pipeline<4 * C::DT, 4>(
+    lds_mfma_pipeline<4 * C::DT, 6>(
         [&](int i) {
           const int t = i % C::DT, sb = i / C::DT / 2, c = (i / C::DT) % 2;
           const int dcol = 32 * t + tr_d;    // first of the 4 d columns this lane addresses
