@@ -1,11 +1,11 @@
-// Softmax attention in fp32 (forward and backward), plus the backward
-// preprocessing kernel (D = rowsum(dO * O)) used by the bf16 path.
+// Softmax attention in fp32: one forward kernel and one backward launch (dQ
+// and dK/dV workgroups side by side).
 //
 // The fp32 path keeps every operation in fp32 FMA arithmetic (no reduced
 // precision step anywhere), as the fp32 workload asks.  Its intended sizes are
-// small and latency-bound, so it uses plain VALU FMA: T = D/16 lanes share one
-// row (query or key), each owning 16 of its D columns, and dot products are
-// finished with lane exchanges.  Key/value (or query/dO) stages are staged in
+// small and latency-bound, so it uses plain VALU FMA: T = D/8 lanes share one
+// row (query or key), each owning 8 of its D columns, and dot products are
+// finished with lane exchanges.  Key/value (or query/dO) rows are staged in
 // LDS and read by broadcast; the loop over them is split across the waves of
 // a workgroup (see below), which keeps the serial chain per lane short.
 //
