@@ -27,14 +27,13 @@ namespace {
 // kernel), each owning kCols of its D columns; a wave holds RW = 64 / T rows and
 // a workgroup is one wave-width of rows served by NW waves.  The loop over the
 // other side (keys, or queries) runs in stages of SUP = NW * KS rows staged
-// in LDS by the whole workgroup; wave w takes rows w KS .. w KS + KS - 1 of
-// each stage, so the serial work per lane is 1 / NW of the loop.  The waves'
+// in LDS by the whole workgroup (KS = 32 at d = 64, 16 at d = 128: a stage
+// fills about 130 KiB); wave w takes rows w KS .. w KS + KS - 1 of each
+// stage, so the serial work per lane is 1 / NW of the loop.  The waves'
 // partial results are combined through LDS at the end (softmax states merged
 // by their maxima, gradients summed).
 constexpr int kCols = 8;    // columns of a row per lane
 constexpr int kWaves = 8;   // NW
-constexpr int kSlice = 16;  // KS: rows of a stage per wave
-constexpr int kStage = kWaves * kSlice;
 
 template <int T>
 __device__ __forceinline__ float group_sum(float v) {
@@ -45,12 +44,19 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Stage rows [r0, r0 + kStage) of a [rows, D] fp32 matrix (row stride sr) into
+// Rows of a stage per wave (KS) and per workgroup (SUP).
+template <int D>
+struct F32Stage {
+  static constexpr int SLICE = D == 64 ? 32 : 16;
+  static constexpr int ROWS = kWaves * SLICE;
+};
+
+// Stage rows [r0, r0 + SUP) of a [rows, D] fp32 matrix (row stride sr) into
 // LDS (packed rows of D floats); rows >= nrows are zero.
 template <int D>
 __device__ __forceinline__ void stage_f32(float* dst, const float* src, int64_t sr, int r0,
                                           int nrows, int tid) {
-  constexpr int V4 = D / 4;
+  constexpr int V4 = D / 4, kStage = F32Stage<D>::ROWS;
   for (int i = tid; i < kStage * V4; i += 64 * kWaves) {
     const int r = i / V4, c = i % V4;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -66,7 +72,7 @@ struct F32Lds {
   static constexpr int T = D / kCols;
   static constexpr int RW = 64 / T;
   static constexpr int CHUNKS = RW * D / 4;  // float4 chunks of an RW x D block
-  static constexpr int STAGE = 2 * kStage * D + 2 * kStage;
+  static constexpr int STAGE = 2 * F32Stage<D>::ROWS * D + 2 * F32Stage<D>::ROWS;
   static constexpr int PART = kWaves * RW * D;
   static constexpr int FLOATS = STAGE > PART + 2 * kWaves * RW ? STAGE : PART + 2 * kWaves * RW;
 };
@@ -98,6 +104,7 @@ __device__ __forceinline__ void put_part(float* part, int D, int RW, int w, int 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
   constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  constexpr int kSlice = F32Stage<D>::SLICE, kStage = F32Stage<D>::ROWS;
   static_assert(F32Lds<D>::CHUNKS <= 64 * kWaves, "one float4 of the output block per thread");
   __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
   float* ks = sm;
@@ -208,6 +215,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm) {
   constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  constexpr int kSlice = F32Stage<D>::SLICE, kStage = F32Stage<D>::ROWS;
   float* ks = sm;
   float* vs = sm + kStage * D;
   const int tid = threadIdx.x;
@@ -292,6 +300,7 @@ __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* sm) {
   constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  constexpr int kSlice = F32Stage<D>::SLICE, kStage = F32Stage<D>::ROWS;
   float* qs = sm;
   float* dos = sm + kStage * D;
   float* lses = sm + 2 * kStage * D;
