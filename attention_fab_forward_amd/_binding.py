@@ -229,6 +229,71 @@ def _strides4(t):
     return (t.stride(0), t.stride(2), t.stride(1))
 
 
+def _distinct(t):
+    """True when no two elements of t share an address (the library's test:
+    sorted by stride, each dimension of size > 1 steps past the span of the
+    smaller ones)."""
+    span = 0
+    for stride, size in sorted((st, sz) for st, sz in zip(t.stride(), t.shape) if sz > 1):
+        if stride <= span:
+            return False
+        span += (size - 1) * stride
+    return True
+
+
+def _shape(t, name, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def attention_shapes(q, k, v):
+    """(b, m, hq, hkv, n, d, dv) of Q [b, m, hq, d], K [b, n, hkv, d],
+    V [b, n, hkv, dv]; ValueError when K and V do not fit Q."""
+    b, m, hq, d = _shape(q, "q", 4)
+    bk, n, hkv, dk = _shape(k, "k", 4)
+    bv, nv, hv, dv = _shape(v, "v", 4)
+    if bk != b or bv != b:
+        raise ValueError(f"q, k, v batch sizes differ: {b}, {bk}, {bv}")
+    if (nv, hv) != (n, hkv):
+        raise ValueError(f"v {tuple(v.shape)} must have k's sequence length and heads "
+                         f"({n}, {hkv})")
+    if dk != d:
+        raise ValueError(f"k's head dim {dk} differs from q's {d}")
+    if hkv < 1 or hq % hkv:
+        raise ValueError(f"query heads {hq} are not a multiple of kv heads {hkv}")
+    return b, m, hq, hkv, n, d, dv
+
+
+def attention_grad_shapes(q, k, v, o, lse, do):
+    """attention_shapes, plus O and dO [b, m, hq, dv] and LSE [b, hq, m]."""
+    b, m, hq, hkv, n, d, dv = attention_shapes(q, k, v)
+    want = (b, m, hq, dv)
+    if _shape(o, "o", 4) != want:
+        raise ValueError(f"o has shape {tuple(o.shape)}, expected {want}")
+    if _shape(do, "do", 4) != want:
+        raise ValueError(f"do has shape {tuple(do.shape)}, expected {want}")
+    if _shape(lse, "lse", 3) != (b, hq, m):
+        raise ValueError(f"lse has shape {tuple(lse.shape)}, expected {(b, hq, m)}")
+    return b, m, hq, hkv, n, d, dv
+
+
+def mlp_shapes(a, bt, c, do=None):
+    """(m, k, n, p) of A [m, k], Bt [n, k], C [n, p] (and dO [m, p])."""
+    m, k = _shape(a, "a", 2)
+    n, kb = _shape(bt, "bt", 2)
+    nc, p = _shape(c, "c", 2)
+    if kb != k:
+        raise ValueError(f"bt [n, k] has k = {kb}, a has k = {k}")
+    if nc != n:
+        raise ValueError(f"c [n, p] has n = {nc}, bt has n = {n}")
+    if do is not None and _shape(do, "do", 2) != (m, p):
+        raise ValueError(f"do has shape {tuple(do.shape)}, expected {(m, p)}")
+    return m, k, n, p
+
+
 def _get_plan(key, build):
     plan = _plans.get(key)
     if plan is None:
@@ -282,6 +347,7 @@ def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offse
     """
     dev, dt = a.device, a.dtype
     if f == "softmax":
+        attention_shapes(a, bt, c)
         for name, t in (("q", a), ("k", bt), ("v", c)):
             _check_tensor(name, t, 4, dev, dt)
         if scale is None:
@@ -305,6 +371,7 @@ def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offse
             raise ValueError("GeLU takes no causal mask")
         if out is not None:
             raise ValueError("out= is for softmax only")
+        mlp_shapes(a, bt, c)
         for name, t in (("a", a), ("bt", bt), ("c", c)):
             _check_tensor(name, t, 2, dev, dt)
         scale = 1.0 if scale is None else scale
@@ -324,21 +391,26 @@ def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None, q_offs
     """Gradients (dA, dBt, dC) of <dO, O> for the forward above.  Over a key
     range (offsets) pass the merged O and LSE of all keys: dA is then the
     range's contribution to dQ.  O may have any layout (dO must share it);
-    the gradients take the layouts of A, Bt and C."""
+    the gradients take the layouts of A, Bt and C.  A primal whose layout
+    maps two elements to one address (say K expanded over heads) is replaced
+    by a packed copy first, and its gradient comes back packed."""
     dev, dt = a.device, a.dtype
     if f == "softmax":
+        if lse is None:
+            raise ValueError("lse must be the contiguous float32 tensor from forward()")
+        attention_grad_shapes(a, bt, c, o, lse, do)
         for name, t in (("q", a), ("k", bt), ("v", c), ("o", o), ("do", do)):
             _check_tensor(name, t, 4, dev, dt)
-        if lse is None or lse.dtype != torch.float32 or not lse.is_contiguous():
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != dev:
             raise ValueError("lse must be the contiguous float32 tensor from forward()")
         if do.stride() != o.stride():
             raise ValueError("dO must have the layout of O")
         if scale is None:
             scale = 1.0 / float(a.shape[3]) ** 0.5
-        if tuple(o.shape) != (a.shape[0], a.shape[1], a.shape[2], c.shape[3]):
-            raise ValueError("O must have shape [b, m, hq, d]")
+        a, bt, c = (t if _distinct(t) else t.contiguous() for t in (a, bt, c))
         plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset, o)
     elif f == "gelu":
+        mlp_shapes(a, bt, c, do)
         for name, t in (("a", a), ("bt", bt), ("c", c), ("do", do)):
             _check_tensor(name, t, 2, dev, dt)
         scale = 1.0 if scale is None else scale
@@ -369,7 +441,18 @@ def merge(o_a, lse_a, o_b, lse_b, out=None):
     b, m, hq, d = o_a.shape
     if o_b.shape != o_a.shape or lse_a.shape != (b, hq, m) or lse_b.shape != (b, hq, m):
         raise ValueError("shape mismatch between the two parts")
-    o, lse = out if out is not None else (torch.empty_like(o_a), torch.empty_like(lse_a))
+    if out is not None:
+        o, lse = out
+        if (not isinstance(o, torch.Tensor) or o.shape != o_a.shape or o.dtype != dt
+                or o.device != dev or not o.is_contiguous()):
+            raise ValueError(f"out o must be a packed {dt} tensor of shape {tuple(o_a.shape)} "
+                             f"on {dev}")
+        if (not isinstance(lse, torch.Tensor) or lse.shape != (b, hq, m)
+                or lse.dtype != torch.float32 or lse.device != dev or not lse.is_contiguous()):
+            raise ValueError(f"out lse must be a contiguous float32 tensor of shape "
+                             f"{(b, hq, m)} on {dev}")
+    else:
+        o, lse = torch.empty_like(o_a), torch.empty_like(lse_a)
     key = ("merge", dt, b, hq, m, d)
     plan = _get_plan(key, lambda: make_problem(SOFTMAX, _dtype_code(o_a), b, hq, hq, m, m, d, d,
                                                1.0, False, None))

@@ -114,6 +114,9 @@ struct fab_plan_s {
   ~fab_plan_s() { delete timer; }
   fab_problem prob;
   int64_t as[3], bs[3], cs[3], os[3];  // resolved {batch, head, row} strides
+  // no two (batch, head, row, col) indices of A / Bt / C share an address, so
+  // their gradients (which take these layouts) can be written
+  bool a_distinct, bt_distinct, c_distinct;
   size_t fwd_ws;
   size_t bwd_ws;
   int mlp_splits;
@@ -167,6 +170,26 @@ fab_status check_strides(const char* name, const int64_t s[3], int64_t cols, int
     return fail(FAB_ERR_BAD_SHAPE, "%s row stride %lld is smaller than its row length %lld", name,
                 (long long)s[2], (long long)cols);
   return FAB_OK;
+}
+
+// True when the map (batch, head, row, col) -> element offset of a tensor of
+// these sizes and strides is one-to-one, by the sufficient test that, with
+// the dimensions of size > 1 sorted by stride, each stride reaches past the
+// whole span of the smaller ones.  A zero batch or head stride (a tensor
+// broadcast over heads) fails it.
+bool distinct_layout(const int64_t s[3], int64_t batch, int64_t heads, int64_t rows,
+                     int64_t cols) {
+  struct Dim {
+    int64_t size, stride;
+  } d[4] = {{cols, 1}, {rows, s[2]}, {heads, s[1]}, {batch, s[0]}};
+  std::sort(d, d + 4, [](const Dim& x, const Dim& y) { return x.stride < y.stride; });
+  int64_t span = 0;  // largest offset reached by the dimensions seen so far
+  for (const Dim& x : d) {
+    if (x.size <= 1) continue;
+    if (x.stride <= span) return false;
+    span += (x.size - 1) * x.stride;
+  }
+  return true;
 }
 
 constexpr int64_t kMaxRows = (int64_t)1 << 30;
@@ -327,6 +350,13 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
   if ((st = check_strides("Bt", tmp.bs, q.k, unit)) != FAB_OK) return st;
   if ((st = check_strides("C", tmp.cs, q.p, unit)) != FAB_OK) return st;
   if ((st = check_strides("O", tmp.os, q.p, unit)) != FAB_OK) return st;
+  if (!distinct_layout(tmp.os, q.batch, q.heads_a, q.m, q.p))
+    return fail(FAB_ERR_BAD_SHAPE, "O strides {%lld, %lld, %lld} map two output elements to one "
+                "address (zero or overlapping batch / head / row strides)", (long long)tmp.os[0],
+                (long long)tmp.os[1], (long long)tmp.os[2]);
+  tmp.a_distinct = distinct_layout(tmp.as, q.batch, q.heads_a, q.m, q.k);
+  tmp.bt_distinct = distinct_layout(tmp.bs, q.batch, q.heads_bc, q.n, q.k);
+  tmp.c_distinct = distinct_layout(tmp.cs, q.batch, q.heads_bc, q.n, q.p);
 
   const char* dt = q.dtype == FAB_BF16 ? "bf16" : "f32";
   if (q.f == FAB_F_SOFTMAX) {
@@ -358,9 +388,10 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
     if (q.dtype != FAB_BF16) return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP runs in bf16 only");
     if (q.batch != 1 || q.heads_a != 1 || q.heads_bc != 1)
       return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs batch == heads == 1");
-    if (q.k % 128 || q.p % 128 || q.k > 1024 || q.p > 1024)
-      return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs k and p multiples of 128, at most 1024");
-    if (!fab::mlp_available()) return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP not built");
+    if (q.k > 1024 || q.p > 1024 || !fab::mlp_shape_supported((int)q.k, (int)q.p))
+      return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP: k = %lld, p = %lld is not a width pair this "
+                  "build runs (each of k and p in {128, 256, 512, 1024})", (long long)q.k,
+                  (long long)q.p);
     int splits = 1;
     tmp.fwd_ws = round_up(fab::mlp_fwd_workspace((int)q.m, (int)q.n, (int)q.k, (int)q.p, &splits), 256);
     tmp.bwd_ws = round_up(fab::mlp_bwd_workspace((int)q.m, (int)q.n, (int)q.k, (int)q.p), 256);
@@ -378,6 +409,9 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
   plan->fwd_ws = tmp.fwd_ws;
   plan->bwd_ws = tmp.bwd_ws;
   plan->mlp_splits = tmp.mlp_splits;
+  plan->a_distinct = tmp.a_distinct;
+  plan->bt_distinct = tmp.bt_distinct;
+  plan->c_distinct = tmp.c_distinct;
   memcpy(plan->desc, tmp.desc, sizeof tmp.desc);
   *plan_out = plan;
   if (fwd_ws) *fwd_ws = plan->fwd_ws;
@@ -482,29 +516,44 @@ fab_status fab_forward(const fab_plan_t* plan, const void* A, const void* Bt, co
   return ok();
 }
 
-fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, const void* C,
-                        const void* O, const float* lse, const void* dO, void* dA, void* dBt,
-                        void* dC, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of fab_backward's tensor arguments (everything but the workspace).
+fab_status check_backward_args(const char* who, const fab_plan_t* plan, const void* A,
+                               const void* Bt, const void* C, const void* O, const float* lse,
+                               const void* dO, const void* dA, const void* dBt, const void* dC) {
   if (!plan || !A || !Bt || !C || !dO || !dA || !dBt || !dC)
-    return fail(FAB_ERR_NULL_ARG, "fab_backward: null argument");
+    return fail(FAB_ERR_NULL_ARG, "%s: null argument", who);
   const fab_problem& q = plan->prob;
   if (!aligned16(A) || !aligned16(Bt) || !aligned16(C) || !aligned16(dO) || !aligned16(dA) ||
       !aligned16(dBt) || !aligned16(dC))
-    return fail(FAB_ERR_ALIGNMENT, "fab_backward: tensor base pointers must be 16-byte aligned");
-  if (workspace_bytes < plan->bwd_ws)
-    return fail(FAB_ERR_WORKSPACE_TOO_SMALL, "fab_backward: workspace %zu < %zu bytes",
-                workspace_bytes, plan->bwd_ws);
-  if (plan->bwd_ws && !workspace) return fail(FAB_ERR_NULL_ARG, "fab_backward: workspace is NULL");
-  if (plan->bwd_ws && !aligned16(workspace))
-    return fail(FAB_ERR_ALIGNMENT, "fab_backward: workspace must be 16-byte aligned");
+    return fail(FAB_ERR_ALIGNMENT, "%s: tensor base pointers must be 16-byte aligned", who);
+  if (!plan->a_distinct || !plan->bt_distinct || !plan->c_distinct)
+    return fail(FAB_ERR_BAD_SHAPE, "%s: the strides of %s map two elements to one address, so "
+                "its gradient cannot be written in that layout (pass a packed copy)", who,
+                !plan->a_distinct ? "A" : !plan->bt_distinct ? "Bt" : "C");
+  if (q.f == FAB_F_SOFTMAX) {
+    if (!O || !lse) return fail(FAB_ERR_NULL_ARG, "%s: softmax needs O and lse", who);
+    if (!aligned16(O)) return fail(FAB_ERR_ALIGNMENT, "%s: O must be 16-byte aligned", who);
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+      return fail(FAB_ERR_ALIGNMENT, "%s: lse must be 4-byte aligned", who);
+  } else if (O || lse) {
+    return fail(FAB_ERR_UNSUPPORTED, "%s: GeLU takes no O / lse", who);
+  }
+  return FAB_OK;
+}
+
+// Enqueues the backward kernels; arguments already checked.
+fab_status backward_launch(const char* who, const fab_plan_t* plan, const void* A, const void* Bt,
+                           const void* C, const void* O, const float* lse, const void* dO,
+                           void* dA, void* dBt, void* dC, void* workspace, void* stream) {
+  const fab_problem& q = plan->prob;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   TimerScope scope(plan->timer);
   if (q.f == FAB_F_SOFTMAX) {
-    if (!O || !lse) return fail(FAB_ERR_NULL_ARG, "fab_backward: softmax needs O and lse");
-    if (!aligned16(O)) return fail(FAB_ERR_ALIGNMENT, "fab_backward: O must be 16-byte aligned");
-    if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
-      return fail(FAB_ERR_ALIGNMENT, "fab_backward: lse must be 4-byte aligned");
     fab::AttnArgs a = attn_args(plan);
     a.q = A, a.k = Bt, a.v = C, a.o = O, a.lse_in = lse, a.dout = dO;
     a.dq = dA, a.dk = dBt, a.dv = dC;
@@ -515,7 +564,6 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, c
     e = q.dtype == FAB_BF16 ? fab::launch_attn_bwd_bf16(a, (int)q.k, s)
                             : fab::launch_attn_bwd_f32(a, (int)q.k, s);
   } else {
-    if (O || lse) return fail(FAB_ERR_UNSUPPORTED, "fab_backward: GeLU takes no O / lse");
     fab::MlpArgs a{};
     a.a = A, a.bt = Bt, a.c = C, a.dout = dO, a.da = dA, a.dbt = dBt, a.dc = dC;
     a.ws = static_cast<float*>(workspace);
@@ -525,8 +573,27 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, c
     a.scale = q.scale;
     e = fab::launch_mlp_bwd_bf16(a, s);
   }
-  if (e != hipSuccess) return fail(FAB_ERR_HIP, "fab_backward: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(FAB_ERR_HIP, "%s: %s", who, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, const void* C,
+                        const void* O, const float* lse, const void* dO, void* dA, void* dBt,
+                        void* dC, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "fab_backward";
+  fab_status st = check_backward_args(who, plan, A, Bt, C, O, lse, dO, dA, dBt, dC);
+  if (st != FAB_OK) return st;
+  if (workspace_bytes < plan->bwd_ws)
+    return fail(FAB_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who,
+                workspace_bytes, plan->bwd_ws);
+  if (plan->bwd_ws && !workspace) return fail(FAB_ERR_NULL_ARG, "%s: workspace is NULL", who);
+  if (plan->bwd_ws && !aligned16(workspace))
+    return fail(FAB_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", who);
+  return backward_launch(who, plan, A, Bt, C, O, lse, dO, dA, dBt, dC, workspace, stream);
 }
 
 fab_status fab_merge(const fab_plan_t* plan, const void* O_a, const float* lse_a,

@@ -143,7 +143,8 @@ hipError_t launch_ulysses(const UlyssesArgs& a, bool pack, hipStream_t s);
 int exp_probe_chains();
 hipError_t launch_exp_probe(int blocks, int iters, float* sink, hipStream_t s);
 
-bool mlp_available();
+// k, p pairs the GeLU MLP kernels are built for
+bool mlp_shape_supported(int k, int p);
 size_t mlp_fwd_workspace(int m, int n, int k, int p, int* splits);
 size_t mlp_bwd_workspace(int m, int n, int k, int p);
 hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s);

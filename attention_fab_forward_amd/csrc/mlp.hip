@@ -630,8 +630,6 @@ hipError_t reduce(const float* part, int splits, int rows, int cols, float scale
 
 }  // namespace
 
-bool mlp_available() { return true; }
-
 size_t mlp_fwd_workspace(int m, int n, int k, int p, int* splits) {
   const MlpLayout L = layout(m, n, k, p);
   *splits = L.split_rows;

@@ -8,11 +8,15 @@ TFLOP/s: forward 4*d flops and backward 10*d flops (its five products, one
 recomputation of S included) per unmasked (query, key) pair, n(n+1)/2 pairs
 per head.
 
-Also reported on the same line: per-kernel durations from HIP events recorded
-around every kernel on the launch stream (the roofline entry uses the
-dominant kernel), peak device memory versus sequence length for the long-
-context grouped-query geometry, a secondary GeLU-MLP measurement, and the CPU
-oracle timed on a bounded sample of the same workload.
+The headline step is timed over K steps with events between steps only; a
+second pass over K steps records HIP events around every kernel on the launch
+stream (the per-kernel durations the roofline entry uses).  Also reported on
+the same line: the GPU clock before and after (amd-smi), peak device memory
+versus sequence length for the long-context grouped-query geometry (with the
+HIP free-memory delta as a cross-check), the other workloads on their seeded
+inputs, a GeLU-MLP measurement with the 256 MB last-level cache flushed
+between repetitions, and the CPU oracle timed on bounded samples of the
+workloads, with the time a full run would take extrapolated from them.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -78,10 +82,7 @@ def time_attention(w, steps, warmup, torch, fab_binding):
         bwd()
     torch.cuda.synchronize()
 
-    # main timed region: K full steps, per-kernel events enabled, an event
-    # between steps for the per-step spread
-    plan.set_timing(True)
-    plan.reset_kernel_times()
+    # main timed region: K full steps, an event between steps (per-step spread)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -94,8 +95,21 @@ def time_attention(w, steps, warmup, torch, fab_binding):
     wall = time.perf_counter() - t0
     step_ms = ev[0].elapsed_time(ev[-1]) / steps
     per_step = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+
+    # second timed region: the same K steps with a HIP event pair around every
+    # kernel (on the launch stream), for the per-kernel durations
+    plan.set_timing(True)
+    plan.reset_kernel_times()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fwd()
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
     kernels = plan.kernel_times()
     plan.set_timing(False)
+    step_ms_kernel_pass = e0.elapsed_time(e1) / steps
 
     def spread(fn):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -112,30 +126,28 @@ def time_attention(w, steps, warmup, torch, fab_binding):
     bwd_ms, bwd_d = spread(bwd)  # backward alone, on the fixed forward outputs
     stats = lambda d: {"median": d[len(d) // 2], "min": d[0], "max": d[-1]}
     return {"step_ms": step_ms, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
-            "kernels": kernels, "inputs": x,
+            "kernels": kernels, "inputs": x, "step_ms_kernel_pass": step_ms_kernel_pass,
             "spread_ms": {"step": stats(per_step), "fwd": stats(fwd_d), "bwd": stats(bwd_d)}}
 
 
-def time_workload(key, reps, torch, fab):
-    """Forward and backward time of another attention configuration, on
-    N(0, 1) inputs drawn on the device (torch generator seeded per tensor).
+def time_workload(key, reps, torch, fab, back_to_back=False):
+    """Forward and backward time of another attention configuration on its
+    seeded inputs (the same PCG64 draws the tests and the oracle use).
 
-    Outputs and workspace are allocated once and the plan's raw calls are
-    enqueued `reps` times back to back between two events (device time per
-    call, host overhead hidden); a second pass records HIP events around
-    every kernel (kernel durations alone)."""
+    Outputs and workspace are allocated once; each repetition enqueues the
+    plan's raw forward and backward calls between events (device time; the
+    reported figures are the medians over `reps`, with min and max); a second
+    pass records HIP events around every kernel (kernel durations alone).
+    back_to_back (latency-bound workloads of microseconds): the reps are
+    enqueued back to back between two events instead, so the host's enqueue
+    time between calls is hidden, and the figures are means."""
     from attention_fab_forward_amd import _binding as B
-    from attention_fab_forward_amd.inputs import WORKLOADS
+    from attention_fab_forward_amd.inputs import WORKLOADS, attention_inputs
     w = WORKLOADS[key]
-    gen = torch.Generator(device="cuda")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-
-    def draw(t, heads):
-        gen.manual_seed(1000 * w.number + t)
-        return torch.randn(w.batch, w.seq, heads, w.d, device="cuda", dtype=torch.float32,
-                           generator=gen).to(dt)
-
-    q, k, v, do = draw(1, w.heads_q), draw(2, w.heads_kv), draw(3, w.heads_kv), draw(4, w.heads_q)
+    x = attention_inputs(w)
+    q, k, v, do = (torch.from_numpy(x[t]).to(dt).cuda() for t in ("q", "k", "v", "do"))
+    del x
     plan = B.attention_plan(q, k, v, w.causal, w.scale())
     o, lse = torch.empty_like(q), torch.empty((w.batch, w.heads_q, w.seq), dtype=torch.float32,
                                               device="cuda")
@@ -156,16 +168,33 @@ def time_workload(key, reps, torch, fab):
     fwd()
     bwd()
     torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    e[0].record(stream)
-    for _ in range(reps):
+    fms, bms = [], []
+    for _ in range(1 if back_to_back else reps):
+        if back_to_back:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            for _ in range(reps):
+                fwd()
+            e[1].record(stream)
+            for _ in range(reps):
+                bwd()
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            fms.append(e[0].elapsed_time(e[1]) / reps)
+            bms.append(e[1].elapsed_time(e[2]) / reps)
+            break
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
         fwd()
-    e[1].record(stream)
-    for _ in range(reps):
+        e[1].record(stream)
         bwd()
-    e[2].record(stream)
-    torch.cuda.synchronize()
-    fm, bm = e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        fms.append(e[0].elapsed_time(e[1]))
+        bms.append(e[1].elapsed_time(e[2]))
+    fms.sort()
+    bms.sort()
+    fm, bm = fms[len(fms) // 2], bms[len(bms) // 2]
     plan.set_timing(True)
     plan.reset_kernel_times()
     for _ in range(reps):
@@ -177,12 +206,15 @@ def time_workload(key, reps, torch, fab):
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return {"fwd_ms": fm, "bwd_ms": bm, "fwd_us": 1e3 * fm, "bwd_us": 1e3 * bm,
+            "fwd_ms_min_max": [fms[0], fms[-1]], "bwd_ms_min_max": [bms[0], bms[-1]],
             "dtype": w.dtype, "fwd_tflops": fwd_fl / fm / 1e9,
             "fwd_bwd_tflops": (fwd_fl + bwd_fl) / (fm + bm) / 1e9,
             "fwd_bwd_pct_bf16_peak": 100.0 * (fwd_fl + bwd_fl) / (fm + bm) / 1e9 / BF16_PEAK_TFLOPS,
             "kernels_avg_ms": kernels, "reps": reps,
-            "timing": "device time per call, calls enqueued back to back",
-            "inputs": "N(0,1) drawn on the device, seeded per tensor"}
+            "timing": ("device time per call, calls enqueued back to back between two events "
+                       "(mean)" if back_to_back else
+                       "device time per call (events around each call), median of reps"),
+            "inputs": "seeded PCG64 draws (the workload's own seeds), rounded to the dtype"}
 
 
 def kernel_flops(w):
@@ -278,6 +310,7 @@ def peak_hbm_sweep(torch, fab, exps=range(12, 21), hq=2, hkv=1):
         torch.cuda.empty_cache()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
+        free0 = torch.cuda.mem_get_info()[0]  # hipMemGetInfo
         q = torch.randn(1, n, hq, 128, device="cuda", dtype=torch.bfloat16)
         k = torch.randn(1, n, hkv, 128, device="cuda", dtype=torch.bfloat16)
         v = torch.randn(1, n, hkv, 128, device="cuda", dtype=torch.bfloat16)
@@ -287,7 +320,12 @@ def peak_hbm_sweep(torch, fab, exps=range(12, 21), hq=2, hkv=1):
         grads = fab.backward(q, k, v, o, lse, do, "softmax", True)
         torch.cuda.synchronize()
         peak = torch.cuda.max_memory_allocated() - base
-        out.append({"n": n, "fwd_peak_bytes": int(fwd_peak), "fwd_bwd_peak_bytes": int(peak)})
+        # device memory that left the free pool over the call (torch's
+        # reserved blocks, rounded up to its allocation granules): at least
+        # the peak, and no more than a granule per tensor above it
+        used = free0 - torch.cuda.mem_get_info()[0]
+        out.append({"n": n, "fwd_peak_bytes": int(fwd_peak), "fwd_bwd_peak_bytes": int(peak),
+                    "hip_free_delta_bytes": int(used)})
         del q, k, v, do, o, lse, grads
     ns = [r["n"] for r in out]
     ys = [r["fwd_bwd_peak_bytes"] for r in out]
@@ -298,9 +336,11 @@ def peak_hbm_sweep(torch, fab, exps=range(12, 21), hq=2, hkv=1):
     a = my - b * mn
     resid = max(abs(y - (a + b * x)) / y for x, y in zip(ns, ys))
     ratios = [ys[i + 1] / ys[i] for i in range(len(ys) - 1)]
+    hip = [r["hip_free_delta_bytes"] / r["fwd_bwd_peak_bytes"] for r in out]
     return {"geometry": f"causal, {hq} query heads / {hkv} kv heads, d=128, bf16, fwd+bwd",
             "points": out, "bytes_per_token": b, "max_rel_residual_linear_fit": resid,
-            "doubling_ratios": ratios}
+            "doubling_ratios": ratios,
+            "hip_free_delta_over_peak": {"min": min(hip), "max": max(hip)}}
 
 
 def time_merge(w, reps, torch, fab):
@@ -467,44 +507,62 @@ def time_mlp(steps, warmup, torch, fab_binding):
                                    plan.fwd_workspace, sp)
     bwd = lambda: plan.backward_raw(P(t["a"]), P(t["bt"]), P(t["c"]), None, None, P(t["do"]),
                                     P(da), P(dbt), P(dc), P(ws), plan.bwd_workspace, sp)
+    # 512 MiB written between repetitions: the 32 MiB of operands (and the
+    # workspace) cannot stay in the 256 MB last-level cache from one
+    # repetition to the next, so each is timed from HBM
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
         fwd()
         bwd()
     torch.cuda.synchronize()
+    fms, sms = [], []
+    for _ in range(steps):
+        flush.fill_(1)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        bwd()
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        fms.append(e[0].elapsed_time(e[1]))
+        sms.append(e[0].elapsed_time(e[2]))
+    fms.sort()
+    sms.sort()
+    fwd_ms, step_ms = fms[len(fms) // 2], sms[len(sms) // 2]
+    # per-kernel durations: a separate pass with events around every kernel
     plan.set_timing(True)
     plan.reset_kernel_times()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
     for _ in range(steps):
+        flush.fill_(1)
         fwd()
         bwd()
-    e1.record(stream)
     torch.cuda.synchronize()
     kernels = plan.kernel_times()
     plan.set_timing(False)
-    e0.record(stream)
-    for _ in range(steps):
-        fwd()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = e0.elapsed_time(e1) / steps
-    step_ms = sum(v[1] for v in kernels.values()) / steps
+    del flush
     gemm = 2 * m * k * n
     fwd_fl, bwd_fl = 2 * gemm, 5 * gemm
     fwd_tf, step_tf = fwd_fl / fwd_ms / 1e9, (fwd_fl + bwd_fl) / step_ms / 1e9
     return {"workload": MLP_WORKLOAD, "fwd_ms": fwd_ms, "fwd_bwd_ms": step_ms,
+            "fwd_ms_min_max": [fms[0], fms[-1]], "fwd_bwd_ms_min_max": [sms[0], sms[-1]],
             "fwd_tflops": fwd_tf, "fwd_bwd_tflops": step_tf,
             "fwd_pct_bf16_peak": 100.0 * fwd_tf / BF16_PEAK_TFLOPS,
             "fwd_bwd_pct_bf16_peak": 100.0 * step_tf / BF16_PEAK_TFLOPS,
+            "timing": ("events around each repetition's forward and forward + backward "
+                       "(median of reps), 512 MiB written between repetitions"),
             "kernels_avg_ms": {k_: v[1] / v[0] for k_, v in kernels.items()},
             "mfma_counters": {k_: measured_mfma(k_) for k_ in kernels if measured_mfma(k_)}}
 
 
-def cpu_baseline(w, x, seconds):
-    """The oracle, unchanged, on a bounded sample of the benchmarked workload:
-    query rows (forward rows and their full backward work), taken in 32-row
-    chunks from the last row of head 0 downwards, then head 1, ..., by a pool of
-    host threads until `seconds` have passed."""
+def oracle_rows_timed(w, x, seconds=None, rows_per_head=None, chunk=32, seed=0):
+    """The oracle, unchanged, on a sample of query rows of a workload: chunks
+    of `chunk` consecutive rows (forward rows and their backward work) at
+    seeded, uniformly random positions over all heads, run by a pool of host
+    threads (one BLAS thread each) until `seconds` have passed, or
+    `rows_per_head` rows of every head.  The oracle materialises full-width
+    rows, so every row costs the same and the full run's time is the sample's
+    time times (all rows / sampled rows)."""
     from concurrent.futures import ThreadPoolExecutor
     import numpy as np
     import oracle
@@ -513,19 +571,24 @@ def cpu_baseline(w, x, seconds):
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     cores = len(os.sched_getaffinity(0))
-    scale = w.scale()
-    n = w.seq
-    chunk = 32
+    scale, n = w.scale(), w.seq
     q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    rng = np.random.default_rng(1000 * w.number + seed)
+    starts = np.arange(0, n - chunk + 1, chunk)
+    if rows_per_head is None:
+        order = [(h, int(r)) for h in range(w.heads_q) for r in starts]
+        order = [order[i] for i in rng.permutation(len(order))]
+    else:
+        order = [(h, int(r)) for h in range(w.heads_q)
+                 for r in np.sort(rng.choice(starts, rows_per_head // chunk, replace=False))]
 
     def work(item):
-        h, r1 = item
-        rows = np.arange(r1 - chunk, r1)
+        h, r0 = item
+        rows = np.arange(r0, r0 + chunk)
         oracle.attention_forward_rows(q, k, v, scale, True, 0, h, rows)
         oracle.attention_backward_rows(q, k, v, do, scale, True, 0, h, rows)
         return rows
 
-    order = [(h, r1) for h in range(w.heads_q) for r1 in range(n, chunk - 1, -chunk)]
     done = []
     t0 = time.perf_counter()
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
@@ -534,7 +597,7 @@ def cpu_baseline(w, x, seconds):
     try:
         with ThreadPoolExecutor(max_workers=cores) as ex:
             pos = 0
-            while time.perf_counter() - t0 < seconds and pos < len(order):
+            while pos < len(order) and (seconds is None or time.perf_counter() - t0 < seconds):
                 batch = order[pos:pos + cores]
                 pos += len(batch)
                 done.extend(ex.map(work, batch))
@@ -543,13 +606,66 @@ def cpu_baseline(w, x, seconds):
             ctx.__exit__(None, None, None)
     elapsed = time.perf_counter() - t0
     rows = np.concatenate(done)
-    flops = float(np.sum(14.0 * w.d * (rows + 1)))
+    flops = float(np.sum(14.0 * w.d * (rows + 1)))  # causal: row i has i + 1 keys
+    frac = len(rows) / (n * w.heads_q)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": elapsed,
-            "sample": f"{len(rows)} query rows ({len(rows) / (n * w.heads_q):.1%} of the rows) of "
-                      f"{WORKLOAD}, last rows of head 0 first: forward rows plus their backward "
-                      "work (fp64 numpy, full-width rows); rate = algorithmic fwd+bwd flops of "
-                      "those rows / wall time"}
+            "seconds": elapsed, "rows": int(len(rows)), "sample_fraction": frac,
+            "extrapolated": True, "extrapolation_factor": 1.0 / frac,
+            "extrapolated_full_seconds": elapsed / frac}
+
+
+def cpu_baseline(w, x, seconds, step_ms):
+    """The oracle on a bounded sample of the benchmarked workload (rows at
+    uniformly random positions over all heads, `seconds` of host time), with
+    the full run's time extrapolated from it."""
+    r = oracle_rows_timed(w, x, seconds=seconds)
+    r["sample"] = (f"{r['rows']} query rows ({r['sample_fraction']:.2%} of the rows) of "
+                   f"{WORKLOAD} in 32-row chunks at seeded uniformly random positions over all "
+                   "heads: forward rows plus their backward work (fp64 numpy, full-width rows); "
+                   "value = algorithmic fwd+bwd flops of those rows / wall time; the full run's "
+                   f"time is extrapolated (x{r['extrapolation_factor']:.1f})")
+    r["gpu_step_ms"] = step_ms
+    r["extrapolated_oracle_over_gpu"] = r["extrapolated_full_seconds"] * 1e3 / step_ms
+    return r
+
+
+def gpu_clock(tag):
+    """Current GPU clocks from amd-smi (None where the tool or field is
+    missing); the raw JSON is kept, trimmed, for inspection."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "-g", "0", "--clock", "--json"],
+                ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            out = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except Exception as e:  # noqa: BLE001 - a missing tool is a result, not an error
+            last = f"{cmd[0]}: {e}"
+            continue
+        if out.returncode != 0:
+            last = f"{cmd[0]}: rc {out.returncode} {out.stderr.strip()[:200]}"
+            continue
+        try:
+            data = json.loads(out.stdout)
+        except ValueError:
+            last = f"{cmd[0]}: unparsable output"
+            continue
+        found = {}
+
+        def walk(node, path):
+            if isinstance(node, dict):
+                for key, val in node.items():
+                    walk(val, f"{path}.{key}" if path else str(key))
+            elif isinstance(node, list):
+                for i, val in enumerate(node):
+                    walk(val, f"{path}[{i}]")
+            elif "gfx" in path.lower() or "sclk" in path.lower():
+                found[path] = node
+
+        walk(data, "")
+        # current clock of each graphics engine (one per XCD), in MHz
+        mhz = [v for k_, v in found.items() if k_.endswith(".clk.value") or k_.endswith("sclk")]
+        return {"when": tag, "tool": cmd[0], "gfx_mhz": mhz if mhz else None,
+                "fields": None if mhz else dict(list(found.items())[:24])}
+    return {"when": tag, "tool": None, "error": last}
 
 
 def main():
@@ -584,10 +700,12 @@ def main():
         sys.exit(1)
     fab.lib()
 
+    clocks = [gpu_clock("before")]
     w = WORKLOADS[WORKLOAD]
     fwd_fl, bwd_fl, unit = attention_flops(w)
     log(f"workload {WORKLOAD}: {unit} unmasked pairs, fwd {fwd_fl:.3e} flop, bwd {bwd_fl:.3e} flop")
     r = time_attention(w, args.steps, args.warmup, torch, fab_binding)
+    clocks.append(gpu_clock("after the timed steps"))
     step_ms, fwd_ms = r["step_ms"], r["fwd_ms"]
     value = (fwd_fl + bwd_fl) / step_ms / 1e9
     kflops = kernel_flops(w)
@@ -643,11 +761,12 @@ def main():
         log("other workloads ...")
         extras["workloads"] = {
             # latency-bound (microseconds of work): reported in us
-            "attn_f32_h1_n256_d64": time_workload("attn_f32_h1_n256_d64", 200, torch, fab),
+            "attn_f32_h1_n256_d64": time_workload("attn_f32_h1_n256_d64", 200, torch, fab,
+                                                  back_to_back=True),
             "attn_causal_bf16_h4_n131072_d128": time_workload(
-                "attn_causal_bf16_h4_n131072_d128", 3, torch, fab),
+                "attn_causal_bf16_h4_n131072_d128", 5, torch, fab),
             "attn_causal_bf16_gqa2_n1048576_d128": time_workload(
-                "attn_causal_bf16_gqa2_n1048576_d128", 1, torch, fab),
+                "attn_causal_bf16_gqa2_n1048576_d128", 3, torch, fab),
         }
     if "merge" in want:
         log("merge ...")
@@ -665,7 +784,23 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline ({args.cpu_seconds:.0f} s) ...")
-        cpu = cpu_baseline(w, r["inputs"], args.cpu_seconds)
+        cpu = cpu_baseline(w, r["inputs"], args.cpu_seconds, step_ms)
+        if "workloads" in want:
+            # the two long-sequence workloads: 256 rows per head, extrapolated
+            from attention_fab_forward_amd.inputs import attention_inputs
+            samples = {}
+            for key in ("attn_causal_bf16_h4_n131072_d128", "attn_causal_bf16_gqa2_n1048576_d128"):
+                log(f"cpu oracle sample of {key} ...")
+                wk = WORKLOADS[key]
+                res = oracle_rows_timed(wk, attention_inputs(wk), rows_per_head=256)
+                res["sample"] = (f"256 query rows per head ({res['sample_fraction']:.3%} of the "
+                                 "rows) in 32-row chunks at seeded uniformly random positions; "
+                                 "full run extrapolated")
+                gpu = extras["workloads"][key]
+                res["extrapolated_oracle_over_gpu"] = (res["extrapolated_full_seconds"] * 1e3
+                                                       / (gpu["fwd_ms"] + gpu["bwd_ms"]))
+                samples[key] = res
+            cpu["other_workloads"] = samples
 
     line = {
         "metric": "f(AB)C fwd / fwd+bwd TFLOP/s and % bf16 MFMA peak; peak HBM vs seq len",
@@ -689,6 +824,8 @@ def main():
         "fwd_ms": fwd_ms,
         "bwd_ms": r["bwd_ms"],
         "spread_ms": r["spread_ms"],
+        "step_ms_with_kernel_events": r["step_ms_kernel_pass"],
+        "gpu_clock": clocks,
         "kernels": kern,
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -106,10 +106,14 @@ typedef struct fab_plan_s fab_plan_t;
  *   softmax, bf16: k == p, k in {64, 128}; any m, n >= 1; causal with any
  *                  offsets.
  *   softmax, f32:  k == p, k in {64, 128}; same rules.
- *   GeLU, bf16:    batch == heads_a == heads_bc == 1, k and p multiples of 128
- *                  and at most 1024, any m, n >= 1, mask NONE.
+ *   GeLU, bf16:    batch == heads_a == heads_bc == 1, each of k and p in
+ *                  {128, 256, 512, 1024}, any m, n >= 1, mask NONE.
  * Row strides must be multiples of 8 elements (bf16) or 4 (f32), and so must
- * the head and batch strides.  On success *plan_out receives a plan that the
+ * the head and batch strides.  O's strides must give every output element its
+ * own address (no zero or overlapping batch / head strides): FAB_ERR_BAD_SHAPE
+ * otherwise.  A, Bt and C may be broadcast (say a zero head stride) for the
+ * forward; fab_backward refuses such a plan, since each gradient takes its
+ * primal's layout.  On success *plan_out receives a plan that the
  * caller releases with fab_plan_destroy, and the two sizes receive the bytes
  * of device workspace fab_forward / fab_backward need (either size pointer
  * may be NULL).  On failure *plan_out is set to NULL. */
@@ -128,7 +132,8 @@ fab_status fab_forward(const fab_plan_t* plan, const void* A, const void* Bt,
 /* Backward pass of L = <dO, O>: dA, dBt, dC (attention: dQ, dK, dV).
  * O and lse must be what fab_forward returned for the same inputs (softmax;
  * pass NULL for both with GeLU).  dO has O's layout; dA, dBt, dC have the
- * layouts of A, Bt, C and are overwritten.  workspace: at least the plan's
+ * layouts of A, Bt, C and are overwritten (FAB_ERR_BAD_SHAPE if one of those
+ * layouts maps two elements to one address).  workspace: at least the plan's
  * backward size.  Enqueued on `stream`. */
 fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt,
                         const void* C, const void* O, const float* lse,

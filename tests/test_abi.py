@@ -78,6 +78,24 @@ def status_of(prob):
     ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": True}, "FAB_ERR_UNSUPPORTED"),
     ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "dtype": B.F32},
      "FAB_ERR_UNSUPPORTED"),
+    # GeLU widths the kernels are built for, and ones they are not
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 1024, "p": 256},
+     "FAB_OK"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 384, "p": 128},
+     "FAB_ERR_UNSUPPORTED"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 128, "p": 768},
+     "FAB_ERR_UNSUPPORTED"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 2048, "p": 128},
+     "FAB_ERR_UNSUPPORTED"),
+    # an output whose heads (or batch entries) share memory is refused
+    ({"strides": {"o_stride": (256 * 4 * 128, 0, 4 * 128)}}, "FAB_ERR_BAD_SHAPE"),
+    ({"batch": 2, "strides": {"o_stride": (0, 128, 4 * 128)}}, "FAB_ERR_BAD_SHAPE"),
+    ({"strides": {"o_stride": (256 * 4 * 128, 64, 4 * 128)}}, "FAB_ERR_BAD_SHAPE"),
+    # inputs broadcast over heads plan fine (the forward only reads them)
+    ({"strides": {"bt_stride": (256 * 128, 0, 128), "c_stride": (256 * 128, 0, 128)}},
+     "FAB_OK"),
+    # an exchange-buffer layout {batch Hl d, head d, row b Hl d} is one-to-one
+    ({"batch": 3, "strides": {"o_stride": (4 * 128, 128, 3 * 4 * 128)}}, "FAB_OK"),
 ])
 def test_plan_validation(kw, expect):
     assert status_of(attn(**kw)) == expect
@@ -203,3 +221,17 @@ def test_exp_probe_count_and_argument_errors():
     assert B.STATUS[L.fab_exp_probe(10, 0, None, None, None)] == "FAB_ERR_BAD_SHAPE"
     assert B.STATUS[L.fab_exp_probe(10, 100, ctypes.c_void_p(0x10002), None, None)] == \
         "FAB_ERR_ALIGNMENT"
+
+
+def test_backward_refuses_gradient_layouts_that_overlap():
+    """A K broadcast over heads (zero head stride) is a valid forward input, but
+    its gradient cannot be written in that layout: the backward refuses
+    before any launch."""
+    L = B.lib()
+    good = ctypes.c_void_p(0x10000)
+    p = B.Plan(attn(strides={"bt_stride": (256 * 128, 0, 128)}))
+    st = L.fab_backward(p._ptr, good, good, good, good, good, good, good, good, good, good,
+                        p.bwd_workspace, None)
+    assert B.STATUS[st] == "FAB_ERR_BAD_SHAPE"
+    assert "Bt" in L.fab_last_error().decode()
+

@@ -7,7 +7,7 @@ import pytest
 
 from attention_fab_forward_amd.inputs import random_array
 from oracle import attention_backward, attention_forward, mlp_backward, mlp_forward
-from fab_testutil import assert_close, to_device, to_host
+from fab_testutil import assert_close, grad_floors, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -32,8 +32,9 @@ def test_attention_function_grads(dtype, d, causal):
     ro, _ = attention_forward(q, k, v, scale, causal)
     rdq, rdk, rdv = attention_backward(q, k, v, do, scale, causal)
     assert_close("O", to_host(o.detach()), ro, dtype)
-    for name, t, r in (("dQ", tq, rdq), ("dK", tk, rdk), ("dV", tv, rdv)):
-        assert_close(name, to_host(t.grad), r, dtype, zero_scale=1.0)
+    fq, fk = grad_floors({"q": q, "k": k, "v": v, "do": do}, scale, causal, ro)
+    for name, t, r, fl in (("dQ", tq, rdq, fq), ("dK", tk, rdk, fk), ("dV", tv, rdv, None)):
+        assert_close(name, to_host(t.grad), r, dtype, floor=fl)
 
 
 def test_gelu_mlp_function_grads():
@@ -75,8 +76,9 @@ def test_block_grads_match_chained_oracle():
     rdq, rdk, rdv = attention_backward(q, k, v, da.reshape(b, n, hq, d), scale, True)
     assert_close("dW1", to_host(blk.w1.grad), dw1, "bf16")
     assert_close("dW2", to_host(blk.w2.grad), dw2, "bf16")
-    for name, t, r in (("dQ", tq, rdq), ("dK", tk, rdk), ("dV", tv, rdv)):
-        assert_close(name, to_host(t.grad), r, "bf16", zero_scale=1.0)
+    fq, fk = grad_floors({"q": q, "k": k, "v": v, "do": da.reshape(b, n, hq, d)}, scale, True, ro)
+    for name, t, r, fl in (("dQ", tq, rdq, fq), ("dK", tk, rdk, fk), ("dV", tv, rdv, None)):
+        assert_close(name, to_host(t.grad), r, "bf16", floor=fl)
     assert isinstance(y, torch.Tensor)
 
 

@@ -68,3 +68,56 @@ def test_product_path_fails_loudly_without_library():
                        env=env, timeout=120)
     assert r.returncode == 0, r.stderr
     assert "raised" in r.stdout and "not built" in r.stdout
+
+
+def test_binding_rejects_mismatched_shapes_before_any_launch():
+    """Shape disagreements between the operands raise in the binding (on the
+    host, before device checks), so no kernel can index past a tensor."""
+    import pytest
+    import torch
+    import attention_fab_forward_amd as fab
+    from attention_fab_forward_amd import _binding as B
+    e = lambda *sh: torch.empty(sh, dtype=torch.bfloat16)
+    q, k, v = e(2, 64, 4, 128), e(2, 80, 2, 128), e(2, 80, 2, 128)
+    assert B.attention_shapes(q, k, v) == (2, 64, 4, 2, 80, 128, 128)
+    bad = {
+        "batch": (q, e(1, 80, 2, 128), v),
+        "v rows": (q, k, e(2, 79, 2, 128)),
+        "v heads": (q, k, e(2, 80, 1, 128)),
+        "k dim": (q, e(2, 80, 2, 64), v),
+        "groups": (e(2, 64, 3, 128), k, v),
+        "rank": (e(64, 4, 128), k, v),
+    }
+    for name, (a_, b_, c_) in bad.items():
+        with pytest.raises(ValueError):
+            fab.forward(a_, b_, c_, "softmax", True)
+    o, do = e(2, 64, 4, 128), e(2, 64, 4, 128)
+    lse = torch.empty(2, 4, 64)
+    B.attention_grad_shapes(q, k, v, o, lse, do)
+    for args in ((q, k, v, e(2, 64, 4, 64), lse, do), (q, k, v, o, lse, e(2, 63, 4, 128)),
+                 (q, k, v, o, torch.empty(2, 64, 4), do), (q, e(2, 80, 2, 64), v, o, lse, do)):
+        with pytest.raises(ValueError):
+            fab.backward(*args, "softmax", True)
+    a, bt, c = e(128, 256), e(512, 256), e(512, 128)
+    assert B.mlp_shapes(a, bt, c, e(128, 128)) == (128, 256, 512, 128)
+    for args in ((a, e(512, 128), c), (a, bt, e(256, 128)), (e(128, 256, 1), bt, c)):
+        with pytest.raises(ValueError):
+            fab.forward(*args, "gelu")
+    with pytest.raises(ValueError):
+        fab.backward(a, bt, c, None, None, e(128, 256), "gelu")
+    with pytest.raises(ValueError):
+        fab.backward(a, bt, e(511, 128), None, None, e(128, 128), "gelu")
+
+
+def test_binding_layout_distinctness():
+    """The binding's one-to-one layout test agrees with the library's rule:
+    expanded (broadcast) tensors overlap, views of a fused projection do not."""
+    import torch
+    from attention_fab_forward_amd import _binding as B
+    k = torch.empty(1, 16, 1, 8)
+    assert B._distinct(k)
+    assert not B._distinct(k.expand(1, 16, 4, 8))
+    big = torch.empty(2, 16, 3, 3, 8)
+    assert B._distinct(big[:, :, :, 1])
+    assert not B._distinct(torch.empty(16, 8).as_strided((16, 8), (4, 1)))
+    assert B._distinct(torch.empty(1, 1, 1, 8).expand(1, 1, 1, 8))
