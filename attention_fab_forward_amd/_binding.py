@@ -30,7 +30,8 @@ EXPORTS = ("fab_plan", "fab_forward", "fab_backward", "fab_plan_destroy",
            "fab_status_string", "fab_last_error", "fab_abi_version",
            "fab_problem_size", "fab_plan_describe", "fab_plan_set_timing",
            "fab_plan_kernel_times", "fab_plan_reset_kernel_times", "fab_merge",
-           "fab_ulysses_sizes", "fab_ulysses_pack", "fab_ulysses_unpack", "fab_exp_probe")
+           "fab_ulysses_sizes", "fab_ulysses_pack", "fab_ulysses_unpack", "fab_exp_probe",
+           "fab_backward_noalloc")
 
 
 class FabProblem(ctypes.Structure):
@@ -85,6 +86,8 @@ def lib():
         L.fab_forward.restype = ctypes.c_int
         L.fab_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.fab_backward.restype = ctypes.c_int
+        L.fab_backward_noalloc.argtypes = [vp] * 11
+        L.fab_backward_noalloc.restype = ctypes.c_int
         L.fab_plan_destroy.argtypes = [vp]
         L.fab_plan_destroy.restype = None
         L.fab_status_string.argtypes = [ctypes.c_int]
@@ -187,6 +190,11 @@ class Plan:
     def backward_raw(self, a, bt, c, o, lse, do, da, dbt, dc, ws, ws_bytes, stream):
         check(lib().fab_backward(self._ptr, a, bt, c, o, lse, do, da, dbt, dc, ws, ws_bytes,
                                  stream))
+
+    def backward_noalloc_raw(self, a, bt, c, o, lse, do, da, dbt, dc, stream):
+        """fab_backward_noalloc: the backward with the library's static scratch
+        in place of a workspace."""
+        check(lib().fab_backward_noalloc(self._ptr, a, bt, c, o, lse, do, da, dbt, dc, stream))
 
     def merge_raw(self, oa, la, ob, lb, oo, lo, stream):
         check(lib().fab_merge(self._ptr, oa, la, ob, lb, oo, lo, stream))

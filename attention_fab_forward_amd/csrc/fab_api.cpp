@@ -577,6 +577,36 @@ fab_status backward_launch(const char* who, const fab_plan_t* plan, const void* 
   return ok();
 }
 
+// Device scratch of fab_backward_noalloc: one copy per GPU, held until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is a stand-in, not device memory); it uses the per-device address that
+// hipGetSymbolAddress returns.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // device address of `scratch`, by device ordinal
+
+// The current device's copy of `scratch`, looked up once per device.
+fab_status static_scratch(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(FAB_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FAB_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", who, dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FAB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -594,6 +624,21 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt, c
   if (plan->bwd_ws && !aligned16(workspace))
     return fail(FAB_ERR_ALIGNMENT, "%s: workspace must be 16-byte aligned", who);
   return backward_launch(who, plan, A, Bt, C, O, lse, dO, dA, dBt, dC, workspace, stream);
+}
+
+fab_status fab_backward_noalloc(const fab_plan_t* plan, const void* A, const void* Bt,
+                                const void* C, const void* O, const float* lse, const void* dO,
+                                void* dA, void* dBt, void* dC, void* stream) {
+  const char* who = "fab_backward_noalloc";
+  fab_status st = check_backward_args(who, plan, A, Bt, C, O, lse, dO, dA, dBt, dC);
+  if (st != FAB_OK) return st;
+  if (plan->bwd_ws > kStaticScratchBytes)
+    return fail(FAB_ERR_WORKSPACE_TOO_SMALL, "%s: this problem needs %zu bytes of scratch; the "
+                "library's static scratch holds %zu (use fab_backward with a workspace)", who,
+                plan->bwd_ws, kStaticScratchBytes);
+  void* ws = nullptr;
+  if (plan->bwd_ws && (st = static_scratch(who, &ws)) != FAB_OK) return st;
+  return backward_launch(who, plan, A, Bt, C, O, lse, dO, dA, dBt, dC, ws, stream);
 }
 
 fab_status fab_merge(const fab_plan_t* plan, const void* O_a, const float* lse_a,

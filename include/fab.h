@@ -35,8 +35,10 @@
  * LSE is packed [batch, heads_a, m] float32.
  *
  * Ownership: the caller owns every device buffer.  The library allocates no
- * device memory and never synchronises: all work is enqueued on the caller's
- * stream.  Temporary device memory is passed in as `workspace`, whose size
+ * device memory (its one static array, the 32 MiB scratch of
+ * fab_backward_noalloc, is reserved by the HIP runtime when it loads the
+ * library's device code on a GPU) and never synchronises: all work is
+ * enqueued on the caller's stream.  Temporary device memory is passed in as `workspace`, whose size
  * fab_plan reports.  Outputs are overwritten, not accumulated.  A plan is an
  * immutable host object; one plan may serve concurrent calls that use
  * distinct workspaces.
@@ -139,6 +141,24 @@ fab_status fab_backward(const fab_plan_t* plan, const void* A, const void* Bt,
                         const void* C, const void* O, const float* lse,
                         const void* dO, void* dA, void* dBt, void* dC,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* fab_backward for callers that cannot allocate device memory at all (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results, with the workspace taken from a
+ * scratch array of 32 MiB that the library holds statically on each GPU it
+ * runs on (from when its device code is loaded there until the process
+ * ends).  The
+ * caller passes inputs and outputs only; nothing is allocated or freed.
+ * A plan whose backward workspace exceeds 32 MiB is refused with
+ * FAB_ERR_WORKSPACE_TOO_SMALL (the attention backward needs 8 bytes per
+ * query row and head, so up to 4 Mi (row, head) pairs fit).  All calls on one
+ * GPU share that array: calls that overlap in time on one GPU (say on two
+ * streams) race on it and must be ordered by the caller.  Arguments,
+ * layouts and errors are as for fab_backward; FAB_ERR_HIP also reports a
+ * failed lookup of the array's device address. */
+fab_status fab_backward_noalloc(const fab_plan_t* plan, const void* A, const void* Bt,
+                                const void* C, const void* O, const float* lse,
+                                const void* dO, void* dA, void* dBt, void* dC, void* stream);
 
 /* Merge two softmax results over disjoint key sets of the same queries (for
  * instance two key ranges computed by fab_forward with k_offset set): with

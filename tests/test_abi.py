@@ -225,8 +225,8 @@ def test_exp_probe_count_and_argument_errors():
 
 def test_backward_refuses_gradient_layouts_that_overlap():
     """A K broadcast over heads (zero head stride) is a valid forward input, but
-    its gradient cannot be written in that layout: the backward refuses
-    before any launch."""
+    its gradient cannot be written in that layout: both backward entry points
+    refuse before any launch."""
     L = B.lib()
     good = ctypes.c_void_p(0x10000)
     p = B.Plan(attn(strides={"bt_stride": (256 * 128, 0, 128)}))
@@ -234,4 +234,27 @@ def test_backward_refuses_gradient_layouts_that_overlap():
                         p.bwd_workspace, None)
     assert B.STATUS[st] == "FAB_ERR_BAD_SHAPE"
     assert "Bt" in L.fab_last_error().decode()
+    st = L.fab_backward_noalloc(p._ptr, good, good, good, good, good, good, good, good, good, None)
+    assert B.STATUS[st] == "FAB_ERR_BAD_SHAPE"
 
+
+def test_backward_noalloc_argument_errors_before_any_launch():
+    L = B.lib()
+    vp = ctypes.c_void_p
+    good = vp(0x10000)
+    p = B.Plan(attn())
+    fn = L.fab_backward_noalloc
+    assert B.STATUS[fn(None, good, good, good, good, good, good, good, good, good, None)] == \
+        "FAB_ERR_NULL_ARG"
+    assert B.STATUS[fn(p._ptr, good, None, good, good, good, good, good, good, good, None)] == \
+        "FAB_ERR_NULL_ARG"
+    assert B.STATUS[fn(p._ptr, good, good, good, None, good, good, good, good, good, None)] == \
+        "FAB_ERR_NULL_ARG"
+    assert B.STATUS[fn(p._ptr, vp(0x10008), good, good, good, good, good, good, good, good,
+                       None)] == "FAB_ERR_ALIGNMENT"
+    # 64 heads x 2^17 rows x 8 bytes of workspace = 64 MiB > the 32 MiB static scratch
+    big = B.Plan(attn(heads_a=64, heads_bc=64, m=1 << 17, n=1 << 17))
+    assert big.bwd_workspace > 32 << 20
+    st = fn(big._ptr, good, good, good, good, good, good, good, good, good, None)
+    assert B.STATUS[st] == "FAB_ERR_WORKSPACE_TOO_SMALL"
+    assert "32" in L.fab_last_error().decode() or str(32 << 20) in L.fab_last_error().decode()
