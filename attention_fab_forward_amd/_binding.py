@@ -16,6 +16,8 @@ LIB_PATH = os.environ.get("FAB_LIBRARY") or os.path.join(
 ABI_VERSION = 3
 
 SOFTMAX, GELU_ERF = 0, 1
+# fp32 softmax kernel family (fab_variant): the library chooses, plain FMA, matrix cores
+VARIANT_AUTO, VARIANT_F32_FMA, VARIANT_F32_MFMA = 0, 1, 2
 MASK_NONE, MASK_CAUSAL = 0, 1
 BF16, F32 = 0, 1
 
@@ -40,7 +42,7 @@ class FabProblem(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("batch", ctypes.c_int64), ("heads_a", ctypes.c_int64),
         ("heads_bc", ctypes.c_int64), ("m", ctypes.c_int64), ("n", ctypes.c_int64),
         ("k", ctypes.c_int64), ("p", ctypes.c_int64), ("scale", ctypes.c_float),
-        ("reserved0", ctypes.c_int32), ("a_stride", ctypes.c_int64 * 3),
+        ("variant", ctypes.c_int32), ("a_stride", ctypes.c_int64 * 3),
         ("bt_stride", ctypes.c_int64 * 3), ("c_stride", ctypes.c_int64 * 3),
         ("o_stride", ctypes.c_int64 * 3), ("q_offset", ctypes.c_int64),
         ("k_offset", ctypes.c_int64),
@@ -134,9 +136,10 @@ def check(status):
 
 
 def make_problem(f, dtype, batch, heads_a, heads_bc, m, n, k, p, scale, causal=False,
-                 strides=None, abi_version=ABI_VERSION, q_offset=0, k_offset=0):
+                 strides=None, abi_version=ABI_VERSION, q_offset=0, k_offset=0, variant=0):
     prob = FabProblem()
     prob.abi_version = abi_version
+    prob.variant = variant
     prob.f, prob.dtype = f, dtype
     prob.mask = MASK_CAUSAL if causal else MASK_NONE
     prob.batch, prob.heads_a, prob.heads_bc = batch, heads_a, heads_bc
@@ -310,9 +313,9 @@ def _get_plan(key, build):
     return plan
 
 
-def attention_plan(q, k, v, causal, scale, q_offset=0, k_offset=0, o=None):
+def attention_plan(q, k, v, causal, scale, q_offset=0, k_offset=0, o=None, variant=0):
     """Plan for these tensors' shapes and strides; O packed [b, m, hq, d]
-    unless `o` gives its layout."""
+    unless `o` gives its layout.  variant: fp32 kernel family (VARIANT_*)."""
     b, m, hq, d = q.shape
     n, hkv = k.shape[1], k.shape[2]
     o_stride = (_strides4(o) if o is not None
@@ -320,10 +323,11 @@ def attention_plan(q, k, v, causal, scale, q_offset=0, k_offset=0, o=None):
     strides = {"a_stride": _strides4(q), "bt_stride": _strides4(k), "c_stride": _strides4(v),
                "o_stride": o_stride}
     key = ("softmax", q.dtype, b, hq, hkv, m, n, d, v.shape[3], float(scale), bool(causal),
-           tuple(sorted(strides.items())), int(q_offset), int(k_offset))
+           tuple(sorted(strides.items())), int(q_offset), int(k_offset), int(variant))
     return _get_plan(key, lambda: make_problem(SOFTMAX, _dtype_code(q), b, hq, hkv, m, n, d,
                                                v.shape[3], scale, causal, strides,
-                                               q_offset=q_offset, k_offset=k_offset))
+                                               q_offset=q_offset, k_offset=k_offset,
+                                               variant=variant))
 
 
 def mlp_plan(a, bt, c, scale):
@@ -343,7 +347,7 @@ def _stream():
 
 
 def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offset=0,
-            out=None):
+            out=None, variant=0):
     """O = f(scale * A Bt^T) C on the GPU.
 
     softmax: a = Q [b, m, hq, d], bt = K [b, n, hkv, d], c = V [b, n, hkv, d];
@@ -352,6 +356,8 @@ def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offse
     that see no key get O = 0, LSE = -inf.  out=(o, lse) writes there; o may
     have any layout with a contiguous last dimension (e.g. an exchange buffer).
     gelu: a [m, k], bt [n, k], c [n, p]; returns (O [m, p], None).  Default scale 1.
+    variant (fp32 softmax only): VARIANT_F32_FMA or VARIANT_F32_MFMA picks the
+    kernel family; 0 lets the library choose by size.
     """
     dev, dt = a.device, a.dtype
     if f == "softmax":
@@ -373,7 +379,7 @@ def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offse
         else:
             o = torch.empty((b, m, hq, c.shape[3]), dtype=dt, device=dev)
             lse = torch.empty((b, hq, m), dtype=torch.float32, device=dev)
-        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset, o)
+        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset, o, variant)
     elif f == "gelu":
         if causal:
             raise ValueError("GeLU takes no causal mask")
@@ -395,7 +401,7 @@ def forward(a, bt, c, f="softmax", causal=False, scale=None, q_offset=0, k_offse
 
 
 def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None, q_offset=0,
-             k_offset=0):
+             k_offset=0, variant=0):
     """Gradients (dA, dBt, dC) of <dO, O> for the forward above.  Over a key
     range (offsets) pass the merged O and LSE of all keys: dA is then the
     range's contribution to dQ.  O may have any layout (dO must share it);
@@ -416,7 +422,7 @@ def backward(a, bt, c, o, lse, do, f="softmax", causal=False, scale=None, q_offs
         if scale is None:
             scale = 1.0 / float(a.shape[3]) ** 0.5
         a, bt, c = (t if _distinct(t) else t.contiguous() for t in (a, bt, c))
-        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset, o)
+        plan = attention_plan(a, bt, c, causal, scale, q_offset, k_offset, o, variant)
     elif f == "gelu":
         mlp_shapes(a, bt, c, do)
         for name, t in (("a", a), ("bt", bt), ("c", c), ("do", do)):

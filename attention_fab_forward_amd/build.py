@@ -33,6 +33,7 @@ FLAGS = [
 FILE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_f32_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

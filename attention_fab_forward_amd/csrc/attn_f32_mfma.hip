@@ -1,0 +1,556 @@
+// Softmax attention in fp32 on the gfx950 fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32): forward, and a backward of three launches
+// (per-row constants, dK/dV, dQ).  For fp32 problems large enough to fill the
+// chip; the plain-FMA kernels of attn_f32.hip serve the small, latency-bound
+// ones.  Every operation stays in fp32 (products, sums, exponentials).
+//
+// Definitions as in the other attention kernels: O = softmax(scale Q K^T
+// [+ causal mask]) V, the block O = f(A B) C of the "Memory-efficient tensor
+// parallelism" abstract, tiled so the score matrix is never stored ("Ulysses
+// Sequence Parallelism", "Contexte Technique"; causal index mask per "AutoSP"
+// 2.A), and its derivative with P recomputed from the saved log-sum-exp
+// ("AutoSP" 2.B):
+//   dP = dO V^T, D_i = rowsum(dO_i * O_i), dS = P (dP - D),
+//   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
+//
+// Layout of one 32 x 32 x 2 product: lane l supplies A[l % 32][l / 32] and
+// B[l / 32][l % 32] and holds D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] in
+// accumulator slot r.  A contraction over 8 g + 4 h + e (h = l / 32, e = 0..3)
+// in product 4 g + e therefore reads each lane's operand as 4 consecutive
+// values, and the contraction index of product j over a 32-row accumulator
+// (8 (j / 4) + 4 h + j % 4) is exactly slot j of that accumulator: S (or dS)
+// slots are the B operands of the products that follow, with no exchange.
+//  * forward: S^T = K Q^T (K rows from LDS, Q in registers), lanes own
+//    queries; O^T += V^T P^T.
+//  * dK/dV: S = Q K^T, dP = dO V^T (Q, dO rows from LDS, K, V in registers),
+//    lanes own keys; dV^T += dO^T P, dK^T += Q^T dS.
+//  * dQ: S^T = K Q^T, dP^T = V dO^T, lanes own queries; dQ^T += K^T dS^T.
+// Tiles of 32 rows are copied global -> LDS asynchronously (double
+// buffered); 16-byte chunk c of row r sits at chunk c ^ (r mod 16), which
+// keeps the 16-byte row reads of 16 lanes on distinct banks.
+#include "fab_device.h"
+#include "fab_internal.h"
+
+namespace fab {
+namespace {
+
+__device__ __forceinline__ f32x16 mfma32f(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+constexpr int kMfmaF32Waves = 4;  // waves per workgroup, 32 rows each
+// Workgroups per CU of the forward and dQ kernels: at d = 128 a wave's
+// operands and accumulators take more than the 256 registers two waves per
+// SIMD leave, so it runs one wave per SIMD with the whole register file.
+template <int D>
+constexpr int f32_mfma_occupancy() { return D == 128 ? 1 : 2; }
+
+template <int D>
+struct F32T {
+  static constexpr int RB = D * 4;          // row bytes
+  static constexpr int ROWS = 32;           // rows of a tile
+  static constexpr int BYTES = ROWS * RB;   // 8 or 16 KiB
+  static constexpr int G = D / 8;           // contraction groups (4 values per half-wave)
+  static constexpr int DT = D / 32;         // 32-wide output tiles
+  static constexpr int CPW = BYTES / 1024 / kMfmaF32Waves;  // 1 KiB copies per wave per tile
+  static_assert(CPW * 1024 * kMfmaF32Waves == BYTES, "tile copies split evenly over the waves");
+};
+
+__device__ __forceinline__ int fswz(int r, int c) { return c ^ (r & 15); }
+
+// 16 bytes (4 floats, logical chunk c) of row r of a tile.
+template <int D>
+__device__ __forceinline__ f32x4 tile_row4(const char* tile, int r, int c) {
+  return *reinterpret_cast<const f32x4*>(tile + r * F32T<D>::RB + 16 * fswz(r, c));
+}
+// Element (r, col) of a tile.
+template <int D>
+__device__ __forceinline__ float tile_at(const char* tile, int r, int col) {
+  return *reinterpret_cast<const float*>(tile + r * F32T<D>::RB + 16 * fswz(r, col >> 2) +
+                                         4 * (col & 3));
+}
+
+// Per-lane sources of the asynchronous copies of a 32-row tile: lane j of
+// this wave's copy i lands at tile byte (wave CPW + i) 1 KiB + 16 j, i.e. row
+// `row[i]`, physical chunk p, and fetches logical chunk p ^ (row mod 16).
+template <int D>
+struct F32Copy {
+  uint32_t off[F32T<D>::CPW];  // byte offset from the tile's first source row
+  int row[F32T<D>::CPW];
+};
+
+template <int D>
+__device__ __forceinline__ F32Copy<D> f32_copy_offsets(int64_t sr, int wave, int lane) {
+  using T = F32T<D>;
+  F32Copy<D> t;
+#pragma unroll
+  for (int i = 0; i < T::CPW; ++i) {
+    const int byte = (wave * T::CPW + i) * 1024 + 16 * lane;
+    const int r = byte / T::RB, pc = (byte % T::RB) / 16;
+    t.row[i] = r;
+    t.off[i] = (uint32_t)(4 * (r * sr + 4 * fswz(r, pc)));
+  }
+  return t;
+}
+
+// Copy rows [r0, r0 + 32) of a [rows, D] fp32 matrix into a tile; rows at or
+// past nrows (ragged last tile only, r0 < nrows) repeat row nrows - 1, whose
+// contributions the callers mask.
+template <int D>
+__device__ __forceinline__ void f32_issue(const F32Copy<D>& t, const float* base, int64_t sr,
+                                          int r0, int nrows, char* tile, int wave) {
+  using T = F32T<D>;
+  const char* src = reinterpret_cast<const char*>(base + (int64_t)r0 * sr);
+  char* dst = tile + wave * T::CPW * 1024;
+  if (r0 + 32 <= nrows) {
+#pragma unroll
+    for (int i = 0; i < T::CPW; ++i) dma16(src, t.off[i], dst + i * 1024);
+  } else {
+#pragma unroll
+    for (int i = 0; i < T::CPW; ++i) {
+      const int64_t shift = min(t.row[i], nrows - 1 - r0) - t.row[i];
+      dma16_at(src + t.off[i] + 4 * shift * sr, dst + i * 1024);
+    }
+  }
+}
+
+// Values of a 32-row tile's per-row constants (LSE log2 e, -D) for
+// accumulator slot r: row 8 (r / 4) + 4 h + r % 4.
+__device__ __forceinline__ void slot_consts(const float* v, int h, float (&out)[16]) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(v) + h;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 x = p[2 * q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * q + e] = x[e];
+  }
+}
+
+// Stores one 32 x 32 transposed accumulator tile (slot r: column
+// 8 (r / 4) + 4 h + r % 4 of the lane's row) times `mul`.
+__device__ __forceinline__ void store_row_tile(float* row, const f32x16& v, int h, float mul) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<f32x4*>(row + 8 * q + 4 * h) =
+        f32x4{v[4 * q] * mul, v[4 * q + 1] * mul, v[4 * q + 2] * mul, v[4 * q + 3] * mul};
+}
+
+// Sum of the contraction over d of a row operand read from a tile (row lq)
+// against this lane's register operand x (4 values per group), in two
+// interleaved accumulators so consecutive products do not depend on each
+// other.
+template <int D>
+__device__ __forceinline__ f32x16 row_product(const char* tile, int lq, int h,
+                                              const f32x4 (&x)[F32T<D>::G]) {
+  f32x16 acc[2] = {};
+#pragma unroll
+  for (int g = 0; g < F32T<D>::G; ++g) {
+    const f32x4 y = tile_row4<D>(tile, lq, 2 * g + h);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e & 1] = mfma32f(y[e], x[g][e], acc[e & 1]);
+  }
+  return acc[0] + acc[1];
+}
+
+// out^T += tile^T S^T over the tile's 32 rows: product j takes tile row
+// 8 (j / 4) + 4 h + j % 4 (the row of slot j) and column 32 t + lq.
+template <int D>
+__device__ __forceinline__ void col_product(const char* tile, int lq, int h, const float (&s)[16],
+                                            f32x16 (&out)[F32T<D>::DT]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int r = 8 * (j >> 2) + 4 * h + (j & 3);
+#pragma unroll
+    for (int t = 0; t < F32T<D>::DT; ++t)
+      out[t] = mfma32f(tile_at<D>(tile, r, 32 * t + lq), s[j], out[t]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// forward: workgroup = 4 waves x 32 queries of one head; key blocks of 32
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void attn_fwd_f32_mfma_kernel(AttnArgs a) {
+  using T = F32T<D>;
+  constexpr int NW = kMfmaF32Waves, BM = 32 * NW, BN = 32;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES];
+  auto ktile = [&](int i) { return smem + (i & 1) * T::BYTES; };
+  auto vtile = [&](int i) { return smem + (2 + (i & 1)) * T::BYTES; };
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lq = lane & 31, h = lane >> 5;
+  const int nqb = (a.m + BM - 1) / BM;
+  int bh, qi;
+  xcd_map(blockIdx.x, a.b * a.hq, nqb, bh, qi);
+  const int hh = bh % a.hq, bi = bh / a.hq;
+  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
+  const int g = hh / a.group;
+  const float* qbase = static_cast<const float*>(a.q) + bi * a.q_sb + hh * a.q_sh;
+  const float* kbase = static_cast<const float*>(a.k) + bi * a.k_sb + g * a.k_sh;
+  const float* vbase = static_cast<const float*>(a.v) + bi * a.v_sb + g * a.v_sh;
+
+  const int q0 = qb * BM + wave * 32;
+  const int myq = q0 + lq;
+  const int kend = CAUSAL ? min(a.n, max(0, qb * BM + BM + a.diag)) : a.n;
+  const int nkb = (kend + BN - 1) / BN;
+  const int nkw = q0 >= a.m ? 0
+                  : CAUSAL ? (q0 + 31 + a.diag < 0 ? 0 : min(nkb, (q0 + 31 + a.diag) / BN + 1))
+                           : nkb;
+  const F32Copy<D> ck = f32_copy_offsets<D>(a.k_sr, wave, lane);
+  const F32Copy<D> cv = f32_copy_offsets<D>(a.v_sr, wave, lane);
+  auto copy = [&](int kb) {
+    f32_issue<D>(ck, kbase, a.k_sr, kb * BN, a.n, ktile(kb), wave);
+    f32_issue<D>(cv, vbase, a.v_sr, kb * BN, a.n, vtile(kb), wave);
+  };
+  if (nkb > 0) copy(0);
+
+  f32x4 qf[T::G];  // Q[myq][8 g + 4 h .. + 3]
+#pragma unroll
+  for (int gi = 0; gi < T::G; ++gi)
+    qf[gi] = myq < a.m ? *reinterpret_cast<const f32x4*>(qbase + (int64_t)myq * a.q_sr + 8 * gi + 4 * h)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x16 o[T::DT] = {};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float cs = a.scale_log2;
+  wait_vmem();
+  lds_barrier();
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) copy(kb + 1);
+    if (kb < nkw) {
+      // slot r: key kb BN + 8 (r / 4) + 4 h + r % 4 of query myq
+      const f32x16 sacc = row_product<D>(ktile(kb), lq, h, qf);
+      float s[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = sacc[r];
+      const int key0 = kb * BN;
+      if ((CAUSAL && key0 + BN - 1 > q0 + a.diag) || key0 + BN > a.n) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if ((CAUSAL && key > myq + a.diag) || key >= a.n) s[r] = -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = pair_max(mx) * cs;
+      // the reference maximum moves only when a probability would exceed 2^8
+      const float m_new = mx > m_run + 8.f ? mx : m_run;
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_ref);
+      const bool rescale = m_new != m_run;
+      float lsum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = fast_exp2(fmaf(s[r], cs, -m_ref));
+        lsum += s[r];
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+      if (__ballot(rescale)) {
+#pragma unroll
+        for (int t = 0; t < T::DT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      }
+      col_product<D>(vtile(kb), lq, h, s, o);
+    }
+    wait_vmem();
+    lds_barrier();
+  }
+
+  // rows that saw no key (offset causal masks): O = 0, LSE = -inf
+  const float l_tot = pair_sum(l_run);
+  if (myq < a.m) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* orow = static_cast<float*>(a.o_out) + bi * a.o_sb + hh * a.o_sh + (int64_t)myq * a.o_sr;
+#pragma unroll
+    for (int t = 0; t < T::DT; ++t) store_row_tile(orow + 32 * t, o[t], h, inv);
+    if (h == 0)
+      a.lse[((int64_t)bi * a.hq + hh) * a.m + myq] =
+          l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward per-row constants: delta = -rowsum(dO * O), lse2 = LSE log2(e)
+// (+inf for a row without keys, so its probabilities are exactly 0)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(AttnArgs a) {
+  constexpr int LPR = D / 4;  // lanes per row, 4 floats each
+  constexpr int RPB = 256 / LPR;
+  const int tid = threadIdx.x;
+  const int64_t orow = (int64_t)blockIdx.x * RPB + tid / LPR;  // rows in O's [b, m, hq] order
+  const int part = tid % LPR;
+  const int64_t total = (int64_t)a.b * a.hq * a.m;
+  float acc = 0.f;
+  int64_t row = 0;
+  if (orow < total) {
+    const int64_t bm = orow / a.hq;
+    const int64_t hh = orow - bm * a.hq;
+    const int64_t bi = bm / a.m;
+    const int64_t i = bm - bi * a.m;
+    row = (bi * a.hq + hh) * a.m + i;
+    const int64_t off = bi * a.o_sb + hh * a.o_sh + i * a.o_sr + 4 * part;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.o) + off);
+    const f32x4 y = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.dout) + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(x[e], y[e], acc);
+  }
+#pragma unroll
+  for (int sft = 1; sft < LPR; sft <<= 1) acc += __shfl_xor(acc, sft, 64);
+  if (orow < total && part == 0) {
+    a.delta[row] = -acc;
+    const float l = a.lse_in[row];
+    a.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: workgroup = 4 waves x 32 keys of one kv head; query blocks of 32
+// (of every query head of the group) stream through two LDS stages.
+// ---------------------------------------------------------------------------
+template <int D>
+struct F32DkdvLds {
+  static constexpr int Q = 0;
+  static constexpr int DO = F32T<D>::BYTES;
+  static constexpr int LSE = 2 * F32T<D>::BYTES;  // 64 floats (rows 32.. unused)
+  static constexpr int DLT = LSE + 256;
+  static constexpr int STAGE = DLT + 256;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kernel(AttnArgs a) {
+  using T = F32T<D>;
+  using L = F32DkdvLds<D>;
+  constexpr int KB = 32 * kMfmaF32Waves, QB = 32;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lq = lane & 31, h = lane >> 5;
+  const int nkb = (a.n + KB - 1) / KB;
+  int gh, kblk;
+  xcd_map(blockIdx.x, a.b * a.hkv, nkb, gh, kblk);  // low key blocks (most queries) first
+  const int g = gh % a.hkv, bi = gh / a.hkv;
+  const int k0w = kblk * KB + wave * 32;
+  const int mykey = k0w + lq;
+  const bool live = k0w < a.n;
+  const float cs = a.scale_log2;
+  const int qb_first = CAUSAL ? max(0, kblk * KB - a.diag) / QB : 0;
+  const int nqb = (a.m + QB - 1) / QB;
+  const int steps_per_head = max(0, nqb - qb_first);
+  const int steps = steps_per_head * a.group;
+
+  const F32Copy<D> cq = f32_copy_offsets<D>(a.q_sr, wave, lane);
+  const F32Copy<D> co = f32_copy_offsets<D>(a.o_sr, wave, lane);
+  auto copy = [&](int hq_idx, int q0, char* st) {
+    const float* qb = static_cast<const float*>(a.q) + bi * a.q_sb + hq_idx * a.q_sh;
+    const float* ob = static_cast<const float*>(a.dout) + bi * a.o_sb + hq_idx * a.o_sh;
+    f32_issue<D>(cq, qb, a.q_sr, q0, a.m, st + L::Q, wave);
+    f32_issue<D>(co, ob, a.o_sr, q0, a.m, st + L::DO, wave);
+    const int64_t r = ((int64_t)bi * a.hq + hq_idx) * a.m;
+    const int i = min(q0 + lane, a.m - 1);  // lanes past the block copy a valid row, unused
+    if (wave == 0) dma4_at(a.lse2 + r + i, st + L::LSE);
+    if (wave == 1) dma4_at(a.delta + r + i, st + L::DLT);
+  };
+  if (steps > 0) copy(g * a.group, qb_first * QB, smem);
+
+  f32x4 kf[T::G], vf[T::G];  // K, V rows of this lane's key
+  {
+    const float* kr = static_cast<const float*>(a.k) + bi * a.k_sb + g * a.k_sh + (int64_t)mykey * a.k_sr;
+    const float* vr = static_cast<const float*>(a.v) + bi * a.v_sb + g * a.v_sh + (int64_t)mykey * a.v_sr;
+#pragma unroll
+    for (int gi = 0; gi < T::G; ++gi) {
+      kf[gi] = mykey < a.n ? *reinterpret_cast<const f32x4*>(kr + 8 * gi + 4 * h) : f32x4{0.f, 0.f, 0.f, 0.f};
+      vf[gi] = mykey < a.n ? *reinterpret_cast<const f32x4*>(vr + 8 * gi + 4 * h) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  f32x16 dk[T::DT] = {}, dv[T::DT] = {};
+  wait_vmem();
+  lds_barrier();
+
+  int hc = 0, qc = 0;  // (head, block) of this step
+  for (int step = 0; step < steps; ++step) {
+    int hn = hc, qn = qc;
+    if (++qn == steps_per_head) {
+      qn = 0;
+      ++hn;
+    }
+    if (step + 1 < steps) copy(g * a.group + hn, (qb_first + qn) * QB, smem + ((step + 1) & 1) * L::STAGE);
+    const int q0 = (qb_first + qc) * QB;
+    hc = hn, qc = qn;
+    const char* st = smem + (step & 1) * L::STAGE;
+    if (live && (!CAUSAL || q0 + QB - 1 + a.diag >= k0w)) {
+      // slot r: query q0 + 8 (r / 4) + 4 h + r % 4 of key mykey
+      const f32x16 sacc = row_product<D>(st + L::Q, lq, h, kf);
+      float lse2[16], ndl[16], p[16];
+      slot_consts(reinterpret_cast<const float*>(st + L::LSE), h, lse2);
+      slot_consts(reinterpret_cast<const float*>(st + L::DLT), h, ndl);
+      const bool need_mask = (CAUSAL && q0 + a.diag < k0w + 31) || q0 + QB > a.m;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(sacc[r], cs, -lse2[r]));
+        if (need_mask) {
+          const int q = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if ((CAUSAL && q + a.diag < mykey) || q >= a.m) p[r] = 0.f;
+        }
+      }
+      col_product<D>(st + L::DO, lq, h, p, dv);  // dV^T += dO^T P
+      const f32x16 dpacc = row_product<D>(st + L::DO, lq, h, vf);
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dpacc[r] + ndl[r]);
+      col_product<D>(st + L::Q, lq, h, ds, dk);  // dK^T += Q^T dS
+    }
+    wait_vmem();
+    lds_barrier();
+  }
+
+  if (!live || mykey >= a.n) return;
+  float* dvrow = static_cast<float*>(a.dv) + bi * a.v_sb + g * a.v_sh + (int64_t)mykey * a.v_sr;
+  float* dkrow = static_cast<float*>(a.dk) + bi * a.k_sb + g * a.k_sh + (int64_t)mykey * a.k_sr;
+#pragma unroll
+  for (int t = 0; t < T::DT; ++t) {
+    store_row_tile(dvrow + 32 * t, dv[t], h, 1.f);
+    store_row_tile(dkrow + 32 * t, dk[t], h, a.scale);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: workgroup = 4 waves x 32 queries of one query head; key blocks of 32
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void attn_dq_f32_mfma_kernel(AttnArgs a) {
+  using T = F32T<D>;
+  constexpr int NW = kMfmaF32Waves, BM = 32 * NW, BN = 32;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES];
+  auto ktile = [&](int i) { return smem + (i & 1) * T::BYTES; };
+  auto vtile = [&](int i) { return smem + (2 + (i & 1)) * T::BYTES; };
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lq = lane & 31, h = lane >> 5;
+  const int nqb = (a.m + BM - 1) / BM;
+  int bh, qi;
+  xcd_map(blockIdx.x, a.b * a.hq, nqb, bh, qi);
+  const int hh = bh % a.hq, bi = bh / a.hq;
+  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
+  const int g = hh / a.group;
+  const float* kbase = static_cast<const float*>(a.k) + bi * a.k_sb + g * a.k_sh;
+  const float* vbase = static_cast<const float*>(a.v) + bi * a.v_sb + g * a.v_sh;
+
+  const int q0 = qb * BM + wave * 32;
+  const int myq = q0 + lq;
+  const bool qlive = myq < a.m;
+  const int kend = CAUSAL ? min(a.n, max(0, qb * BM + BM + a.diag)) : a.n;
+  const int nkb = (kend + BN - 1) / BN;
+  const F32Copy<D> ck = f32_copy_offsets<D>(a.k_sr, wave, lane);
+  const F32Copy<D> cv = f32_copy_offsets<D>(a.v_sr, wave, lane);
+  auto copy = [&](int kb) {
+    f32_issue<D>(ck, kbase, a.k_sr, kb * BN, a.n, ktile(kb), wave);
+    f32_issue<D>(cv, vbase, a.v_sr, kb * BN, a.n, vtile(kb), wave);
+  };
+  if (nkb > 0) copy(0);
+
+  f32x4 qf[T::G], df[T::G];  // Q, dO rows of this lane's query
+  {
+    const float* qr = static_cast<const float*>(a.q) + bi * a.q_sb + hh * a.q_sh + (int64_t)myq * a.q_sr;
+    const float* dr = static_cast<const float*>(a.dout) + bi * a.o_sb + hh * a.o_sh + (int64_t)myq * a.o_sr;
+#pragma unroll
+    for (int gi = 0; gi < T::G; ++gi) {
+      qf[gi] = qlive ? *reinterpret_cast<const f32x4*>(qr + 8 * gi + 4 * h) : f32x4{0.f, 0.f, 0.f, 0.f};
+      df[gi] = qlive ? *reinterpret_cast<const f32x4*>(dr + 8 * gi + 4 * h) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  const int64_t ridx = ((int64_t)bi * a.hq + hh) * a.m + myq;
+  const float lse2 = qlive ? a.lse2[ridx] : INFINITY;
+  const float ndl = qlive ? a.delta[ridx] : 0.f;
+  f32x16 dq[T::DT] = {};
+  const float cs = a.scale_log2;
+  wait_vmem();
+  lds_barrier();
+
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) copy(kb + 1);
+    const int key0 = kb * BN;
+    if (q0 < a.m && (!CAUSAL || key0 <= q0 + 31 + a.diag)) {
+      // slot r: key key0 + 8 (r / 4) + 4 h + r % 4 of query myq
+      const f32x16 sacc = row_product<D>(ktile(kb), lq, h, qf);
+      const f32x16 dpacc = row_product<D>(vtile(kb), lq, h, df);
+      const bool need_mask = (CAUSAL && key0 + BN - 1 > q0 + a.diag) || key0 + BN > a.n;
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(sacc[r], cs, -lse2));
+        if (need_mask) {
+          const int key = key0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if ((CAUSAL && key > myq + a.diag) || key >= a.n) p = 0.f;
+        }
+        ds[r] = p * (dpacc[r] + ndl);
+      }
+      col_product<D>(ktile(kb), lq, h, ds, dq);  // dQ^T += K^T dS^T
+    }
+    wait_vmem();
+    lds_barrier();
+  }
+
+  if (!qlive) return;
+  float* out = static_cast<float*>(a.dq) + bi * a.q_sb + hh * a.q_sh + (int64_t)myq * a.q_sr;
+#pragma unroll
+  for (int t = 0; t < T::DT; ++t) store_row_tile(out + 32 * t, dq[t], h, a.scale);
+}
+
+template <int D>
+hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
+  const int nqb = (a.m + 32 * kMfmaF32Waves - 1) / (32 * kMfmaF32Waves);
+  const dim3 grid((unsigned)nqb * a.hq * a.b), block(64 * kMfmaF32Waves);
+  if (a.causal)
+    FAB_TIMED("attn_fwd_f32_mfma", s, hipLaunchKernelGGL((attn_fwd_f32_mfma_kernel<D, true>), grid, block, 0, s, a));
+  else
+    FAB_TIMED("attn_fwd_f32_mfma", s, hipLaunchKernelGGL((attn_fwd_f32_mfma_kernel<D, false>), grid, block, 0, s, a));
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
+  {
+    constexpr int rpb = 256 / (D / 4);
+    const int64_t rows = (int64_t)a.b * a.hq * a.m;
+    const dim3 gp((unsigned)((rows + rpb - 1) / rpb)), block(256);
+    FAB_TIMED("attn_bwd_prep_f32", s, hipLaunchKernelGGL((attn_bwd_prep_f32_kernel<D>), gp, block, 0, s, a));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int kb = 32 * kMfmaF32Waves;
+  const dim3 gk((unsigned)((a.n + kb - 1) / kb) * a.hkv * a.b);
+  const dim3 gq((unsigned)((a.m + kb - 1) / kb) * a.hq * a.b);
+  const dim3 block(64 * kMfmaF32Waves);
+  if (a.causal) {
+    FAB_TIMED("attn_bwd_dkdv_f32_mfma", s, hipLaunchKernelGGL((attn_dkdv_f32_mfma_kernel<D, true>), gk, block, 0, s, a));
+    FAB_TIMED("attn_bwd_dq_f32_mfma", s, hipLaunchKernelGGL((attn_dq_f32_mfma_kernel<D, true>), gq, block, 0, s, a));
+  } else {
+    FAB_TIMED("attn_bwd_dkdv_f32_mfma", s, hipLaunchKernelGGL((attn_dkdv_f32_mfma_kernel<D, false>), gk, block, 0, s, a));
+    FAB_TIMED("attn_bwd_dq_f32_mfma", s, hipLaunchKernelGGL((attn_dq_f32_mfma_kernel<D, false>), gq, block, 0, s, a));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_f32_mfma(const AttnArgs& a, int d, hipStream_t s) {
+  if (d == 128) return fwd_d<128>(a, s);
+  if (d == 64) return fwd_d<64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_bwd_f32_mfma(const AttnArgs& a, int d, hipStream_t s) {
+  if (d == 128) return bwd_d<128>(a, s);
+  if (d == 64) return bwd_d<64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fab

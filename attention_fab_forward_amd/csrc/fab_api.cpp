@@ -120,6 +120,7 @@ struct fab_plan_s {
   size_t fwd_ws;
   size_t bwd_ws;
   int mlp_splits;
+  bool f32_mfma;  // fp32 softmax on the matrix cores
   char desc[256];
 };
 
@@ -312,7 +313,10 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
     return fail(FAB_ERR_UNSUPPORTED, "unknown mask %d", q.mask);
   if (q.dtype != FAB_BF16 && q.dtype != FAB_F32)
     return fail(FAB_ERR_UNSUPPORTED, "unknown dtype %d", q.dtype);
-  if (q.reserved0 != 0) return fail(FAB_ERR_BAD_SHAPE, "reserved0 must be 0");
+  if (q.variant < FAB_VARIANT_AUTO || q.variant > FAB_VARIANT_F32_MFMA)
+    return fail(FAB_ERR_BAD_SHAPE, "unknown variant %d", q.variant);
+  if (q.variant != FAB_VARIANT_AUTO && !(q.f == FAB_F_SOFTMAX && q.dtype == FAB_F32))
+    return fail(FAB_ERR_UNSUPPORTED, "variant %d applies to fp32 softmax problems only", q.variant);
   if (q.batch < 1 || q.heads_a < 1 || q.heads_bc < 1 || q.m < 1 || q.n < 1 || q.k < 1 || q.p < 1)
     return fail(FAB_ERR_BAD_SHAPE, "sizes must be >= 1 (batch %lld heads %lld/%lld m %lld n %lld "
                 "k %lld p %lld)", (long long)q.batch, (long long)q.heads_a,
@@ -341,6 +345,8 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
   const int64_t unit = q.dtype == FAB_BF16 ? 8 : 4;
   fab_plan_s tmp;
   tmp.prob = q;
+  tmp.f32_mfma = false;
+  tmp.mlp_splits = 0;
   resolve(q.a_stride, q.m, q.heads_a, q.k, tmp.as);
   resolve(q.bt_stride, q.n, q.heads_bc, q.k, tmp.bs);
   resolve(q.c_stride, q.n, q.heads_bc, q.p, tmp.cs);
@@ -365,11 +371,28 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
     if (q.k != 64 && q.k != 128)
       return fail(FAB_ERR_UNSUPPORTED, "softmax head dim %lld not in {64, 128}", (long long)q.k);
     if (!(q.scale > 0.f)) return fail(FAB_ERR_UNSUPPORTED, "softmax scale must be > 0");
+    // the kernels' per-lane copy offsets are 32-bit byte offsets within a
+    // tile of up to 64 rows
+    for (const int64_t* sr : {&tmp.as[2], &tmp.bs[2], &tmp.cs[2], &tmp.os[2]})
+      if (*sr >= ((int64_t)1 << 24))
+        return fail(FAB_ERR_UNSUPPORTED, "row stride %lld is beyond this build's limit of 2^24 "
+                    "elements", (long long)*sr);
     tmp.fwd_ws = 0;
-    // bf16 path: -D and LSE * log2(e) per query row; the fp32 path forms D
-    // inside its backward kernel and needs no workspace
+    // fp32: the matrix-core kernels (or when asked) once the problem has at
+    // least 64 blocks of 128 queries and 2^22 unmasked (query, key) pairs;
+    // below that their few workgroups leave most of the chip idle and the
+    // plain-FMA kernels, with 4-16 rows per workgroup, finish first
+    const double pairs = (double)q.batch * q.heads_a * q.m * q.n *
+                         (q.mask == FAB_MASK_CAUSAL ? 0.5 : 1.0);
+    const int64_t qblocks = q.batch * q.heads_a * ((q.m + 127) / 128);
+    tmp.f32_mfma = q.dtype == FAB_F32 &&
+                   (q.variant == FAB_VARIANT_F32_MFMA ||
+                    (q.variant == FAB_VARIANT_AUTO && qblocks >= 64 &&
+                     pairs >= (double)((int64_t)1 << 22)));
+    // bf16 and fp32 matrix-core backward: -D and LSE * log2(e) per query row;
+    // the plain-FMA fp32 backward forms D inside its kernel (no workspace)
     const size_t rows = (size_t)q.batch * q.heads_a * q.m;
-    tmp.bwd_ws = q.dtype == FAB_BF16 ? round_up(rows * sizeof(float) * 2, 256) : 0;
+    tmp.bwd_ws = (q.dtype == FAB_BF16 || tmp.f32_mfma) ? round_up(rows * sizeof(float) * 2, 256) : 0;
     if (q.dtype == FAB_BF16)
       snprintf(tmp.desc, sizeof tmp.desc,
                "attention %s d=%lld %s group=%lld fwd[BM=%d BN=%d grid=%lld] "
@@ -379,9 +402,9 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
                (long long)((q.m + fab::kAttnFwdBM - 1) / fab::kAttnFwdBM * q.heads_a * q.batch),
                fab::kAttnBwdBM, fab::kAttnBwdKB, fab::kAttnBwdQB);
     else
-      snprintf(tmp.desc, sizeof tmp.desc, "attention %s d=%lld %s group=%lld (fp32 FMA)", dt,
+      snprintf(tmp.desc, sizeof tmp.desc, "attention %s d=%lld %s group=%lld (%s)", dt,
                (long long)q.k, q.mask == FAB_MASK_CAUSAL ? "causal" : "full",
-               (long long)(q.heads_a / q.heads_bc));
+               (long long)(q.heads_a / q.heads_bc), tmp.f32_mfma ? "fp32 MFMA" : "fp32 FMA");
   } else {
     if (q.mask != FAB_MASK_NONE) return fail(FAB_ERR_UNSUPPORTED, "GeLU takes no mask");
     if (q.q_offset || q.k_offset) return fail(FAB_ERR_UNSUPPORTED, "GeLU takes no mask offsets");
@@ -409,6 +432,7 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
   plan->fwd_ws = tmp.fwd_ws;
   plan->bwd_ws = tmp.bwd_ws;
   plan->mlp_splits = tmp.mlp_splits;
+  plan->f32_mfma = tmp.f32_mfma;
   plan->a_distinct = tmp.a_distinct;
   plan->bt_distinct = tmp.bt_distinct;
   plan->c_distinct = tmp.c_distinct;
@@ -499,6 +523,7 @@ fab_status fab_forward(const fab_plan_t* plan, const void* A, const void* Bt, co
     fab::AttnArgs a = attn_args(plan);
     a.q = A, a.k = Bt, a.v = C, a.o_out = O, a.lse = lse;
     e = q.dtype == FAB_BF16 ? fab::launch_attn_fwd_bf16(a, (int)q.k, s)
+        : plan->f32_mfma    ? fab::launch_attn_fwd_f32_mfma(a, (int)q.k, s)
                             : fab::launch_attn_fwd_f32(a, (int)q.k, s);
   } else {
     if (lse) return fail(FAB_ERR_UNSUPPORTED, "fab_forward: GeLU takes no lse");
@@ -557,11 +582,12 @@ fab_status backward_launch(const char* who, const fab_plan_t* plan, const void* 
     fab::AttnArgs a = attn_args(plan);
     a.q = A, a.k = Bt, a.v = C, a.o = O, a.lse_in = lse, a.dout = dO;
     a.dq = dA, a.dk = dBt, a.dv = dC;
-    if (q.dtype == FAB_BF16) {  // the fp32 path uses no workspace
+    if (q.dtype == FAB_BF16 || plan->f32_mfma) {  // the fp32 FMA path uses no workspace
       a.delta = static_cast<float*>(workspace);
       a.lse2 = a.delta + (size_t)q.batch * q.heads_a * q.m;
     }
     e = q.dtype == FAB_BF16 ? fab::launch_attn_bwd_bf16(a, (int)q.k, s)
+        : plan->f32_mfma    ? fab::launch_attn_bwd_f32_mfma(a, (int)q.k, s)
                             : fab::launch_attn_bwd_f32(a, (int)q.k, s);
   } else {
     fab::MlpArgs a{};

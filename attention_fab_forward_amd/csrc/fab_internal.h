@@ -137,6 +137,8 @@ hipError_t launch_attn_merge(const MergeArgs& a, int d, bool bf16, hipStream_t s
 hipError_t launch_attn_bwd_bf16(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const AttnArgs& a, int d, hipStream_t s);
 hipError_t launch_attn_bwd_f32(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_fwd_f32_mfma(const AttnArgs& a, int d, hipStream_t s);
+hipError_t launch_attn_bwd_f32_mfma(const AttnArgs& a, int d, hipStream_t s);
 
 hipError_t launch_ulysses(const UlyssesArgs& a, bool pack, hipStream_t s);
 

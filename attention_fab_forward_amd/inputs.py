@@ -58,6 +58,11 @@ WORKLOADS = {
     "attn_causal_bf16_gqa2_n1048576_d128": Workload(
         "attn_causal_bf16_gqa2_n1048576_d128", 5, "softmax", "bf16", True, 1.0,
         1, 2, 1, 1 << 20, 128),
+    # fp32 causal attention large enough for the fp32 matrix cores:
+    # 8 heads, n = 4096, d = 128
+    "attn_causal_f32_h8_n4096_d128": Workload(
+        "attn_causal_f32_h8_n4096_d128", 6, "softmax", "f32", True, 1.0,
+        1, 8, 8, 4096, 128),
 }
 
 

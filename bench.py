@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 flop/clk, dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
+F32_MATRIX_PEAK_TFLOPS = 157.3  # dense fp32 MFMA
 WORKLOAD = "attn_causal_bf16_h32_n32768_d128"
 MLP_WORKLOAD = "mlp_gelu_m4096_k1024_n4096_p1024"
 
@@ -203,9 +204,16 @@ def time_workload(key, reps, torch, fab, back_to_back=False):
     kernels = {name: tot / cnt for name, (cnt, tot) in plan.kernel_times().items()}
     plan.set_timing(False)
     fwd_fl, bwd_fl, _ = attention_flops(w)
+    family = plan.describe()
     del q, k, v, do, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
-    return {"fwd_ms": fm, "bwd_ms": bm, "fwd_us": 1e3 * fm, "bwd_us": 1e3 * bm,
+    extra = {}
+    if w.dtype == "f32":
+        extra = {"fwd_pct_f32_matrix_peak": 100.0 * fwd_fl / fm / 1e9 / F32_MATRIX_PEAK_TFLOPS,
+                 "fwd_bwd_pct_f32_matrix_peak":
+                     100.0 * (fwd_fl + bwd_fl) / (fm + bm) / 1e9 / F32_MATRIX_PEAK_TFLOPS}
+    return {**extra, "plan": family, "fwd_ms": fm, "bwd_ms": bm, "fwd_us": 1e3 * fm,
+            "bwd_us": 1e3 * bm,
             "fwd_ms_min_max": [fms[0], fms[-1]], "bwd_ms_min_max": [bms[0], bms[-1]],
             "dtype": w.dtype, "fwd_tflops": fwd_fl / fm / 1e9,
             "fwd_bwd_tflops": (fwd_fl + bwd_fl) / (fm + bm) / 1e9,
@@ -631,8 +639,13 @@ def cpu_baseline(w, x, seconds, step_ms):
 
 def gpu_clock(tag):
     """Current GPU clocks from amd-smi (None where the tool or field is
-    missing); the raw JSON is kept, trimmed, for inspection."""
+    missing); the raw JSON is kept, trimmed, for inspection.  Skipped under
+    rocprofv3 (its variables are in the environment): the tool's child would
+    carry the profiler's library into a second program."""
     import subprocess
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return {"when": tag, "tool": None, "gfx_mhz": None,
+                "fields": "not read: running under rocprofv3"}
     for cmd in (["amd-smi", "metric", "-g", "0", "--clock", "--json"],
                 ["rocm-smi", "--showclocks", "--json"]):
         try:
@@ -679,7 +692,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip every measurement besides the benchmarked workload")
     ap.add_argument("--extras", default="all",
-                    help="comma list of extra measurements: sweep, workloads, merge, ulysses, "
+                    help="comma list of extra measurements: sweep, workloads, f32, merge, ulysses, "
                          "activation, mlp (default all)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run a plain device copy of this many MiB "
@@ -757,17 +770,19 @@ def main():
         # the sequence-parallel rank share's geometry (4 heads), up to its
         # full n = 2^17
         extras["peak_hbm_vs_seq_rank_share"] = peak_hbm_sweep(torch, fab, range(12, 18), 4, 4)
-    if "workloads" in want:
+    if "workloads" in want or "f32" in want:
         log("other workloads ...")
-        extras["workloads"] = {
+        # (repetitions, back to back); the fp32 ones alone with --extras f32
+        reps = {
             # latency-bound (microseconds of work): reported in us
-            "attn_f32_h1_n256_d64": time_workload("attn_f32_h1_n256_d64", 200, torch, fab,
-                                                  back_to_back=True),
-            "attn_causal_bf16_h4_n131072_d128": time_workload(
-                "attn_causal_bf16_h4_n131072_d128", 5, torch, fab),
-            "attn_causal_bf16_gqa2_n1048576_d128": time_workload(
-                "attn_causal_bf16_gqa2_n1048576_d128", 3, torch, fab),
+            "attn_f32_h1_n256_d64": (200, True),
+            "attn_causal_f32_h8_n4096_d128": (10, False),
+            "attn_causal_bf16_h4_n131072_d128": (5, False),
+            "attn_causal_bf16_gqa2_n1048576_d128": (3, False),
         }
+        extras["workloads"] = {
+            key: time_workload(key, r_, torch, fab, back_to_back=b2b)
+            for key, (r_, b2b) in reps.items() if "workloads" in want or "_f32_" in key}
     if "merge" in want:
         log("merge ...")
         extras["merge"] = time_merge(w, 20, torch, fab)

@@ -74,6 +74,13 @@ typedef enum {
 typedef enum { FAB_F_SOFTMAX = 0, FAB_F_GELU_ERF = 1 } fab_function;
 typedef enum { FAB_MASK_NONE = 0, FAB_MASK_CAUSAL = 1 } fab_mask;
 typedef enum { FAB_BF16 = 0, FAB_F32 = 1 } fab_dtype;
+/* Kernel family of an fp32 softmax problem (any other problem takes 0):
+ * FAB_VARIANT_F32_FMA, plain fp32 FMA kernels (for small problems, where
+ * launch latency dominates); FAB_VARIANT_F32_MFMA, the fp32 matrix cores
+ * (v_mfma_f32_32x32x2_f32).  Both compute in fp32 throughout; 0 chooses by
+ * size (the matrix cores once batch * heads_a * ceil(m / 128) >= 64 and
+ * there are 2^22 or more unmasked (query, key) pairs). */
+typedef enum { FAB_VARIANT_AUTO = 0, FAB_VARIANT_F32_FMA = 1, FAB_VARIANT_F32_MFMA = 2 } fab_variant;
 
 /* Full description of one problem.  Zero-initialise, then fill in. */
 typedef struct {
@@ -86,7 +93,7 @@ typedef struct {
   int64_t heads_bc;    /* heads of Bt and C (kv heads); divides heads_a       */
   int64_t m, n, k, p;  /* matrix sizes above                                  */
   float scale;         /* f is applied to scale * (A Bt^T)                    */
-  int32_t reserved0;   /* must be 0                                           */
+  int32_t variant;     /* fab_variant: 0 lets the library choose             */
   /* element strides {batch, head, row}; all-zero = packed [b, rows, h, cols] */
   int64_t a_stride[3];
   int64_t bt_stride[3];
@@ -111,7 +118,7 @@ typedef struct fab_plan_s fab_plan_t;
  *   GeLU, bf16:    batch == heads_a == heads_bc == 1, each of k and p in
  *                  {128, 256, 512, 1024}, any m, n >= 1, mask NONE.
  * Row strides must be multiples of 8 elements (bf16) or 4 (f32), and so must
- * the head and batch strides.  O's strides must give every output element its
+ * the head and batch strides; softmax row strides stay below 2^24 elements.  O's strides must give every output element its
  * own address (no zero or overlapping batch / head strides): FAB_ERR_BAD_SHAPE
  * otherwise.  A, Bt and C may be broadcast (say a zero head stride) for the
  * forward; fab_backward refuses such a plan, since each gradient takes its

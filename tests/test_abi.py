@@ -96,6 +96,16 @@ def status_of(prob):
      "FAB_OK"),
     # an exchange-buffer layout {batch Hl d, head d, row b Hl d} is one-to-one
     ({"batch": 3, "strides": {"o_stride": (4 * 128, 128, 3 * 4 * 128)}}, "FAB_OK"),
+    # fp32 kernel family: fp32 softmax only, known values only
+    ({"dtype": B.F32, "variant": B.VARIANT_F32_MFMA}, "FAB_OK"),
+    ({"dtype": B.F32, "variant": B.VARIANT_F32_FMA}, "FAB_OK"),
+    ({"variant": B.VARIANT_F32_MFMA}, "FAB_ERR_UNSUPPORTED"),
+    ({"dtype": B.F32, "variant": 3}, "FAB_ERR_BAD_SHAPE"),
+    ({"dtype": B.F32, "variant": -1}, "FAB_ERR_BAD_SHAPE"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "variant": 1},
+     "FAB_ERR_UNSUPPORTED"),
+    # row strides the kernels' 32-bit copy offsets cannot address
+    ({"strides": {"a_stride": (1 << 30, 1 << 24, 1 << 25)}}, "FAB_ERR_UNSUPPORTED"),
 ])
 def test_plan_validation(kw, expect):
     assert status_of(attn(**kw)) == expect
@@ -106,8 +116,24 @@ def test_plan_workspace_and_describe():
     assert p.fwd_workspace == 0
     assert p.bwd_workspace >= 4 * 256 * 4
     assert "attention bf16 d=128 causal" in p.describe()
-    # the fp32 backward forms D inside its kernel: no workspace
-    assert B.Plan(attn(dtype=B.F32, k=64, p=64)).bwd_workspace == 0
+    # the fp32 FMA backward forms D inside its kernel: no workspace
+    small = B.Plan(attn(dtype=B.F32, k=64, p=64))
+    assert small.bwd_workspace == 0 and "fp32 FMA" in small.describe()
+    # the fp32 matrix-core backward keeps -D and LSE log2(e) per row (8 bytes)
+    forced = B.Plan(attn(dtype=B.F32, k=64, p=64, variant=B.VARIANT_F32_MFMA))
+    assert "fp32 MFMA" in forced.describe() and forced.bwd_workspace >= 4 * 256 * 8
+
+
+@pytest.mark.parametrize("m,heads,causal,mfma", [
+    (256, 1, False, False),          # the small fp32 workload: plain FMA
+    (1024, 8, False, True),          # 64 query blocks, 2^23 pairs: matrix cores
+    (2048, 1, False, False),         # 2^22 pairs but only 16 query blocks
+    (8192, 1, True, True),           # 64 query blocks, 2^25 causal pairs
+    (512, 16, True, False),          # 64 query blocks, 2^21 causal pairs
+])
+def test_fp32_kernel_family_by_size(m, heads, causal, mfma):
+    p = B.Plan(attn(dtype=B.F32, heads_a=heads, heads_bc=heads, m=m, n=m, causal=causal))
+    assert ("fp32 MFMA" in p.describe()) == mfma, p.describe()
 
 
 def test_null_and_alignment_errors_before_any_launch():

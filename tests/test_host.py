@@ -34,6 +34,7 @@ def test_attention_work_counts():
         "attn_causal_bf16_h32_n32768_d128": (8_796_361_457_664, 21_990_903_644_160),
         "attn_causal_bf16_h4_n131072_d128": (17_592_320_262_144, 43_980_800_655_360),
         "attn_causal_bf16_gqa2_n1048576_d128": (562_950_490_292_224, 1_407_376_225_730_560),
+        "attn_causal_f32_h8_n4096_d128": (34_368_126_976, 85_920_317_440),
     }
     for key, (fwd, bwd) in expect.items():
         f, g, unit = b.attention_flops(WORKLOADS[key])
