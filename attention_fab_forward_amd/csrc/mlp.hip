@@ -33,18 +33,20 @@ constexpr int kPad = 64;        // padding of the packed copies' row count
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// GeLU' needs Phi(x) and the Gaussian density; both come from one
-// exponential with erf from Abramowitz and Stegun, Handbook of Mathematical
-// Functions, formula 7.1.26 (absolute error below 1.5e-7, far inside the bf16
-// rounding dH receives next), whose factor exp(-x^2 / 2) is the density's.
-// GeLU alone keeps the library erf (cheaper when the density is not needed).
+// GeLU = x Phi(x) and GeLU' = Phi(x) + x phi(x) take Phi from erf by
+// Abramowitz and Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (absolute error below 1.5e-7, far inside the bf16 rounding G and dH receive
+// next); its factor exp(-x^2 / 2) is also the density phi up to 1 / sqrt(2 pi).
+// The formula has no branches (the library erf switches between two
+// polynomials with a divergent branch), so its instructions can be scheduled
+// between the matrix products.
 struct NormalParts {
   float cdf;  // Phi(x)
   float e;    // exp(-x^2 / 2)
 };
 __device__ __forceinline__ NormalParts normal_parts(float x) {
   const float z = fabsf(x) * 0.7071067811865476f;
-  const float t = __frcp_rn(fmaf(0.3275911f, z, 1.f));
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.f));  // v_rcp_f32, 1 ulp
   float poly = fmaf(1.061405429f, t, -1.453152027f);
   poly = fmaf(poly, t, 1.421413741f);
   poly = fmaf(poly, t, -0.284496736f);
@@ -55,9 +57,7 @@ __device__ __forceinline__ NormalParts normal_parts(float x) {
   const float erf = x < 0.f ? -erf_abs : erf_abs;
   return {fmaf(0.5f, erf, 0.5f), e};
 }
-__device__ __forceinline__ float gelu_f(float x) {
-  return 0.5f * x * (1.f + erff(x * 0.7071067811865476f));
-}
+__device__ __forceinline__ float gelu_f(float x) { return x * normal_parts(x).cdf; }
 __device__ __forceinline__ float gelu_grad_f(float x) {
   const NormalParts n = normal_parts(x);
   return fmaf(x * 0.3989422804014327f, n.e, n.cdf);
@@ -73,7 +73,9 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
 //  * "column" fragments (second-product operands, X transposed): fragment
 //    (R, T, c), R over cols / 32, T over rows_pad / 32, c in {0, 1}, lane l:
 //    X[32 T + 16 (l / 32) + 8 c + e][32 R + perm_row(l % 32)]; stored at
-//    ((R * rows_pad / 32 + T) * 2 + c) * 512.
+//    ((T * cols / 32 + R) * 2 + c) * 512, so the fragments of one 32-row step
+//    T are contiguous (a step's copies spread over every L2 channel instead of
+//    landing 64 rows_pad bytes apart, on one channel).
 // Rows of X at or past `rows` read as zero.  rows_pad % 64 == 0, cols % 64 == 0.
 __global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* x, int64_t ld, int rows,
                                                         int cols, int64_t pieces, uint16_t* out) {
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64
   }
   __syncthreads();
   // write the 2 (R) x 2 (T) x 2 (c) fragments of this 64 x 64 block
-  const int tt = rows_pad / 32;
+  const int nr = cols / 32;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int piece = tid + 256 * u;
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       v[w] = (uint32_t)tile[xr + 2 * w][xc] | ((uint32_t)tile[xr + 2 * w + 1][xc] << 16);
-    const int64_t frag = ((int64_t)(c0 / 32 + rl) * tt + (r0 / 32 + tl)) * 2 + c;
+    const int64_t frag = ((int64_t)(r0 / 32 + tl) * nr + (c0 / 32 + rl)) * 2 + c;
     stg16(out + frag * 512 + l * 8, v);
   }
 }
@@ -217,122 +219,233 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Waits until at most N LDS (and scalar memory) operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_lds_reads_but() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
+}
+// Inside step i of lds_mfma_pipeline<N, DEPTH>: waits until operand i's LDS
+// read has completed.  At that point at most min(DEPTH - 1, N - 1 - i) reads
+// were issued after it (LDS operations complete in order); i is a constant
+// once the pipeline is unrolled, so the branches fold away.
+template <int N, int DEPTH>
+__device__ __forceinline__ void wait_operand_read(int i) {
+  static_assert(DEPTH >= 1 && DEPTH <= 4, "pipeline depth");
+  const int newer = N - 1 - i < DEPTH - 1 ? N - 1 - i : DEPTH - 1;
+  if (newer >= 3) wait_lds_reads_but<3>();
+  else if (newer == 2) wait_lds_reads_but<2>();
+  else if (newer == 1) wait_lds_reads_but<1>();
+  else wait_lds_reads_but<0>();
+}
 
 // ---------------------------------------------------------------------------
-// forward: workgroup = 32 rows of A, one split of the n tiles
+// forward: workgroup = 64 rows of A (two 32-row tiles), one split of the n
+// tiles, four waves with the whole register file each.
+//
+// The output block O [64 rows, p] stays in registers for the whole n loop
+// (wave w owns columns [w p / 4, (w + 1) p / 4) of both row tiles), so every
+// Bt and C^T fragment a wave stages serves 64 rows: twice the operand reuse
+// of 32-row blocks, which halves the L2 -> CU bytes per MFMA.  The first
+// product's contraction k is split over the waves (wave w: [w k / 4,
+// (w + 1) k / 4)); each wave keeps its A slice of both row tiles in registers
+// and forms partial H^T tiles for both.  Each wave then finishes a quarter of
+// the 64 x 32 chunk (tile w / 2, slots 8 (w % 2) .. + 7 of every lane): it
+// sums its own partials with the three the other waves left in LDS, applies
+// GeLU once per element and publishes bf16 G.  Per n chunk j:
+//   H^T(j) partials (MFMA) -> stash, read G(j - 1) -> barrier ->
+//   finish(j) (sums, GeLU) and O^T += C^T(j - 1) G^T(j - 1) (MFMA)
+//   -> publish G(j) -> barrier
+// (the GeLU of chunk j and the second product of chunk j - 1 are independent,
+// so the scheduler may interleave their instructions).  The Bt and C^T fragments of a wave are private to it (contraction slice,
+// output slice): they are copied global -> LDS asynchronously into per-wave
+// regions and need only wave-local waits.  Each 1 KiB slot is refilled with
+// the next chunk's fragment as soon as the product reading it has its operand
+// in registers (Bt(j + 1) during H(j), C^T(j) during the second product of
+// chunk j - 1), so every copy has about a chunk's time to land.  The
+// workspace holds Bt and C^T packed in MFMA operand order, one chunk's
+// fragments contiguous.
 // ---------------------------------------------------------------------------
-// NW waves split the first product's contraction (k / NW each, summed through
-// LDS) and the output columns (p / NW each).
-template <int K, int P>
-constexpr int mlp_fwd_waves() { return (K >= 128 && P >= 256) ? 8 : 4; }
+constexpr int kFwdWaves = 4;
 
 template <int K, int P>
-__global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(MlpArgs a, const uint16_t* ctf,
-                                                         int tt, int tiles_per_split,
-                                                         float* part) {
-  constexpr int NW = mlp_fwd_waves<K, P>();
-  constexpr int kq = K / NW, kc = kq / 16;
-  constexpr int pq = P / NW, pt = pq / 32;
-  static_assert(kc >= 1 && pt >= 1, "each wave needs a 16-deep slice of k and 32 columns of p");
-  // Bt tile slices: wave w holds rows n0 .. n0 + 31, columns w kq .. w kq + kq - 1,
-  // LDS row r = tile row perm_row(r), 16-byte chunk c at physical chunk c ^ (r % LPR)
-  constexpr int RB = 2 * kq;        // bytes of one slice row
-  constexpr int LPR = kq / 8;       // 16-byte chunks (copy lanes) per row
-  constexpr int RPI = 64 / LPR;     // rows per 1 KiB copy
-  static_assert(kc * 1024 == 32 * RB, "a slice is kc 1 KiB copies");
-  __shared__ __attribute__((aligned(1024))) char bsh[NW * 32 * RB];
-  __shared__ __attribute__((aligned(16))) float red[NW * 64 * 16];  // partial H tiles
-  __shared__ __attribute__((aligned(16))) uint32_t gsh[64 * 8];     // G tile, bf16 pairs
+struct FwdShape {
+  static constexpr int kq = K / kFwdWaves, kc = kq / 16;  // k slice, 16-deep steps
+  static constexpr int pq = P / kFwdWaves, pt = pq / 32;  // p slice, 32-wide tiles
+  static_assert(kc >= 1 && pt >= 1, "k >= 64 and p >= 128");
+  static constexpr int BT = kc * 1024;        // Bt fragments of one wave, one chunk
+  static constexpr int CT = pt * 2 * 1024;    // C^T fragments of one wave, one chunk
+  static constexpr int RED = 4 * 3 * 2048;    // partial H: 8 values per lane per (wave, other wave)
+  static constexpr int GSH = 2 * 2 * 1024;    // G of the chunk: 2 row tiles x 2 halves
+  static constexpr int LDS = kFwdWaves * (BT + CT) + RED + GSH;
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+template <int K, int P>
+__global__ __launch_bounds__(64 * kFwdWaves, 1) void mlp_fwd_kernel(
+    MlpArgs a, const uint16_t* btr, const uint16_t* ctf, int mb, int splits,
+    int tiles_per_split, float* part) {
+  using S = FwdShape<K, P>;
+  constexpr int kc = S::kc, pt = S::pt;
+  __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int lq = lane & 31, lg = lane >> 5;
-  const int row = blockIdx.x * 32 + lq;
-  const bool rlive = row < a.m;
-  const uint16_t* A = static_cast<const uint16_t*>(a.a);
-  const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
-  char* const mybt = bsh + wave * 32 * RB;
+  const int lq = lane & 31;
+  char* const bsh = lds + wave * S::BT;
+  char* const csh = lds + kFwdWaves * S::BT + wave * S::CT;
+  char* const red = lds + kFwdWaves * (S::BT + S::CT);
+  char* const gsh = red + S::RED;
 
-  u32x4 af[kc];
+  // workgroup i runs on XCD i % 8: give each XCD whole runs of one split, so
+  // the workgroups sharing an L2 stream the same n range of Bt and C
+  int lid = blockIdx.x;
+  const int total = mb * splits;
+  if (total % 8 == 0) lid = (lid % 8) * (total / 8) + lid / 8;
+  const int split = lid / mb, rb = lid % mb;
+  const int ntiles = (a.n + 31) / 32;
+  const int j0 = split * tiles_per_split;
+  const int j1 = min(ntiles, j0 + tiles_per_split);
+
+  // A slices of both row tiles: B operands of H^T = Bt A^T
+  const uint16_t* A = static_cast<const uint16_t*>(a.a);
+  u32x4 af[2][kc];
 #pragma unroll
-  for (int c = 0; c < kc; ++c)
-    af[c] = rlive ? ldg16(A + (int64_t)row * a.a_sr + wave * kq + 16 * c + 8 * lg)
-                              : u32x4{0, 0, 0, 0};
-  f32x16 o[pt];
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = rb * 64 + 32 * rt + lq;
+#pragma unroll
+    for (int c = 0; c < kc; ++c)
+      af[rt][c] = row < a.m ? ldg16(A + (int64_t)row * a.a_sr + wave * S::kq + 16 * c + 8 * (lane >> 5))
+                            : u32x4{0, 0, 0, 0};
+  }
+  f32x16 o[pt][2];
 #pragma unroll
   for (int t = 0; t < pt; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][rt][r] = 0.f;
 
-  const int ntiles = (a.n + 31) / 32;
-  const int jt0 = blockIdx.y * tiles_per_split;
-  const int jt1 = min(ntiles, jt0 + tiles_per_split);
-  // Copy i of lane l fills LDS row r = RPI i + l / LPR, physical chunk l % LPR,
-  // from the 256-byte-or-less row segment of tile row perm_row(r): each copy
-  // instruction reads RPI whole row segments (coalesced), unlike register
-  // loads in MFMA operand order (32 rows x 32 bytes each).
-  uint32_t boff[kc];
-#pragma unroll
-  for (int i = 0; i < kc; ++i) {
-    const int r = RPI * i + lane / LPR, pc = lane % LPR;
-    boff[i] = (uint32_t)(2 * ((int64_t)perm_row(r) * a.bt_sr + 8 * (pc ^ (r % LPR))));
-  }
-  auto copy_bt = [&](int jt) {
-    const int n0 = jt * 32;
-    const uint16_t* base = Bt + (int64_t)n0 * a.bt_sr + wave * kq;
-    if (n0 + 32 <= a.n) {
-#pragma unroll
-      for (int i = 0; i < kc; ++i) dma16(base, boff[i], mybt + i * 1024);
-    } else {  // ragged last tile: rows past n read row n - 1 (their C^T rows are zero)
-#pragma unroll
-      for (int i = 0; i < kc; ++i) {
-        const int r = RPI * i + lane / LPR, pc = lane % LPR;
-        const int tr = min(perm_row(r), a.n - 1 - n0);
-        dma16_at(base + (int64_t)tr * a.bt_sr + 8 * (pc ^ (r % LPR)), mybt + i * 1024);
-      }
-    }
+  // Fragment c of Bt chunk j: row fragment (j, wave kc + c), 1 KiB; fragment
+  // i = 2 t + c of C^T chunk j: column fragment (wave pt + t, j, c).  Slot i of
+  // a wave's region is refilled with the next chunk's fragment i as soon as
+  // the product that reads it has its operand in registers, so each copy has a
+  // whole chunk period to land.
+  auto bt_src = [&](int j) { return btr + ((int64_t)j * (K / 16) + wave * kc) * 512; };
+  auto c_src = [&](int j, int i) {
+    return ctf + (((int64_t)j * (P / 32) + wave * pt + i / 2) * 2 + i % 2) * 512;
   };
-  if (jt0 < jt1) copy_bt(jt0);
-  for (int jt = jt0; jt < jt1; ++jt) {
-    const int n0 = jt * 32;
-    u32x4 cfr[pt][2];
+  auto copy_c = [&](int j) {
 #pragma unroll
-    for (int t = 0; t < pt; ++t) {
-      // column fragments (wave pq / 32 + t, jt, c) of C: 1 KiB each
-      const uint16_t* cf = ctf + (((int64_t)(wave * pq / 32 + t) * tt + jt) * 2) * 512 + lane * 8;
-      cfr[t][0] = ldg16(cf);
-      cfr[t][1] = ldg16(cf + 512);
+    for (int i = 0; i < 2 * pt; ++i) dma16(c_src(j, i), 16 * lane, csh + i * 1024);
+  };
+  // O^T += C^T G^T over one chunk, G from registers (g[rt][half]); with
+  // REFILL, slot i then receives fragment i of chunk jn
+  constexpr int kDepth2 = 2;
+  auto second_product = [&]<bool REFILL>(const u32x4 (&g)[2][2], int jn) {
+    lds_mfma_pipeline<2 * pt, kDepth2>(
+        [&](int i) { return lds16(csh + i * 1024 + 16 * lane); },
+        [&](int i, const u32x4& x) {
+          o[i / 2][0] = mfma32(x, g[0][i % 2], o[i / 2][0]);
+          o[i / 2][1] = mfma32(x, g[1][i % 2], o[i / 2][1]);
+          if constexpr (REFILL) {
+            wait_operand_read<2 * pt, kDepth2>(i);  // slot i's read is complete
+            dma16(c_src(jn, i), 16 * lane, csh + i * 1024);
+          }
+        });
+  };
+
+  // this wave's quarter of the chunk: row tile wave / 2, slots 8 (wave % 2) .. + 7
+  const int mine_rt = wave >> 1, mine_h = wave & 1;
+  // G of the previous chunk (bf16, the second product's B operands); read
+  // from gsh before the barrier after which the waves overwrite it
+  u32x4 g[2][2];
+  auto read_g = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) g[rt][hh] = lds16(gsh + (rt * 2 + hh) * 1024 + 16 * lane);
+  };
+  // one n chunk; PREV: the previous chunk's second product runs alongside
+  // this chunk's GeLU (false only for the first chunk)
+  constexpr int kDepth1 = 3;
+  auto chunk = [&]<bool PREV>(int j) {
+    // this chunk's Bt (the C^T copies issued after it may still be in flight)
+    if (PREV) wait_copies<2 * pt>();
+    else wait_copies<0>();
+    f32x16 hp[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) hp[0][r] = hp[1][r] = 0.f;
+    // the last chunk copies itself again (its slots are read before each copy):
+    // keeps the copy count, and so the waits, the same for every chunk
+    const uint16_t* next = bt_src(min(j + 1, j1 - 1));
+    lds_mfma_pipeline<kc, kDepth1>(
+        [&](int c) { return lds16(bsh + c * 1024 + 16 * lane); },
+        [&](int c, const u32x4& x) {
+          hp[0] = mfma32(x, af[0][c], hp[0]);
+          hp[1] = mfma32(x, af[1][c], hp[1]);
+          wait_operand_read<kc, kDepth1>(c);  // slot c's read is complete
+          dma16(next + c * 512, 16 * lane, bsh + c * 1024);
+        });
+    // stash the quarters the other waves finish: 8 values per lane each, at
+    // red + ((owner * 3 + k) * 2 + half) * 1024, k = this wave's rank among
+    // the owner's three sources
+#pragma unroll
+    for (int u = 0; u < kFwdWaves; ++u) {
+      if (u == wave) continue;
+      const int k = wave < u ? wave : wave - 1;
+      char* dst = red + ((u * 3 + k) * 2) * 1024 + 16 * lane;
+      const f32x16& h = hp[u >> 1];
+      const int s0 = 8 * (u & 1);
+      *reinterpret_cast<f32x4*>(dst) = f32x4{h[s0], h[s0 + 1], h[s0 + 2], h[s0 + 3]};
+      *reinterpret_cast<f32x4*>(dst + 1024) = f32x4{h[s0 + 4], h[s0 + 5], h[s0 + 6], h[s0 + 7]};
     }
-    wait_copies<2 * pt>();  // this tile's Bt slice; the C^T loads above stay in flight
-    f32x16 hp;
+    float own[8];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) hp[r] = 0.f;
-    lds_mfma_pipeline<kc, 4>(
-        [&](int c) { return lds16(mybt + lq * RB + 16 * ((2 * c + lg) ^ (lq % LPR))); },
-        [&](int c, const u32x4& x) { hp = mfma32(x, af[c], hp); });
-    stash_tile(red, wave, lane, hp);
-    __syncthreads();
-    // C^T of this tile has had the first product and the barrier to arrive;
-    // waiting here (a wait the compiler sees) keeps its own wait before the
-    // second product from also covering the next tile's Bt copy issued below
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    wait_lds_reads();  // this wave's reads of its Bt slice are done
-    if (jt + 1 < jt1) copy_bt(jt + 1);
-    // slot r of lane l: row `row`, column n0 + 16 lg + r
-    finish_tile<NW, false>(red, nullptr, gsh, wave, lane, a.scale);
-    __syncthreads();
-    u32x4 gb[2];
-    gb[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
-    gb[1] = *reinterpret_cast<const u32x4*>(gsh + lane * 8 + 4);
-#pragma unroll
-    for (int t = 0; t < pt; ++t) {
-      o[t] = mfma32(cfr[t][0], gb[0], o[t]);
-      o[t] = mfma32(cfr[t][1], gb[1], o[t]);
+    for (int e = 0; e < 8; ++e) {
+      const float x0 = mine_rt ? hp[1][e] : hp[0][e];
+      const float x1 = mine_rt ? hp[1][8 + e] : hp[0][8 + e];
+      own[e] = mine_h ? x1 : x0;
     }
+    if constexpr (PREV) read_g();
+    lds_barrier();
+    if (PREV) wait_copies<kc>();  // C^T(j - 1); the next chunk's Bt stays in flight
+    // finish this wave's quarter of chunk j while the previous chunk's second
+    // product runs
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(red + ((wave * 3 + k) * 2 + hh) * 1024 + 16 * lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) own[4 * hh + e] += x[e];
+      }
+    if constexpr (PREV) second_product.template operator()<true>(g, j);
+    u32x4 gv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gv[e] = pack_bf16(gelu_f(a.scale * own[2 * e]), gelu_f(a.scale * own[2 * e + 1]));
+    sts16(gsh + (mine_rt * 2 + mine_h) * 1024 + 16 * lane, gv);
+    if constexpr (!PREV) copy_c(j);
+    lds_barrier();
+  };
+  if (j0 < j1) {
+#pragma unroll
+    for (int c = 0; c < kc; ++c) dma16(bt_src(j0) + c * 512, 16 * lane, bsh + c * 1024);
+    chunk.template operator()<false>(j0);
+  }
+  for (int j = j0 + 1; j < j1; ++j) chunk.template operator()<true>(j);
+  if (j0 < j1) {
+    read_g();
+    wait_copies<0>();
+    second_product.template operator()<false>(g, 0);
   }
   wait_copies<0>();
-  if (!rlive) return;
-  float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.p + wave * pq + 16 * lg;
 #pragma unroll
-  for (int t = 0; t < pt; ++t) store_tile_f32(dst + 32 * t, o[t]);
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = rb * 64 + 32 * rt + lq;
+    if (row >= a.m) continue;
+    float* dst = part + ((int64_t)split * a.m + row) * a.p + wave * S::pq + 16 * (lane >> 5);
+#pragma unroll
+    for (int t = 0; t < pt; ++t) store_tile_f32(dst + 32 * t, o[t][rt]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -346,18 +459,19 @@ __global__ __launch_bounds__((64 * mlp_fwd_waves<K, P>())) void mlp_fwd_kernel(M
 // while the partial tiles do.
 // ---------------------------------------------------------------------------
 
-// Copies this wave's kt x 2 column fragments (32 R0 + 32 t rows of the
-// transposed operand, tile T, halves c) into its LDS region: fragment (t, c)
-// lands at region + (2 t + c) * 1024, lane l's 16 bytes at + 16 l, which is
-// where that lane reads them back.  Each copy reads 1 KiB of contiguous memory.
-template <int kt>
-__device__ __forceinline__ void copy_second_operand(const uint16_t* xf, int tt, int r0, int T,
-                                                    int lane, char* region) {
+// Copies this wave's kt x 2 column fragments (R = r0 + t of the transposed
+// operand's nr, step T, halves c) into its LDS region: fragment (t, c) lands
+// at region + (2 t + c) * 1024, lane l's 16 bytes at + 16 l, which is where
+// that lane reads them back.  The 2 kt fragments are 2 kt KiB of contiguous
+// memory.
+template <int kt, int nr>
+__device__ __forceinline__ void copy_second_operand(const uint16_t* xf, int r0, int T, int lane,
+                                                    char* region) {
 #pragma unroll
   for (int t = 0; t < kt; ++t)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      dma16(xf + (((int64_t)(r0 + t) * tt + T) * 2 + c) * 512, 16 * lane, region + (2 * t + c) * 1024);
+      dma16(xf + (((int64_t)T * nr + r0 + t) * 2 + c) * 512, 16 * lane, region + (2 * t + c) * 1024);
 }
 
 // Wave count of a backward kernel whose first product contracts over K (and P
@@ -369,7 +483,7 @@ constexpr int mlp_bwd_waves() { return (K >= 128 && P >= 128 && OUT >= 256) ? 8 
 // dA: workgroup = 32 rows of A, one split of the n tiles.
 template <int K, int P>
 __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_kernel(
-    MlpArgs a, const uint16_t* btr, const uint16_t* cr, const uint16_t* btc, int tt,
+    MlpArgs a, const uint16_t* btr, const uint16_t* cr, const uint16_t* btc,
     int tiles_per_split, float* part) {
   constexpr int NW = mlp_bwd_waves<K, P, K>();
   __shared__ __attribute__((aligned(16))) float red[2 * NW * 64 * 16];  // partial H, dG tiles
@@ -416,7 +530,6 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
   };
   if (jt0 < jt1) load_rows(jt0);
   for (int jt = jt0; jt < jt1; ++jt) {
-    const int n0 = jt * 32;
     f32x16 hp, gp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) hp[r] = gp[r] = 0.f;
@@ -425,12 +538,12 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
 #pragma unroll
     for (int c = 0; c < pc; ++c) gp = mfma32(cfr[c], df[c], gp);
     wait_lds_reads();  // the previous tile's reads of tmine are done
-    copy_second_operand<kt>(btc, tt, wave * kq / 32, jt, lane, tmine);
+    copy_second_operand<kt, K / 32>(btc, wave * kq / 32, jt, lane, tmine);
     load_rows(min(jt + 1, jt1 - 1));  // unconditional: a branch here costs register copies
     stash_tile(red, wave, lane, hp);
     stash_tile(red + NW * 64 * 16, wave, lane, gp);
     __syncthreads();
-    // slot r of lane l: row `row`, column n0 + 16 lg + r
+    // slot r of lane l: row `row`, column 32 jt + 16 lg + r
     finish_tile<NW, true>(red, red + NW * 64 * 16, gsh, wave, lane, a.scale);
     __syncthreads();
     u32x4 db[2];
@@ -456,7 +569,7 @@ constexpr int mlp_bwd_col_waves() { return mlp_bwd_waves<K, (WANT_DB ? P : 128),
 
 template <int K, int P, bool WANT_DB>
 __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp_bwd_col_kernel(
-    MlpArgs a, const uint16_t* ar, const uint16_t* dor, const uint16_t* xc, int tt,
+    MlpArgs a, const uint16_t* ar, const uint16_t* dor, const uint16_t* xc,
     int tiles_per_split, float* part) {
   constexpr int NW = mlp_bwd_col_waves<K, P, WANT_DB>();
   __shared__ __attribute__((aligned(16))) float red[(WANT_DB ? 2 : 1) * NW * 64 * 16];
@@ -509,7 +622,6 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
   };
   if (it0 < it1) load_rows(it0);
   for (int it = it0; it < it1; ++it) {
-    const int r0 = it * 32;
     f32x16 hp, gp;
 #pragma unroll
     for (int r = 0; r < 16; ++r) hp[r] = gp[r] = 0.f;
@@ -520,12 +632,12 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
       for (int c = 0; c < pc; ++c) gp = mfma32(ofr[c], cf[c], gp);
     }
     wait_lds_reads();  // the previous tile's reads of tmine are done
-    copy_second_operand<ot>(xc, tt, wave * oq / 32, it, lane, tmine);
+    copy_second_operand<ot, (WANT_DB ? K : P) / 32>(xc, wave * oq / 32, it, lane, tmine);
     load_rows(min(it + 1, it1 - 1));  // unconditional: a branch here costs register copies
     stash_tile(red, wave, lane, hp);
     if constexpr (WANT_DB) stash_tile(red + NW * 64 * 16, wave, lane, gp);
     __syncthreads();
-    // slot r of lane l: column `col`, row r0 + 16 lg + r
+    // slot r of lane l: column `col`, row 32 it + 16 lg + r
     finish_tile<NW, WANT_DB>(red, red + NW * 64 * 16, gsh, wave, lane, a.scale);
     __syncthreads();
     u32x4 xb[2];
@@ -546,10 +658,11 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
 }
 
 struct MlpLayout {
-  int split_rows;   // splits of the n loop for the row-block kernels
-  int split_cols;   // splits of the m loop for the column-block kernel
+  int split_fwd;    // splits of the n loop for the forward (64-row blocks)
+  int split_rows;   // splits of the n loop for the row-block backward kernel
+  int split_cols;   // splits of the m loop for the column-block kernels
   int64_t m_pad, n_pad;
-  size_t fwd_ct, fwd_part, fwd_total;
+  size_t fwd_btr, fwd_ct, fwd_part, fwd_total;
   // row fragments of Bt, C, A, dO; column fragments of Bt, A, dO; partials
   size_t bwd_btr, bwd_cr, bwd_ar, bwd_dor, bwd_btc, bwd_ac, bwd_doc, bwd_pa, bwd_pb, bwd_pc, bwd_total;
 };
@@ -563,15 +676,18 @@ int pick_splits(int blocks, int tiles) {
 MlpLayout layout(int m, int n, int k, int p) {
   MlpLayout L{};
   const int mb = (m + 31) / 32, nb = (n + 31) / 32;
+  L.split_fwd = pick_splits((m + 63) / 64, nb);
   L.split_rows = pick_splits(mb, nb);
   L.split_cols = pick_splits(nb, mb);
   L.m_pad = (int64_t)round_up(m, kPad);
   L.n_pad = (int64_t)round_up(n, kPad);
   size_t off = 0;
+  L.fwd_btr = off;
+  off = round_up(off + (size_t)k * L.n_pad * 2, 256);
   L.fwd_ct = off;
   off = round_up(off + (size_t)p * L.n_pad * 2, 256);
   L.fwd_part = off;
-  off = round_up(off + (size_t)L.split_rows * m * p * 4, 256);
+  off = round_up(off + (size_t)L.split_fwd * m * p * 4, 256);
   L.fwd_total = off;
   off = 0;
   for (size_t* slot : {&L.bwd_btr, &L.bwd_btc}) {
@@ -632,7 +748,7 @@ hipError_t reduce(const float* part, int splits, int rows, int cols, float scale
 
 size_t mlp_fwd_workspace(int m, int n, int k, int p, int* splits) {
   const MlpLayout L = layout(m, n, k, p);
-  *splits = L.split_rows;
+  *splits = L.split_fwd;
   return L.fwd_total;
 }
 
@@ -641,12 +757,13 @@ size_t mlp_bwd_workspace(int m, int n, int k, int p) { return layout(m, n, k, p)
 namespace {
 
 template <int K, int P>
-hipError_t fwd_kp(const MlpArgs& a, const MlpLayout& L, const uint16_t* ctf, float* part, hipStream_t s) {
-  const int ntiles = (a.n + 31) / 32;
-  const int per = (ntiles + L.split_rows - 1) / L.split_rows;
-  const dim3 grid((unsigned)((a.m + 31) / 32), (unsigned)L.split_rows),
-      block(64 * mlp_fwd_waves<K, P>());
-  FAB_TIMED("mlp_fwd", s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, ctf, (int)(L.n_pad / 32), per, part));
+hipError_t fwd_kp(const MlpArgs& a, const MlpLayout& L, const uint16_t* btr, const uint16_t* ctf,
+                  float* part, hipStream_t s) {
+  const int ntiles = (a.n + 31) / 32, mb = (a.m + 63) / 64;
+  const int per = (ntiles + L.split_fwd - 1) / L.split_fwd;
+  const dim3 grid((unsigned)(mb * L.split_fwd)), block(64 * kFwdWaves);
+  FAB_TIMED("mlp_fwd", s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, btr, ctf,
+                                             mb, L.split_fwd, per, part));
   return hipGetLastError();
 }
 
@@ -654,21 +771,20 @@ template <int K, int P>
 hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const char* ws, float* pa, float* pb,
                   float* pc, hipStream_t s) {
   auto frag = [&](size_t off) { return reinterpret_cast<const uint16_t*>(ws + off); };
-  const int ttn = (int)(L.n_pad / 32), ttm = (int)(L.m_pad / 32);
   const int ntiles = (a.n + 31) / 32, mtiles = (a.m + 31) / 32;
   const int per_n = (ntiles + L.split_rows - 1) / L.split_rows;
   const int per_m = (mtiles + L.split_cols - 1) / L.split_cols;
   FAB_TIMED("mlp_bwd_da", s, hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)mtiles, (unsigned)L.split_rows),
                      dim3(64 * mlp_bwd_waves<K, P, K>()), 0, s, a, frag(L.bwd_btr), frag(L.bwd_cr),
-                     frag(L.bwd_btc), ttn, per_n, pa));
+                     frag(L.bwd_btc), per_n, pa));
   FAB_TIMED("mlp_bwd_dbt", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, true>),
                      dim3((unsigned)ntiles, (unsigned)L.split_cols),
                      dim3(64 * mlp_bwd_col_waves<K, P, true>()), 0, s, a, frag(L.bwd_ar), frag(L.bwd_dor),
-                     frag(L.bwd_ac), ttm, per_m, pb));
+                     frag(L.bwd_ac), per_m, pb));
   FAB_TIMED("mlp_bwd_dc", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, false>),
                      dim3((unsigned)ntiles, (unsigned)L.split_cols),
                      dim3(64 * mlp_bwd_col_waves<K, P, false>()), 0, s, a, frag(L.bwd_ar), frag(L.bwd_dor),
-                     frag(L.bwd_doc), ttm, per_m, pc));
+                     frag(L.bwd_doc), per_m, pc));
   return hipGetLastError();
 }
 
@@ -704,13 +820,16 @@ hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s) {
   if (!mlp_shape_supported(a.k, a.p)) return hipErrorInvalidValue;
   const MlpLayout L = layout(a.m, a.n, a.k, a.p);
   char* ws = reinterpret_cast<char*>(a.ws);
+  uint16_t* btr = reinterpret_cast<uint16_t*>(ws + L.fwd_btr);
   uint16_t* ctf = reinterpret_cast<uint16_t*>(ws + L.fwd_ct);
   float* part = reinterpret_cast<float*>(ws + L.fwd_part);
-  hipError_t e = pack_cols(a.c, a.c_sr, a.n, a.p, L.n_pad, ctf, s);
+  hipError_t e = pack_rows(a.bt, a.bt_sr, a.n, a.k, L.n_pad, btr, s);
   if (e != hipSuccess) return e;
-  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() { return fwd_kp<K, P>(a, L, ctf, part, s); });
+  e = pack_cols(a.c, a.c_sr, a.n, a.p, L.n_pad, ctf, s);
   if (e != hipSuccess) return e;
-  return reduce(part, L.split_rows, a.m, a.p, 1.f, a.o, a.o_sr, s);
+  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() { return fwd_kp<K, P>(a, L, btr, ctf, part, s); });
+  if (e != hipSuccess) return e;
+  return reduce(part, L.split_fwd, a.m, a.p, 1.f, a.o, a.o_sr, s);
 }
 
 hipError_t launch_mlp_bwd_bf16(const MlpArgs& a, hipStream_t s) {
