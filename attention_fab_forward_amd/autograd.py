@@ -66,7 +66,7 @@ def attention(q, k, v, causal=False, scale=None):
 
 
 def gelu_mlp(a, bt, c, scale=1.0):
-    """a [m, k], bt [n, k], c [n, p] bf16; k and p multiples of 128, <= 1024."""
+    """a [m, k], bt [n, k], c [n, p] bf16; k and p multiples of 64, <= 1024."""
     return FabGeluMlpFn.apply(a, bt, c, float(scale))
 
 
@@ -74,7 +74,7 @@ class AttentionMlpBlock(torch.nn.Module):
     """Attention followed by the GeLU MLP on its output rows.
 
     w1: [ffn, hq d] (the nn.Linear weight of the first product, i.e. Bt),
-    w2: [ffn, out] (C).  hq d and out must be multiples of 128, at most 1024.
+    w2: [ffn, out] (C).  hq d and out must be multiples of 64, at most 1024.
     """
 
     def __init__(self, hidden, ffn, out, device="cuda", dtype=torch.bfloat16, seed=0):

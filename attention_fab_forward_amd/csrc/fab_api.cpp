@@ -413,7 +413,7 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
       return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP needs batch == heads == 1");
     if (q.k > 1024 || q.p > 1024 || !fab::mlp_shape_supported((int)q.k, (int)q.p))
       return fail(FAB_ERR_UNSUPPORTED, "GeLU MLP: k = %lld, p = %lld is not a width pair this "
-                  "build runs (each of k and p in {128, 256, 512, 1024})", (long long)q.k,
+                  "build runs (each of k and p a multiple of 64 from 64 to 1024)", (long long)q.k,
                   (long long)q.p);
     int splits = 1;
     tmp.fwd_ws = round_up(fab::mlp_fwd_workspace((int)q.m, (int)q.n, (int)q.k, (int)q.p, &splits), 256);

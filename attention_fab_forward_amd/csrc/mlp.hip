@@ -76,23 +76,27 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
 //    ((T * cols / 32 + R) * 2 + c) * 512, so the fragments of one 32-row step
 //    T are contiguous (a step's copies spread over every L2 channel instead of
 //    landing 64 rows_pad bytes apart, on one channel).
-// Rows of X at or past `rows` read as zero.  rows_pad % 64 == 0, cols % 64 == 0.
+// The fragments cover cols_pad columns (the kernels' compiled width, a power
+// of two from 128); rows of X at or past `rows` and columns at or past `cols`
+// read as zero.  rows_pad % 64 == 0, cols % 64 == 0, cols <= cols_pad.
 __global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* x, int64_t ld, int rows,
-                                                        int cols, int64_t pieces, uint16_t* out) {
+                                                        int cols, int cols_pad, int64_t pieces,
+                                                        uint16_t* out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte piece
   if (i >= pieces) return;
   const int l = (int)(i & 63);
   const int64_t f = i >> 6;
-  const int nj = cols / 16;
+  const int nj = cols_pad / 16;
   const int j = (int)(f % nj);
   const int64_t R = f / nj;
   const int64_t row = 32 * R + perm_row(l & 31);
-  const u32x4 v = row < rows ? ldg16(x + row * ld + 16 * j + 8 * (l >> 5)) : u32x4{0, 0, 0, 0};
+  const int col = 16 * j + 8 * (l >> 5);
+  const u32x4 v = row < rows && col < cols ? ldg16(x + row * ld + col) : u32x4{0, 0, 0, 0};
   stg16(out + i * 8, v);
 }
 
 __global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64_t ld, int rows,
-                                                        int cols, int rows_pad, uint16_t* out) {
+                                                        int cols, int cols_pad, uint16_t* out) {
   __shared__ uint16_t tile[64][64 + 2];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int tid = threadIdx.x;
@@ -112,7 +116,7 @@ __global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64
   }
   __syncthreads();
   // write the 2 (R) x 2 (T) x 2 (c) fragments of this 64 x 64 block
-  const int nr = cols / 32;
+  const int nr = cols_pad / 32;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int piece = tid + 256 * u;
@@ -312,9 +316,10 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void mlp_fwd_kernel(
   for (int rt = 0; rt < 2; ++rt) {
     const int row = rb * 64 + 32 * rt + lq;
 #pragma unroll
-    for (int c = 0; c < kc; ++c)
-      af[rt][c] = row < a.m ? ldg16(A + (int64_t)row * a.a_sr + wave * S::kq + 16 * c + 8 * (lane >> 5))
-                            : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < kc; ++c) {
+      const int col = wave * S::kq + 16 * c + 8 * (lane >> 5);  // zero past k (padded width)
+      af[rt][c] = row < a.m && col < a.k ? ldg16(A + (int64_t)row * a.a_sr + col) : u32x4{0, 0, 0, 0};
+    }
   }
   f32x16 o[pt][2];
 #pragma unroll
@@ -442,9 +447,11 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void mlp_fwd_kernel(
   for (int rt = 0; rt < 2; ++rt) {
     const int row = rb * 64 + 32 * rt + lq;
     if (row >= a.m) continue;
-    float* dst = part + ((int64_t)split * a.m + row) * a.p + wave * S::pq + 16 * (lane >> 5);
+    const int col0 = wave * S::pq + 16 * (lane >> 5);
+    float* dst = part + ((int64_t)split * a.m + row) * a.p + col0;
 #pragma unroll
-    for (int t = 0; t < pt; ++t) store_tile_f32(dst + 32 * t, o[t][rt]);
+    for (int t = 0; t < pt; ++t)
+      if (col0 + 32 * t < a.p) store_tile_f32(dst + 32 * t, o[t][rt]);  // p <= padded width
   }
 }
 
@@ -500,15 +507,18 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
   const uint16_t* A = static_cast<const uint16_t*>(a.a);
     const uint16_t* dO = static_cast<const uint16_t*>(a.dout);
 
+  // columns past k (or p) read as zero: the compiled widths K, P may exceed them
   u32x4 af[kc], df[pc];
 #pragma unroll
-  for (int c = 0; c < kc; ++c)
-    af[c] = rlive ? ldg16(A + (int64_t)row * a.a_sr + wave * kq + 16 * c + 8 * lg)
-                  : u32x4{0, 0, 0, 0};
+  for (int c = 0; c < kc; ++c) {
+    const int ck = wave * kq + 16 * c + 8 * lg;
+    af[c] = rlive && ck < a.k ? ldg16(A + (int64_t)row * a.a_sr + ck) : u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
-  for (int c = 0; c < pc; ++c)
-    df[c] = rlive ? ldg16(dO + (int64_t)row * a.o_sr + wave * pq + 16 * c + 8 * lg)
-                  : u32x4{0, 0, 0, 0};
+  for (int c = 0; c < pc; ++c) {
+    const int cp = wave * pq + 16 * c + 8 * lg;
+    df[c] = rlive && cp < a.p ? ldg16(dO + (int64_t)row * a.o_sr + cp) : u32x4{0, 0, 0, 0};
+  }
   f32x16 acc[kt];
 #pragma unroll
   for (int t = 0; t < kt; ++t)
@@ -557,9 +567,11 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
     }
   }
   if (!rlive) return;
-  float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.k + wave * kq + 16 * lg;
+  const int col0 = wave * kq + 16 * lg;
+  float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.k + col0;
 #pragma unroll
-  for (int t = 0; t < kt; ++t) store_tile_f32(dst + 32 * t, acc[t]);
+  for (int t = 0; t < kt; ++t)
+    if (col0 + 32 * t < a.k) store_tile_f32(dst + 32 * t, acc[t]);
 }
 
 // dBt (WANT_DB) or dC (!WANT_DB): workgroup = 32 columns of n, one split of
@@ -588,16 +600,19 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
   const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
   const uint16_t* Cm = static_cast<const uint16_t*>(a.c);
 
+  // columns past k (or p) read as zero: the compiled widths K, P may exceed them
   u32x4 bf[kc], cf[pc];
 #pragma unroll
-  for (int c = 0; c < kc; ++c)
-    bf[c] = clive ? ldg16(Bt + (int64_t)col * a.bt_sr + wave * kq + 16 * c + 8 * lg)
-                  : u32x4{0, 0, 0, 0};
+  for (int c = 0; c < kc; ++c) {
+    const int ck = wave * kq + 16 * c + 8 * lg;
+    bf[c] = clive && ck < a.k ? ldg16(Bt + (int64_t)col * a.bt_sr + ck) : u32x4{0, 0, 0, 0};
+  }
   if constexpr (WANT_DB) {
 #pragma unroll
-    for (int c = 0; c < pc; ++c)
-      cf[c] = clive ? ldg16(Cm + (int64_t)col * a.c_sr + wave * pq + 16 * c + 8 * lg)
-                    : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < pc; ++c) {
+      const int cp = wave * pq + 16 * c + 8 * lg;
+      cf[c] = clive && cp < a.p ? ldg16(Cm + (int64_t)col * a.c_sr + cp) : u32x4{0, 0, 0, 0};
+    }
   }
   f32x16 acc[ot];
 #pragma unroll
@@ -652,9 +667,11 @@ __global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp
   }
   if (!clive) return;
   const int ocols = WANT_DB ? a.k : a.p;
-  float* dst = part + ((int64_t)blockIdx.y * a.n + col) * ocols + wave * oq + 16 * lg;
+  const int col0 = wave * oq + 16 * lg;
+  float* dst = part + ((int64_t)blockIdx.y * a.n + col) * ocols + col0;
 #pragma unroll
-  for (int t = 0; t < ot; ++t) store_tile_f32(dst + 32 * t, acc[t]);
+  for (int t = 0; t < ot; ++t)
+    if (col0 + 32 * t < ocols) store_tile_f32(dst + 32 * t, acc[t]);
 }
 
 struct MlpLayout {
@@ -673,8 +690,13 @@ int pick_splits(int blocks, int tiles) {
   return s < 1 ? 1 : s;
 }
 
+// The width the kernels are compiled for that holds x (a multiple of 64 up to
+// 1024): operands are zero-padded to it in the packed copies.
+int padded_width(int x) { return x <= 128 ? 128 : x <= 256 ? 256 : x <= 512 ? 512 : 1024; }
+
 MlpLayout layout(int m, int n, int k, int p) {
   MlpLayout L{};
+  const int kw = padded_width(k), pw = padded_width(p);
   const int mb = (m + 31) / 32, nb = (n + 31) / 32;
   L.split_fwd = pick_splits((m + 63) / 64, nb);
   L.split_rows = pick_splits(mb, nb);
@@ -683,26 +705,26 @@ MlpLayout layout(int m, int n, int k, int p) {
   L.n_pad = (int64_t)round_up(n, kPad);
   size_t off = 0;
   L.fwd_btr = off;
-  off = round_up(off + (size_t)k * L.n_pad * 2, 256);
+  off = round_up(off + (size_t)kw * L.n_pad * 2, 256);
   L.fwd_ct = off;
-  off = round_up(off + (size_t)p * L.n_pad * 2, 256);
+  off = round_up(off + (size_t)pw * L.n_pad * 2, 256);
   L.fwd_part = off;
   off = round_up(off + (size_t)L.split_fwd * m * p * 4, 256);
   L.fwd_total = off;
   off = 0;
   for (size_t* slot : {&L.bwd_btr, &L.bwd_btc}) {
     *slot = off;
-    off = round_up(off + (size_t)k * L.n_pad * 2, 256);
+    off = round_up(off + (size_t)kw * L.n_pad * 2, 256);
   }
   L.bwd_cr = off;
-  off = round_up(off + (size_t)p * L.n_pad * 2, 256);
+  off = round_up(off + (size_t)pw * L.n_pad * 2, 256);
   for (size_t* slot : {&L.bwd_ar, &L.bwd_ac}) {
     *slot = off;
-    off = round_up(off + (size_t)k * L.m_pad * 2, 256);
+    off = round_up(off + (size_t)kw * L.m_pad * 2, 256);
   }
   for (size_t* slot : {&L.bwd_dor, &L.bwd_doc}) {
     *slot = off;
-    off = round_up(off + (size_t)p * L.m_pad * 2, 256);
+    off = round_up(off + (size_t)pw * L.m_pad * 2, 256);
   }
   L.bwd_pa = off;
   off = round_up(off + (size_t)L.split_rows * m * k * 4, 256);
@@ -714,23 +736,24 @@ MlpLayout layout(int m, int n, int k, int p) {
   return L;
 }
 
-// Row fragments of X [rows][cols] (rows padded to rows_pad with zeros).
-hipError_t pack_rows(const void* x, int64_t ld, int rows, int cols, int64_t rows_pad, void* out,
-                     hipStream_t s) {
-  const int64_t pieces = rows_pad * cols / 8;
+// Row fragments of X [rows][cols], zero-padded to rows_pad x cols_pad.
+hipError_t pack_rows(const void* x, int64_t ld, int rows, int cols, int cols_pad, int64_t rows_pad,
+                     void* out, hipStream_t s) {
+  const int64_t pieces = rows_pad * cols_pad / 8;
   const dim3 grid((unsigned)((pieces + 255) / 256)), block(256);
   FAB_TIMED("mlp_pack", s, hipLaunchKernelGGL(pack_rows_kernel, grid, block, 0, s,
-                     static_cast<const uint16_t*>(x), ld, rows, cols, pieces,
+                     static_cast<const uint16_t*>(x), ld, rows, cols, cols_pad, pieces,
                      static_cast<uint16_t*>(out)));
   return hipGetLastError();
 }
 
-// Column fragments of X [rows][cols], i.e. row fragments of X^T.
-hipError_t pack_cols(const void* x, int64_t ld, int rows, int cols, int64_t rows_pad, void* out,
-                     hipStream_t s) {
-  const dim3 grid((unsigned)(rows_pad / 64), (unsigned)(cols / 64)), block(256);
+// Column fragments of X [rows][cols] (row fragments of X^T), zero-padded to
+// rows_pad x cols_pad.
+hipError_t pack_cols(const void* x, int64_t ld, int rows, int cols, int cols_pad, int64_t rows_pad,
+                     void* out, hipStream_t s) {
+  const dim3 grid((unsigned)(rows_pad / 64), (unsigned)(cols_pad / 64)), block(256);
   FAB_TIMED("mlp_pack", s, hipLaunchKernelGGL(pack_cols_kernel, grid, block, 0, s,
-                     static_cast<const uint16_t*>(x), ld, rows, cols, (int)rows_pad,
+                     static_cast<const uint16_t*>(x), ld, rows, cols, cols_pad,
                      static_cast<uint16_t*>(out)));
   return hipGetLastError();
 }
@@ -812,22 +835,23 @@ hipError_t dispatch_kp(int k, int p, F&& fn) {
 }  // namespace
 
 bool mlp_shape_supported(int k, int p) {
-  auto ok = [](int x) { return x == 128 || x == 256 || x == 512 || x == 1024; };
+  auto ok = [](int x) { return x >= 64 && x <= 1024 && x % 64 == 0; };
   return ok(k) && ok(p);
 }
 
 hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s) {
   if (!mlp_shape_supported(a.k, a.p)) return hipErrorInvalidValue;
   const MlpLayout L = layout(a.m, a.n, a.k, a.p);
+  const int kw = padded_width(a.k), pw = padded_width(a.p);
   char* ws = reinterpret_cast<char*>(a.ws);
   uint16_t* btr = reinterpret_cast<uint16_t*>(ws + L.fwd_btr);
   uint16_t* ctf = reinterpret_cast<uint16_t*>(ws + L.fwd_ct);
   float* part = reinterpret_cast<float*>(ws + L.fwd_part);
-  hipError_t e = pack_rows(a.bt, a.bt_sr, a.n, a.k, L.n_pad, btr, s);
+  hipError_t e = pack_rows(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, btr, s);
   if (e != hipSuccess) return e;
-  e = pack_cols(a.c, a.c_sr, a.n, a.p, L.n_pad, ctf, s);
+  e = pack_cols(a.c, a.c_sr, a.n, a.p, pw, L.n_pad, ctf, s);
   if (e != hipSuccess) return e;
-  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() { return fwd_kp<K, P>(a, L, btr, ctf, part, s); });
+  e = dispatch_kp(kw, pw, [&]<int K, int P>() { return fwd_kp<K, P>(a, L, btr, ctf, part, s); });
   if (e != hipSuccess) return e;
   return reduce(part, L.split_fwd, a.m, a.p, 1.f, a.o, a.o_sr, s);
 }
@@ -835,19 +859,20 @@ hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s) {
 hipError_t launch_mlp_bwd_bf16(const MlpArgs& a, hipStream_t s) {
   if (!mlp_shape_supported(a.k, a.p)) return hipErrorInvalidValue;
   const MlpLayout L = layout(a.m, a.n, a.k, a.p);
+  const int kw = padded_width(a.k), pw = padded_width(a.p);
   char* ws = reinterpret_cast<char*>(a.ws);
   float* pa = reinterpret_cast<float*>(ws + L.bwd_pa);
   float* pb = reinterpret_cast<float*>(ws + L.bwd_pb);
   float* pc = reinterpret_cast<float*>(ws + L.bwd_pc);
   hipError_t e;
-  if ((e = pack_rows(a.bt, a.bt_sr, a.n, a.k, L.n_pad, ws + L.bwd_btr, s)) != hipSuccess) return e;
-  if ((e = pack_rows(a.c, a.c_sr, a.n, a.p, L.n_pad, ws + L.bwd_cr, s)) != hipSuccess) return e;
-  if ((e = pack_rows(a.a, a.a_sr, a.m, a.k, L.m_pad, ws + L.bwd_ar, s)) != hipSuccess) return e;
-  if ((e = pack_rows(a.dout, a.o_sr, a.m, a.p, L.m_pad, ws + L.bwd_dor, s)) != hipSuccess) return e;
-  if ((e = pack_cols(a.bt, a.bt_sr, a.n, a.k, L.n_pad, ws + L.bwd_btc, s)) != hipSuccess) return e;
-  if ((e = pack_cols(a.a, a.a_sr, a.m, a.k, L.m_pad, ws + L.bwd_ac, s)) != hipSuccess) return e;
-  if ((e = pack_cols(a.dout, a.o_sr, a.m, a.p, L.m_pad, ws + L.bwd_doc, s)) != hipSuccess) return e;
-  e = dispatch_kp(a.k, a.p, [&]<int K, int P>() { return bwd_kp<K, P>(a, L, ws, pa, pb, pc, s); });
+  if ((e = pack_rows(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, ws + L.bwd_btr, s)) != hipSuccess) return e;
+  if ((e = pack_rows(a.c, a.c_sr, a.n, a.p, pw, L.n_pad, ws + L.bwd_cr, s)) != hipSuccess) return e;
+  if ((e = pack_rows(a.a, a.a_sr, a.m, a.k, kw, L.m_pad, ws + L.bwd_ar, s)) != hipSuccess) return e;
+  if ((e = pack_rows(a.dout, a.o_sr, a.m, a.p, pw, L.m_pad, ws + L.bwd_dor, s)) != hipSuccess) return e;
+  if ((e = pack_cols(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, ws + L.bwd_btc, s)) != hipSuccess) return e;
+  if ((e = pack_cols(a.a, a.a_sr, a.m, a.k, kw, L.m_pad, ws + L.bwd_ac, s)) != hipSuccess) return e;
+  if ((e = pack_cols(a.dout, a.o_sr, a.m, a.p, pw, L.m_pad, ws + L.bwd_doc, s)) != hipSuccess) return e;
+  e = dispatch_kp(kw, pw, [&]<int K, int P>() { return bwd_kp<K, P>(a, L, ws, pa, pb, pc, s); });
   if (e != hipSuccess) return e;
   if ((e = reduce(pa, L.split_rows, a.m, a.k, a.scale, a.da, a.a_sr, s)) != hipSuccess) return e;
   if ((e = reduce(pb, L.split_cols, a.n, a.k, a.scale, a.dbt, a.bt_sr, s)) != hipSuccess) return e;

@@ -115,8 +115,10 @@ typedef struct fab_plan_s fab_plan_t;
  *   softmax, bf16: k == p, k in {64, 128}; any m, n >= 1; causal with any
  *                  offsets.
  *   softmax, f32:  k == p, k in {64, 128}; same rules.
- *   GeLU, bf16:    batch == heads_a == heads_bc == 1, each of k and p in
- *                  {128, 256, 512, 1024}, any m, n >= 1, mask NONE.
+ *   GeLU, bf16:    batch == heads_a == heads_bc == 1, each of k and p a
+ *                  multiple of 64 from 64 to 1024, any m, n >= 1, mask NONE
+ *                  (the kernels run at the next width of 128, 256, 512 or
+ *                  1024, with the operands zero-padded in the workspace).
  * Row strides must be multiples of 8 elements (bf16) or 4 (f32), and so must
  * the head and batch strides; softmax row strides stay below 2^24 elements.  O's strides must give every output element its
  * own address (no zero or overlapping batch / head strides): FAB_ERR_BAD_SHAPE

@@ -78,14 +78,20 @@ def status_of(prob):
     ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": True}, "FAB_ERR_UNSUPPORTED"),
     ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "dtype": B.F32},
      "FAB_ERR_UNSUPPORTED"),
-    # GeLU widths the kernels are built for, and ones they are not
+    # GeLU widths: multiples of 64 from 64 to 1024
     ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 1024, "p": 256},
      "FAB_OK"),
     ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 384, "p": 128},
+     "FAB_OK"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 64, "p": 960},
+     "FAB_OK"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 96, "p": 128},
      "FAB_ERR_UNSUPPORTED"),
-    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 128, "p": 768},
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 128, "p": 32},
      "FAB_ERR_UNSUPPORTED"),
     ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 2048, "p": 128},
+     "FAB_ERR_UNSUPPORTED"),
+    ({"f": B.GELU_ERF, "heads_a": 1, "heads_bc": 1, "causal": False, "k": 128, "p": 1088},
      "FAB_ERR_UNSUPPORTED"),
     # an output whose heads (or batch entries) share memory is refused
     ({"strides": {"o_stride": (256 * 4 * 128, 0, 4 * 128)}}, "FAB_ERR_BAD_SHAPE"),

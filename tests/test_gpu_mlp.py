@@ -90,6 +90,18 @@ def test_every_supported_width_pair(k, p):
     check(x, 1.0)
 
 
+@pytest.mark.parametrize("k,p", [(64, 128), (128, 64), (192, 320), (320, 192), (64, 64),
+                                 (448, 960), (960, 576), (1024, 64)])
+def test_widths_between_the_compiled_ones(k, p):
+    """k and p multiples of 64 that the kernels run zero-padded to the next
+    compiled width (128, 256, 512, 1024): the padding must not leak into any
+    output or gradient."""
+    m, n = 130, 97
+    x = {"a": random_array(121, (m, k), 0.1, "bf16"), "bt": random_array(122, (n, k), 0.1, "bf16"),
+         "c": random_array(123, (n, p), 0.1, "bf16"), "do": random_array(124, (m, p), 1.0, "bf16")}
+    check(x, 1.0)
+
+
 def mlp_cases(count=24, seed=77):
     rng = np.random.default_rng(seed)
     out = []
