@@ -10,19 +10,23 @@
 // ("AutoSP" 2.B):
 //   dH = dG * GeLU'(H), dA = scale dH Bt, dBt = scale dH^T A, dC = GeLU(H)^T dO.
 //
-// Schedule ("lanes = rows" as in the attention kernels): a workgroup of NW
-// waves (8, or 4 for the smallest k and p) owns 32 rows (or 32 columns of n
-// for the dBt/dC kernel).  The long contractions of the first products
-// (k, p <= 1024) are split across the NW waves, each keeping its 1 / NW of
-// the resident operand in registers; the partial 32 x 32 tiles are summed
-// through LDS and each wave finishes 16 / NW of every lane's tile entries
-// (GeLU or GeLU'), so each erf is evaluated once.  Each wave then owns 1 / NW
-// of the output columns for the second product.  Streamed operands are read
-// from copies of the inputs (never of the intermediate) that small kernels
-// pack into the workspace first, in MFMA operand order, so each load reads
-// 1 KiB of contiguous memory (see the packing kernels below).  The n (or m)
-// loop is split across workgroups; the fp32 partial sums are added by a final
-// elementwise kernel.
+// Two kernels, each used twice through the symmetry of H = scale A Bt^T in
+// (A, Bt):
+//  * mlp_fwd_kernel (64-row blocks): O[i] = sum_j GeLU(H_ij) C_j, and with the
+//    roles of (A, Bt, C) taken by (Bt, A, dO), dC[j] = sum_i GeLU(H_ij) dO_i;
+//  * mlp_bwd_da_kernel (32-row blocks): dA[i] = scale sum_j dH_ij Bt_j, and
+//    with (A, dO, Bt, C) taken by (Bt, C, A, dO), dBt[j] = scale sum_i dH_ij A_i.
+// Lanes own rows as in the attention kernels.  The long contractions of the
+// first products (k, p <= 1024) are split across the waves, each keeping its
+// slice of the resident operand in registers; the partial 32 x 32 tiles are
+// summed through LDS and each wave finishes a share of every lane's tile
+// entries (GeLU or GeLU'), so each erf is evaluated once; each wave then owns
+// a slice of the output columns for the second product.  Streamed operands are
+// read from copies of the inputs (never of the intermediate) that small
+// kernels pack into the workspace first, in MFMA operand order, so each load
+// or async copy reads 1 KiB of contiguous memory (see the packing kernels
+// below).  The streamed loop is split across workgroups; the fp32 partial
+// sums are added by a final elementwise kernel.
 #include "fab_device.h"
 #include "fab_internal.h"
 
@@ -167,12 +171,11 @@ __device__ __forceinline__ void store_tile_f32(float* dst, const f32x16& v) {
 // so every 8-byte write or read of a wave covers 512 contiguous bytes (no bank
 // conflicts; a lane-major layout puts a wave's reads 64 bytes apart).
 //
-// finish_tile sums the NW partial tiles of H (and of dG when GRAD) and writes
-// GeLU(scale H) (or dG * GeLU'(scale H) when GRAD) as bf16 pairs to gsh; wave
-// w takes slots [16 w / NW, 16 (w + 1) / NW) of every lane, so each erf is
-// evaluated once.  Caller: barrier before (partials written) and after (gsh
-// complete).
-template <int NW, bool GRAD>
+// finish_tile sums the NW partial tiles of H and of dG and writes
+// dH = dG * GeLU'(scale H) as bf16 pairs to gsh; wave w takes slots
+// [16 w / NW, 16 (w + 1) / NW) of every lane, so each erf is evaluated once.
+// Caller: barrier before (partials written) and after (gsh complete).
+template <int NW>
 __device__ __forceinline__ void finish_tile(const float* red_h, const float* red_g, uint32_t* gsh,
                                             int wave, int lane, float scale) {
   constexpr int SPW = 16 / NW;
@@ -190,15 +193,13 @@ __device__ __forceinline__ void finish_tile(const float* red_h, const float* red
       const f32x2 x = rh[idx];
       h[j] += x[0];
       h[j + 1] += x[1];
-      if constexpr (GRAD) {
-        const f32x2 y = rg[idx];
-        g[j] += y[0];
-        g[j + 1] += y[1];
-      }
+      const f32x2 y = rg[idx];
+      g[j] += y[0];
+      g[j + 1] += y[1];
     }
   float x[SPW];
 #pragma unroll
-  for (int j = 0; j < SPW; ++j) x[j] = GRAD ? g[j] * gelu_grad_f(scale * h[j]) : gelu_f(scale * h[j]);
+  for (int j = 0; j < SPW; ++j) x[j] = g[j] * gelu_grad_f(scale * h[j]);
 #pragma unroll
   for (int j = 0; j < SPW; j += 2) gsh[lane * 8 + (wave * SPW + j) / 2] = pack_bf16(x[j], x[j + 1]);
 }
@@ -456,9 +457,9 @@ __global__ __launch_bounds__(64 * kFwdWaves, 1) void mlp_fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// backward.  Both kernels below recompute one 32 x 32 tile of H (and of dG for
-// the gradient of the first product) per step, split over NW waves along the
-// contraction, then finish it with finish_tile and feed it to the second
+// backward: dA (and, with the roles swapped, dBt).  The kernel recomputes one
+// 32 x 32 tile of H and of dG per step, split over NW waves along the
+// contractions, finishes dH with finish_tile and feeds it to the second
 // product.  After this tile's first-product MFMAs, the tile's transposed
 // second-product operand is copied asynchronously into LDS and the rows of
 // the next tile's first-product operands are loaded into registers, so both
@@ -554,7 +555,7 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
     stash_tile(red + NW * 64 * 16, wave, lane, gp);
     __syncthreads();
     // slot r of lane l: row `row`, column 32 jt + 16 lg + r
-    finish_tile<NW, true>(red, red + NW * 64 * 16, gsh, wave, lane, a.scale);
+    finish_tile<NW>(red, red + NW * 64 * 16, gsh, wave, lane, a.scale);
     __syncthreads();
     u32x4 db[2];
     db[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
@@ -574,110 +575,11 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
     if (col0 + 32 * t < a.k) store_tile_f32(dst + 32 * t, acc[t]);
 }
 
-// dBt (WANT_DB) or dC (!WANT_DB): workgroup = 32 columns of n, one split of
-// the m tiles.  dBt needs H and dG; dC needs only G = GeLU(H).
-template <int K, int P, bool WANT_DB>
-constexpr int mlp_bwd_col_waves() { return mlp_bwd_waves<K, (WANT_DB ? P : 128), (WANT_DB ? K : P)>(); }
-
-template <int K, int P, bool WANT_DB>
-__global__ __launch_bounds__((64 * mlp_bwd_col_waves<K, P, WANT_DB>())) void mlp_bwd_col_kernel(
-    MlpArgs a, const uint16_t* ar, const uint16_t* dor, const uint16_t* xc,
-    int tiles_per_split, float* part) {
-  constexpr int NW = mlp_bwd_col_waves<K, P, WANT_DB>();
-  __shared__ __attribute__((aligned(16))) float red[(WANT_DB ? 2 : 1) * NW * 64 * 16];
-  constexpr int kq = K / NW, kc = kq / 16;
-  constexpr int pq = P / NW, pc = WANT_DB ? pq / 16 : 1;
-  // output columns of this kernel: k (dBt) or p (dC), 1 / NW per wave
-  constexpr int oq = WANT_DB ? kq : pq, ot = oq / 32;
-  __shared__ __attribute__((aligned(16))) uint32_t gsh[64 * 8];
-  __shared__ __attribute__((aligned(16))) char tsh[NW * ot * 2048];  // xt pieces, per wave
-  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int lq = lane & 31, lg = lane >> 5;
-  const int col = blockIdx.x * 32 + lq;  // index along n
-  const bool clive = col < a.n;
-  char* const tmine = tsh + wave * ot * 2048;
-  static_assert(kc >= 1 && pc >= 1 && ot >= 1, "slice too small for the wave count");
-  const uint16_t* Bt = static_cast<const uint16_t*>(a.bt);
-  const uint16_t* Cm = static_cast<const uint16_t*>(a.c);
-
-  // columns past k (or p) read as zero: the compiled widths K, P may exceed them
-  u32x4 bf[kc], cf[pc];
-#pragma unroll
-  for (int c = 0; c < kc; ++c) {
-    const int ck = wave * kq + 16 * c + 8 * lg;
-    bf[c] = clive && ck < a.k ? ldg16(Bt + (int64_t)col * a.bt_sr + ck) : u32x4{0, 0, 0, 0};
-  }
-  if constexpr (WANT_DB) {
-#pragma unroll
-    for (int c = 0; c < pc; ++c) {
-      const int cp = wave * pq + 16 * c + 8 * lg;
-      cf[c] = clive && cp < a.p ? ldg16(Cm + (int64_t)col * a.c_sr + cp) : u32x4{0, 0, 0, 0};
-    }
-  }
-  f32x16 acc[ot];
-#pragma unroll
-  for (int t = 0; t < ot; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
-
-  const int mtiles = (a.m + 31) / 32;
-  const int it0 = blockIdx.y * tiles_per_split;
-  const int it1 = min(mtiles, it0 + tiles_per_split);
-  u32x4 afr[kc], ofr[pc];
-  // row fragments (it, wave kc + c) of A and (it, wave pc + c) of dO
-  auto load_rows = [&](int it) {
-    const uint16_t* ap = ar + ((int64_t)it * (K / 16) + wave * kc) * 512 + lane * 8;
-#pragma unroll
-    for (int c = 0; c < kc; ++c) afr[c] = ldg16(ap + c * 512);
-    if constexpr (WANT_DB) {
-      const uint16_t* op = dor + ((int64_t)it * (P / 16) + wave * pc) * 512 + lane * 8;
-#pragma unroll
-      for (int c = 0; c < pc; ++c) ofr[c] = ldg16(op + c * 512);
-    }
-  };
-  if (it0 < it1) load_rows(it0);
-  for (int it = it0; it < it1; ++it) {
-    f32x16 hp, gp;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) hp[r] = gp[r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < kc; ++c) hp = mfma32(afr[c], bf[c], hp);
-    if constexpr (WANT_DB) {
-#pragma unroll
-      for (int c = 0; c < pc; ++c) gp = mfma32(ofr[c], cf[c], gp);
-    }
-    wait_lds_reads();  // the previous tile's reads of tmine are done
-    copy_second_operand<ot, (WANT_DB ? K : P) / 32>(xc, wave * oq / 32, it, lane, tmine);
-    load_rows(min(it + 1, it1 - 1));  // unconditional: a branch here costs register copies
-    stash_tile(red, wave, lane, hp);
-    if constexpr (WANT_DB) stash_tile(red + NW * 64 * 16, wave, lane, gp);
-    __syncthreads();
-    // slot r of lane l: column `col`, row 32 it + 16 lg + r
-    finish_tile<NW, WANT_DB>(red, red + NW * 64 * 16, gsh, wave, lane, a.scale);
-    __syncthreads();
-    u32x4 xb[2];
-    xb[0] = *reinterpret_cast<const u32x4*>(gsh + lane * 8);
-    xb[1] = *reinterpret_cast<const u32x4*>(gsh + lane * 8 + 4);
-    wait_copies<kc + (WANT_DB ? pc : 0)>();  // the next tile's row loads stay in flight
-#pragma unroll
-    for (int t = 0; t < ot; ++t) {
-      acc[t] = mfma32(lds16(tmine + (2 * t) * 1024 + 16 * lane), xb[0], acc[t]);
-      acc[t] = mfma32(lds16(tmine + (2 * t + 1) * 1024 + 16 * lane), xb[1], acc[t]);
-    }
-  }
-  if (!clive) return;
-  const int ocols = WANT_DB ? a.k : a.p;
-  const int col0 = wave * oq + 16 * lg;
-  float* dst = part + ((int64_t)blockIdx.y * a.n + col) * ocols + col0;
-#pragma unroll
-  for (int t = 0; t < ot; ++t)
-    if (col0 + 32 * t < ocols) store_tile_f32(dst + 32 * t, acc[t]);
-}
-
 struct MlpLayout {
   int split_fwd;    // splits of the n loop for the forward (64-row blocks)
   int split_rows;   // splits of the n loop for the row-block backward kernel
-  int split_cols;   // splits of the m loop for the column-block kernels
+  int split_cols;   // splits of the m loop for the dBt kernel
+  int split_dc;     // splits of the m loop for dC (the forward kernel, 64-column blocks)
   int64_t m_pad, n_pad;
   size_t fwd_btr, fwd_ct, fwd_part, fwd_total;
   // row fragments of Bt, C, A, dO; column fragments of Bt, A, dO; partials
@@ -701,6 +603,7 @@ MlpLayout layout(int m, int n, int k, int p) {
   L.split_fwd = pick_splits((m + 63) / 64, nb);
   L.split_rows = pick_splits(mb, nb);
   L.split_cols = pick_splits(nb, mb);
+  L.split_dc = pick_splits((n + 63) / 64, mb);
   L.m_pad = (int64_t)round_up(m, kPad);
   L.n_pad = (int64_t)round_up(n, kPad);
   size_t off = 0;
@@ -731,7 +634,7 @@ MlpLayout layout(int m, int n, int k, int p) {
   L.bwd_pb = off;
   off = round_up(off + (size_t)L.split_cols * n * k * 4, 256);
   L.bwd_pc = off;
-  off = round_up(off + (size_t)L.split_cols * n * p * 4, 256);
+  off = round_up(off + (size_t)L.split_dc * n * p * 4, 256);
   L.bwd_total = off;
   return L;
 }
@@ -779,14 +682,17 @@ size_t mlp_bwd_workspace(int m, int n, int k, int p) { return layout(m, n, k, p)
 
 namespace {
 
+// The forward kernel: for every row i of a.a, sum over the streamed rows j of
+// GeLU(scale a.a_i . X_j) Y_j, with X's row fragments in btr and Y's column
+// fragments in ctf.  It also computes dC (a.a = Bt, X = A, Y = dO).
 template <int K, int P>
-hipError_t fwd_kp(const MlpArgs& a, const MlpLayout& L, const uint16_t* btr, const uint16_t* ctf,
-                  float* part, hipStream_t s) {
+hipError_t fwd_kp(const char* name, const MlpArgs& a, int splits, const uint16_t* btr,
+                  const uint16_t* ctf, float* part, hipStream_t s) {
   const int ntiles = (a.n + 31) / 32, mb = (a.m + 63) / 64;
-  const int per = (ntiles + L.split_fwd - 1) / L.split_fwd;
-  const dim3 grid((unsigned)(mb * L.split_fwd)), block(64 * kFwdWaves);
-  FAB_TIMED("mlp_fwd", s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, btr, ctf,
-                                             mb, L.split_fwd, per, part));
+  const int per = (ntiles + splits - 1) / splits;
+  const dim3 grid((unsigned)(mb * splits)), block(64 * kFwdWaves);
+  FAB_TIMED(name, s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, btr, ctf, mb,
+                                        splits, per, part));
   return hipGetLastError();
 }
 
@@ -800,15 +706,27 @@ hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const char* ws, float* p
   FAB_TIMED("mlp_bwd_da", s, hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)mtiles, (unsigned)L.split_rows),
                      dim3(64 * mlp_bwd_waves<K, P, K>()), 0, s, a, frag(L.bwd_btr), frag(L.bwd_cr),
                      frag(L.bwd_btc), per_n, pa));
-  FAB_TIMED("mlp_bwd_dbt", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, true>),
-                     dim3((unsigned)ntiles, (unsigned)L.split_cols),
-                     dim3(64 * mlp_bwd_col_waves<K, P, true>()), 0, s, a, frag(L.bwd_ar), frag(L.bwd_dor),
+  // dBt[j] = scale sum_i (C_j . dO_i) GeLU'(scale Bt_j . A_i) A_i: the dA
+  // kernel with the roles of (A, dO, Bt, C) taken by (Bt, C, A, dO)
+  MlpArgs u = a;
+  u.a = a.bt;
+  u.a_sr = a.bt_sr;
+  u.dout = a.c;
+  u.o_sr = a.c_sr;
+  u.m = a.n;
+  u.n = a.m;
+  FAB_TIMED("mlp_bwd_dbt", s, hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)ntiles, (unsigned)L.split_cols),
+                     dim3(64 * mlp_bwd_waves<K, P, K>()), 0, s, u, frag(L.bwd_ar), frag(L.bwd_dor),
                      frag(L.bwd_ac), per_m, pb));
-  FAB_TIMED("mlp_bwd_dc", s, hipLaunchKernelGGL((mlp_bwd_col_kernel<K, P, false>),
-                     dim3((unsigned)ntiles, (unsigned)L.split_cols),
-                     dim3(64 * mlp_bwd_col_waves<K, P, false>()), 0, s, a, frag(L.bwd_ar), frag(L.bwd_dor),
-                     frag(L.bwd_doc), per_m, pc));
-  return hipGetLastError();
+  if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  // dC[j] = sum_i GeLU(scale Bt_j . A_i) dO_i: the forward with the roles of
+  // (A, Bt, C) taken by (Bt, A, dO), on 64-column blocks of n
+  MlpArgs t = a;
+  t.a = a.bt;
+  t.a_sr = a.bt_sr;
+  t.m = a.n;
+  t.n = a.m;
+  return fwd_kp<K, P>("mlp_bwd_dc", t, L.split_dc, frag(L.bwd_ar), frag(L.bwd_doc), pc, s);
 }
 
 // Calls fn.template operator()<K, P>() for the supported sizes.
@@ -851,7 +769,9 @@ hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   e = pack_cols(a.c, a.c_sr, a.n, a.p, pw, L.n_pad, ctf, s);
   if (e != hipSuccess) return e;
-  e = dispatch_kp(kw, pw, [&]<int K, int P>() { return fwd_kp<K, P>(a, L, btr, ctf, part, s); });
+  e = dispatch_kp(kw, pw, [&]<int K, int P>() {
+    return fwd_kp<K, P>("mlp_fwd", a, L.split_fwd, btr, ctf, part, s);
+  });
   if (e != hipSuccess) return e;
   return reduce(part, L.split_fwd, a.m, a.p, 1.f, a.o, a.o_sr, s);
 }
@@ -876,7 +796,7 @@ hipError_t launch_mlp_bwd_bf16(const MlpArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   if ((e = reduce(pa, L.split_rows, a.m, a.k, a.scale, a.da, a.a_sr, s)) != hipSuccess) return e;
   if ((e = reduce(pb, L.split_cols, a.n, a.k, a.scale, a.dbt, a.bt_sr, s)) != hipSuccess) return e;
-  return reduce(pc, L.split_cols, a.n, a.p, 1.f, a.dc, a.c_sr, s);
+  return reduce(pc, L.split_dc, a.n, a.p, 1.f, a.dc, a.c_sr, s);
 }
 
 }  // namespace fab
