@@ -287,9 +287,8 @@ struct FwdShape {
 };
 
 template <int K, int P>
-__global__ __launch_bounds__(64 * kFwdWaves, 1) void mlp_fwd_kernel(
-    MlpArgs a, const uint16_t* btr, const uint16_t* ctf, int mb, int splits,
-    int tiles_per_split, float* part) {
+__device__ __forceinline__ void mlp_fwd_body(MlpArgs a, const uint16_t* btr, const uint16_t* ctf,
+                                             int mb, int splits, int tiles_per_split, float* part) {
   using S = FwdShape<K, P>;
   constexpr int kc = S::kc, pt = S::pt;
   __shared__ __attribute__((aligned(1024))) char lds[S::LDS];
@@ -490,9 +489,9 @@ constexpr int mlp_bwd_waves() { return (K >= 128 && P >= 128 && OUT >= 256) ? 8 
 
 // dA: workgroup = 32 rows of A, one split of the n tiles.
 template <int K, int P>
-__global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_kernel(
-    MlpArgs a, const uint16_t* btr, const uint16_t* cr, const uint16_t* btc,
-    int tiles_per_split, float* part) {
+__device__ __forceinline__ void mlp_bwd_da_body(MlpArgs a, const uint16_t* btr, const uint16_t* cr,
+                                                const uint16_t* btc, int tiles_per_split,
+                                                float* part) {
   constexpr int NW = mlp_bwd_waves<K, P, K>();
   __shared__ __attribute__((aligned(16))) float red[2 * NW * 64 * 16];  // partial H, dG tiles
   constexpr int kq = K / NW, kc = kq / 16, kt = kq / 32;
@@ -573,6 +572,29 @@ __global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_ke
 #pragma unroll
   for (int t = 0; t < kt; ++t)
     if (col0 + 32 * t < a.k) store_tile_f32(dst + 32 * t, acc[t]);
+}
+
+// The two bodies each back two kernels (same code, names of their own so
+// profiles tell the launches apart): the forward and dC; dA and dBt.
+template <int K, int P>
+__global__ __launch_bounds__(64 * kFwdWaves, 1) void mlp_fwd_kernel(
+    MlpArgs a, const uint16_t* btr, const uint16_t* ctf, int mb, int splits, int per, float* part) {
+  mlp_fwd_body<K, P>(a, btr, ctf, mb, splits, per, part);
+}
+template <int K, int P>
+__global__ __launch_bounds__(64 * kFwdWaves, 1) void mlp_bwd_dc_kernel(
+    MlpArgs a, const uint16_t* btr, const uint16_t* ctf, int mb, int splits, int per, float* part) {
+  mlp_fwd_body<K, P>(a, btr, ctf, mb, splits, per, part);
+}
+template <int K, int P>
+__global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_da_kernel(
+    MlpArgs a, const uint16_t* btr, const uint16_t* cr, const uint16_t* btc, int per, float* part) {
+  mlp_bwd_da_body<K, P>(a, btr, cr, btc, per, part);
+}
+template <int K, int P>
+__global__ __launch_bounds__((64 * mlp_bwd_waves<K, P, K>())) void mlp_bwd_dbt_kernel(
+    MlpArgs a, const uint16_t* btr, const uint16_t* cr, const uint16_t* btc, int per, float* part) {
+  mlp_bwd_da_body<K, P>(a, btr, cr, btc, per, part);
 }
 
 struct MlpLayout {
@@ -685,14 +707,18 @@ namespace {
 // The forward kernel: for every row i of a.a, sum over the streamed rows j of
 // GeLU(scale a.a_i . X_j) Y_j, with X's row fragments in btr and Y's column
 // fragments in ctf.  It also computes dC (a.a = Bt, X = A, Y = dO).
-template <int K, int P>
-hipError_t fwd_kp(const char* name, const MlpArgs& a, int splits, const uint16_t* btr,
-                  const uint16_t* ctf, float* part, hipStream_t s) {
+template <int K, int P, bool DC>
+hipError_t fwd_kp(const MlpArgs& a, int splits, const uint16_t* btr, const uint16_t* ctf,
+                  float* part, hipStream_t s) {
   const int ntiles = (a.n + 31) / 32, mb = (a.m + 63) / 64;
   const int per = (ntiles + splits - 1) / splits;
   const dim3 grid((unsigned)(mb * splits)), block(64 * kFwdWaves);
-  FAB_TIMED(name, s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, btr, ctf, mb,
-                                        splits, per, part));
+  if (DC)
+    FAB_TIMED("mlp_bwd_dc", s, hipLaunchKernelGGL((mlp_bwd_dc_kernel<K, P>), grid, block, 0, s, a, btr,
+                                                  ctf, mb, splits, per, part));
+  else
+    FAB_TIMED("mlp_fwd", s, hipLaunchKernelGGL((mlp_fwd_kernel<K, P>), grid, block, 0, s, a, btr, ctf,
+                                               mb, splits, per, part));
   return hipGetLastError();
 }
 
@@ -715,7 +741,7 @@ hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const char* ws, float* p
   u.o_sr = a.c_sr;
   u.m = a.n;
   u.n = a.m;
-  FAB_TIMED("mlp_bwd_dbt", s, hipLaunchKernelGGL((mlp_bwd_da_kernel<K, P>), dim3((unsigned)ntiles, (unsigned)L.split_cols),
+  FAB_TIMED("mlp_bwd_dbt", s, hipLaunchKernelGGL((mlp_bwd_dbt_kernel<K, P>), dim3((unsigned)ntiles, (unsigned)L.split_cols),
                      dim3(64 * mlp_bwd_waves<K, P, K>()), 0, s, u, frag(L.bwd_ar), frag(L.bwd_dor),
                      frag(L.bwd_ac), per_m, pb));
   if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
@@ -726,7 +752,7 @@ hipError_t bwd_kp(const MlpArgs& a, const MlpLayout& L, const char* ws, float* p
   t.a_sr = a.bt_sr;
   t.m = a.n;
   t.n = a.m;
-  return fwd_kp<K, P>("mlp_bwd_dc", t, L.split_dc, frag(L.bwd_ar), frag(L.bwd_doc), pc, s);
+  return fwd_kp<K, P, true>(t, L.split_dc, frag(L.bwd_ar), frag(L.bwd_doc), pc, s);
 }
 
 // Calls fn.template operator()<K, P>() for the supported sizes.
@@ -770,7 +796,7 @@ hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s) {
   e = pack_cols(a.c, a.c_sr, a.n, a.p, pw, L.n_pad, ctf, s);
   if (e != hipSuccess) return e;
   e = dispatch_kp(kw, pw, [&]<int K, int P>() {
-    return fwd_kp<K, P>("mlp_fwd", a, L.split_fwd, btr, ctf, part, s);
+    return fwd_kp<K, P, false>(a, L.split_fwd, btr, ctf, part, s);
   });
   if (e != hipSuccess) return e;
   return reduce(part, L.split_fwd, a.m, a.p, 1.f, a.o, a.o_sr, s);

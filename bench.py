@@ -252,8 +252,8 @@ ROCPROF_NAMES = {
     "attn_bwd_prep": ("attn_bwd_prep_bf16_kernel<128>", "attn_bwd.hip"),
     "mlp_fwd": ("mlp_fwd_kernel<1024, 1024>", "mlp.hip"),
     "mlp_bwd_da": ("mlp_bwd_da_kernel<1024, 1024>", "mlp.hip"),
-    "mlp_bwd_dbt": ("mlp_bwd_col_kernel<1024, 1024, true>", "mlp.hip"),
-    "mlp_bwd_dc": ("mlp_bwd_col_kernel<1024, 1024, false>", "mlp.hip"),
+    "mlp_bwd_dbt": ("mlp_bwd_dbt_kernel<1024, 1024>", "mlp.hip"),
+    "mlp_bwd_dc": ("mlp_bwd_dc_kernel<1024, 1024>", "mlp.hip"),
 }
 
 
@@ -268,13 +268,14 @@ def source_hash(src):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when that summary is missing or was taken from different kernel sources."""
+def measured_traffic(kernel, workload=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of the
+    workload (default: the benchmarked one), or None when that summary is
+    missing or was taken from different kernel sources."""
     if kernel not in ROCPROF_NAMES:
         return None
     rname, src = ROCPROF_NAMES[kernel]
-    path = os.path.join(ROOT, "profiles", f"{WORKLOAD}.hbm_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"{workload or WORKLOAD}.hbm_counters.txt")
     if not os.path.exists(path):
         return None
     want = f"{src}:{source_hash(src)}"
@@ -560,7 +561,9 @@ def time_mlp(steps, warmup, torch, fab_binding):
             "timing": ("events around each repetition's forward and forward + backward "
                        "(median of reps), 512 MiB written between repetitions"),
             "kernels_avg_ms": {k_: v[1] / v[0] for k_, v in kernels.items()},
-            "mfma_counters": {k_: measured_mfma(k_) for k_ in kernels if measured_mfma(k_)}}
+            "mfma_counters": {k_: measured_mfma(k_) for k_ in kernels if measured_mfma(k_)},
+            "hbm_traffic_bytes": {k_: measured_traffic(k_, MLP_WORKLOAD) for k_ in kernels
+                                  if measured_traffic(k_, MLP_WORKLOAD)}}
 
 
 def oracle_rows_timed(w, x, seconds=None, rows_per_head=None, chunk=32, seed=0):
