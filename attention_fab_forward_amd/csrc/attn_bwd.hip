@@ -268,41 +268,57 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
       u32x4 pb[2][2];
       if (work) {
         const bool need_mask = (CAUSAL && q0 + a.diag < k0w + 31) || q0 + C::TILE > a.m;
-        // S for both query sub-blocks first, at raised wave priority, so the
-        // exponentials below overlap the partner wave's dP products on this SIMD
-        f32x16 s[2];
+        // S of both query sub-blocks at raised wave priority, so the P wave
+        // gets the MFMA pipe ahead of its partner's dP products; one
+        // straight-line phase per mask case (and the LSE read up front), so the
+        // first sub-block's exponentials can be scheduled between the second
+        // sub-block's S products
+        auto phase1 = [&]<bool MASK>() {
+          f32x16 s[2];
 #pragma unroll
-        for (int sq = 0; sq < 2; ++sq)
+          for (int sq = 0; sq < 2; ++sq)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[sq][r] = 0.f;
-        __builtin_amdgcn_s_setprio(2);
-        lds_mfma_pipeline<2 * C::DC, 4>(
-            [&](int i) { return read_nat<D>(st + L::Q, i / C::DC, i % C::DC, lq, lg); },
-            [&](int i, const u32x4& x) { s[i / C::DC] = mfma32(x, kv[i % C::DC], s[i / C::DC]); });
-        __builtin_amdgcn_s_setprio(0);
+            for (int r = 0; r < 16; ++r) s[sq][r] = 0.f;
+          // LSE of both halves first: the exponentials then wait on nothing but S
+          f32x4 lse[2][4];
 #pragma unroll
-        for (int sq = 0; sq < 2; ++sq) {
-          if (need_mask) {
+          for (int sq = 0; sq < 2; ++sq)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int q = q0 + 32 * sq + 16 * lg + r;
-              if ((CAUSAL && q + a.diag < mykey) || q >= a.m) s[sq][r] = -INFINITY;
+            for (int j = 0; j < 4; ++j)
+              lse[sq][j] = reinterpret_cast<const f32x4*>(st + L::LSE)[8 * sq + 4 * lg + j];
+          __builtin_amdgcn_s_setprio(2);
+          lds_mfma_pipeline<C::DC, 4>(
+              [&](int i) { return read_nat<D>(st + L::Q, 0, i, lq, lg); },
+              [&](int i, const u32x4& x) { s[0] = mfma32(x, kv[i], s[0]); });
+          lds_mfma_pipeline<C::DC, 4>(
+              [&](int i) { return read_nat<D>(st + L::Q, 1, i, lq, lg); },
+              [&](int i, const u32x4& x) { s[1] = mfma32(x, kv[i], s[1]); });
+#pragma unroll
+          for (int sq = 0; sq < 2; ++sq) {
+            if constexpr (MASK) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int q = q0 + 32 * sq + 16 * lg + r;
+                if ((CAUSAL && q + a.diag < mykey) || q >= a.m) s[sq][r] = -INFINITY;
+              }
             }
-          }
-          const f32x4* l2 = reinterpret_cast<const f32x4*>(st + L::LSE) + 8 * sq + 4 * lg;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 lse2 = l2[j];
-            f32x4 p;
+            for (int j = 0; j < 4; ++j) {
+              const f32x4 lse2 = lse[sq][j];
+              f32x4 p;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[sq][4 * j + e], cs, -lse2[e]));
-            pb[sq][j >> 1][2 * (j & 1)] = pack_bf16(p[0], p[1]);
-            pb[sq][j >> 1][2 * (j & 1) + 1] = pack_bf16(p[2], p[3]);
+              for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(s[sq][4 * j + e], cs, -lse2[e]));
+              pb[sq][j >> 1][2 * (j & 1)] = pack_bf16(p[0], p[1]);
+              pb[sq][j >> 1][2 * (j & 1) + 1] = pack_bf16(p[2], p[3]);
+            }
+            // P goes to the partner in the bf16 form the dV products use
+            px[(2 * sq) * 64] = pb[sq][0];
+            px[(2 * sq + 1) * 64] = pb[sq][1];
           }
-          // P goes to the partner in the bf16 form the dV products use
-          px[(2 * sq) * 64] = pb[sq][0];
-          px[(2 * sq + 1) * 64] = pb[sq][1];
-        }
+          __builtin_amdgcn_s_setprio(0);
+        };
+        if (need_mask) phase1.template operator()<true>();
+        else phase1.template operator()<false>();
       }
       lds_barrier();  // P visible to the dS waves
       if (work) {
