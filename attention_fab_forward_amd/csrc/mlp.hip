@@ -232,8 +232,10 @@ __device__ __forceinline__ void wait_lds_reads_but() {
 }
 // Inside step i of lds_mfma_pipeline<N, DEPTH>: waits until operand i's LDS
 // read has completed.  At that point at most min(DEPTH - 1, N - 1 - i) reads
-// were issued after it (LDS operations complete in order); i is a constant
-// once the pipeline is unrolled, so the branches fold away.
+// were issued after it, and LDS operations complete in order (the counter
+// also counts scalar memory loads, which do not; the loops that use this
+// issue none: their kernel arguments are loaded before the loop); i is a
+// constant once the pipeline is unrolled, so the branches fold away.
 template <int N, int DEPTH>
 __device__ __forceinline__ void wait_operand_read(int i) {
   static_assert(DEPTH >= 1 && DEPTH <= 4, "pipeline depth");
