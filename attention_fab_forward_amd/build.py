@@ -29,11 +29,15 @@ FLAGS = [
 
 # Per-source extra flags.  The attention kernels keep MFMA accumulators in
 # arch VGPRs (their softmax / gradient math reads them every step; AGPR
-# residency would add a copy per element).
+# residency would add a copy per element).  The GeLU MLP kernels ask for the
+# same; the forward's 64-row output block still overflows into AGPRs, while
+# its partial H tiles no longer pass through them (forward and dC about 4 %
+# faster, alternating runs).
 FILE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "attn_f32_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "mlp.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 
