@@ -26,7 +26,12 @@
 // kernels pack into the workspace first, in MFMA operand order, so each load
 // or async copy reads 1 KiB of contiguous memory (see the packing kernels
 // below).  The streamed loop is split across workgroups; the fp32 partial
-// sums are added by a final elementwise kernel.
+// sums are added by a final elementwise kernel.  The second products put the
+// register operand (G, dH) on the MFMA's row side, so an accumulator tile holds
+// output rows by slot and output columns by lane: each partial-sum store of a
+// wave then writes whole 128-byte lines (one per row and half-wave) instead
+// of 32 bytes of each of 32 lines, which at the end of a kernel, when every
+// workgroup stores at once, is four times fewer L2 writes.
 #include "fab_device.h"
 #include "fab_internal.h"
 
@@ -160,12 +165,6 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* part, in
   stg16(out + r * ld_out + c, v);
 }
 
-__device__ __forceinline__ void store_tile_f32(float* dst, const f32x16& v) {
-  f32x4* d = reinterpret_cast<f32x4*>(dst);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) d[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-}
-
 // Partial tiles live in LDS as float pairs, slot-pair major: pair q (slots
 // 2q, 2q + 1) of wave w's partial for lane l at float2 index (8 w + q) 64 + l,
 // so every 8-byte write or read of a wave covers 512 contiguous bytes (no bank
@@ -261,7 +260,7 @@ __device__ __forceinline__ void wait_operand_read(int i) {
 // sums its own partials with the three the other waves left in LDS, applies
 // GeLU once per element and publishes bf16 G.  Per n chunk j:
 //   H^T(j) partials (MFMA) -> stash, read G(j - 1) -> barrier ->
-//   finish(j) (sums, GeLU) and O^T += C^T(j - 1) G^T(j - 1) (MFMA)
+//   finish(j) (sums, GeLU) and O += G(j - 1) C(j - 1) (MFMA)
 //   -> publish G(j) -> barrier
 // (the GeLU of chunk j and the second product of chunk j - 1 are independent,
 // so the scheduler may interleave their instructions).  The Bt and C^T fragments of a wave are private to it (contraction slice,
@@ -344,15 +343,16 @@ __device__ __forceinline__ void mlp_fwd_body(MlpArgs a, const uint16_t* btr, con
 #pragma unroll
     for (int i = 0; i < 2 * pt; ++i) dma16(c_src(j, i), 16 * lane, csh + i * 1024);
   };
-  // O^T += C^T G^T over one chunk, G from registers (g[rt][half]); with
-  // REFILL, slot i then receives fragment i of chunk jn
+  // O += G C over one chunk, G from registers (g[rt][half], the A operands;
+  // a C^T fragment read as the B operand is C); with REFILL, slot i then
+  // receives fragment i of chunk jn
   constexpr int kDepth2 = 2;
   auto second_product = [&]<bool REFILL>(const u32x4 (&g)[2][2], int jn) {
     lds_mfma_pipeline<2 * pt, kDepth2>(
         [&](int i) { return lds16(csh + i * 1024 + 16 * lane); },
         [&](int i, const u32x4& x) {
-          o[i / 2][0] = mfma32(x, g[0][i % 2], o[i / 2][0]);
-          o[i / 2][1] = mfma32(x, g[1][i % 2], o[i / 2][1]);
+          o[i / 2][0] = mfma32(g[0][i % 2], x, o[i / 2][0]);
+          o[i / 2][1] = mfma32(g[1][i % 2], x, o[i / 2][1]);
           if constexpr (REFILL) {
             wait_operand_read<2 * pt, kDepth2>(i);  // slot i's read is complete
             dma16(c_src(jn, i), 16 * lane, csh + i * 1024);
@@ -362,7 +362,7 @@ __device__ __forceinline__ void mlp_fwd_body(MlpArgs a, const uint16_t* btr, con
 
   // this wave's quarter of the chunk: row tile wave / 2, slots 8 (wave % 2) .. + 7
   const int mine_rt = wave >> 1, mine_h = wave & 1;
-  // G of the previous chunk (bf16, the second product's B operands); read
+  // G of the previous chunk (bf16, the second product's A operands); read
   // from gsh before the barrier after which the waves overwrite it
   u32x4 g[2][2];
   auto read_g = [&]() {
@@ -445,16 +445,22 @@ __device__ __forceinline__ void mlp_fwd_body(MlpArgs a, const uint16_t* btr, con
     second_product.template operator()<false>(g, 0);
   }
   wait_copies<0>();
+  // o[t][rt] holds O rows rb 64 + 32 rt + 8 (r / 4) + 4 (lane / 32) + r % 4,
+  // column wave pq + 32 t + perm_row(lane % 32): lanes 0..31 (and 32..63)
+  // of one store fill one 128-byte line of a row
+  const int col0 = wave * S::pq + perm_row(lq);
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = rb * 64 + 32 * rt + lq;
-    if (row >= a.m) continue;
-    const int col0 = wave * S::pq + 16 * (lane >> 5);
-    float* dst = part + ((int64_t)split * a.m + row) * a.p + col0;
+  for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int t = 0; t < pt; ++t)
-      if (col0 + 32 * t < a.p) store_tile_f32(dst + 32 * t, o[t][rt]);  // p <= padded width
-  }
+    for (int t = 0; t < pt; ++t) {
+      if (wave * S::pq + 32 * t >= a.p) continue;  // p <= padded width, p % 32 == 0
+      float* dst = part + ((int64_t)split * a.m + rb * 64 + 32 * rt + 4 * (lane >> 5)) * a.p + col0 + 32 * t;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = 8 * (r >> 2) + (r & 3);
+        if (rb * 64 + 32 * rt + 4 * (lane >> 5) + dr < a.m) dst[(int64_t)dr * a.p] = o[t][rt][r];
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -564,16 +570,24 @@ __device__ __forceinline__ void mlp_bwd_da_body(MlpArgs a, const uint16_t* btr, 
     wait_copies<kc + pc>();  // the next tile's row loads stay in flight
 #pragma unroll
     for (int t = 0; t < kt; ++t) {
-      acc[t] = mfma32(lds16(tmine + (2 * t) * 1024 + 16 * lane), db[0], acc[t]);
-      acc[t] = mfma32(lds16(tmine + (2 * t + 1) * 1024 + 16 * lane), db[1], acc[t]);
+      acc[t] = mfma32(db[0], lds16(tmine + (2 * t) * 1024 + 16 * lane), acc[t]);
+      acc[t] = mfma32(db[1], lds16(tmine + (2 * t + 1) * 1024 + 16 * lane), acc[t]);
     }
   }
-  if (!rlive) return;
-  const int col0 = wave * kq + 16 * lg;
-  float* dst = part + ((int64_t)blockIdx.y * a.m + row) * a.k + col0;
+  // acc[t] holds dA rows 32 blockIdx.x + 8 (r / 4) + 4 lg + r % 4, column
+  // wave kq + 32 t + perm_row(lane % 32): each store fills one 128-byte line
+  // of two rows
+  const int r0 = blockIdx.x * 32 + 4 * lg;
+  float* dst = part + ((int64_t)blockIdx.y * a.m + r0) * a.k + wave * kq + perm_row(lq);
 #pragma unroll
-  for (int t = 0; t < kt; ++t)
-    if (col0 + 32 * t < a.k) store_tile_f32(dst + 32 * t, acc[t]);
+  for (int t = 0; t < kt; ++t) {
+    if (wave * kq + 32 * t >= a.k) continue;  // k <= padded width, k % 32 == 0
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dr = 8 * (r >> 2) + (r & 3);
+      if (r0 + dr < a.m) dst[(int64_t)dr * a.k + 32 * t] = acc[t][r];
+    }
+  }
 }
 
 // The two bodies each back two kernels (same code, names of their own so
