@@ -149,8 +149,8 @@ __device__ __forceinline__ void issue_vec64(const float* src, int i0, int count,
 //  * dS wave (waves 4-7): holds V; dP - D = dO V^T - D; dS = P (dP - D) with
 //    the bf16 P; dK^T += Q^T dS.
 // Query blocks of 64 (all query heads of the group) stream through two LDS
-// stages; each step has two barriers: P written -> P read, and end of step
-// (stage and P buffer released).
+// stages, copied by the dS waves; each step has two barriers: P written -> P
+// read, and end of step (stage and P buffer released).
 // ---------------------------------------------------------------------------
 constexpr int kDkdvWaves = 8;
 
@@ -166,15 +166,15 @@ struct DkdvLds {
   static constexpr int BYTES = PX + 4 * PX_GROUP;
 };
 
-template <int D>
-__device__ __forceinline__ void dkdv_issue(const AttnArgs& a, const TileOffsets<D, kDkdvWaves>& tq,
-                                           const TileOffsets<D, kDkdvWaves>& to, int bi, int h,
+template <int D, int NW>
+__device__ __forceinline__ void dkdv_issue(const AttnArgs& a, const TileOffsets<D, NW>& tq,
+                                           const TileOffsets<D, NW>& to, int bi, int h,
                                            int q0, char* st, int wave, int lane) {
   using L = DkdvLds<D>;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
   const uint16_t* ob = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
-  issue_tile<D, kDkdvWaves>(tq, qb, a.q_sr, q0, a.m, st + L::Q, wave, lane);
-  issue_tile<D, kDkdvWaves>(to, ob, a.o_sr, q0, a.m, st + L::DO, wave, lane);
+  issue_tile<D, NW>(tq, qb, a.q_sr, q0, a.m, st + L::Q, wave, lane);
+  issue_tile<D, NW>(to, ob, a.o_sr, q0, a.m, st + L::DO, wave, lane);
   const int64_t r = ((int64_t)bi * a.hq + h) * a.m;
   if (wave == 0) issue_vec64(a.lse2 + r, q0, a.m, st + L::LSE, lane);
   if (wave == 1) issue_vec64(a.delta + r, q0, a.m, st + L::DLT, lane);
@@ -187,7 +187,11 @@ template <int D, bool CAUSAL, bool SAME>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using L = DkdvLds<D>;
-  using TO = TileOffsets<D, kDkdvWaves>;
+  // An LDS write waits while global -> LDS copies of its wave are in flight,
+  // so the dS waves (which write no LDS in the step loop) issue every tile
+  // copy and the P waves' P writes do not wait on copies of their own.
+  constexpr int CW = kDkdvWaves / 2;
+  using TO = TileOffsets<D, CW>;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   const int tid = threadIdx.x;
@@ -215,9 +219,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const int steps_per_head = max(0, nqb - qb_first);
   const int steps = steps_per_head * a.group;
   const bool group_live = k0w < a.n;
-  const TO tq = tile_offsets<D, kDkdvWaves>(a.q_sr, wave, lane);
-  const TO to = SAME ? tq : tile_offsets<D, kDkdvWaves>(a.o_sr, wave, lane);
-  if (steps > 0) dkdv_issue<D>(a, tq, to, bi, g * a.group, qb_first * C::TILE, smem, wave, lane);
+  const int cw = p_role ? 0 : wave - CW;  // copy index of a dS wave
+  const TO tq = tile_offsets<D, CW>(a.q_sr, cw, lane);
+  const TO to = SAME ? tq : tile_offsets<D, CW>(a.o_sr, cw, lane);
+  if (steps > 0 && !p_role) dkdv_issue<D, CW>(a, tq, to, bi, g * a.group, qb_first * C::TILE, smem, cw, lane);
 
   // this wave's operand: K (P wave) or V (dS wave) rows of its 32 keys
   u32x4 kv[C::DC];
@@ -244,9 +249,9 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   // g * group + s / steps_per_head; the loops advance (head, block) counters
   // instead of dividing.  prefetch copies the tiles of the step after (nh, nq).
   auto prefetch = [&](int step, int nh, int nq) {
-    if (step + 1 < steps)
-      dkdv_issue<D>(a, tq, to, bi, g * a.group + nh, (qb_first + nq) * C::TILE,
-                    smem + ((step + 1) & 1) * L::STAGE, wave, lane);
+    if (step + 1 < steps && !p_role)
+      dkdv_issue<D, CW>(a, tq, to, bi, g * a.group + nh, (qb_first + nq) * C::TILE,
+                        smem + ((step + 1) & 1) * L::STAGE, cw, lane);
   };
   auto advance = [&](int& hh, int& qq) {
     if (++qq == steps_per_head) {
