@@ -52,8 +52,6 @@ struct F32T {
   static constexpr int BYTES = ROWS * RB;   // 8 or 16 KiB
   static constexpr int G = D / 8;           // contraction groups (4 values per half-wave)
   static constexpr int DT = D / 32;         // 32-wide output tiles
-  static constexpr int CPW = BYTES / 1024 / kMfmaF32Waves;  // 1 KiB copies per wave per tile
-  static_assert(CPW * 1024 * kMfmaF32Waves == BYTES, "tile copies split evenly over the waves");
 };
 
 __device__ __forceinline__ int fswz(int r, int c) { return c ^ (r & 15); }
@@ -70,22 +68,26 @@ __device__ __forceinline__ float tile_at(const char* tile, int r, int col) {
                                          4 * (col & 3));
 }
 
-// Per-lane sources of the asynchronous copies of a 32-row tile: lane j of
-// this wave's copy i lands at tile byte (wave CPW + i) 1 KiB + 16 j, i.e. row
-// `row[i]`, physical chunk p, and fetches logical chunk p ^ (row mod 16).
-template <int D>
+// Per-lane sources of the asynchronous copies of a 32-row tile shared by NWC
+// waves: lane j of copying wave w's copy i lands at tile byte (w CPW + i)
+// 1 KiB + 16 j, i.e. row `row[i]`, physical chunk p, and fetches logical
+// chunk p ^ (row mod 16).
+template <int D, int NWC = kMfmaF32Waves>
 struct F32Copy {
-  uint32_t off[F32T<D>::CPW];  // byte offset from the tile's first source row
-  int row[F32T<D>::CPW];
+  static constexpr int CPW = F32T<D>::BYTES / 1024 / NWC;  // 1 KiB copies per wave per tile
+  static_assert(CPW * 1024 * NWC == F32T<D>::BYTES, "tile copies split evenly over the waves");
+  uint32_t off[CPW];  // byte offset from the tile's first source row
+  int row[CPW];
 };
 
-template <int D>
-__device__ __forceinline__ F32Copy<D> f32_copy_offsets(int64_t sr, int wave, int lane) {
+template <int D, int NWC = kMfmaF32Waves>
+__device__ __forceinline__ F32Copy<D, NWC> f32_copy_offsets(int64_t sr, int wave, int lane) {
   using T = F32T<D>;
-  F32Copy<D> t;
+  using Cp = F32Copy<D, NWC>;
+  Cp t;
 #pragma unroll
-  for (int i = 0; i < T::CPW; ++i) {
-    const int byte = (wave * T::CPW + i) * 1024 + 16 * lane;
+  for (int i = 0; i < Cp::CPW; ++i) {
+    const int byte = (wave * Cp::CPW + i) * 1024 + 16 * lane;
     const int r = byte / T::RB, pc = (byte % T::RB) / 16;
     t.row[i] = r;
     t.off[i] = (uint32_t)(4 * (r * sr + 4 * fswz(r, pc)));
@@ -96,18 +98,18 @@ __device__ __forceinline__ F32Copy<D> f32_copy_offsets(int64_t sr, int wave, int
 // Copy rows [r0, r0 + 32) of a [rows, D] fp32 matrix into a tile; rows at or
 // past nrows (ragged last tile only, r0 < nrows) repeat row nrows - 1, whose
 // contributions the callers mask.
-template <int D>
-__device__ __forceinline__ void f32_issue(const F32Copy<D>& t, const float* base, int64_t sr,
+template <int D, int NWC>
+__device__ __forceinline__ void f32_issue(const F32Copy<D, NWC>& t, const float* base, int64_t sr,
                                           int r0, int nrows, char* tile, int wave) {
-  using T = F32T<D>;
+  constexpr int CPW = F32Copy<D, NWC>::CPW;
   const char* src = reinterpret_cast<const char*>(base + (int64_t)r0 * sr);
-  char* dst = tile + wave * T::CPW * 1024;
+  char* dst = tile + wave * CPW * 1024;
   if (r0 + 32 <= nrows) {
 #pragma unroll
-    for (int i = 0; i < T::CPW; ++i) dma16(src, t.off[i], dst + i * 1024);
+    for (int i = 0; i < CPW; ++i) dma16(src, t.off[i], dst + i * 1024);
   } else {
 #pragma unroll
-    for (int i = 0; i < T::CPW; ++i) {
+    for (int i = 0; i < CPW; ++i) {
       const int64_t shift = min(t.row[i], nrows - 1 - r0) - t.row[i];
       dma16_at(src + t.off[i] + 4 * shift * sr, dst + i * 1024);
     }
@@ -167,19 +169,31 @@ __device__ __forceinline__ void col_product(const char* tile, int lq, int h, con
 }
 
 // ---------------------------------------------------------------------------
-// forward: workgroup = 4 waves x 32 queries of one head; key blocks of 32
+// forward: workgroup = 64 queries of one head (two 32-query tiles) x the two
+// halves of their key range, one wave per (tile, half); key blocks of 32.
+// Splitting the key range halves the serial work of the longest rows, whose
+// workgroups (the last query blocks under a causal mask) otherwise set the
+// kernel's time when there are about as many workgroups as CUs.  Each half
+// streams its own K / V blocks through two LDS stages; at the end the halves'
+// running states (unnormalised O, row maximum, partial sums) are combined
+// through LDS with the usual rescaling to the larger maximum.
 // ---------------------------------------------------------------------------
+constexpr int kF32FwdBM = 64;  // queries per forward workgroup
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void attn_fwd_f32_mfma_kernel(AttnArgs a) {
   using T = F32T<D>;
-  constexpr int NW = kMfmaF32Waves, BM = 32 * NW, BN = 32;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES];
-  auto ktile = [&](int i) { return smem + (i & 1) * T::BYTES; };
-  auto vtile = [&](int i) { return smem + (2 + (i & 1)) * T::BYTES; };
+  constexpr int BM = kF32FwdBM, BN = 32;
+  static_assert(kMfmaF32Waves == 4 && BM == 64, "two query tiles x two key halves");
+  __shared__ __attribute__((aligned(1024))) char smem[8 * T::BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, h = lane >> 5;
+  const int half = wave >> 1, qt = wave & 1;  // key half, query tile
+  char* const hs = smem + half * 4 * T::BYTES;
+  auto ktile = [&](int i) { return hs + (i & 1) * T::BYTES; };
+  auto vtile = [&](int i) { return hs + (2 + (i & 1)) * T::BYTES; };
   const int nqb = (a.m + BM - 1) / BM;
   int bh, qi;
   xcd_map(blockIdx.x, a.b * a.hq, nqb, bh, qi);
@@ -190,20 +204,27 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
   const float* kbase = static_cast<const float*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const float* vbase = static_cast<const float*>(a.v) + bi * a.v_sb + g * a.v_sh;
 
-  const int q0 = qb * BM + wave * 32;
+  const int q0 = qb * BM + qt * 32;
   const int myq = q0 + lq;
   const int kend = CAUSAL ? min(a.n, max(0, qb * BM + BM + a.diag)) : a.n;
   const int nkb = (kend + BN - 1) / BN;
+  // half 0: key blocks [0, nkb / 2), half 1: [nkb / 2, nkb); every wave runs
+  // the longer half's iteration count (the same barriers)
+  const int nkb0 = nkb / 2;
+  const int kb_begin = half ? nkb0 : 0, kb_end = half ? nkb : nkb0;
+  const int nloop = nkb - nkb0;
+  // blocks past this tile's last live key are skipped
   const int nkw = q0 >= a.m ? 0
                   : CAUSAL ? (q0 + 31 + a.diag < 0 ? 0 : min(nkb, (q0 + 31 + a.diag) / BN + 1))
                            : nkb;
-  const F32Copy<D> ck = f32_copy_offsets<D>(a.k_sr, wave, lane);
-  const F32Copy<D> cv = f32_copy_offsets<D>(a.v_sr, wave, lane);
-  auto copy = [&](int kb) {
-    f32_issue<D>(ck, kbase, a.k_sr, kb * BN, a.n, ktile(kb), wave);
-    f32_issue<D>(cv, vbase, a.v_sr, kb * BN, a.n, vtile(kb), wave);
+  const F32Copy<D, 2> ck = f32_copy_offsets<D, 2>(a.k_sr, qt, lane);
+  const F32Copy<D, 2> cv = f32_copy_offsets<D, 2>(a.v_sr, qt, lane);
+  // block kb of this half into stage i
+  auto copy = [&](int kb, int i) {
+    f32_issue<D, 2>(ck, kbase, a.k_sr, kb * BN, a.n, ktile(i), qt);
+    f32_issue<D, 2>(cv, vbase, a.v_sr, kb * BN, a.n, vtile(i), qt);
   };
-  if (nkb > 0) copy(0);
+  if (kb_begin < kb_end) copy(kb_begin, 0);
 
   f32x4 qf[T::G];  // Q[myq][8 g + 4 h .. + 3]
 #pragma unroll
@@ -216,11 +237,12 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
   wait_vmem();
   lds_barrier();
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) copy(kb + 1);
-    if (kb < nkw) {
+  for (int it = 0; it < nloop; ++it) {
+    const int kb = kb_begin + it;
+    if (kb + 1 < kb_end) copy(kb + 1, it + 1);
+    if (kb < kb_end && kb < nkw) {
       // slot r: key kb BN + 8 (r / 4) + 4 h + r % 4 of query myq
-      const f32x16 sacc = row_product<D>(ktile(kb), lq, h, qf);
+      const f32x16 sacc = row_product<D>(ktile(it), lq, h, qf);
       float s[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = sacc[r];
@@ -255,10 +277,38 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
       }
-      col_product<D>(vtile(kb), lq, h, s, o);
+      col_product<D>(vtile(it), lq, h, s, o);
     }
     wait_vmem();
     lds_barrier();
+  }
+
+  // half 1 hands its state to half 0 through the (now free) stages:
+  // per query tile, 16 DT accumulator values, the maximum and the partial sum
+  // of each lane, lane-minor
+  float* xs = reinterpret_cast<float*>(smem) + qt * (16 * T::DT + 2) * 64;
+  if (half == 1) {
+#pragma unroll
+    for (int t = 0; t < T::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xs[(16 * t + r) * 64 + lane] = o[t][r];
+    xs[16 * T::DT * 64 + lane] = m_run;
+    xs[(16 * T::DT + 1) * 64 + lane] = l_run;
+  }
+  lds_barrier();
+  if (half == 1) return;
+  {
+    const float m1 = xs[16 * T::DT * 64 + lane], l1 = xs[(16 * T::DT + 1) * 64 + lane];
+    const float mm = fmaxf(m_run, m1);
+    // a half that saw no key contributes nothing (its maximum is -inf)
+    const float f0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mm);
+    const float f1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+#pragma unroll
+    for (int t = 0; t < T::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] = fmaf(o[t][r], f0, xs[(16 * t + r) * 64 + lane] * f1);
+    l_run = fmaf(l_run, f0, l1 * f1);
+    m_run = mm;
   }
 
   // rows that saw no key (offset causal masks): O = 0, LSE = -inf
@@ -310,8 +360,12 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: workgroup = 4 waves x 32 keys of one kv head; query blocks of 32
-// (of every query head of the group) stream through two LDS stages.
+// dK, dV: workgroup = 64 keys of one kv head (two 32-key tiles) x the two
+// halves of their steps (query blocks of 32, of every query head of the
+// group), one wave per (tile, half); each half streams its own Q / dO blocks
+// through two LDS stages, and half 0 adds half 1's partial dK, dV at the end
+// (the split halves the serial work of the first key blocks, which see every
+// query under a causal mask).
 // ---------------------------------------------------------------------------
 template <int D>
 struct F32DkdvLds {
@@ -321,22 +375,26 @@ struct F32DkdvLds {
   static constexpr int DLT = LSE + 256;
   static constexpr int STAGE = DLT + 256;
 };
+constexpr int kF32BwdB = 64;  // keys (dK, dV) or queries (dQ) per backward workgroup
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kernel(AttnArgs a) {
   using T = F32T<D>;
   using L = F32DkdvLds<D>;
-  constexpr int KB = 32 * kMfmaF32Waves, QB = 32;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE];
+  constexpr int KB = kF32BwdB, QB = 32;
+  static_assert(kMfmaF32Waves == 4 && KB == 64, "two key tiles x two step halves");
+  __shared__ __attribute__((aligned(1024))) char smem[4 * L::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, h = lane >> 5;
+  const int half = wave >> 1, kt = wave & 1;  // step half, key tile
+  char* const hs = smem + half * 2 * L::STAGE;
   const int nkb = (a.n + KB - 1) / KB;
   int gh, kblk;
   xcd_map(blockIdx.x, a.b * a.hkv, nkb, gh, kblk);  // low key blocks (most queries) first
   const int g = gh % a.hkv, bi = gh / a.hkv;
-  const int k0w = kblk * KB + wave * 32;
+  const int k0w = kblk * KB + kt * 32;
   const int mykey = k0w + lq;
   const bool live = k0w < a.n;
   const float cs = a.scale_log2;
@@ -344,20 +402,28 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kern
   const int nqb = (a.m + QB - 1) / QB;
   const int steps_per_head = max(0, nqb - qb_first);
   const int steps = steps_per_head * a.group;
+  // half 0: steps [0, steps / 2), half 1: [steps / 2, steps); every wave runs
+  // the longer half's iteration count (the same barriers)
+  const int s0 = steps / 2;
+  const int st_begin = half ? s0 : 0, st_end = half ? steps : s0;
+  const int nloop = steps - s0;
 
-  const F32Copy<D> cq = f32_copy_offsets<D>(a.q_sr, wave, lane);
-  const F32Copy<D> co = f32_copy_offsets<D>(a.o_sr, wave, lane);
+  const F32Copy<D, 2> cq = f32_copy_offsets<D, 2>(a.q_sr, kt, lane);
+  const F32Copy<D, 2> co = f32_copy_offsets<D, 2>(a.o_sr, kt, lane);
   auto copy = [&](int hq_idx, int q0, char* st) {
     const float* qb = static_cast<const float*>(a.q) + bi * a.q_sb + hq_idx * a.q_sh;
     const float* ob = static_cast<const float*>(a.dout) + bi * a.o_sb + hq_idx * a.o_sh;
-    f32_issue<D>(cq, qb, a.q_sr, q0, a.m, st + L::Q, wave);
-    f32_issue<D>(co, ob, a.o_sr, q0, a.m, st + L::DO, wave);
+    f32_issue<D, 2>(cq, qb, a.q_sr, q0, a.m, st + L::Q, kt);
+    f32_issue<D, 2>(co, ob, a.o_sr, q0, a.m, st + L::DO, kt);
     const int64_t r = ((int64_t)bi * a.hq + hq_idx) * a.m;
     const int i = min(q0 + lane, a.m - 1);  // lanes past the block copy a valid row, unused
-    if (wave == 0) dma4_at(a.lse2 + r + i, st + L::LSE);
-    if (wave == 1) dma4_at(a.delta + r + i, st + L::DLT);
+    if (kt == 0) dma4_at(a.lse2 + r + i, st + L::LSE);
+    else dma4_at(a.delta + r + i, st + L::DLT);
   };
-  if (steps > 0) copy(g * a.group, qb_first * QB, smem);
+  // (head, block) of this half's first step
+  int hc = steps_per_head > 0 ? st_begin / steps_per_head : 0;
+  int qc = st_begin - hc * steps_per_head;
+  if (st_begin < st_end) copy(g * a.group + hc, (qb_first + qc) * QB, hs);
 
   f32x4 kf[T::G], vf[T::G];  // K, V rows of this lane's key
   {
@@ -373,18 +439,18 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kern
   wait_vmem();
   lds_barrier();
 
-  int hc = 0, qc = 0;  // (head, block) of this step
-  for (int step = 0; step < steps; ++step) {
+  for (int it = 0; it < nloop; ++it) {
+    const int step = st_begin + it;
     int hn = hc, qn = qc;
     if (++qn == steps_per_head) {
       qn = 0;
       ++hn;
     }
-    if (step + 1 < steps) copy(g * a.group + hn, (qb_first + qn) * QB, smem + ((step + 1) & 1) * L::STAGE);
+    if (step + 1 < st_end) copy(g * a.group + hn, (qb_first + qn) * QB, hs + ((it + 1) & 1) * L::STAGE);
     const int q0 = (qb_first + qc) * QB;
     hc = hn, qc = qn;
-    const char* st = smem + (step & 1) * L::STAGE;
-    if (live && (!CAUSAL || q0 + QB - 1 + a.diag >= k0w)) {
+    const char* st = hs + (it & 1) * L::STAGE;
+    if (step < st_end && live && (!CAUSAL || q0 + QB - 1 + a.diag >= k0w)) {
       // slot r: query q0 + 8 (r / 4) + 4 h + r % 4 of key mykey
       const f32x16 sacc = row_product<D>(st + L::Q, lq, h, kf);
       float lse2[16], ndl[16], p[16];
@@ -410,7 +476,26 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kern
     lds_barrier();
   }
 
-  if (!live || mykey >= a.n) return;
+  // half 1's partial dK, dV to half 0 through the (now free) stages, lane-minor
+  float* xs = reinterpret_cast<float*>(smem) + kt * (32 * T::DT) * 64;
+  if (half == 1) {
+#pragma unroll
+    for (int t = 0; t < T::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        xs[(16 * t + r) * 64 + lane] = dk[t][r];
+        xs[(16 * (T::DT + t) + r) * 64 + lane] = dv[t][r];
+      }
+  }
+  lds_barrier();
+  if (half == 1 || !live || mykey >= a.n) return;
+#pragma unroll
+  for (int t = 0; t < T::DT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[t][r] += xs[(16 * t + r) * 64 + lane];
+      dv[t][r] += xs[(16 * (T::DT + t) + r) * 64 + lane];
+    }
   float* dvrow = static_cast<float*>(a.dv) + bi * a.v_sb + g * a.v_sh + (int64_t)mykey * a.v_sr;
   float* dkrow = static_cast<float*>(a.dk) + bi * a.k_sb + g * a.k_sh + (int64_t)mykey * a.k_sr;
 #pragma unroll
@@ -421,19 +506,24 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kern
 }
 
 // ---------------------------------------------------------------------------
-// dQ: workgroup = 4 waves x 32 queries of one query head; key blocks of 32
+// dQ: workgroup = 64 queries of one query head (two 32-query tiles) x the two
+// halves of their key range, one wave per (tile, half), key blocks of 32;
+// half 0 adds half 1's partial dQ at the end.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void attn_dq_f32_mfma_kernel(AttnArgs a) {
   using T = F32T<D>;
-  constexpr int NW = kMfmaF32Waves, BM = 32 * NW, BN = 32;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * T::BYTES];
-  auto ktile = [&](int i) { return smem + (i & 1) * T::BYTES; };
-  auto vtile = [&](int i) { return smem + (2 + (i & 1)) * T::BYTES; };
+  constexpr int BM = kF32BwdB, BN = 32;
+  static_assert(kMfmaF32Waves == 4 && BM == 64, "two query tiles x two key halves");
+  __shared__ __attribute__((aligned(1024))) char smem[8 * T::BYTES];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lq = lane & 31, h = lane >> 5;
+  const int half = wave >> 1, qt = wave & 1;  // key half, query tile
+  char* const hs = smem + half * 4 * T::BYTES;
+  auto ktile = [&](int i) { return hs + (i & 1) * T::BYTES; };
+  auto vtile = [&](int i) { return hs + (2 + (i & 1)) * T::BYTES; };
   const int nqb = (a.m + BM - 1) / BM;
   int bh, qi;
   xcd_map(blockIdx.x, a.b * a.hq, nqb, bh, qi);
@@ -443,18 +533,21 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
   const float* kbase = static_cast<const float*>(a.k) + bi * a.k_sb + g * a.k_sh;
   const float* vbase = static_cast<const float*>(a.v) + bi * a.v_sb + g * a.v_sh;
 
-  const int q0 = qb * BM + wave * 32;
+  const int q0 = qb * BM + qt * 32;
   const int myq = q0 + lq;
   const bool qlive = myq < a.m;
   const int kend = CAUSAL ? min(a.n, max(0, qb * BM + BM + a.diag)) : a.n;
   const int nkb = (kend + BN - 1) / BN;
-  const F32Copy<D> ck = f32_copy_offsets<D>(a.k_sr, wave, lane);
-  const F32Copy<D> cv = f32_copy_offsets<D>(a.v_sr, wave, lane);
-  auto copy = [&](int kb) {
-    f32_issue<D>(ck, kbase, a.k_sr, kb * BN, a.n, ktile(kb), wave);
-    f32_issue<D>(cv, vbase, a.v_sr, kb * BN, a.n, vtile(kb), wave);
+  const int nkb0 = nkb / 2;
+  const int kb_begin = half ? nkb0 : 0, kb_end = half ? nkb : nkb0;
+  const int nloop = nkb - nkb0;
+  const F32Copy<D, 2> ck = f32_copy_offsets<D, 2>(a.k_sr, qt, lane);
+  const F32Copy<D, 2> cv = f32_copy_offsets<D, 2>(a.v_sr, qt, lane);
+  auto copy = [&](int kb, int i) {
+    f32_issue<D, 2>(ck, kbase, a.k_sr, kb * BN, a.n, ktile(i), qt);
+    f32_issue<D, 2>(cv, vbase, a.v_sr, kb * BN, a.n, vtile(i), qt);
   };
-  if (nkb > 0) copy(0);
+  if (kb_begin < kb_end) copy(kb_begin, 0);
 
   f32x4 qf[T::G], df[T::G];  // Q, dO rows of this lane's query
   {
@@ -474,13 +567,14 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
   wait_vmem();
   lds_barrier();
 
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) copy(kb + 1);
+  for (int it = 0; it < nloop; ++it) {
+    const int kb = kb_begin + it;
+    if (kb + 1 < kb_end) copy(kb + 1, it + 1);
     const int key0 = kb * BN;
-    if (q0 < a.m && (!CAUSAL || key0 <= q0 + 31 + a.diag)) {
+    if (kb < kb_end && q0 < a.m && (!CAUSAL || key0 <= q0 + 31 + a.diag)) {
       // slot r: key key0 + 8 (r / 4) + 4 h + r % 4 of query myq
-      const f32x16 sacc = row_product<D>(ktile(kb), lq, h, qf);
-      const f32x16 dpacc = row_product<D>(vtile(kb), lq, h, df);
+      const f32x16 sacc = row_product<D>(ktile(it), lq, h, qf);
+      const f32x16 dpacc = row_product<D>(vtile(it), lq, h, df);
       const bool need_mask = (CAUSAL && key0 + BN - 1 > q0 + a.diag) || key0 + BN > a.n;
       float ds[16];
 #pragma unroll
@@ -492,13 +586,26 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
         }
         ds[r] = p * (dpacc[r] + ndl);
       }
-      col_product<D>(ktile(kb), lq, h, ds, dq);  // dQ^T += K^T dS^T
+      col_product<D>(ktile(it), lq, h, ds, dq);  // dQ^T += K^T dS^T
     }
     wait_vmem();
     lds_barrier();
   }
 
-  if (!qlive) return;
+  // half 1's partial dQ to half 0 through the (now free) stages, lane-minor
+  float* xs = reinterpret_cast<float*>(smem) + qt * (16 * T::DT) * 64;
+  if (half == 1) {
+#pragma unroll
+    for (int t = 0; t < T::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xs[(16 * t + r) * 64 + lane] = dq[t][r];
+  }
+  lds_barrier();
+  if (half == 1 || !qlive) return;
+#pragma unroll
+  for (int t = 0; t < T::DT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[t][r] += xs[(16 * t + r) * 64 + lane];
   float* out = static_cast<float*>(a.dq) + bi * a.q_sb + hh * a.q_sh + (int64_t)myq * a.q_sr;
 #pragma unroll
   for (int t = 0; t < T::DT; ++t) store_row_tile(out + 32 * t, dq[t], h, a.scale);
@@ -506,7 +613,7 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
 
 template <int D>
 hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
-  const int nqb = (a.m + 32 * kMfmaF32Waves - 1) / (32 * kMfmaF32Waves);
+  const int nqb = (a.m + kF32FwdBM - 1) / kF32FwdBM;
   const dim3 grid((unsigned)nqb * a.hq * a.b), block(64 * kMfmaF32Waves);
   if (a.causal)
     FAB_TIMED("attn_fwd_f32_mfma", s, hipLaunchKernelGGL((attn_fwd_f32_mfma_kernel<D, true>), grid, block, 0, s, a));
@@ -525,7 +632,7 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int kb = 32 * kMfmaF32Waves;
+  const int kb = kF32BwdB;
   const dim3 gk((unsigned)((a.n + kb - 1) / kb) * a.hkv * a.b);
   const dim3 gq((unsigned)((a.m + kb - 1) / kb) * a.hq * a.b);
   const dim3 block(64 * kMfmaF32Waves);
