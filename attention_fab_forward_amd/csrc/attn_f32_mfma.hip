@@ -141,30 +141,60 @@ __device__ __forceinline__ void store_row_tile(float* row, const f32x16& v, int 
 // against this lane's register operand x (4 values per group), in two
 // interleaved accumulators so consecutive products do not depend on each
 // other.
-template <int D>
+// With AHEAD > 0 the tile reads run AHEAD groups ahead of the products that
+// take them (one wave per SIMD at d = 128 leaves no other wave to cover LDS
+// latency); AHEAD = 0 leaves the order to the compiler, for the kernel whose
+// live registers leave no room for the read-ahead buffers (dK/dV).
+template <int D, int AHEAD>
 __device__ __forceinline__ f32x16 row_product(const char* tile, int lq, int h,
                                               const f32x4 (&x)[F32T<D>::G]) {
   f32x16 acc[2] = {};
+  if constexpr (AHEAD > 0) {
+    lds_mfma_pipeline<F32T<D>::G, AHEAD>(
+        [&](int g) { return __builtin_bit_cast(u32x4, tile_row4<D>(tile, lq, 2 * g + h)); },
+        [&](int g, const u32x4& yv) {
+          const f32x4 y = __builtin_bit_cast(f32x4, yv);
 #pragma unroll
-  for (int g = 0; g < F32T<D>::G; ++g) {
-    const f32x4 y = tile_row4<D>(tile, lq, 2 * g + h);
+          for (int e = 0; e < 4; ++e) acc[e & 1] = mfma32f(y[e], x[g][e], acc[e & 1]);
+        });
+  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e & 1] = mfma32f(y[e], x[g][e], acc[e & 1]);
+    for (int g = 0; g < F32T<D>::G; ++g) {
+      const f32x4 y = tile_row4<D>(tile, lq, 2 * g + h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e & 1] = mfma32f(y[e], x[g][e], acc[e & 1]);
+    }
   }
   return acc[0] + acc[1];
 }
 
 // out^T += tile^T S^T over the tile's 32 rows: product j takes tile row
 // 8 (j / 4) + 4 h + j % 4 (the row of slot j) and column 32 t + lq.
-template <int D>
+template <int D, int AHEAD>
 __device__ __forceinline__ void col_product(const char* tile, int lq, int h, const float (&s)[16],
                                             f32x16 (&out)[F32T<D>::DT]) {
+  constexpr int DT = F32T<D>::DT;
+  static_assert(DT <= 4, "one read group holds a row's DT values");
+  if constexpr (AHEAD > 0) {
+    lds_mfma_pipeline<16, AHEAD>(
+        [&](int j) {
+          const int r = 8 * (j >> 2) + 4 * h + (j & 3);
+          u32x4 v = {0, 0, 0, 0};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 8 * (j >> 2) + 4 * h + (j & 3);
+          for (int t = 0; t < DT; ++t) v[t] = __float_as_uint(tile_at<D>(tile, r, 32 * t + lq));
+          return v;
+        },
+        [&](int j, const u32x4& v) {
 #pragma unroll
-    for (int t = 0; t < F32T<D>::DT; ++t)
-      out[t] = mfma32f(tile_at<D>(tile, r, 32 * t + lq), s[j], out[t]);
+          for (int t = 0; t < DT; ++t) out[t] = mfma32f(__uint_as_float(v[t]), s[j], out[t]);
+        });
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 8 * (j >> 2) + 4 * h + (j & 3);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) out[t] = mfma32f(tile_at<D>(tile, r, 32 * t + lq), s[j], out[t]);
+    }
   }
 }
 
@@ -242,7 +272,7 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
     if (kb + 1 < kb_end) copy(kb + 1, it + 1);
     if (kb < kb_end && kb < nkw) {
       // slot r: key kb BN + 8 (r / 4) + 4 h + r % 4 of query myq
-      const f32x16 sacc = row_product<D>(ktile(it), lq, h, qf);
+      const f32x16 sacc = row_product<D, 4>(ktile(it), lq, h, qf);
       float s[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = sacc[r];
@@ -277,7 +307,7 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
       }
-      col_product<D>(vtile(it), lq, h, s, o);
+      col_product<D, 4>(vtile(it), lq, h, s, o);
     }
     wait_vmem();
     lds_barrier();
@@ -383,6 +413,7 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kern
   using L = F32DkdvLds<D>;
   constexpr int KB = kF32BwdB, QB = 32;
   static_assert(kMfmaF32Waves == 4 && KB == 64, "two key tiles x two step halves");
+  constexpr int kDkdvAhead = D == 128 ? 0 : 4;  // at d = 128 the read-ahead buffers would spill
   __shared__ __attribute__((aligned(1024))) char smem[4 * L::STAGE];
 
   const int tid = threadIdx.x;
@@ -452,7 +483,7 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kern
     const char* st = hs + (it & 1) * L::STAGE;
     if (step < st_end && live && (!CAUSAL || q0 + QB - 1 + a.diag >= k0w)) {
       // slot r: query q0 + 8 (r / 4) + 4 h + r % 4 of key mykey
-      const f32x16 sacc = row_product<D>(st + L::Q, lq, h, kf);
+      const f32x16 sacc = row_product<D, kDkdvAhead>(st + L::Q, lq, h, kf);
       float lse2[16], ndl[16], p[16];
       slot_consts(reinterpret_cast<const float*>(st + L::LSE), h, lse2);
       slot_consts(reinterpret_cast<const float*>(st + L::DLT), h, ndl);
@@ -465,12 +496,12 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, 1) void attn_dkdv_f32_mfma_kern
           if ((CAUSAL && q + a.diag < mykey) || q >= a.m) p[r] = 0.f;
         }
       }
-      col_product<D>(st + L::DO, lq, h, p, dv);  // dV^T += dO^T P
-      const f32x16 dpacc = row_product<D>(st + L::DO, lq, h, vf);
+      col_product<D, kDkdvAhead>(st + L::DO, lq, h, p, dv);  // dV^T += dO^T P
+      const f32x16 dpacc = row_product<D, kDkdvAhead>(st + L::DO, lq, h, vf);
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) ds[r] = p[r] * (dpacc[r] + ndl[r]);
-      col_product<D>(st + L::Q, lq, h, ds, dk);  // dK^T += Q^T dS
+      col_product<D, kDkdvAhead>(st + L::Q, lq, h, ds, dk);  // dK^T += Q^T dS
     }
     wait_vmem();
     lds_barrier();
@@ -515,6 +546,7 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
   using T = F32T<D>;
   constexpr int BM = kF32BwdB, BN = 32;
   static_assert(kMfmaF32Waves == 4 && BM == 64, "two query tiles x two key halves");
+  constexpr int kDqAhead = D == 128 ? 4 : 2;  // two waves per SIMD at d = 64: 256 registers
   __shared__ __attribute__((aligned(1024))) char smem[8 * T::BYTES];
 
   const int tid = threadIdx.x;
@@ -573,8 +605,8 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
     const int key0 = kb * BN;
     if (kb < kb_end && q0 < a.m && (!CAUSAL || key0 <= q0 + 31 + a.diag)) {
       // slot r: key key0 + 8 (r / 4) + 4 h + r % 4 of query myq
-      const f32x16 sacc = row_product<D>(ktile(it), lq, h, qf);
-      const f32x16 dpacc = row_product<D>(vtile(it), lq, h, df);
+      const f32x16 sacc = row_product<D, kDqAhead>(ktile(it), lq, h, qf);
+      const f32x16 dpacc = row_product<D, kDqAhead>(vtile(it), lq, h, df);
       const bool need_mask = (CAUSAL && key0 + BN - 1 > q0 + a.diag) || key0 + BN > a.n;
       float ds[16];
 #pragma unroll
@@ -586,7 +618,7 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
         }
         ds[r] = p * (dpacc[r] + ndl);
       }
-      col_product<D>(ktile(it), lq, h, ds, dq);  // dQ^T += K^T dS^T
+      col_product<D, kDqAhead>(ktile(it), lq, h, ds, dq);  // dQ^T += K^T dS^T
     }
     wait_vmem();
     lds_barrier();
