@@ -379,15 +379,16 @@ fab_status fab_plan(const fab_problem* prob, fab_plan_t** plan_out, size_t* fwd_
                     "elements", (long long)*sr);
     tmp.fwd_ws = 0;
     // fp32: the matrix-core kernels (or when asked) once the problem has at
-    // least 64 blocks of 128 queries and 2^22 unmasked (query, key) pairs;
-    // below that their few workgroups leave most of the chip idle and the
-    // plain-FMA kernels, with 4-16 rows per workgroup, finish first
+    // least 32 blocks of 64 queries at d = 128 (64 at d = 64, where the
+    // plain-FMA kernels are cheaper per pair) and 2^22 unmasked (query, key)
+    // pairs; below that their few workgroups leave most of the chip idle and
+    // the plain-FMA kernels, with 4-16 rows per workgroup, finish first
     const double pairs = (double)q.batch * q.heads_a * q.m * q.n *
                          (q.mask == FAB_MASK_CAUSAL ? 0.5 : 1.0);
-    const int64_t qblocks = q.batch * q.heads_a * ((q.m + 127) / 128);
+    const int64_t qblocks = q.batch * q.heads_a * ((q.m + 63) / 64);
     tmp.f32_mfma = q.dtype == FAB_F32 &&
                    (q.variant == FAB_VARIANT_F32_MFMA ||
-                    (q.variant == FAB_VARIANT_AUTO && qblocks >= 64 &&
+                    (q.variant == FAB_VARIANT_AUTO && qblocks >= (q.k == 128 ? 32 : 64) &&
                      pairs >= (double)((int64_t)1 << 22)));
     // bf16 and fp32 matrix-core backward: -D and LSE * log2(e) per query row;
     // the plain-FMA fp32 backward forms D inside its kernel (no workspace)

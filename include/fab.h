@@ -78,8 +78,9 @@ typedef enum { FAB_BF16 = 0, FAB_F32 = 1 } fab_dtype;
  * FAB_VARIANT_F32_FMA, plain fp32 FMA kernels (for small problems, where
  * launch latency dominates); FAB_VARIANT_F32_MFMA, the fp32 matrix cores
  * (v_mfma_f32_32x32x2_f32).  Both compute in fp32 throughout; 0 chooses by
- * size (the matrix cores once batch * heads_a * ceil(m / 128) >= 64 and
- * there are 2^22 or more unmasked (query, key) pairs). */
+ * size (the matrix cores once batch * heads_a * ceil(m / 64) >= 32 at
+ * k = 128, or >= 64 at k = 64, and there are 2^22 or more unmasked (query,
+ * key) pairs). */
 typedef enum { FAB_VARIANT_AUTO = 0, FAB_VARIANT_F32_FMA = 1, FAB_VARIANT_F32_MFMA = 2 } fab_variant;
 
 /* Full description of one problem.  Zero-initialise, then fill in. */

@@ -130,15 +130,18 @@ def test_plan_workspace_and_describe():
     assert "fp32 MFMA" in forced.describe() and forced.bwd_workspace >= 4 * 256 * 8
 
 
-@pytest.mark.parametrize("m,heads,causal,mfma", [
-    (256, 1, False, False),          # the small fp32 workload: plain FMA
-    (1024, 8, False, True),          # 64 query blocks, 2^23 pairs: matrix cores
-    (2048, 1, False, False),         # 2^22 pairs but only 16 query blocks
-    (8192, 1, True, True),           # 64 query blocks, 2^25 causal pairs
-    (512, 16, True, False),          # 64 query blocks, 2^21 causal pairs
+@pytest.mark.parametrize("m,heads,d,causal,mfma", [
+    (256, 1, 128, False, False),     # 4 blocks of 64 queries: plain FMA
+    (1024, 1, 128, False, False),    # 16 blocks of 64 queries
+    (2048, 1, 128, False, True),     # 32 blocks at d = 128, 2^22 pairs: matrix cores
+    (1024, 8, 128, False, True),     # 128 blocks, 2^23 pairs
+    (8192, 1, 128, True, True),      # 128 blocks, 2^25 causal pairs
+    (512, 16, 128, True, False),     # 128 blocks but 2^21 causal pairs
+    (2048, 1, 64, False, False),     # 32 blocks: d = 64 needs 64
+    (4096, 1, 64, False, True),      # 64 blocks at d = 64, 2^24 pairs
 ])
-def test_fp32_kernel_family_by_size(m, heads, causal, mfma):
-    p = B.Plan(attn(dtype=B.F32, heads_a=heads, heads_bc=heads, m=m, n=m, causal=causal))
+def test_fp32_kernel_family_by_size(m, heads, d, causal, mfma):
+    p = B.Plan(attn(dtype=B.F32, heads_a=heads, heads_bc=heads, m=m, n=m, k=d, p=d, causal=causal))
     assert ("fp32 MFMA" in p.describe()) == mfma, p.describe()
 
 

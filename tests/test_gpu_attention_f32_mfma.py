@@ -86,8 +86,9 @@ def test_strided_views(d):
                                                (4096, 2, 1, 64, False),
                                                (8192, 1, 1, 128, True)])
 def test_large_chosen_by_size(n, hq, hkv, d, causal):
-    """Sizes the library runs on the matrix cores by itself (64 blocks of
-    128 queries and 2^22 unmasked pairs), every element against the oracle."""
+    """Sizes the library runs on the matrix cores by itself (32 blocks of 64
+    queries at d = 128, 64 at d = 64, and 2^22 unmasked pairs), every element
+    against the oracle."""
     run_check(inputs(3500 + n + d, 1, n, n, hq, hkv, d), causal, float(np.float32(d ** -0.5)),
               variant=B.VARIANT_AUTO)
 
