@@ -23,9 +23,10 @@
 //    with the transposing ds_read_b64_tr_b16, the source lanes addressing the
 //    d columns in perm_row order so every lane owns 16 consecutive outputs.
 //  * K and V tiles are copied global -> LDS asynchronously
-//    (global_load_lds_dwordx4, no register staging) into two stages; each LDS
-//    row is 16-byte-chunk XOR-swizzled so the MFMA operand reads are free of
-//    bank conflicts, the swizzle being applied on the global address side.
+//    (global_load_lds_dwordx4, no register staging) into two stages, by the
+//    wave group whose first phase is the softmax; each LDS row is
+//    16-byte-chunk XOR-swizzled so the MFMA operand reads are free of bank
+//    conflicts, the swizzle being applied on the global address side.
 //  * The running maximum is only moved when a block's maximum exceeds it by
 //    more than 2^8 (probabilities then stay below 256, well inside bf16), so
 //    the accumulator rescale is rare.
@@ -48,8 +49,6 @@ struct FwdCfg {
   static constexpr int TILE = BN * RB;      // bytes of one K or V tile
   static constexpr int STAGE = 2 * TILE;
   static constexpr int RPI = 1024 / RB;     // rows per 1 KiB async copy
-  static constexpr int CPW = TILE / 1024 / NW;  // async copies per wave per tile
-  static_assert(CPW * NW * 1024 == TILE, "tile copies must split evenly over the waves");
   static constexpr int DT = D / 32;         // 32-wide output tiles
   static constexpr int DC = D / 16;         // 16-deep contraction chunks
 };
@@ -62,32 +61,35 @@ __device__ __forceinline__ int v_swz(int r, int c) {
   return c ^ ((4 * (r & 3)) & (FwdCfg<D>::CPR - 1));
 }
 
-// Async copies of one key block of K and V into an LDS stage.  Wave w fills
-// 1 KiB blocks [w * CPW, (w+1) * CPW) of each tile; lane j of copy i writes
+// Async copies of one key block of K and V into an LDS stage, by NWC copying
+// waves.  Copying wave w fills 1 KiB blocks [w * CPW, (w+1) * CPW) of each
+// tile; lane j of copy i writes
 // LDS row r = (w * CPW + i) * RPI + j / CPR, physical chunk j % CPR.  The
 // per-lane element offsets inside a block are fixed for the whole kernel, so
 // they are computed once; each step only advances the wave-uniform base.
-template <int D>
+template <int D, int NWC>
 struct TileOffsets {
-  uint32_t k[FwdCfg<D>::CPW], v[FwdCfg<D>::CPW];  // byte offsets within a block
+  static constexpr int CPW = FwdCfg<D>::TILE / 1024 / NWC;  // copies per copying wave per tile
+  static_assert(CPW * NWC * 1024 == FwdCfg<D>::TILE, "tile copies must split evenly");
+  uint32_t k[CPW], v[CPW];  // byte offsets within a block
 };
 
-// LDS row written by lane `lane` of wave `wave` in copy i; K holds tile key
-// perm_row(r) there, V tile key r.
-template <int D>
+// LDS row written by lane `lane` of copying wave `wave` in copy i; K holds
+// tile key perm_row(r) there, V tile key r.
+template <int D, int NWC>
 __device__ __forceinline__ int copy_row(int wave, int lane, int i) {
   using C = FwdCfg<D>;
-  return (wave * C::CPW + i) * C::RPI + lane / C::CPR;
+  return (wave * TileOffsets<D, NWC>::CPW + i) * C::RPI + lane / C::CPR;
 }
 
-template <int D>
-__device__ __forceinline__ TileOffsets<D> tile_offsets(int64_t k_sr, int64_t v_sr, int wave,
-                                                       int lane) {
+template <int D, int NWC>
+__device__ __forceinline__ TileOffsets<D, NWC> tile_offsets(int64_t k_sr, int64_t v_sr, int wave,
+                                                            int lane) {
   using C = FwdCfg<D>;
-  TileOffsets<D> t;
+  TileOffsets<D, NWC> t;
 #pragma unroll
-  for (int i = 0; i < C::CPW; ++i) {
-    const int r = copy_row<D>(wave, lane, i);
+  for (int i = 0; i < TileOffsets<D, NWC>::CPW; ++i) {
+    const int r = copy_row<D, NWC>(wave, lane, i);
     const int pc = lane % C::CPR;
     const int kr = perm_row(r & 31) + (r & ~31);
     t.k[i] = (uint32_t)(2 * (kr * k_sr + 8 * k_swz<D>(r, pc)));
@@ -100,20 +102,21 @@ __device__ __forceinline__ TileOffsets<D> tile_offsets(int64_t k_sr, int64_t v_s
 // (natural order) into an LDS tile.  Rows past n (only in a ragged last block)
 // are clamped to row n - 1: their scores are masked, so their probabilities
 // are zero.
-template <int D, bool IS_K>
-__device__ __forceinline__ void issue_kv(const TileOffsets<D>& t, const uint16_t* base,
+template <int D, bool IS_K, int NWC>
+__device__ __forceinline__ void issue_kv(const TileOffsets<D, NWC>& t, const uint16_t* base,
                                          int64_t sr, int key0, int n, char* tile, int wave,
                                          int lane) {
   using C = FwdCfg<D>;
+  constexpr int CPW = TileOffsets<D, NWC>::CPW;
   const char* src = reinterpret_cast<const char*>(base + (int64_t)key0 * sr);
-  char* dst = tile + wave * C::CPW * 1024;
+  char* dst = tile + wave * CPW * 1024;
   if (key0 + C::BN <= n) {
 #pragma unroll
-    for (int i = 0; i < C::CPW; ++i) dma16(src, IS_K ? t.k[i] : t.v[i], dst + i * 1024);
+    for (int i = 0; i < CPW; ++i) dma16(src, IS_K ? t.k[i] : t.v[i], dst + i * 1024);
   } else {
 #pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
-      const int r = copy_row<D>(wave, lane, i);
+    for (int i = 0; i < CPW; ++i) {
+      const int r = copy_row<D, NWC>(wave, lane, i);
       const int kr = IS_K ? perm_row(r & 31) + (r & ~31) : r;
       const int64_t shift = min(kr, n - 1 - key0) - kr;  // row shift for clamping
       dma16_at(src + (IS_K ? t.k[i] : t.v[i]) + 2 * shift * sr, dst + i * 1024);
@@ -158,12 +161,18 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   const int nkw = q0 >= a.m ? 0
                   : CAUSAL ? (q0 + 31 + a.diag < 0 ? 0 : min(nkb, (q0 + 31 + a.diag) / C::BN + 1))
                            : nkb;
-  const TileOffsets<D> toff = tile_offsets<D>(a.k_sr, a.v_sr, wave, lane);
+  // The second wave group issues every K / V copy: its phase 1 is VALU work
+  // (softmax), which absorbs the time the copies take to go out at the
+  // L2 -> CU rate, while the first group's products start at once.
+  constexpr int NWC = C::NW / 2;
+  const bool copier = wave >= NWC;
+  const int cw = copier ? wave - NWC : 0;
+  const TileOffsets<D, NWC> toff = tile_offsets<D, NWC>(a.k_sr, a.v_sr, cw, lane);
   auto copy_k = [&](int kb) {
-    issue_kv<D, true>(toff, kbase, a.k_sr, kb * C::BN, a.n, kbuf(kb), wave, lane);
+    if (copier) issue_kv<D, true, NWC>(toff, kbase, a.k_sr, kb * C::BN, a.n, kbuf(kb), cw, lane);
   };
   auto copy_v = [&](int kb) {
-    issue_kv<D, false>(toff, vbase, a.v_sr, kb * C::BN, a.n, vbuf(kb), wave, lane);
+    if (copier) issue_kv<D, false, NWC>(toff, vbase, a.v_sr, kb * C::BN, a.n, vbuf(kb), cw, lane);
   };
   copy_k(0);
 
