@@ -23,8 +23,8 @@
 //    with the transposing ds_read_b64_tr_b16, the source lanes addressing the
 //    d columns in perm_row order so every lane owns 16 consecutive outputs.
 //  * K and V tiles are copied global -> LDS asynchronously
-//    (global_load_lds_dwordx4, no register staging) into two stages, by the
-//    wave group whose first phase is the softmax; each LDS row is
+//    (global_load_lds_dwordx4, no register staging) into two stages, each
+//    wave group issuing one tile during its softmax phase; each LDS row is
 //    16-byte-chunk XOR-swizzled so the MFMA operand reads are free of bank
 //    conflicts, the swizzle being applied on the global address side.
 //  * The running maximum is only moved when a block's maximum exceeds it by
@@ -161,20 +161,20 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   const int nkw = q0 >= a.m ? 0
                   : CAUSAL ? (q0 + 31 + a.diag < 0 ? 0 : min(nkb, (q0 + 31 + a.diag) / C::BN + 1))
                            : nkb;
-  // The second wave group issues every K / V copy: its phase 1 is VALU work
-  // (softmax), which absorbs the time the copies take to go out at the
-  // L2 -> CU rate, while the first group's products start at once.
+  // Copies go out at the L2 -> CU rate and hold up the wave that issues
+  // them, so each wave group issues one tile in its softmax phase: the second
+  // group K (at the start of an iteration), the first group V (after the
+  // first barrier); the group running its products issues none.
   constexpr int NWC = C::NW / 2;
-  const bool copier = wave >= NWC;
-  const int cw = copier ? wave - NWC : 0;
+  const int cw = wave % NWC;
   const TileOffsets<D, NWC> toff = tile_offsets<D, NWC>(a.k_sr, a.v_sr, cw, lane);
   auto copy_k = [&](int kb) {
-    if (copier) issue_kv<D, true, NWC>(toff, kbase, a.k_sr, kb * C::BN, a.n, kbuf(kb), cw, lane);
+    issue_kv<D, true, NWC>(toff, kbase, a.k_sr, kb * C::BN, a.n, kbuf(kb), cw, lane);
   };
   auto copy_v = [&](int kb) {
-    if (copier) issue_kv<D, false, NWC>(toff, vbase, a.v_sr, kb * C::BN, a.n, vbuf(kb), cw, lane);
+    issue_kv<D, false, NWC>(toff, vbase, a.v_sr, kb * C::BN, a.n, vbuf(kb), cw, lane);
   };
-  copy_k(0);
+  if (wave >= NWC) copy_k(0);
 
   // Q^T fragments: lane holds Q[myq][16c + 8lg .. +7] for every chunk c.
   u32x4 qf[C::DC];
@@ -291,11 +291,8 @@ attn_fwd_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
   // copies issued in iteration j: K[j + 1] and V[j] (their buffers held
-  // K[j - 1] and V[j - 2], read by both groups before the previous barrier)
-  auto copy_step = [&](int j) {
-    if (j + 1 < nkb) copy_k(j + 1);
-    if (j < nkb) copy_v(j);
-  };
+  // K[j - 1] and V[j - 2], read by both groups before the previous barrier);
+  // V[j] is first read in iteration j + 1
 
   wait_vmem();
   lds_barrier();
@@ -309,17 +306,17 @@ attn_fwd_bf16_kernel(AttnArgs a) {
   if (wave < 4) {
     int j = 0;
     for (; j <= nkb; ++j) {
-      copy_step(j);
       if (j < nkw) compute_s(s, kbuf(j));
       if (j >= 1 && j <= nkw) pv(j - 1);
       lds_barrier();
+      if (j < nkb) copy_v(j);
       if (j < nkw) softmax(j);
       wait_vmem();
       lds_barrier();
     }
   } else {
     for (int j = 0; j <= nkb; ++j) {
-      copy_step(j);
+      if (j + 1 < nkb) copy_k(j + 1);
       if (j >= 1 && j <= nkw) softmax(j - 1);
       lds_barrier();
       if (j < nkw) compute_s(s, kbuf(j));
