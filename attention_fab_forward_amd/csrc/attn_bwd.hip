@@ -187,9 +187,10 @@ template <int D, bool CAUSAL, bool SAME>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using L = DkdvLds<D>;
-  // An LDS write waits while global -> LDS copies of its wave are in flight,
-  // so the dS waves (which write no LDS in the step loop) issue every tile
-  // copy and the P waves' P writes do not wait on copies of their own.
+  // Copies go out at the L2 -> CU rate and hold up the wave that issues them,
+  // and an LDS write waits while copies are going out; so the dS waves, which
+  // write no LDS in the step loop, issue every tile copy, and the P waves go
+  // straight to their S products and P writes.
   constexpr int CW = kDkdvWaves / 2;
   using TO = TileOffsets<D, CW>;
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
