@@ -10,8 +10,8 @@
 //  * attn_dkdv_bf16_kernel: one workgroup per 128 keys of one kv head, in four
 //    32-key groups each served by a pair of waves with split roles (P / dV and
 //    dP / dS / dK).  K and V stay in registers; query blocks of 64 (and all
-//    query heads of the group) stream through a double-buffered LDS.  dK^T and
-//    dV^T accumulate in registers.
+//    query heads of the group) stream through a three-stage LDS ring, copied
+//    two steps ahead.  dK^T and dV^T accumulate in registers.
 //  * attn_dq_bf16_kernel: one workgroup per 32 x NW queries (NW waves, 8 by
 //    default) of one query head.  Q, dO, LSE and D stay in registers; key
 //    blocks of 64 stream through LDS (K and V natural, K read transposed).
@@ -148,9 +148,10 @@ __device__ __forceinline__ void issue_vec64(const float* src, int i0, int count,
 //    through LDS; dV^T += dO^T P.
 //  * dS wave (waves 4-7): holds V; dP - D = dO V^T - D; dS = P (dP - D) with
 //    the bf16 P; dK^T += Q^T dS.
-// Query blocks of 64 (all query heads of the group) stream through two LDS
-// stages, copied by the dS waves; each step has two barriers: P written -> P
-// read, and end of step (stage and P buffer released).
+// Query blocks of 64 (all query heads of the group) stream through three LDS
+// stages, copied two steps ahead (Q by the P waves, dO and the row constants by
+// the dS waves); each step has two barriers: P written -> P read, and end of
+// step (stage and P buffer released).
 // ---------------------------------------------------------------------------
 constexpr int kDkdvWaves = 8;
 
@@ -161,19 +162,27 @@ struct DkdvLds {
   static constexpr int LSE = 2 * BwdCfg<D>::TBYTES;    // LSE * log2(e), 64 floats
   static constexpr int DLT = LSE + 256;                // -D, 64 floats
   static constexpr int STAGE = DLT + 256;
-  static constexpr int PX = 2 * STAGE;                 // P exchange: [group][sq][c][lane] 8 x bf16
+  static constexpr int STAGES = 3;                     // steps s, s + 1, s + 2 in flight
+  static constexpr int PX = STAGES * STAGE;            // P exchange: [group][sq][c][lane] 8 x bf16
   static constexpr int PX_GROUP = 2 * 2 * 64 * 16;     // 4 KiB per 32-key group
   static constexpr int BYTES = PX + 4 * PX_GROUP;
 };
 
+// The Q tile of one step (copied by the P waves, NW of them) ...
 template <int D, int NW>
-__device__ __forceinline__ void dkdv_issue(const AttnArgs& a, const TileOffsets<D, NW>& tq,
-                                           const TileOffsets<D, NW>& to, int bi, int h,
-                                           int q0, char* st, int wave, int lane) {
+__device__ __forceinline__ void dkdv_issue_q(const AttnArgs& a, const TileOffsets<D, NW>& tq,
+                                             int bi, int h, int q0, char* st, int wave, int lane) {
   using L = DkdvLds<D>;
   const uint16_t* qb = static_cast<const uint16_t*>(a.q) + bi * a.q_sb + h * a.q_sh;
-  const uint16_t* ob = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
   issue_tile<D, NW>(tq, qb, a.q_sr, q0, a.m, st + L::Q, wave, lane);
+}
+// ... and its dO tile, LSE log2(e) and -D rows (by the dS waves: copying waves
+// 0 and 1 issue one vector copy more than the others).
+template <int D, int NW>
+__device__ __forceinline__ void dkdv_issue_o(const AttnArgs& a, const TileOffsets<D, NW>& to,
+                                             int bi, int h, int q0, char* st, int wave, int lane) {
+  using L = DkdvLds<D>;
+  const uint16_t* ob = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
   issue_tile<D, NW>(to, ob, a.o_sr, q0, a.m, st + L::DO, wave, lane);
   const int64_t r = ((int64_t)bi * a.hq + h) * a.m;
   if (wave == 0) issue_vec64(a.lse2 + r, q0, a.m, st + L::LSE, lane);
@@ -188,11 +197,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using L = DkdvLds<D>;
   // Copies go out at the L2 -> CU rate and hold up the wave that issues them,
-  // and an LDS write waits while copies are going out; so the dS waves, which
-  // write no LDS in the step loop, issue every tile copy, and the P waves go
-  // straight to their S products and P writes.
+  // and an LDS write waits while copies are going out.  Three stages hold
+  // steps s, s + 1 and s + 2: the P waves copy the Q tile of step s + 2 after
+  // their dV products (in the slack before the second barrier, their P writes
+  // long done), the dS waves copy its dO tile and row constants at the start
+  // of step s; each wave then waits only for its copies of step s + 1.
   constexpr int CW = kDkdvWaves / 2;
   using TO = TileOffsets<D, CW>;
+  constexpr int kCopiesP = TO::CPW;  // Q tile copies per P wave and step
   __shared__ __attribute__((aligned(1024))) char smem[L::BYTES];
 
   const int tid = threadIdx.x;
@@ -220,10 +232,16 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   const int steps_per_head = max(0, nqb - qb_first);
   const int steps = steps_per_head * a.group;
   const bool group_live = k0w < a.n;
-  const int cw = p_role ? 0 : wave - CW;  // copy index of a dS wave
-  const TO tq = tile_offsets<D, CW>(a.q_sr, cw, lane);
-  const TO to = SAME ? tq : tile_offsets<D, CW>(a.o_sr, cw, lane);
-  if (steps > 0 && !p_role) dkdv_issue<D, CW>(a, tq, to, bi, g * a.group, qb_first * C::TILE, smem, cw, lane);
+  const int cw = wave % CW;  // copy index within the role
+  const TO tofs = tile_offsets<D, CW>(p_role ? a.q_sr : a.o_sr, cw, lane);
+  // steps 0 and 1 up front
+  auto issue_step = [&](int hh, int qq, int stage) {
+    char* st = smem + stage * L::STAGE;
+    if (p_role) dkdv_issue_q<D, CW>(a, tofs, bi, g * a.group + hh, (qb_first + qq) * C::TILE, st, cw, lane);
+    else dkdv_issue_o<D, CW>(a, tofs, bi, g * a.group + hh, (qb_first + qq) * C::TILE, st, cw, lane);
+  };
+  if (steps > 0) issue_step(0, 0, 0);
+  if (steps > 1) issue_step(steps_per_head > 1 ? 0 : 1, steps_per_head > 1 ? 1 : 0, 1);
 
   // this wave's operand: K (P wave) or V (dS wave) rows of its 32 keys
   u32x4 kv[C::DC];
@@ -248,27 +266,23 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   // step), so each loop keeps only its own role's invariants in registers.
   // Step s covers query block qb_first + s % steps_per_head of query head
   // g * group + s / steps_per_head; the loops advance (head, block) counters
-  // instead of dividing.  prefetch copies the tiles of the step after (nh, nq).
-  auto prefetch = [&](int step, int nh, int nq) {
-    if (step + 1 < steps && !p_role)
-      dkdv_issue<D, CW>(a, tq, to, bi, g * a.group + nh, (qb_first + nq) * C::TILE,
-                        smem + ((step + 1) & 1) * L::STAGE, cw, lane);
-  };
+  // instead of dividing, for this step and for step s + 2.
   auto advance = [&](int& hh, int& qq) {
     if (++qq == steps_per_head) {
       qq = 0;
       ++hh;
     }
   };
+  int h2 = 0, q2 = 0;  // (head, block) of step + 2
+  advance(h2, q2);
+  advance(h2, q2);
   if (p_role) {
     int hc = 0, qc = 0;  // (head, block) of this step
+    int sc = 0;          // stage of this step
     for (int step = 0; step < steps; ++step) {
-      int hn = hc, qn = qc;
-      advance(hn, qn);
-      prefetch(step, hn, qn);
       const int q0 = (qb_first + qc) * C::TILE;
-      hc = hn, qc = qn;
-      const char* st = smem + (step & 1) * L::STAGE;
+      const char* st = smem + sc * L::STAGE;
+      const int s2 = sc == 0 ? 2 : sc - 1;  // stage of step + 2
       // A key group skips a query block when every query precedes all its keys.
       const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 + a.diag >= k0w);
       u32x4 pb[2][2];
@@ -337,18 +351,25 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
               acc[(i / 2) % C::DT] = mfma32(x, pb[i / (2 * C::DT)][i % 2], acc[(i / 2) % C::DT]);
             });
       }
-      wait_vmem();
+      if (step + 2 < steps) {
+        issue_step(h2, q2, s2);
+        wait_copies<kCopiesP>();  // step + 1's Q tile; step + 2's stays in flight
+      } else {
+        wait_copies<0>();
+      }
       lds_barrier();
+      advance(hc, qc);
+      advance(h2, q2);
+      sc = sc == 2 ? 0 : sc + 1;
     }
   } else {
     int hc = 0, qc = 0;  // (head, block) of this step
+    int sc = 0;          // stage of this step
     for (int step = 0; step < steps; ++step) {
-      int hn = hc, qn = qc;
-      advance(hn, qn);
-      prefetch(step, hn, qn);
       const int q0 = (qb_first + qc) * C::TILE;
-      hc = hn, qc = qn;
-      const char* st = smem + (step & 1) * L::STAGE;
+      const char* st = smem + sc * L::STAGE;
+      const bool pf = step + 2 < steps;
+      if (pf) issue_step(h2, q2, sc == 0 ? 2 : sc - 1);
       const bool work = group_live && (!CAUSAL || q0 + C::TILE - 1 + a.diag >= k0w);
       f32x16 dp[2];
       if (work) {
@@ -390,8 +411,14 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
           __builtin_amdgcn_s_setprio(0);
         }
       }
-      wait_vmem();
+      // step + 1's dO tile and row constants; step + 2's stay in flight
+      if (!pf) wait_copies<0>();
+      else if (cw < 2) wait_copies<kCopiesP + 1>();
+      else wait_copies<kCopiesP>();
       lds_barrier();
+      advance(hc, qc);
+      advance(h2, q2);
+      sc = sc == 2 ? 0 : sc + 1;
     }
   }
 

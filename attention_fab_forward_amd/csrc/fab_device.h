@@ -156,6 +156,16 @@ __device__ __forceinline__ void lds_barrier() {
 // (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
+// Waits until at most N of this wave's vector memory operations are
+// outstanding; they complete in issue order, so this waits for all but the
+// last N issued (a copy pipeline keeps its newest tiles in flight).  Assembly
+// with a memory clobber, so LDS accesses stay on their side of it.
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Combine each lane's value with that of lane l ^ 32 (v_permlane32_swap:
 // afterwards one register holds x[l % 32], the other x[l % 32 + 32] in every
 // lane).

@@ -214,14 +214,8 @@ __device__ __forceinline__ void stash_tile(float* red, int wave, int lane, const
 // byte pieces it copied, so only a wave-local wait is needed).  The copies are
 // issued right before the next tile's row loads, and vector memory operations
 // complete in issue order, so waiting until only those N loads remain
-// outstanding waits for exactly the copies.  These waits are assembly with a
-// memory clobber so LDS accesses stay on their side.
-// Waits for the copies while the N loads issued after them stay in flight.
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+// outstanding (wait_copies<N>) waits for exactly the copies.
+
 __device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Waits until at most N LDS (and scalar memory) operations are outstanding.
 template <int N>
