@@ -455,11 +455,14 @@ struct DqStage {
 // the S / dP tiles holds key key0 + 32 sb + 16 (l / 32) + r for query myq[qt].
 // need_mask (wave-uniform; diagonal or ragged blocks): masked scores are set
 // to -inf in one uniform branch, so full blocks pay nothing for masking.
-template <int D, bool CAUSAL, int QT>
+// ndt[qt]: -D of query myq[qt] in all 16 slots.  NDT: the dP products start
+// from that tile, so dP - D comes out of the MFMAs (one add per element
+// fewer); otherwise only its first slot is read and -D is added afterwards.
+template <int D, bool CAUSAL, int QT, bool NDT>
 __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][BwdCfg<D>::DC],
                                          const u32x4 (&df)[QT][BwdCfg<D>::DC],
                                          f32x16 (&dq)[QT][BwdCfg<D>::DT], const int (&myq)[QT],
-                                         const float (&lse2)[QT], const float (&ndl)[QT],
+                                         const float (&lse2)[QT], const f32x16 (&ndt)[QT],
                                          bool need_mask, int key0, int n, int diag, float cs, int lq,
                                          int lg, int tr_d, int tr_row) {
   using C = BwdCfg<D>;
@@ -468,9 +471,16 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
   for (int sb = 0; sb < 2; ++sb) {
     f32x16 s[QT], dp[QT];
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
+    for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[qt][r] = dp[qt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) s[qt][r] = 0.f;
+      if constexpr (NDT) {
+        dp[qt] = ndt[qt];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[qt][r] = 0.f;
+      }
+    }
     // operand i: d chunk c = i / 2 of K (i even, for S) or V (i odd, for dP)
     auto kv_read = [&](int i) { return read_nat<D>(st + (i % 2 ? S::V : S::K), sb, i / 2, lq, lg); };
     if constexpr (QT == 1) {
@@ -505,7 +515,7 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(s[qt][r], cs, -lse2[qt]));
-        ds[r] = p * (dp[qt][r] + ndl[qt]);
+        ds[r] = NDT ? p * dp[qt][r] : p * (dp[qt][r] + ndt[qt][0]);
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -573,7 +583,8 @@ attn_dq_bf16_kernel(AttnArgs a) {
   const uint16_t* obase = static_cast<const uint16_t*>(a.dout) + bi * a.o_sb + h * a.o_sh;
   int myq[QT];
   u32x4 qf[QT][C::DC], df[QT][C::DC];
-  float lse2[QT], ndl[QT];  // LSE * log2(e) and -D of the lane's query
+  float lse2[QT];   // LSE * log2(e) of the lane's query
+  f32x16 ndt[QT];  // its -D, in every slot
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     myq[qt] = q0 + 32 * qt + lq;
@@ -587,7 +598,9 @@ attn_dq_bf16_kernel(AttnArgs a) {
     }
     const int64_t ridx = ((int64_t)bi * a.hq + h) * a.m + myq[qt];
     lse2[qt] = live ? a.lse2[ridx] : INFINITY;
-    ndl[qt] = live ? a.delta[ridx] : 0.f;
+    const float ndl = live ? a.delta[ridx] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndt[qt][r] = ndl;
   }
   f32x16 dq[QT][C::DT];
 #pragma unroll
@@ -611,8 +624,9 @@ attn_dq_bf16_kernel(AttnArgs a) {
     const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 32 * QT - 1 + a.diag);
     if (wave_work) {
       const bool need_mask = (CAUSAL && key0 + C::TILE - 1 > q0 + a.diag) || key0 + C::TILE > a.n;
-      dq_block<D, CAUSAL, QT>(st, qf, df, dq, myq, lse2, ndl, need_mask, key0, a.n, a.diag, cs, lq,
-                              lg, tr_d, tr_row);
+      // with one set of copy offsets (SAME) there are registers for the -D tile
+      dq_block<D, CAUSAL, QT, SAME>(st, qf, df, dq, myq, lse2, ndt, need_mask, key0, a.n, a.diag,
+                                    cs, lq, lg, tr_d, tr_row);
     }
     wait_vmem();
     lds_barrier();
