@@ -307,10 +307,10 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
             for (int j = 0; j < 4; ++j)
               lse[sq][j] = reinterpret_cast<const f32x4*>(st + L::LSE)[8 * sq + 4 * lg + j];
           __builtin_amdgcn_s_setprio(2);
-          lds_mfma_pipeline<C::DC, 4>(
+          lds_mfma_pipeline<C::DC, 3>(
               [&](int i) { return read_nat<D>(st + L::Q, 0, i, lq, lg); },
               [&](int i, const u32x4& x) { s[0] = mfma32(x, kv[i], s[0]); });
-          lds_mfma_pipeline<C::DC, 4>(
+          lds_mfma_pipeline<C::DC, 3>(
               [&](int i) { return read_nat<D>(st + L::Q, 1, i, lq, lg); },
               [&](int i, const u32x4& x) { s[1] = mfma32(x, kv[i], s[1]); });
 #pragma unroll
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
       lds_barrier();  // P visible to the dS waves
       if (work) {
         // operand i: query sub-block i / (2 DT), output tile (i / 2) % DT, chunk i % 2
-        lds_mfma_pipeline<4 * C::DT, 4>(
+        lds_mfma_pipeline<4 * C::DT, 6>(
             [&](int i) {
               return read_tr<D>(st + L::DO, (i / 2) % C::DT, i / (2 * C::DT), i % 2, lg, tr_d, tr_row);
             },
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
           // raised priority while issuing dK, as for dQ (the dS wave has just
           // finished its VALU work; its partner's dV products wait)
           __builtin_amdgcn_s_setprio(2);
-          lds_mfma_pipeline<2 * C::DT, 4>(
+          lds_mfma_pipeline<2 * C::DT, 3>(
               [&](int i) { return read_tr<D>(st + L::Q, i / 2, sq, i % 2, lg, tr_d, tr_row); },
               [&](int i, const u32x4& x) { acc[i / 2] = mfma32(x, db[i % 2], acc[i / 2]); });
           __builtin_amdgcn_s_setprio(0);
@@ -455,10 +455,9 @@ struct DqStage {
 // the S / dP tiles holds key key0 + 32 sb + 16 (l / 32) + r for query myq[qt].
 // need_mask (wave-uniform; diagonal or ragged blocks): masked scores are set
 // to -inf in one uniform branch, so full blocks pay nothing for masking.
-// ndt[qt]: -D of query myq[qt] in all 16 slots.  NDT: the dP products start
-// from that tile, so dP - D comes out of the MFMAs (one add per element
-// fewer); otherwise only its first slot is read and -D is added afterwards.
-template <int D, bool CAUSAL, int QT, bool NDT>
+// ndt[qt]: -D of query myq[qt] in all 16 slots; the dP products start from
+// that tile, so dP - D comes out of the MFMAs (one add per element fewer).
+template <int D, bool CAUSAL, int QT>
 __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][BwdCfg<D>::DC],
                                          const u32x4 (&df)[QT][BwdCfg<D>::DC],
                                          f32x16 (&dq)[QT][BwdCfg<D>::DT], const int (&myq)[QT],
@@ -474,17 +473,12 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
     for (int qt = 0; qt < QT; ++qt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[qt][r] = 0.f;
-      if constexpr (NDT) {
-        dp[qt] = ndt[qt];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dp[qt][r] = 0.f;
-      }
+      dp[qt] = ndt[qt];
     }
     // operand i: d chunk c = i / 2 of K (i even, for S) or V (i odd, for dP)
     auto kv_read = [&](int i) { return read_nat<D>(st + (i % 2 ? S::V : S::K), sb, i / 2, lq, lg); };
     if constexpr (QT == 1) {
-      lds_mfma_pipeline<2 * C::DC, 4>(kv_read, [&](int i, const u32x4& x) {
+      lds_mfma_pipeline<2 * C::DC, 3>(kv_read, [&](int i, const u32x4& x) {
         if (i % 2) dp[0] = mfma32(x, df[0][i / 2], dp[0]);
         else s[0] = mfma32(x, qf[0][i / 2], s[0]);
       });
@@ -515,7 +509,7 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(s[qt][r], cs, -lse2[qt]));
-        ds[r] = NDT ? p * dp[qt][r] : p * (dp[qt][r] + ndt[qt][0]);
+        ds[r] = p * dp[qt][r];
       }
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -529,7 +523,7 @@ __device__ __forceinline__ void dq_block(const char* st, const u32x4 (&qf)[QT][B
       // dS gets the MFMA pipe first, so the two waves of a SIMD drift out of
       // phase and one's dS work overlaps the other's products
       __builtin_amdgcn_s_setprio(2);
-      lds_mfma_pipeline<2 * C::DT, 4>(kt_read, [&](int i, const u32x4& x) {
+      lds_mfma_pipeline<2 * C::DT, 3>(kt_read, [&](int i, const u32x4& x) {
         dq[0][i % C::DT] = mfma32(x, db[0][i / C::DT], dq[0][i % C::DT]);
       });
       __builtin_amdgcn_s_setprio(0);
@@ -624,9 +618,8 @@ attn_dq_bf16_kernel(AttnArgs a) {
     const bool wave_work = wave_live && (!CAUSAL || key0 <= q0 + 32 * QT - 1 + a.diag);
     if (wave_work) {
       const bool need_mask = (CAUSAL && key0 + C::TILE - 1 > q0 + a.diag) || key0 + C::TILE > a.n;
-      // with one set of copy offsets (SAME) there are registers for the -D tile
-      dq_block<D, CAUSAL, QT, SAME>(st, qf, df, dq, myq, lse2, ndt, need_mask, key0, a.n, a.diag,
-                                    cs, lq, lg, tr_d, tr_row);
+      dq_block<D, CAUSAL, QT>(st, qf, df, dq, myq, lse2, ndt, need_mask, key0, a.n, a.diag, cs,
+                              lq, lg, tr_d, tr_row);
     }
     wait_vmem();
     lds_barrier();
