@@ -88,26 +88,41 @@ __device__ __forceinline__ float gelu_grad_f(float x) {
 // The fragments cover cols_pad columns (the kernels' compiled width, a power
 // of two from 128); rows of X at or past `rows` and columns at or past `cols`
 // read as zero.  rows_pad % 64 == 0, cols % 64 == 0, cols <= cols_pad.
-__global__ __launch_bounds__(256) void pack_rows_kernel(const uint16_t* x, int64_t ld, int rows,
-                                                        int cols, int cols_pad, int64_t pieces,
-                                                        uint16_t* out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte piece
+// One pack job: row fragments (cols_kind 0) or column fragments (1) of
+// X [rows][cols], zero-padded to rows_pad x cols_pad, on workgroups
+// [block0, block0 + blocks) of a batched launch.
+struct PackJob {
+  const uint16_t* x;
+  uint16_t* out;
+  int64_t ld, rows_pad;
+  int rows, cols, cols_pad, cols_kind, block0;
+};
+// Up to seven jobs per launch (the backward packs seven operand copies).
+struct PackJobs {
+  PackJob j[7];
+  int n;
+};
+
+// Row fragments, workgroup b: 256 consecutive 16-byte pieces.
+__device__ __forceinline__ void pack_rows_block(const PackJob& J, int b) {
+  const int64_t pieces = J.rows_pad * J.cols_pad / 8;
+  const int64_t i = (int64_t)b * 256 + threadIdx.x;  // one 16-byte piece
   if (i >= pieces) return;
   const int l = (int)(i & 63);
   const int64_t f = i >> 6;
-  const int nj = cols_pad / 16;
+  const int nj = J.cols_pad / 16;
   const int j = (int)(f % nj);
   const int64_t R = f / nj;
   const int64_t row = 32 * R + perm_row(l & 31);
   const int col = 16 * j + 8 * (l >> 5);
-  const u32x4 v = row < rows && col < cols ? ldg16(x + row * ld + col) : u32x4{0, 0, 0, 0};
-  stg16(out + i * 8, v);
+  const u32x4 v = row < J.rows && col < J.cols ? ldg16(J.x + row * J.ld + col) : u32x4{0, 0, 0, 0};
+  stg16(J.out + i * 8, v);
 }
 
-__global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64_t ld, int rows,
-                                                        int cols, int cols_pad, uint16_t* out) {
-  __shared__ uint16_t tile[64][64 + 2];
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+// Column fragments, workgroup b: one 64 x 64 block of X through LDS.
+__device__ __forceinline__ void pack_cols_block(const PackJob& J, int b, uint16_t (*tile)[64 + 2]) {
+  const int gx = (int)(J.rows_pad / 64);
+  const int r0 = (b % gx) * 64, c0 = (b / gx) * 64;
   const int tid = threadIdx.x;
   // load 64 x 64 of X: 512 chunks of 8 elements, 2 per thread
 #pragma unroll
@@ -116,7 +131,7 @@ __global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64
     const int r = i / 8, ch = i % 8;
     const int gr = r0 + r, gc = c0 + ch * 8;
     u32x4 v = {0, 0, 0, 0};
-    if (gr < rows && gc < cols) v = ldg16(x + (int64_t)gr * ld + gc);
+    if (gr < J.rows && gc < J.cols) v = ldg16(J.x + (int64_t)gr * J.ld + gc);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       tile[r][ch * 8 + 2 * w] = (uint16_t)(v[w] & 0xffff);
@@ -125,7 +140,7 @@ __global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64
   }
   __syncthreads();
   // write the 2 (R) x 2 (T) x 2 (c) fragments of this 64 x 64 block
-  const int nr = cols_pad / 32;
+  const int nr = J.cols_pad / 32;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int piece = tid + 256 * u;
@@ -137,21 +152,48 @@ __global__ __launch_bounds__(256) void pack_cols_kernel(const uint16_t* x, int64
     for (int w = 0; w < 4; ++w)
       v[w] = (uint32_t)tile[xr + 2 * w][xc] | ((uint32_t)tile[xr + 2 * w + 1][xc] << 16);
     const int64_t frag = ((int64_t)(r0 / 32 + tl) * nr + (c0 / 32 + rl)) * 2 + c;
-    stg16(out + frag * 512 + l * 8, v);
+    stg16(J.out + frag * 512 + l * 8, v);
   }
 }
 
-// out[r][c] = bf16(scale * sum_s part[s][r][c]); part packed [splits][rows][cols].
-__global__ __launch_bounds__(256) void reduce_parts_kernel(const float* part, int splits, int rows,
-                                                           int cols, float scale, uint16_t* out,
-                                                           int64_t ld_out) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  const int64_t total = (int64_t)rows * cols;
+// Every pack job of a pass in one launch (jobs in block0 order); a
+// workgroup finds its job by a uniform scan of at most seven entries.
+__global__ __launch_bounds__(256) void pack_kernel(PackJobs jobs) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int b = blockIdx.x;
+  int k = 0;
+  while (k + 1 < jobs.n && b >= jobs.j[k + 1].block0) ++k;
+  const PackJob& J = jobs.j[k];
+  if (J.cols_kind) pack_cols_block(J, b - J.block0, tile);
+  else pack_rows_block(J, b - J.block0);
+}
+
+// One reduction job: out[r][c] = bf16(scale * sum_s part[s][r][c]), part
+// packed [splits][rows][cols], on workgroups [block0, block0 + blocks).
+struct ReduceJob {
+  const float* part;
+  uint16_t* out;
+  int64_t ld_out;
+  float scale;
+  int splits, rows, cols, block0;
+};
+struct ReduceJobs {
+  ReduceJob j[3];
+  int n;
+};
+
+__global__ __launch_bounds__(256) void reduce_parts_kernel(ReduceJobs jobs) {
+  const int b = blockIdx.x;
+  int k = 0;
+  while (k + 1 < jobs.n && b >= jobs.j[k + 1].block0) ++k;
+  const ReduceJob& J = jobs.j[k];
+  const int64_t i = ((int64_t)(b - J.block0) * 256 + threadIdx.x) * 8;
+  const int64_t total = (int64_t)J.rows * J.cols;
   if (i >= total) return;
-  const int64_t r = i / cols, c = i % cols;
+  const int64_t r = i / J.cols, c = i % J.cols;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int s = 0; s < splits; ++s) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(part + (int64_t)s * total + i);
+  for (int s = 0; s < J.splits; ++s) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(J.part + (int64_t)s * total + i);
     const f32x4 x = src[0], y = src[1];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -161,8 +203,8 @@ __global__ __launch_bounds__(256) void reduce_parts_kernel(const float* part, in
   }
   u32x4 v;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) v[w] = pack_bf16(acc[2 * w] * scale, acc[2 * w + 1] * scale);
-  stg16(out + r * ld_out + c, v);
+  for (int w = 0; w < 4; ++w) v[w] = pack_bf16(acc[2 * w] * J.scale, acc[2 * w + 1] * J.scale);
+  stg16(J.out + r * J.ld_out + c, v);
 }
 
 // Partial tiles live in LDS as float pairs, slot-pair major: pair q (slots
@@ -671,36 +713,46 @@ MlpLayout layout(int m, int n, int k, int p) {
   return L;
 }
 
-// Row fragments of X [rows][cols], zero-padded to rows_pad x cols_pad.
-hipError_t pack_rows(const void* x, int64_t ld, int rows, int cols, int cols_pad, int64_t rows_pad,
-                     void* out, hipStream_t s) {
-  const int64_t pieces = rows_pad * cols_pad / 8;
-  const dim3 grid((unsigned)((pieces + 255) / 256)), block(256);
-  FAB_TIMED("mlp_pack", s, hipLaunchKernelGGL(pack_rows_kernel, grid, block, 0, s,
-                     static_cast<const uint16_t*>(x), ld, rows, cols, cols_pad, pieces,
-                     static_cast<uint16_t*>(out)));
-  return hipGetLastError();
-}
+// Pack jobs of one pass, launched together by run().
+struct Packer {
+  PackJobs jobs{};
+  int blocks = 0;
+  // Row fragments of X [rows][cols], zero-padded to rows_pad x cols_pad.
+  void rows(const void* x, int64_t ld, int rows, int cols, int cols_pad, int64_t rows_pad, void* out) {
+    add(x, ld, rows, cols, cols_pad, rows_pad, out, 0,
+        (int)((rows_pad * cols_pad / 8 + 255) / 256));
+  }
+  // Column fragments of X [rows][cols] (row fragments of X^T).
+  void cols(const void* x, int64_t ld, int rows, int cols, int cols_pad, int64_t rows_pad, void* out) {
+    add(x, ld, rows, cols, cols_pad, rows_pad, out, 1, (int)(rows_pad / 64) * (cols_pad / 64));
+  }
+  void add(const void* x, int64_t ld, int rows, int cols, int cols_pad, int64_t rows_pad, void* out,
+           int kind, int nblocks) {
+    PackJob& J = jobs.j[jobs.n++];
+    J = {static_cast<const uint16_t*>(x), static_cast<uint16_t*>(out), ld, rows_pad, rows, cols,
+         cols_pad, kind, blocks};
+    blocks += nblocks;
+  }
+  hipError_t run(hipStream_t s) {
+    FAB_TIMED("mlp_pack", s, hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, jobs));
+    return hipGetLastError();
+  }
+};
 
-// Column fragments of X [rows][cols] (row fragments of X^T), zero-padded to
-// rows_pad x cols_pad.
-hipError_t pack_cols(const void* x, int64_t ld, int rows, int cols, int cols_pad, int64_t rows_pad,
-                     void* out, hipStream_t s) {
-  const dim3 grid((unsigned)(rows_pad / 64), (unsigned)(cols_pad / 64)), block(256);
-  FAB_TIMED("mlp_pack", s, hipLaunchKernelGGL(pack_cols_kernel, grid, block, 0, s,
-                     static_cast<const uint16_t*>(x), ld, rows, cols, cols_pad,
-                     static_cast<uint16_t*>(out)));
-  return hipGetLastError();
-}
-
-hipError_t reduce(const float* part, int splits, int rows, int cols, float scale, void* out,
-                  int64_t ld_out, hipStream_t s) {
-  const int64_t total = (int64_t)rows * cols / 8;
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-  FAB_TIMED("mlp_reduce", s, hipLaunchKernelGGL(reduce_parts_kernel, grid, block, 0, s, part, splits, rows, cols, scale,
-                     static_cast<uint16_t*>(out), ld_out));
-  return hipGetLastError();
-}
+// Split-sum reductions of one pass, launched together by run().
+struct Reducer {
+  ReduceJobs jobs{};
+  int blocks = 0;
+  void add(const float* part, int splits, int rows, int cols, float scale, void* out, int64_t ld_out) {
+    ReduceJob& J = jobs.j[jobs.n++];
+    J = {part, static_cast<uint16_t*>(out), ld_out, scale, splits, rows, cols, blocks};
+    blocks += (int)(((int64_t)rows * cols / 8 + 255) / 256);
+  }
+  hipError_t run(hipStream_t s) {
+    FAB_TIMED("mlp_reduce", s, hipLaunchKernelGGL(reduce_parts_kernel, dim3((unsigned)blocks), dim3(256), 0, s, jobs));
+    return hipGetLastError();
+  }
+};
 
 }  // namespace
 
@@ -801,15 +853,18 @@ hipError_t launch_mlp_fwd_bf16(const MlpArgs& a, hipStream_t s) {
   uint16_t* btr = reinterpret_cast<uint16_t*>(ws + L.fwd_btr);
   uint16_t* ctf = reinterpret_cast<uint16_t*>(ws + L.fwd_ct);
   float* part = reinterpret_cast<float*>(ws + L.fwd_part);
-  hipError_t e = pack_rows(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, btr, s);
-  if (e != hipSuccess) return e;
-  e = pack_cols(a.c, a.c_sr, a.n, a.p, pw, L.n_pad, ctf, s);
+  Packer pk;
+  pk.rows(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, btr);
+  pk.cols(a.c, a.c_sr, a.n, a.p, pw, L.n_pad, ctf);
+  hipError_t e = pk.run(s);
   if (e != hipSuccess) return e;
   e = dispatch_kp(kw, pw, [&]<int K, int P>() {
     return fwd_kp<K, P, false>(a, L.split_fwd, btr, ctf, part, s);
   });
   if (e != hipSuccess) return e;
-  return reduce(part, L.split_fwd, a.m, a.p, 1.f, a.o, a.o_sr, s);
+  Reducer rd;
+  rd.add(part, L.split_fwd, a.m, a.p, 1.f, a.o, a.o_sr);
+  return rd.run(s);
 }
 
 hipError_t launch_mlp_bwd_bf16(const MlpArgs& a, hipStream_t s) {
@@ -820,19 +875,23 @@ hipError_t launch_mlp_bwd_bf16(const MlpArgs& a, hipStream_t s) {
   float* pa = reinterpret_cast<float*>(ws + L.bwd_pa);
   float* pb = reinterpret_cast<float*>(ws + L.bwd_pb);
   float* pc = reinterpret_cast<float*>(ws + L.bwd_pc);
-  hipError_t e;
-  if ((e = pack_rows(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, ws + L.bwd_btr, s)) != hipSuccess) return e;
-  if ((e = pack_rows(a.c, a.c_sr, a.n, a.p, pw, L.n_pad, ws + L.bwd_cr, s)) != hipSuccess) return e;
-  if ((e = pack_rows(a.a, a.a_sr, a.m, a.k, kw, L.m_pad, ws + L.bwd_ar, s)) != hipSuccess) return e;
-  if ((e = pack_rows(a.dout, a.o_sr, a.m, a.p, pw, L.m_pad, ws + L.bwd_dor, s)) != hipSuccess) return e;
-  if ((e = pack_cols(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, ws + L.bwd_btc, s)) != hipSuccess) return e;
-  if ((e = pack_cols(a.a, a.a_sr, a.m, a.k, kw, L.m_pad, ws + L.bwd_ac, s)) != hipSuccess) return e;
-  if ((e = pack_cols(a.dout, a.o_sr, a.m, a.p, pw, L.m_pad, ws + L.bwd_doc, s)) != hipSuccess) return e;
+  Packer pk;
+  pk.rows(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, ws + L.bwd_btr);
+  pk.rows(a.c, a.c_sr, a.n, a.p, pw, L.n_pad, ws + L.bwd_cr);
+  pk.rows(a.a, a.a_sr, a.m, a.k, kw, L.m_pad, ws + L.bwd_ar);
+  pk.rows(a.dout, a.o_sr, a.m, a.p, pw, L.m_pad, ws + L.bwd_dor);
+  pk.cols(a.bt, a.bt_sr, a.n, a.k, kw, L.n_pad, ws + L.bwd_btc);
+  pk.cols(a.a, a.a_sr, a.m, a.k, kw, L.m_pad, ws + L.bwd_ac);
+  pk.cols(a.dout, a.o_sr, a.m, a.p, pw, L.m_pad, ws + L.bwd_doc);
+  hipError_t e = pk.run(s);
+  if (e != hipSuccess) return e;
   e = dispatch_kp(kw, pw, [&]<int K, int P>() { return bwd_kp<K, P>(a, L, ws, pa, pb, pc, s); });
   if (e != hipSuccess) return e;
-  if ((e = reduce(pa, L.split_rows, a.m, a.k, a.scale, a.da, a.a_sr, s)) != hipSuccess) return e;
-  if ((e = reduce(pb, L.split_cols, a.n, a.k, a.scale, a.dbt, a.bt_sr, s)) != hipSuccess) return e;
-  return reduce(pc, L.split_dc, a.n, a.p, 1.f, a.dc, a.c_sr, s);
+  Reducer rd;
+  rd.add(pa, L.split_rows, a.m, a.k, a.scale, a.da, a.a_sr);
+  rd.add(pb, L.split_cols, a.n, a.k, a.scale, a.dbt, a.bt_sr);
+  rd.add(pc, L.split_dc, a.n, a.p, 1.f, a.dc, a.c_sr);
+  return rd.run(s);
 }
 
 }  // namespace fab
