@@ -189,10 +189,9 @@ __device__ __forceinline__ void dkdv_issue_o(const AttnArgs& a, const TileOffset
   if (wave == 1) issue_vec64(a.delta + r, q0, a.m, st + L::DLT, lane);
 }
 
-// SAME: Q and dO have equal row strides, so one set of copy offsets serves both.
 // Accumulator slot r of the S / dP tiles of query sub-block sq holds query
 // q0 + 32 sq + 16 (l / 32) + r for the lane's key k0 + l % 32.
-template <int D, bool CAUSAL, bool SAME>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attn_dkdv_bf16_kernel(AttnArgs a) {
   using C = BwdCfg<D>;
   using L = DkdvLds<D>;
@@ -708,14 +707,14 @@ hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
   const int nkb = (a.n + kAttnBwdKB - 1) / kAttnBwdKB;
   const int nqb = (a.m + kAttnBwdBM - 1) / kAttnBwdBM;
   const dim3 gk((unsigned)nkb * a.hkv * a.b), gq((unsigned)nqb * a.hq * a.b);
-  const bool same_qo = a.q_sr == a.o_sr, same_kv = a.k_sr == a.v_sr;
-#define FAB_DKDV(C, S) FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, C, S>), gk, dim3(64 * kDkdvWaves), 0, s, a))
+  const bool same_kv = a.k_sr == a.v_sr;
+#define FAB_DKDV(C) FAB_TIMED("attn_bwd_dkdv_bf16", s, hipLaunchKernelGGL((attn_dkdv_bf16_kernel<D, C>), gk, dim3(64 * kDkdvWaves), 0, s, a))
 #define FAB_DQ(C, S) FAB_TIMED("attn_bwd_dq_bf16", s, hipLaunchKernelGGL((attn_dq_bf16_kernel<D, C, QT, S>), gq, dim3(64 * kAttnDqWaves), 0, s, a))
   if (a.causal) {
-    if (same_qo) FAB_DKDV(true, true); else FAB_DKDV(true, false);
+    FAB_DKDV(true);
     if (same_kv) FAB_DQ(true, true); else FAB_DQ(true, false);
   } else {
-    if (same_qo) FAB_DKDV(false, true); else FAB_DKDV(false, false);
+    FAB_DKDV(false);
     if (same_kv) FAB_DQ(false, true); else FAB_DQ(false, false);
   }
 #undef FAB_DKDV

@@ -247,7 +247,7 @@ def kernel_bytes(w):
 # rocprofv3 names and source files of the kernels bench.py reports
 ROCPROF_NAMES = {
     "attn_fwd_bf16": ("attn_fwd_bf16_kernel<128, true>", "attn_fwd.hip"),
-    "attn_bwd_dkdv_bf16": ("attn_dkdv_bf16_kernel<128, true, true>", "attn_bwd.hip"),
+    "attn_bwd_dkdv_bf16": ("attn_dkdv_bf16_kernel<128, true>", "attn_bwd.hip"),
     "attn_bwd_dq_bf16": ("attn_dq_bf16_kernel<128, true, 1, true>", "attn_bwd.hip"),
     "attn_bwd_prep": ("attn_bwd_prep_bf16_kernel<128>", "attn_bwd.hip"),
     "mlp_fwd": ("mlp_fwd_kernel<1024, 1024>", "mlp.hip"),
