@@ -35,12 +35,22 @@ namespace {
 constexpr int kCols = 8;    // columns of a row per lane
 constexpr int kWaves = 8;   // NW
 
+// Sum over the T consecutive lanes of a row with DPP lane moves inside the
+// 16-lane DPP rows (no LDS permutes): swap neighbours, swap pairs (each quad
+// then holds its sum in every lane), then add the mirrored half-row and row,
+// which pair each quad (or 8-lane half) with the other one.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
 template <int T>
 __device__ __forceinline__ float group_sum(float v) {
-  if constexpr (T >= 2) v += __shfl_xor(v, 1, 64);
-  if constexpr (T >= 4) v += __shfl_xor(v, 2, 64);
-  if constexpr (T >= 8) v += __shfl_xor(v, 4, 64);
-  if constexpr (T >= 16) v += __shfl_xor(v, 8, 64);
+  static_assert(T == 1 || T == 2 || T == 4 || T == 8 || T == 16, "rows within one DPP row");
+  if constexpr (T >= 2) v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if constexpr (T >= 4) v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if constexpr (T >= 8) v += dpp_move<0x141>(v);  // row_half_mirror
+  if constexpr (T >= 16) v += dpp_move<0x140>(v); // row_mirror
   return v;
 }
 
@@ -156,13 +166,13 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
       mx = fmaxf(mx, s[j]);
     }
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
     float lsum = 0.f;
 #pragma unroll
     for (int i = 0; i < kCols; ++i) o[i] *= alpha;
 #pragma unroll
     for (int j = 0; j < kSlice; ++j) {
-      const float p = s[j] == -INFINITY ? 0.f : exp2f(s[j] - m_new);
+      const float p = s[j] == -INFINITY ? 0.f : fast_exp2(s[j] - m_new);
       lsum += p;
 #pragma unroll
       for (int i = 0; i < kCols; ++i) o[i] = fmaf(p, vt[j * D + i], o[i]);
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
   if (mm != -INFINITY) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float e = exp2f(pm[w * RW + r] - mm);  // 0 for a wave that saw no key
+      const float e = fast_exp2(pm[w * RW + r] - mm);  // 0 for a wave that saw no key
       ll = fmaf(pl[w * RW + r], e, ll);
       acc += e * *reinterpret_cast<const f32x4*>(po + (w * RW + r) * D + 4 * c);
     }
@@ -276,7 +286,7 @@ __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm
       dpacc = group_sum<T>(dpacc);
       const int key = kw + j;
       const bool dead = !live || key >= a.n || (CAUSAL && key > q + a.diag);
-      const float p = dead ? 0.f : exp2f(sacc * cs - lse2);
+      const float p = dead ? 0.f : fast_exp2(sacc * cs - lse2);
       const float ds = p * (dpacc - dlt);
 #pragma unroll
       for (int i = 0; i < kCols; ++i) dq[i] = fmaf(ds, kt[j * D + i], dq[i]);
@@ -376,7 +386,7 @@ __device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* 
         const int qi = qw + j;
         const bool dead = !live || qi >= a.m || (CAUSAL && key > qi + a.diag);
         const int js = wave * kSlice + j;
-        const float p = dead ? 0.f : exp2f(sacc * cs - lses[js]);
+        const float p = dead ? 0.f : fast_exp2(sacc * cs - lses[js]);
         const float ds = p * (dpacc - dls[js]);
 #pragma unroll
         for (int i = 0; i < kCols; ++i) {
