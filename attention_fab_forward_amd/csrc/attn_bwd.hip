@@ -682,8 +682,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_bf16_kernel(AttnArgs a) {
     for (int w = 0; w < 4; ++w)
       acc += bf16_lo(x[w]) * bf16_lo(y[w]) + bf16_hi(x[w]) * bf16_hi(y[w]);
   }
-#pragma unroll
-  for (int sft = 1; sft < LPR; sft <<= 1) acc += __shfl_xor(acc, sft, 64);
+  acc = lane_group_sum<LPR>(acc);
   if (orow < total && part == 0) {
     a.delta[row] = -acc;
     // a row without keys (LSE = -inf) gets +inf, so its P = exp2(S - inf) = 0

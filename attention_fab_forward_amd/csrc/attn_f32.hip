@@ -35,25 +35,6 @@ namespace {
 constexpr int kCols = 8;    // columns of a row per lane
 constexpr int kWaves = 8;   // NW
 
-// Sum over the T consecutive lanes of a row with DPP lane moves inside the
-// 16-lane DPP rows (no LDS permutes): swap neighbours, swap pairs (each quad
-// then holds its sum in every lane), then add the mirrored half-row and row,
-// which pair each quad (or 8-lane half) with the other one.
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, false));
-}
-template <int T>
-__device__ __forceinline__ float group_sum(float v) {
-  static_assert(T == 1 || T == 2 || T == 4 || T == 8 || T == 16, "rows within one DPP row");
-  if constexpr (T >= 2) v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  if constexpr (T >= 4) v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  if constexpr (T >= 8) v += dpp_move<0x141>(v);  // row_half_mirror
-  if constexpr (T >= 16) v += dpp_move<0x140>(v); // row_mirror
-  return v;
-}
-
 // Rows of a stage per wave (KS) and per workgroup (SUP).
 template <int D>
 struct F32Stage {
@@ -159,7 +140,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < kCols; ++i) acc = fmaf(qr[i], kt[j * D + i], acc);
-      acc = group_sum<T>(acc);
+      acc = lane_group_sum<T>(acc);
       const int key = kw + j;
       const bool dead = key >= a.n || (CAUSAL && key > q + a.diag);
       s[j] = dead ? -INFINITY : acc * cs;
@@ -261,7 +242,7 @@ __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm
     const float* orow = static_cast<const float*>(a.o) + ooff;
 #pragma unroll
     for (int i = 0; i < kCols; ++i) dlt = fmaf(dor[i], live ? orow[i] : 0.f, dlt);
-    dlt = group_sum<T>(dlt);
+    dlt = lane_group_sum<T>(dlt);
   }
   const float cs = a.scale_log2;
   const int kend = CAUSAL ? min(a.n, max(0, qb * RW + RW + a.diag)) : a.n;
@@ -282,8 +263,8 @@ __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm
         sacc = fmaf(qr[i], kt[j * D + i], sacc);
         dpacc = fmaf(dor[i], vt[j * D + i], dpacc);
       }
-      sacc = group_sum<T>(sacc);
-      dpacc = group_sum<T>(dpacc);
+      sacc = lane_group_sum<T>(sacc);
+      dpacc = lane_group_sum<T>(dpacc);
       const int key = kw + j;
       const bool dead = !live || key >= a.n || (CAUSAL && key > q + a.diag);
       const float p = dead ? 0.f : fast_exp2(sacc * cs - lse2);
@@ -365,7 +346,7 @@ __device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* 
         float dl = 0.f;
 #pragma unroll
         for (int i = 0; i < kCols; ++i) dl = fmaf(drow[i], ok ? orow[i] : 0.f, dl);
-        dl = group_sum<T>(dl);
+        dl = lane_group_sum<T>(dl);
         if (part == 0) dls[r] = dl;
       }
       __syncthreads();
@@ -381,8 +362,8 @@ __device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* 
           sacc = fmaf(kr[i], qt[j * D + i], sacc);
           dpacc = fmaf(vr[i], dt[j * D + i], dpacc);
         }
-        sacc = group_sum<T>(sacc);
-        dpacc = group_sum<T>(dpacc);
+        sacc = lane_group_sum<T>(sacc);
+        dpacc = lane_group_sum<T>(dpacc);
         const int qi = qw + j;
         const bool dead = !live || qi >= a.m || (CAUSAL && key > qi + a.diag);
         const int js = wave * kSlice + j;

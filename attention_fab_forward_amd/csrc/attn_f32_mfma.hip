@@ -380,8 +380,7 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_f32_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc = fmaf(x[e], y[e], acc);
   }
-#pragma unroll
-  for (int sft = 1; sft < LPR; sft <<= 1) acc += __shfl_xor(acc, sft, 64);
+  acc = lane_group_sum<LPR>(acc);
   if (orow < total && part == 0) {
     a.delta[row] = -acc;
     const float l = a.lse_in[row];

@@ -166,6 +166,29 @@ __device__ __forceinline__ void wait_copies() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Sum over aligned groups of T consecutive lanes (T a power of two up to 64),
+// returned in every lane of the group: DPP moves folded into the adds inside
+// each 16-lane DPP row (neighbour and pair swaps within quads, after which
+// each quad holds its sum in every lane, then the half-row and row mirrors,
+// which pair the quads and the 8-lane halves), a lane exchange beyond.  The
+// additions are those of an xor butterfly, so the sum is the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+template <int T>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(T >= 1 && T <= 64 && (T & (T - 1)) == 0, "a power of two up to 64 lanes");
+  if constexpr (T >= 2) v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if constexpr (T >= 4) v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if constexpr (T >= 8) v += dpp_move<0x141>(v);  // row_half_mirror
+  if constexpr (T >= 16) v += dpp_move<0x140>(v); // row_mirror
+  if constexpr (T >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (T >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 // Combine each lane's value with that of lane l ^ 32 (v_permlane32_swap:
 // afterwards one register holds x[l % 32], the other x[l % 32 + 32] in every
 // lane).
