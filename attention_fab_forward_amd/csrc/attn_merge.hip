@@ -47,11 +47,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeArgs a) {
   const float mx = fmaxf(la, lb);
   float wa = 0.f, wb = 0.f, lse = -INFINITY;
   if (mx != -INFINITY) {
-    const float ea = expf(la - mx), eb = expf(lb - mx);
+    // base-2 hardware exponential and logarithm and one reciprocal (each
+    // within a few ulp, far inside the bf16 rounding of O and the fp32 LSE
+    // bound; the library functions' range handling cost 3 % of the kernel)
+    const float ea = fast_exp2((la - mx) * kLog2e), eb = fast_exp2((lb - mx) * kLog2e);
     const float sum = ea + eb;
-    wa = ea / sum;
-    wb = eb / sum;
-    lse = mx + logf(sum);
+    const float inv = __builtin_amdgcn_rcpf(sum);
+    wa = ea * inv;
+    wb = eb * inv;
+    lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
   }
   const int64_t off = bi * a.o_sb + h * a.o_sh + i * a.o_sr + part * EPL;
   if constexpr (BF16) {
