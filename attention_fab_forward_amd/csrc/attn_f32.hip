@@ -42,17 +42,33 @@ struct F32Stage {
   static constexpr int ROWS = kWaves * SLICE;
 };
 
-// Stage rows [r0, r0 + SUP) of a [rows, D] fp32 matrix (row stride sr) into
-// LDS (packed rows of D floats); rows >= nrows are zero.
+// Stage rows [r0, r0 + SUP) of two [rows, D] fp32 matrices (row strides sx,
+// sy) into LDS as packed rows of D floats; rows >= nrows are zero.  Each
+// thread issues all its global loads before its first LDS store, so a stage
+// pays the global latency about once instead of once per 16-byte piece.
 template <int D>
-__device__ __forceinline__ void stage_f32(float* dst, const float* src, int64_t sr, int r0,
-                                          int nrows, int tid) {
+__device__ __forceinline__ void stage2_f32(float* dx, const float* x, int64_t sx, float* dy,
+                                           const float* y, int64_t sy, int r0, int nrows, int tid) {
   constexpr int V4 = D / 4, kStage = F32Stage<D>::ROWS;
-  for (int i = tid; i < kStage * V4; i += 64 * kWaves) {
+  constexpr int N = kStage * V4 / (64 * kWaves);  // pieces per thread and matrix
+  static_assert(N * 64 * kWaves == kStage * V4, "a stage splits evenly over the threads");
+  f32x4 vx[N], vy[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int i = tid + u * 64 * kWaves;
     const int r = i / V4, c = i % V4;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (r0 + r < nrows) v = *reinterpret_cast<const f32x4*>(src + (int64_t)(r0 + r) * sr + 4 * c);
-    *reinterpret_cast<f32x4*>(dst + r * D + 4 * c) = v;
+    const bool live = r0 + r < nrows;
+    vx[u] = live ? *reinterpret_cast<const f32x4*>(x + (int64_t)(r0 + r) * sx + 4 * c)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    vy[u] = live ? *reinterpret_cast<const f32x4*>(y + (int64_t)(r0 + r) * sy + 4 * c)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int i = tid + u * 64 * kWaves;
+    const int r = i / V4, c = i % V4;
+    *reinterpret_cast<f32x4*>(dx + r * D + 4 * c) = vx[u];
+    *reinterpret_cast<f32x4*>(dy + r * D + 4 * c) = vy[u];
   }
 }
 
@@ -126,8 +142,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
   const int kend = CAUSAL ? min(a.n, max(0, qb * RW + RW + a.diag)) : a.n;
   for (int k0 = 0; k0 < kend; k0 += kStage) {
     __syncthreads();
-    stage_f32<D>(ks, kbase, a.k_sr, k0, a.n, tid);
-    stage_f32<D>(vs, vbase, a.v_sr, k0, a.n, tid);
+    stage2_f32<D>(ks, kbase, a.k_sr, vs, vbase, a.v_sr, k0, a.n, tid);
     __syncthreads();
     const int kw = k0 + wave * kSlice;
     if (kw >= kend) continue;  // wave-uniform
@@ -248,8 +263,7 @@ __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm
   const int kend = CAUSAL ? min(a.n, max(0, qb * RW + RW + a.diag)) : a.n;
   for (int k0 = 0; k0 < kend; k0 += kStage) {
     __syncthreads();
-    stage_f32<D>(ks, kbase, a.k_sr, k0, a.n, tid);
-    stage_f32<D>(vs, vbase, a.v_sr, k0, a.n, tid);
+    stage2_f32<D>(ks, kbase, a.k_sr, vs, vbase, a.v_sr, k0, a.n, tid);
     __syncthreads();
     const int kw = k0 + wave * kSlice;
     if (kw >= kend) continue;  // wave-uniform
@@ -327,8 +341,7 @@ __device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* 
     const int64_t rbase = ((int64_t)bi * a.hq + h) * a.m;
     for (int q0 = qstart; q0 < a.m; q0 += kStage) {
       __syncthreads();
-      stage_f32<D>(qs, qbase, a.q_sr, q0, a.m, tid);
-      stage_f32<D>(dos, dobase, a.o_sr, q0, a.m, tid);
+      stage2_f32<D>(qs, qbase, a.q_sr, dos, dobase, a.o_sr, q0, a.m, tid);
       if (tid < kStage) {
         const bool ok = q0 + tid < a.m;
         lses[tid] = ok ? a.lse_in[rbase + q0 + tid] * kLog2e : 0.f;
