@@ -24,7 +24,7 @@ namespace fab {
 namespace {
 
 // Lane layout: T = D / kCols lanes share one row (query, or key in the dK/dV
-// kernel), each owning kCols of its D columns; a wave holds RW = 64 / T rows and
+// kernel), each owning kCols (= KC) of its D columns; a wave holds RW = 64 / T rows and
 // a workgroup is one wave-width of rows served by NW waves.  The loop over the
 // other side (keys, or queries) runs in stages of SUP = NW * KS rows staged
 // in LDS by the whole workgroup (KS = 32 at d = 64, 16 at d = 128: a stage
@@ -32,7 +32,10 @@ namespace {
 // stage, so the serial work per lane is 1 / NW of the loop.  The waves'
 // partial results are combined through LDS at the end (softmax states merged
 // by their maxima, gradients summed).
-constexpr int kCols = 8;    // columns of a row per lane
+// KC, the columns of a row per lane, is 8, or 4 at d = 64 for launches that
+// would otherwise leave CUs idle (twice the workgroups, each with half the
+// rows; 16 lanes a row either way: 32 would need an exchange across DPP rows).
+constexpr int kCUs = 256;
 constexpr int kWaves = 8;   // NW
 
 // Rows of a stage per wave (KS) and per workgroup (SUP).
@@ -74,9 +77,9 @@ __device__ __forceinline__ void stage2_f32(float* dx, const float* x, int64_t sx
 
 // LDS floats: a stage of two [kStage, D] matrices (+ two kStage vectors), or
 // the cross-wave combination area (NW x RW x D partial rows + 2 NW RW scalars).
-template <int D>
+template <int D, int KC>
 struct F32Lds {
-  static constexpr int T = D / kCols;
+  static constexpr int T = D / KC;
   static constexpr int RW = 64 / T;
   static constexpr int CHUNKS = RW * D / 4;  // float4 chunks of an RW x D block
   static constexpr int STAGE = 2 * F32Stage<D>::ROWS * D + 2 * F32Stage<D>::ROWS;
@@ -86,9 +89,9 @@ struct F32Lds {
 
 // Sum of the NW waves' partial rows part[w][r][:] (r < RW) for float4 chunk
 // `tid` (< CHUNKS) of the RW x D block: returns the chunk, row r = tid / (D / 4).
-template <int D>
+template <int D, int KC>
 __device__ __forceinline__ f32x4 sum_parts(const float* part, int tid) {
-  constexpr int RW = F32Lds<D>::RW;
+  constexpr int RW = F32Lds<D, KC>::RW;
   const int r = tid / (D / 4), c = tid % (D / 4);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -96,24 +99,26 @@ __device__ __forceinline__ f32x4 sum_parts(const float* part, int tid) {
   return acc;
 }
 
-// Writes this lane's kCols partial columns of row `row` (0..RW-1) for wave w.
+// Writes this lane's NC partial columns of row `row` (0..RW-1) for wave w.
+template <int NC>
 __device__ __forceinline__ void put_part(float* part, int D, int RW, int w, int row, int col0,
-                                         const float (&x)[kCols]) {
+                                         const float (&x)[NC]) {
   float* dst = part + (w * RW + row) * D + col0;
 #pragma unroll
-  for (int i = 0; i < kCols; i += 4)
+  for (int i = 0; i < NC; i += 4)
     *reinterpret_cast<f32x4*>(dst + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
 }
 
 // ---------------------------------------------------------------------------
 // forward: workgroup = RW queries of one head, keys split over the waves
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, int KC, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
-  constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  constexpr int kCols = KC;
+  constexpr int T = F32Lds<D, KC>::T, RW = F32Lds<D, KC>::RW;
   constexpr int kSlice = F32Stage<D>::SLICE, kStage = F32Stage<D>::ROWS;
-  static_assert(F32Lds<D>::CHUNKS <= 64 * kWaves, "one float4 of the output block per thread");
-  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
+  static_assert(F32Lds<D, KC>::CHUNKS <= 64 * kWaves, "one float4 of the output block per thread");
+  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D, KC>::FLOATS];
   float* ks = sm;
   float* vs = sm + kStage * D;
   const int tid = threadIdx.x;
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
   // O = sum_w o_w 2^(m_w - M) / L
   __syncthreads();
   float* po = sm;
-  float* pm = sm + F32Lds<D>::PART;
+  float* pm = sm + F32Lds<D, KC>::PART;
   float* pl = pm + kWaves * RW;
   put_part(po, D, RW, wave, lane / T, part * kCols, o);
   if (part == 0) {
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
   __syncthreads();
   const int r = tid / (D / 4), c = tid % (D / 4);
   const int qo = qb * RW + r;
-  if (tid >= F32Lds<D>::CHUNKS || qo >= a.m) return;
+  if (tid >= F32Lds<D, KC>::CHUNKS || qo >= a.m) return;
   float mm = -INFINITY;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, pm[w * RW + r]);
@@ -218,9 +223,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_fwd_f32_kernel(AttnArgs a) {
 // are independent), so the two run side by side.
 // dQ: workgroup = RW queries of one head, keys split over the waves
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, int KC, bool CAUSAL>
 __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm) {
-  constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  constexpr int kCols = KC;
+  constexpr int T = F32Lds<D, KC>::T, RW = F32Lds<D, KC>::RW;
   constexpr int kSlice = F32Stage<D>::SLICE, kStage = F32Stage<D>::ROWS;
   float* ks = sm;
   float* vs = sm + kStage * D;
@@ -292,8 +298,8 @@ __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm
   __syncthreads();
   const int r = tid / (D / 4), c = tid % (D / 4);
   const int qo = qb * RW + r;
-  if (tid >= F32Lds<D>::CHUNKS || qo >= a.m) return;
-  const f32x4 x = sum_parts<D>(sm, tid) * a.scale;
+  if (tid >= F32Lds<D, KC>::CHUNKS || qo >= a.m) return;
+  const f32x4 x = sum_parts<D, KC>(sm, tid) * a.scale;
   *reinterpret_cast<f32x4*>(static_cast<float*>(a.dq) + bi * a.q_sb + h * a.q_sh +
                             (int64_t)qo * a.q_sr + 4 * c) = x;
 }
@@ -302,9 +308,10 @@ __device__ __forceinline__ void dq_f32_body(const AttnArgs& a, int id, float* sm
 // dK, dV: workgroup = RW keys of one kv head; the group's query heads and rows
 // split over the waves
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, int KC, bool CAUSAL>
 __device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* sm) {
-  constexpr int T = F32Lds<D>::T, RW = F32Lds<D>::RW;
+  constexpr int kCols = KC;
+  constexpr int T = F32Lds<D, KC>::T, RW = F32Lds<D, KC>::RW;
   constexpr int kSlice = F32Stage<D>::SLICE, kStage = F32Stage<D>::ROWS;
   float* qs = sm;
   float* dos = sm + kStage * D;
@@ -392,12 +399,12 @@ __device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* 
   }
   const int r = tid / (D / 4), c = tid % (D / 4);
   const int ko = kblk * RW + r;
-  const bool out_ok = tid < F32Lds<D>::CHUNKS && ko < a.n;
+  const bool out_ok = tid < F32Lds<D, KC>::CHUNKS && ko < a.n;
   __syncthreads();
   put_part(sm, D, RW, wave, lane / T, part * kCols, dk);
   __syncthreads();
   if (out_ok) {
-    const f32x4 x = sum_parts<D>(sm, tid) * a.scale;
+    const f32x4 x = sum_parts<D, KC>(sm, tid) * a.scale;
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.dk) + bi * a.k_sb + g * a.k_sh +
                               (int64_t)ko * a.k_sr + 4 * c) = x;
   }
@@ -405,44 +412,65 @@ __device__ __forceinline__ void dkdv_f32_body(const AttnArgs& a, int id, float* 
   put_part(sm, D, RW, wave, lane / T, part * kCols, dv);
   __syncthreads();
   if (out_ok) {
-    const f32x4 y = sum_parts<D>(sm, tid);
+    const f32x4 y = sum_parts<D, KC>(sm, tid);
     *reinterpret_cast<f32x4*>(static_cast<float*>(a.dv) + bi * a.v_sb + g * a.v_sh +
                               (int64_t)ko * a.v_sr + 4 * c) = y;
   }
 }
 
-template <int D>
-hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
-  constexpr int RW = F32Lds<D>::RW;
+template <int D, int KC>
+hipError_t fwd_dk(const AttnArgs& a, hipStream_t s) {
+  constexpr int RW = F32Lds<D, KC>::RW;
   const dim3 grid((unsigned)((a.m + RW - 1) / RW) * a.hq * a.b), block(64 * kWaves);
   if (a.causal)
-    FAB_TIMED("attn_fwd_f32", s, hipLaunchKernelGGL((attn_fwd_f32_kernel<D, true>), grid, block, 0, s, a));
+    FAB_TIMED("attn_fwd_f32", s, hipLaunchKernelGGL((attn_fwd_f32_kernel<D, KC, true>), grid, block, 0, s, a));
   else
-    FAB_TIMED("attn_fwd_f32", s, hipLaunchKernelGGL((attn_fwd_f32_kernel<D, false>), grid, block, 0, s, a));
+    FAB_TIMED("attn_fwd_f32", s, hipLaunchKernelGGL((attn_fwd_f32_kernel<D, KC, false>), grid, block, 0, s, a));
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kWaves) void attn_bwd_f32_kernel(AttnArgs a, int nq) {
-  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D>::FLOATS];
-  if ((int)blockIdx.x < nq)
-    dq_f32_body<D, CAUSAL>(a, (int)blockIdx.x, sm);
-  else
-    dkdv_f32_body<D, CAUSAL>(a, (int)blockIdx.x - nq, sm);
+template <int D>
+hipError_t fwd_d(const AttnArgs& a, hipStream_t s) {
+  constexpr int RW8 = F32Lds<D, 8>::RW;
+  const int64_t wgs = (a.m + RW8 - 1) / RW8 * (int64_t)a.hq * a.b;
+  if constexpr (D == 64) {
+    if (wgs < kCUs) return fwd_dk<D, 4>(a, s);
+  }
+  return fwd_dk<D, 8>(a, s);
 }
 
-template <int D>
-hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
-  constexpr int RW = F32Lds<D>::RW;
+template <int D, int KC, bool CAUSAL>
+__global__ __launch_bounds__(64 * kWaves) void attn_bwd_f32_kernel(AttnArgs a, int nq) {
+  __shared__ __attribute__((aligned(16))) float sm[F32Lds<D, KC>::FLOATS];
+  if ((int)blockIdx.x < nq)
+    dq_f32_body<D, KC, CAUSAL>(a, (int)blockIdx.x, sm);
+  else
+    dkdv_f32_body<D, KC, CAUSAL>(a, (int)blockIdx.x - nq, sm);
+}
+
+template <int D, int KC>
+hipError_t bwd_dk(const AttnArgs& a, hipStream_t s) {
+  constexpr int RW = F32Lds<D, KC>::RW;
   const dim3 block(64 * kWaves);
   const int nq = (a.m + RW - 1) / RW * a.hq * a.b;
   const int nk = (a.n + RW - 1) / RW * a.hkv * a.b;
   const dim3 grid((unsigned)(nq + nk));
   if (a.causal)
-    FAB_TIMED("attn_bwd_f32", s, hipLaunchKernelGGL((attn_bwd_f32_kernel<D, true>), grid, block, 0, s, a, nq));
+    FAB_TIMED("attn_bwd_f32", s, hipLaunchKernelGGL((attn_bwd_f32_kernel<D, KC, true>), grid, block, 0, s, a, nq));
   else
-    FAB_TIMED("attn_bwd_f32", s, hipLaunchKernelGGL((attn_bwd_f32_kernel<D, false>), grid, block, 0, s, a, nq));
+    FAB_TIMED("attn_bwd_f32", s, hipLaunchKernelGGL((attn_bwd_f32_kernel<D, KC, false>), grid, block, 0, s, a, nq));
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t bwd_d(const AttnArgs& a, hipStream_t s) {
+  constexpr int RW8 = F32Lds<D, 8>::RW;
+  const int64_t wgs = (a.m + RW8 - 1) / RW8 * (int64_t)a.hq * a.b +
+                      (a.n + RW8 - 1) / RW8 * (int64_t)a.hkv * a.b;
+  if constexpr (D == 64) {
+    if (wgs < kCUs) return bwd_dk<D, 4>(a, s);
+  }
+  return bwd_dk<D, 8>(a, s);
 }
 
 }  // namespace
