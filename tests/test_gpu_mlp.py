@@ -123,3 +123,19 @@ def test_random_shape(i, m, n, k, p, sigma, scale):
          "c": random_array(2002 + 4 * i, (n, p), sigma, "bf16"),
          "do": random_array(2003 + 4 * i, (m, p), 1.0, "bf16")}
     check(x, scale)
+
+
+def test_forward_and_backward_are_deterministic():
+    """The split partial sums are added by a fixed-order reduction (no
+    atomics): two calls on the same inputs give bitwise-identical O, dA, dBt
+    and dC at the full size."""
+    import attention_fab_forward_amd as fab
+    import torch
+    x = mlp_inputs(WORKLOADS["mlp_gelu_m4096_k1024_n4096_p1024"])
+    a, bt, c, do = (to_device(x[n], "bf16") for n in ("a", "bt", "c", "do"))
+    outs = []
+    for _ in range(2):
+        o, _lse = fab.forward(a, bt, c, "gelu", False, 1.0)
+        outs.append((o,) + tuple(fab.backward(a, bt, c, None, None, do, "gelu", False, 1.0)))
+    for name, u, w in zip(("O", "dA", "dBt", "dC"), outs[0], outs[1]):
+        assert torch.equal(u, w), name
