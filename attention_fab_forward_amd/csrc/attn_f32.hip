@@ -103,6 +103,7 @@ __device__ __forceinline__ f32x4 sum_parts(const float* part, int tid) {
 template <int NC>
 __device__ __forceinline__ void put_part(float* part, int D, int RW, int w, int row, int col0,
                                          const float (&x)[NC]) {
+  static_assert(NC % 4 == 0, "columns are written as whole float4 chunks");
   float* dst = part + (w * RW + row) * D + col0;
 #pragma unroll
   for (int i = 0; i < NC; i += 4)

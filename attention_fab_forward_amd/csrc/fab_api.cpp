@@ -52,13 +52,22 @@ struct KernelTimer {
   void begin(const char* name, hipStream_t s) {
     pending = name;
     pending_start = get();
-    if (pending_start) hipEventRecord(pending_start, s);
+    if (pending_start && hipEventRecord(pending_start, s) != hipSuccess) {
+      failed = true;
+      free_events.push_back(pending_start);
+      pending_start = nullptr;
+    }
   }
   void end(hipStream_t s) {
-    hipEvent_t stop = get();
-    if (stop && pending_start) {
-      hipEventRecord(stop, s);
-      recs.push_back({pending, pending_start, stop});
+    if (pending_start) {
+      hipEvent_t stop = get();
+      if (stop && hipEventRecord(stop, s) == hipSuccess) {
+        recs.push_back({pending, pending_start, stop});
+      } else {
+        failed = true;
+        free_events.push_back(pending_start);
+        if (stop) free_events.push_back(stop);
+      }
     }
     pending = nullptr;
     pending_start = nullptr;
@@ -81,11 +90,11 @@ struct KernelTimer {
   }
   ~KernelTimer() {
     for (Rec& r : recs) {
-      hipEventSynchronize(r.stop);
+      (void)hipEventSynchronize(r.stop);
       free_events.push_back(r.start);
       free_events.push_back(r.stop);
     }
-    for (hipEvent_t e : free_events) hipEventDestroy(e);
+    for (hipEvent_t e : free_events) (void)hipEventDestroy(e);
   }
 };
 
