@@ -27,9 +27,14 @@
 //    wave group issuing one tile during its softmax phase; each LDS row is
 //    16-byte-chunk XOR-swizzled so the MFMA operand reads are free of bank
 //    conflicts, the swizzle being applied on the global address side.
-//  * The running maximum is only moved when a block's maximum exceeds it by
-//    more than 2^8 (probabilities then stay below 256, well inside bf16), so
-//    the accumulator rescale is rare.
+//  * A block's exponentials are taken against the running reference m (a row
+//    maximum of earlier blocks) without forming the block's own row maximum.
+//    Only a block that would carry some row's probabilities past a sum of
+//    2^32, or a row with no reference yet, takes its row maximum; the
+//    reference then moves when that maximum exceeds it by more than 2^8 (one
+//    accumulator rescale).  fp32 and bf16 keep their relative precision at
+//    any scale, and per row O and l stay below (keys / 64) 2^32 max|V|, far
+//    inside fp32's range, so the result is that of the plain definition.
 //  * Causal blocks are dispatched longest-first; blocks above the diagonal
 //    are never loaded; a wave skips key blocks fully masked for it.
 #include "fab_device.h"
@@ -213,9 +218,9 @@ attn_fwd_bf16_kernel(AttnArgs a) {
         [&](int i, const u32x4& x) { s[i % 2] = mfma32(x, qf[i / 2], s[i % 2]); });
   };
 
-  // Online softmax of block j on the VALU: mask, row maximum, P_j (bf16,
-  // packed as the next MFMA's B operand), row sum, O rescale when the running
-  // maximum moves.
+  // Online softmax of block j on the VALU: mask, P_j (bf16, packed as the
+  // next MFMA's B operand) and its row sum; the row maximum and the O rescale
+  // only when the reference has to move.
   f32x16 s[2];
   u32x4 pb[2][2];
   auto softmax = [&](int j) {
@@ -229,41 +234,55 @@ attn_fwd_bf16_kernel(AttnArgs a) {
           if ((CAUSAL && key > myq + a.diag) || key >= a.n) s[sb][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // P_j against the running reference m (a row maximum of earlier blocks,
+    // in log2 units): only a block whose probabilities for some row would sum
+    // to 2^32 or more, or a row with no reference yet (its first keys: the
+    // exponent is then +inf or NaN), takes the row maximum of S_j and may move
+    // the reference.  fp32 and bf16 keep their relative precision at any
+    // scale, so how far p sits above 1 changes no result.
+    auto exponentials = [&](float ref) {
+      float sum = 0.f;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int sb = 0; sb < 2; ++sb) {
+        float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-    mx = pair_max(mx) * cs;
-    // move the reference maximum only when p would otherwise exceed 2^8
-    const float m_new = mx > m_run + 8.f ? mx : m_run;
-    // a row that has seen no key yet (offset causal masks) keeps m = -inf and
-    // takes 0 as the exponent reference: its probabilities are exactly 0
-    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_ref);
-    const bool rescale = m_new != m_run;
-    float lsum = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(fmaf(s[sb][r], cs, -ref));
+          sum += p[r];
+        }
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      float p[16];
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = fast_exp2(fmaf(s[sb][r], cs, -m_ref));
-        lsum += p[r];
+          for (int w = 0; w < 4; ++w) pb[sb][c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
       }
+      return sum;
+    };
+    float lsum = exponentials(m_run);
+    if (__ballot(!(lsum < 0x1p32f))) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) pb[sb][c][w] = pack_bf16(p[8 * c + 2 * w], p[8 * c + 2 * w + 1]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      mx = pair_max(mx) * cs;
+      // move the reference maximum only when p would otherwise exceed 2^8
+      const float m_new = mx > m_run + 8.f ? mx : m_run;
+      // a row that has seen no key yet (offset causal masks) keeps m = -inf and
+      // takes 0 as the exponent reference: its probabilities are exactly 0
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_ref);
+      const bool rescale = m_new != m_run;
+      lsum = exponentials(m_ref);
+      l_run *= alpha;
+      m_run = m_new;
+      if (__ballot(rescale)) {
+#pragma unroll
+        for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+      }
     }
-    l_run = l_run * alpha + lsum;
-    m_run = m_new;
-    if (__ballot(rescale)) {
-#pragma unroll
-      for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
-    }
+    l_run += lsum;
   };
   // O^T += V_j^T P_j^T.  Operand i: output tile t = i % DT, keys
   // 32 sb + 16 lg + 8 c + e with (sb, c) = (i / DT / 2, i / DT % 2), read as
