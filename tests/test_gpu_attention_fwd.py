@@ -94,6 +94,28 @@ def test_large_scores_stay_finite():
     check_fwd({"q": q, "k": k, "v": v}, "bf16", True, 0.0883883461356163)
 
 
+@pytest.mark.parametrize("growth", [12.0, 40.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_rising_along_the_keys(growth, causal):
+    """Every row's scores rise steadily along the keys, by `growth` (in log2
+    units) per 64-key block, up to a few hundred: each block's exponentials
+    are taken against a reference that trails the row maximum, so in-block
+    probabilities reach about 2^growth before the reference catches up (at
+    12 it mostly stays put; at 40 a block's sum passes 2^32 and the reference
+    moves at nearly every block).  O and the LSE still match the plain
+    definition."""
+    from attention_fab_forward_amd.inputs import round_to_bf16
+    b, n, h, d = 1, 1024, 2, 128
+    scale = float(np.float32(d ** -0.5))
+    # score of key j in log2 units: 0.5 d c_j scale log2(e)
+    per_key = growth / 64 / (0.5 * d * scale * 1.4426950408889634)
+    c = round_to_bf16((np.arange(n) * per_key).astype(np.float32))
+    q = np.full((b, n, h, d), 0.5, np.float32)
+    k = np.ascontiguousarray(np.broadcast_to(c[None, :, None, None], (b, n, h, d)), np.float32)
+    v = random_array(121, (b, n, h, d), 1.0, "bf16")
+    check_fwd({"q": q, "k": k, "v": v}, "bf16", causal, scale)
+
+
 def test_forward_is_deterministic():
     import attention_fab_forward_amd as fab
     x = attention_inputs(WORKLOADS["attn_causal_bf16_h32_n32768_d128"], seq=2048,
