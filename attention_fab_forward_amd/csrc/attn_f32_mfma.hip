@@ -284,30 +284,44 @@ __global__ __launch_bounds__(64 * kMfmaF32Waves, f32_mfma_occupancy<D>()) void a
           if ((CAUSAL && key > myq + a.diag) || key >= a.n) s[r] = -INFINITY;
         }
       }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = pair_max(mx) * cs;
-      // the reference maximum moves only when a probability would exceed 2^8
-      const float m_new = mx > m_run + 8.f ? mx : m_run;
-      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_ref);
-      const bool rescale = m_new != m_run;
-      float lsum = 0.f;
+      // exponentials against the running reference m (a row maximum of
+      // earlier blocks); only a block whose probabilities for some row would
+      // sum to 2^32 or more, or a row with no reference yet (the exponent is
+      // then +inf or NaN), takes the row maximum and may move m.  fp32 keeps
+      // its relative precision at any scale, so the result is unchanged.
+      float p[16], lsum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[r] = fast_exp2(fmaf(s[r], cs, -m_ref));
-        lsum += s[r];
+        p[r] = fast_exp2(fmaf(s[r], cs, -m_run));
+        lsum += p[r];
       }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-      if (__ballot(rescale)) {
+      if (__ballot(!(lsum < 0x1p32f))) {
+        float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < T::DT; ++t)
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = pair_max(mx) * cs;
+        // the reference moves only when a probability would exceed 2^8
+        const float m_new = mx > m_run + 8.f ? mx : m_run;
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_ref);
+        const bool rescale = m_new != m_run;
+        lsum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(fmaf(s[r], cs, -m_ref));
+          lsum += p[r];
+        }
+        l_run *= alpha;
+        m_run = m_new;
+        if (__ballot(rescale)) {
+#pragma unroll
+          for (int t = 0; t < T::DT; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+        }
       }
-      col_product<D, 4>(vtile(it), lq, h, s, o);
+      l_run += lsum;
+      col_product<D, 4>(vtile(it), lq, h, p, o);
     }
     wait_vmem();
     lds_barrier();
