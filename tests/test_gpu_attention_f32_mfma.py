@@ -98,3 +98,33 @@ def test_forced_fma_family_still_runs_large():
     would choose the matrix cores."""
     run_check(inputs(3600, 1, 1024, 1024, 8, 4, 64), False, 0.125, variant=B.VARIANT_F32_FMA,
               expect_mfma=False)
+
+
+
+
+@pytest.mark.parametrize("a", [1.0, 4.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_rising_along_the_keys(a, causal):
+    """The matrix-core forward on scores that rise along the keys up to 0 at
+    each row's last visible key: raw score a (j - i) causal, a (j - n + 1)
+    otherwise, from two nonzero columns holding small integers times a power
+    of two, so every product and sum is exact in fp32.  With scale 1/sqrt(128)
+    that is about 8 (a = 1) or 33 (a = 4) log2 units per 64 keys: the
+    exponentials run against a reference that trails the row maximum, and the
+    LSE stays small.  O and the LSE meet the fp32 bound."""
+    import attention_fab_forward_amd as fab
+    b, n, h, d = 1, 1024, 2, 128
+    scale = float(np.float32(d ** -0.5))
+    rows = np.arange(n, dtype=np.float32) if causal else np.full(n, n - 1.0, np.float32)
+    q = np.zeros((b, n, h, d), np.float32)
+    k = np.zeros((b, n, h, d), np.float32)
+    q[..., 0] = a
+    q[..., 1] = (-a * rows)[None, :, None]
+    k[..., 0] = np.arange(n, dtype=np.float32)[None, :, None]
+    k[..., 1] = 1.0
+    x = {"q": q, "k": k, "v": random_array(131, (b, n, h, d))}
+    qt, kt, vt = (to_device(x[t], "f32") for t in ("q", "k", "v"))
+    o, lse = fab.forward(qt, kt, vt, "softmax", causal, scale, variant=MFMA)
+    ro, rl = attention_forward(x["q"], x["k"], x["v"], scale, causal)
+    assert_close("O", to_host(o), ro, "f32")
+    assert_lse(lse.cpu().numpy().astype(np.float64), rl, "f32")
